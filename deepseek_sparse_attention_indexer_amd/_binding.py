@@ -1,0 +1,257 @@
+"""ctypes marshalling for libdsa.so (argument conversion only; no compute here)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libdsa.so")
+
+
+if not os.path.exists(lib_path()):
+    raise ImportError(
+        f"{lib_path()} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+        "or python -m deepseek_sparse_attention_indexer_amd.build)")
+
+_lib = C.CDLL(lib_path())
+
+DSA_OK, DSA_ERR_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
+ENTRY_TOPK, ENTRY_MLA_DECODE, ENTRY_MLA_PREFILL, ENTRY_DECODE = 1, 2, 3, 4
+KEY_BF16, KEY_FP8 = 0, 1
+KV_BF16, KV_FP8_UNIFORM, KV_FP8_DS_MLA = 0, 1, 2
+
+
+class _Paging(C.Structure):
+    _fields_ = [("page_size", C.c_int32), ("_pad0", C.c_int32), ("block_table", C.c_void_p),
+                ("bt_stride", C.c_int64), ("req_base", C.c_void_p)]
+
+
+class _KeyCache(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("_pad0", C.c_int32), ("data", C.c_void_p),
+                ("scale", C.c_void_p), ("n_slots", C.c_int64), ("paging", _Paging)]
+
+
+class _KVCache(C.Structure):
+    _fields_ = [("format", C.c_int32), ("d_nope", C.c_int32), ("d_rope", C.c_int32),
+                ("_pad0", C.c_int32), ("data", C.c_void_p), ("scales", C.c_void_p),
+                ("n_slots", C.c_int64), ("paging", _Paging)]
+
+
+class _Rows(C.Structure):
+    _fields_ = [("T", C.c_int32), ("n_req", C.c_int32), ("row_req", C.c_void_p),
+                ("row_len", C.c_void_p), ("n_max", C.c_int32), ("_pad0", C.c_int32)]
+
+
+class _Problem(C.Structure):
+    _fields_ = [("T", C.c_int32), ("n_max", C.c_int32), ("topk", C.c_int32), ("H", C.c_int32),
+                ("n_idx", C.c_int32), ("_pad0", C.c_int32)]
+
+
+_P = C.c_void_p
+_I64 = C.c_int64
+_I32 = C.c_int32
+_F = C.c_float
+_SZ = C.c_size_t
+
+_sigs = {
+    "dsa_index_scores": [_P, _I64, _P, _I64, C.POINTER(_KeyCache), C.POINTER(_Rows), _I32, _I32, _F,
+                         _P, _I64, _P],
+    "dsa_topk": [_P, _I64, C.POINTER(_Rows), _I32, _P, _I64, _P, _P, _SZ, _P],
+    "dsa_sparse_mla_decode": [_P, _I64, C.POINTER(_KVCache), _P, _I64, _I32, C.POINTER(_KVCache), _P,
+                              _I64, _I32, _I32, _I32, _I32, _I32, _F, _P, _I64, _P, _P, _SZ, _P],
+    "dsa_sparse_mla_prefill": [_P, _I64, C.POINTER(_KVCache), _P, _I64, _I32, C.POINTER(_KVCache), _P,
+                               _I64, _I32, C.POINTER(_Rows), _I32, _I32, _I32, _F, _P, _I64, _P, _P,
+                               _SZ, _P],
+    "dsa_decode": [_P, _I64, _P, _I64, _P, _I64, C.POINTER(_KeyCache), C.POINTER(_KVCache),
+                   C.POINTER(_Rows), _I32, _I32, _I32, _I32, _I32, _I32, _F, _F, _P, _I64, _P, _P,
+                   _I64, _P, _P, _SZ, _P],
+    "dsa_workspace_init": [_P, _SZ, _P],
+}
+for _name, _args in _sigs.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = C.c_int32
+_lib.dsa_workspace_size.argtypes = [_I32, C.POINTER(_Problem)]
+_lib.dsa_workspace_size.restype = _SZ
+_lib.dsa_status_string.argtypes = [_I32]
+_lib.dsa_status_string.restype = C.c_char_p
+_lib.dsa_abi_version.argtypes = []
+_lib.dsa_abi_version.restype = _I32
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {dsa_status_string(status)} (status {status})")
+
+
+def dsa_status_string(status: int) -> str:
+    return _lib.dsa_status_string(int(status)).decode()
+
+
+def dsa_abi_version() -> int:
+    return int(_lib.dsa_abi_version())
+
+
+def _check(status: int, where: str):
+    if status != DSA_OK:
+        raise DSAError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: Optional[torch.Tensor], name: str):
+    if t is not None and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _paging(page_size, block_table, req_base) -> _Paging:
+    _dev(block_table, "block_table")
+    _dev(req_base, "req_base")
+    stride = int(block_table.stride(0)) if block_table is not None else 0
+    return _Paging(int(page_size), 0, _ptr(block_table), stride, _ptr(req_base))
+
+
+class KeyCache:
+    """Indexer key cache: data [slots, di] (bf16 or uint8 fp8 bytes), fp8 scale [slots] fp32."""
+
+    def __init__(self, data: torch.Tensor, scale: Optional[torch.Tensor] = None, page_size: int = 1,
+                 block_table: Optional[torch.Tensor] = None, req_base: Optional[torch.Tensor] = None):
+        _dev(data, "data")
+        _dev(scale, "scale")
+        self.keep = (data, scale, block_table, req_base)
+        self.dtype = KEY_FP8 if data.dtype == torch.uint8 else KEY_BF16
+        self.c = _KeyCache(self.dtype, 0, _ptr(data), _ptr(scale), int(data.shape[0]),
+                           _paging(page_size, block_table, req_base))
+
+
+class KVCache:
+    """Latent cache. fmt 'bf16': data [slots, D] bf16; 'fp8_uniform': uint8 [slots, D] + scales
+    [slots, D/64] fp32; 'fp8_ds_mla': uint8 [pages, page_size * 584]."""
+
+    def __init__(self, fmt: str, data: torch.Tensor, d_nope: int, d_rope: int, page_size: int = 1,
+                 block_table: Optional[torch.Tensor] = None, req_base: Optional[torch.Tensor] = None,
+                 scales: Optional[torch.Tensor] = None):
+        _dev(data, "data")
+        _dev(scales, "scales")
+        self.keep = (data, scales, block_table, req_base)
+        f = {"bf16": KV_BF16, "fp8_uniform": KV_FP8_UNIFORM, "fp8_ds_mla": KV_FP8_DS_MLA}[fmt]
+        n_slots = int(data.shape[0]) * (page_size if fmt == "fp8_ds_mla" else 1)
+        self.c = _KVCache(f, int(d_nope), int(d_rope), 0, _ptr(data), _ptr(scales), n_slots,
+                          _paging(page_size, block_table, req_base))
+
+
+class Rows:
+    """Query rows: row_len [T] int32 (device), optional row_req [T] int32, n_req, n_max (host)."""
+
+    def __init__(self, row_len: torch.Tensor, n_req: int, n_max: int,
+                 row_req: Optional[torch.Tensor] = None):
+        _dev(row_len, "row_len")
+        _dev(row_req, "row_req")
+        self.keep = (row_len, row_req)
+        self.T = int(row_len.shape[0])
+        self.c = _Rows(self.T, int(n_req), _ptr(row_req), _ptr(row_len), int(n_max), 0)
+
+
+def dsa_workspace_size(entry: int, T: int = 0, n_max: int = 0, topk: int = 0, H: int = 0,
+                       n_idx: int = 0) -> int:
+    p = _Problem(int(T), int(n_max), int(topk), int(H), int(n_idx), 0)
+    n = int(_lib.dsa_workspace_size(int(entry), C.byref(p)))
+    if n == (1 << 64) - 1:
+        raise DSAError(DSA_ERR_ARG, "dsa_workspace_size")
+    return n
+
+
+def dsa_workspace_init(ws: torch.Tensor, stream=None):
+    _check(_lib.dsa_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "dsa_workspace_init")
+
+
+class Workspace:
+    """A device byte buffer initialised for the library (grown on demand)."""
+
+    def __init__(self, nbytes: int = 0, device="cuda"):
+        self.device = device
+        self.buf = None
+        self.ensure(nbytes)
+
+    def ensure(self, nbytes: int):
+        nbytes = max(int(nbytes), 1 << 23)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            dsa_workspace_init(self.buf)
+        return self
+
+    @property
+    def ptr(self):
+        return _ptr(self.buf)
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+
+def dsa_index_scores(q_idx, w, keys: KeyCache, rows: Rows, Hi: int, di: int, index_scale: float,
+                     logits, stream=None):
+    _check(_lib.dsa_index_scores(_ptr(q_idx), int(q_idx.stride(0)), _ptr(w), int(w.stride(0)),
+                                 C.byref(keys.c), C.byref(rows.c), int(Hi), int(di),
+                                 float(index_scale), _ptr(logits), int(logits.stride(0)),
+                                 _stream(stream)), "dsa_index_scores")
+
+
+def dsa_topk(logits, rows: Rows, topk: int, indices, lens, ws: Optional[Workspace], stream=None):
+    _check(_lib.dsa_topk(_ptr(logits), int(logits.stride(0)), C.byref(rows.c), int(topk),
+                         _ptr(indices), int(indices.stride(0)), _ptr(lens),
+                         ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)),
+           "dsa_topk")
+
+
+def dsa_sparse_mla_decode(q, kv: KVCache, idx, extra_kv: Optional[KVCache], extra_idx, B: int,
+                          H: int, d_qk: int, d_v: int, softmax_scale: float, out, lse,
+                          ws: Optional[Workspace], stream=None):
+    n_idx = int(idx.shape[1]) if idx is not None else 0
+    n_extra = int(extra_idx.shape[1]) if extra_idx is not None else 0
+    _check(_lib.dsa_sparse_mla_decode(
+        _ptr(q), int(q.stride(0)), C.byref(kv.c), _ptr(idx), int(idx.stride(0)) if idx is not None else 0,
+        n_idx, C.byref(extra_kv.c) if extra_kv else None, _ptr(extra_idx),
+        int(extra_idx.stride(0)) if extra_idx is not None else 0, n_extra, int(B), int(H), int(d_qk),
+        int(d_v), float(softmax_scale), _ptr(out), int(out.stride(0)), _ptr(lse),
+        ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)), "dsa_sparse_mla_decode")
+
+
+def dsa_sparse_mla_prefill(q, kv: KVCache, idx, extra_kv: Optional[KVCache], extra_idx, rows: Rows,
+                           H: int, d_qk: int, d_v: int, softmax_scale: float, out, lse,
+                           ws: Optional[Workspace] = None, stream=None):
+    n_idx = int(idx.shape[1]) if idx is not None else 0
+    n_extra = int(extra_idx.shape[1]) if extra_idx is not None else 0
+    _check(_lib.dsa_sparse_mla_prefill(
+        _ptr(q), int(q.stride(0)), C.byref(kv.c), _ptr(idx), int(idx.stride(0)) if idx is not None else 0,
+        n_idx, C.byref(extra_kv.c) if extra_kv else None, _ptr(extra_idx),
+        int(extra_idx.stride(0)) if extra_idx is not None else 0, n_extra, C.byref(rows.c), int(H),
+        int(d_qk), int(d_v), float(softmax_scale), _ptr(out), int(out.stride(0)), _ptr(lse),
+        ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)), "dsa_sparse_mla_prefill")
+
+
+def dsa_decode(q, q_idx, w, keys: KeyCache, kv: KVCache, rows: Rows, H: int, d_qk: int, d_v: int,
+               Hi: int, di: int, topk: int, index_scale: float, softmax_scale: float, out, lse,
+               idx_out, lens_out, ws: Workspace, stream=None):
+    _check(_lib.dsa_decode(
+        _ptr(q), int(q.stride(0)), _ptr(q_idx), int(q_idx.stride(0)), _ptr(w), int(w.stride(0)),
+        C.byref(keys.c), C.byref(kv.c), C.byref(rows.c), int(H), int(d_qk), int(d_v), int(Hi), int(di),
+        int(topk), float(index_scale), float(softmax_scale), _ptr(out), int(out.stride(0)), _ptr(lse),
+        _ptr(idx_out), int(idx_out.stride(0)) if idx_out is not None else 0, _ptr(lens_out),
+        ws.ptr, ws.nbytes, _stream(stream)), "dsa_decode")

@@ -1,0 +1,101 @@
+// Device helpers shared by the DSA kernels (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+namespace dsa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16x16x32 bf16 MFMA. Lane l supplies A[l%16][8(l/16)+j] and B[8(l/16)+j][l%16] (j = 0..7)
+// and receives C[4(l/16)+r][l%16] (r = 0..3); verified on gfx950 by an in-bounds probe.
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Paging of a token cache, resolved on the host into device-friendly fields.
+struct Paging {
+  const int32_t* bt;      // block table or nullptr
+  const int32_t* req_base;
+  int64_t bt_stride;
+  int64_t n_slots;        // tokens in the cache (pages * page_size when paged)
+  int32_t page;           // tokens per page
+  int32_t page_shift;     // log2(page) if a power of two, else -1
+  int32_t n_pages;        // n_slots / page
+  int32_t _pad;
+};
+
+// Logical position s of request b -> slot, clamped into the cache (a table entry or a
+// position outside the caller's contract yields some in-cache slot, never a wild address).
+__device__ __forceinline__ int64_t slot_of(const Paging& p, int b, int s) {
+  if (p.bt) {
+    int lp, off;
+    if (p.page_shift >= 0) { lp = s >> p.page_shift; off = s & (p.page - 1); }
+    else { lp = s / p.page; off = s - lp * p.page; }
+    lp = min(max(lp, 0), (int)p.bt_stride - 1);
+    int pg = p.bt[(int64_t)b * p.bt_stride + lp];
+    pg = min(max(pg, 0), p.n_pages - 1);
+    return (int64_t)pg * p.page + off;
+  }
+  int64_t sl = (int64_t)p.req_base[b] + s;
+  return sl < 0 ? 0 : (sl >= p.n_slots ? p.n_slots - 1 : sl);
+}
+
+// Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 and +0 share a key.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f == 0.0f) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Two fp32 that are exactly representable in bf16 -> packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// fp32 -> bf16 round-to-nearest-even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+}
+
+// 4 OCP e4m3 bytes -> 4 floats (gfx950's conversion is the OCP e4m3fn decode).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
+  f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+}
+
+// 8 fp8 bytes -> 8 bf16 (exact: an e4m3 value has 4 significant bits and fits bf16's range).
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t raw) {
+  float f[8];
+  fp8x4_to_f32(raw[0], f);
+  fp8x4_to_f32(raw[1], f + 4);
+  u32x4_t r;
+  r[0] = pack_bf16_exact(f[0], f[1]);
+  r[1] = pack_bf16_exact(f[2], f[3]);
+  r[2] = pack_bf16_exact(f[4], f[5]);
+  r[3] = pack_bf16_exact(f[6], f[7]);
+  return r;
+}
+
+// 2^(e-127) for a UE8M0 byte 1..254 (exact, built from the exponent field).
+__device__ __forceinline__ float ue8m0_scale(uint32_t e) { return __uint_as_float(e << 23); }
+
+template <typename T>
+__device__ __forceinline__ T wave_bcast_first(T v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+}  // namespace dsa

@@ -1,0 +1,572 @@
+// C ABI of the DSA layer hot path: argument checks, workspace carving, launch policies.
+// See include/dsa.h for the contract of every entry point.
+#include <math.h>
+#include <algorithm>
+#include <stdint.h>
+#include <string.h>
+
+#include "dsa.h"
+#include "kernels.hpp"
+
+using namespace dsa;
+
+namespace {
+
+// ---------------------------------------------------------------- workspace layout
+// Header of control words that are zero at rest (every entry restores them before its last
+// kernel ends). It has a fixed size, so data regions of one problem never overlap control
+// words of another and one workspace can serve every entry and problem size.
+constexpr int kMaxLongRows = 64;                  // long-row top-k rows per launch batch
+constexpr int64_t kMaxCounters = 1 << 16;         // split-merge tickets per launch
+constexpr int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+constexpr int64_t kOffCtl = 0;
+constexpr int64_t kOffHist = align256(kOffCtl + kMaxLongRows * (int64_t)sizeof(TopkCtl));
+constexpr int64_t kOffCtr = align256(kOffHist + (int64_t)kMaxLongRows * kHistSlices * kHistBins * 4);
+constexpr int64_t kHeaderBytes = align256(kOffCtr + kMaxCounters * 4);
+
+struct Carve {
+  int64_t off = kHeaderBytes;
+  int64_t take(int64_t bytes) {
+    const int64_t o = off;
+    off = align256(off + bytes);
+    return o;
+  }
+};
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int log2_exact(int v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+dsa_status check_paging(const dsa_paging& p, int64_t n_slots) {
+  if (p.page_size < 1 || n_slots < 1) return DSA_ERR_ARG;
+  if (p.block_table) {
+    if (p.bt_stride < 1 || n_slots % p.page_size) return DSA_ERR_ARG;
+    if (n_slots / p.page_size > INT32_MAX) return DSA_ERR_UNSUPPORTED;
+  } else if (!p.req_base) {
+    return DSA_ERR_ARG;
+  }
+  return DSA_OK;
+}
+
+Paging make_paging(const dsa_paging& p, int64_t n_slots) {
+  Paging g;
+  g.bt = p.block_table;
+  g.req_base = p.req_base;
+  g.bt_stride = p.bt_stride;
+  g.n_slots = n_slots;
+  g.page = p.page_size;
+  g.page_shift = log2_exact(p.page_size);
+  g.n_pages = (int32_t)(n_slots / p.page_size);
+  g._pad = 0;
+  return g;
+}
+
+dsa_status check_rows(const dsa_rows* r) {
+  if (!r || r->T < 0 || r->n_max < 0) return DSA_ERR_ARG;
+  if (r->T > 0 && (!r->row_len || r->n_req < 1)) return DSA_ERR_ARG;
+  if (r->T > 0 && !r->row_req && r->T > r->n_req) return DSA_ERR_ARG;  // row t is request t
+  if (r->T > 65535) return DSA_ERR_UNSUPPORTED;   // grid y/z limit of the row axis
+  return DSA_OK;
+}
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+// ---------------------------------------------------------------- attention policy
+struct MlaPlan {
+  int ht;          // head tiles per workgroup
+  int n_split;
+  int rows_per_split;
+};
+
+MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
+  MlaPlan p;
+  const int tiles = H / 16;
+  if (!decode) {
+    p.ht = tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1);
+    p.n_split = 1;
+    p.rows_per_split = ((ntot + 31) / 32) * 32;
+    return p;
+  }
+  p.ht = 1;   // decode: one head tile per workgroup, four row streams
+  const int64_t base = (int64_t)T * tiles;
+  const int max_split = max(1, (ntot + 127) / 128);
+  int s = (int)std::max<int64_t>(1, (512 + base - 1) / base);
+  s = min(s, max_split);
+  if (base * s > kMaxCounters) s = 1;
+  int rps = (ntot + s - 1) / s;
+  rps = ((rps + 31) / 32) * 32;
+  if (rps < 32) rps = 32;
+  p.rows_per_split = rps;
+  p.n_split = max(1, (ntot + rps - 1) / rps);
+  if (p.n_split == 1) p.rows_per_split = max(32, ((ntot + 31) / 32) * 32);
+  return p;
+}
+
+int64_t mla_ws_bytes(int T, int H, int ntot, bool decode) {
+  const MlaPlan p = plan_mla(T, H, ntot, decode);
+  if (p.n_split <= 1) return 0;
+  return align256((int64_t)T * H * p.n_split * 512 * 4) + align256((int64_t)T * H * p.n_split * 8);
+}
+
+int64_t topk_ws_bytes(int T, int n_max) {
+  if (n_max <= kTopkLdsMax) return 0;
+  const int64_t rows = min(T, kMaxLongRows);
+  return 2 * align256(rows * (int64_t)n_max * 4);
+}
+
+int logits_ld(int n_max) { return ((max(n_max, 1) + 63) / 64) * 64; }
+
+dsa_status check_kv(const dsa_kv_cache* kv, int d_qk) {
+  if (!kv || !kv->data || !al16(kv->data)) return DSA_ERR_ARG;
+  dsa_status s = check_paging(kv->paging, kv->n_slots);
+  if (s != DSA_OK) return s;
+  if (kv->d_nope + kv->d_rope != d_qk) return DSA_ERR_ARG;
+  switch (kv->format) {
+    case DSA_KV_BF16:
+      if (d_qk != 576 && d_qk != 512) return DSA_ERR_UNSUPPORTED;
+      break;
+    case DSA_KV_FP8_UNIFORM:
+      if (!kv->scales || !al4(kv->scales)) return DSA_ERR_ARG;
+      if (d_qk != 576 && d_qk != 512) return DSA_ERR_UNSUPPORTED;
+      break;
+    case DSA_KV_FP8_DS_MLA:
+      if (kv->d_nope != 448 || kv->d_rope != 64) return DSA_ERR_UNSUPPORTED;
+      if (!kv->paging.block_table && kv->n_slots % kv->paging.page_size) return DSA_ERR_ARG;
+      break;
+    default:
+      return DSA_ERR_UNSUPPORTED;
+  }
+  return DSA_OK;
+}
+
+KvDev make_kv(const dsa_kv_cache* kv) {
+  KvDev d;
+  d.data = static_cast<const uint8_t*>(kv->data);
+  d.scales = kv->scales;
+  d.pg = make_paging(kv->paging, kv->n_slots);
+  return d;
+}
+
+struct MlaIn {
+  const void* q;
+  int64_t ld_q;
+  const dsa_kv_cache* kv;
+  const int32_t* idx;
+  int64_t ld_idx;
+  int32_t n_idx;
+  const dsa_kv_cache* extra_kv;
+  const int32_t* extra_idx;
+  int64_t ld_extra;
+  int32_t n_extra;
+  int32_t T;
+  const int32_t* row_req;
+  int32_t n_req;
+  int32_t H, d_qk, d_v;
+  float softmax_scale;
+  void* out;
+  int64_t ld_out;
+  float* lse;
+};
+
+dsa_status check_mla(const MlaIn& m) {
+  if (m.T < 0 || m.H <= 0 || m.n_idx < 0 || m.n_extra < 0) return DSA_ERR_ARG;
+  if (m.T > 65535) return DSA_ERR_UNSUPPORTED;
+  if (m.H % 16) return DSA_ERR_UNSUPPORTED;
+  if (m.d_v != 512) return DSA_ERR_UNSUPPORTED;
+  if (m.d_qk != 512 && m.d_qk != 576) return DSA_ERR_UNSUPPORTED;
+  if (!std::isfinite(m.softmax_scale)) return DSA_ERR_ARG;
+  if (m.T == 0) return DSA_OK;
+  if (!m.q || !al16(m.q) || m.ld_q < (int64_t)m.H * m.d_qk || m.ld_q % 8) return DSA_ERR_ARG;
+  if (!m.out || !al16(m.out) || m.ld_out < (int64_t)m.H * m.d_v || m.ld_out % 8) return DSA_ERR_ARG;
+  if (m.lse && !al4(m.lse)) return DSA_ERR_ARG;
+  dsa_status s = check_kv(m.kv, m.d_qk);
+  if (s != DSA_OK) return s;
+  if (m.n_idx > 0 && (!m.idx || !al4(m.idx) || m.ld_idx < m.n_idx)) return DSA_ERR_ARG;
+  if (m.n_extra > 0) {
+    if (!m.extra_idx || !al4(m.extra_idx) || m.ld_extra < m.n_extra) return DSA_ERR_ARG;
+    s = check_kv(m.extra_kv, m.d_qk);
+    if (s != DSA_OK) return s;
+    if (m.extra_kv->format != m.kv->format) return DSA_ERR_UNSUPPORTED;
+  }
+  return DSA_OK;
+}
+
+dsa_status run_mla(const MlaIn& m, bool decode, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (m.T == 0) return DSA_OK;
+  const int ntot = m.n_idx + m.n_extra;
+  const MlaPlan p = plan_mla(m.T, m.H, ntot, decode);
+  MlaArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(m.q);
+  a.ld_q = m.ld_q;
+  a.kv[0] = make_kv(m.kv);
+  a.kv[1] = m.n_extra > 0 ? make_kv(m.extra_kv) : a.kv[0];
+  a.idx[0] = m.idx;
+  a.idx[1] = m.n_extra > 0 ? m.extra_idx : m.idx;
+  a.ld_idx[0] = m.ld_idx;
+  a.ld_idx[1] = m.n_extra > 0 ? m.ld_extra : m.ld_idx;
+  a.n_idx[0] = m.n_idx;
+  a.n_idx[1] = m.n_extra;
+  a.row_req = m.row_req;
+  a.n_req = m.n_req;
+  a.H = m.H;
+  a.n_split = p.n_split;
+  a.rows_per_split = p.rows_per_split;
+  a.scale_log2 = m.softmax_scale * kLog2e;
+  a.out = static_cast<uint16_t*>(m.out);
+  a.ld_out = m.ld_out;
+  a.lse = m.lse;
+  if (p.n_split > 1) {
+    const int64_t need = kHeaderBytes + mla_ws_bytes(m.T, m.H, ntot, decode);
+    if (!ws || (int64_t)ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    Carve cv;
+    a.part_o = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * m.H * p.n_split * 512 * 4));
+    a.part_ml = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * m.H * p.n_split * 8));
+    a.counters = reinterpret_cast<uint32_t*>(w + kOffCtr);
+  }
+  int fmt = m.kv->format == DSA_KV_BF16 ? kFmtBf16 : (m.kv->format == DSA_KV_FP8_UNIFORM ? kFmtUniform : kFmtDsMla);
+  return hip_status(launch_sparse_mla(a, fmt, m.d_qk, p.ht, m.T, st));
+}
+
+// ---------------------------------------------------------------- top-k driver
+struct TopkIn {
+  const float* logits;
+  int64_t ld_logits;
+  const dsa_rows* rows;
+  int32_t topk;
+  int32_t* indices;
+  int64_t ld_idx;
+  int32_t* lens;
+};
+
+dsa_status check_topk(const TopkIn& k) {
+  dsa_status s = check_rows(k.rows);
+  if (s != DSA_OK) return s;
+  if (k.topk < 1) return DSA_ERR_ARG;
+  if (k.topk > 65536) return DSA_ERR_UNSUPPORTED;
+  if (k.rows->T == 0) return DSA_OK;
+  if (!k.logits || !al4(k.logits) || k.ld_logits < k.rows->n_max) return DSA_ERR_ARG;
+  if (!k.indices || !al4(k.indices) || k.ld_idx < k.topk || !k.lens || !al4(k.lens)) return DSA_ERR_ARG;
+  return DSA_OK;
+}
+
+// hist_ready: the first-digit histogram of rows [0, T) was already accumulated (fused in the
+// score kernel; only when T <= kMaxLongRows).
+dsa_status run_topk(const TopkIn& k, bool hist_ready, void* ws, size_t ws_bytes, hipStream_t st) {
+  const dsa_rows& r = *k.rows;
+  if (r.T == 0) return DSA_OK;
+  TopkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.logits = k.logits;
+  a.ld_logits = k.ld_logits;
+  a.row_len = r.row_len;
+  a.n_max = r.n_max;
+  a.topk = k.topk;
+  a.indices = k.indices;
+  a.ld_idx = k.ld_idx;
+  a.lens = k.lens;
+  if (r.n_max <= kTopkLdsMax) return hip_status(launch_topk_lds(a, r.T, st));
+  const int64_t need = kHeaderBytes + topk_ws_bytes(r.T, r.n_max);
+  if (!ws || (int64_t)ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  Carve cv;
+  const int64_t rows_b = min(r.T, kMaxLongRows);
+  a.cand_key = reinterpret_cast<uint32_t*>(w + cv.take(rows_b * (int64_t)r.n_max * 4));
+  a.cand_pos = reinterpret_cast<int32_t*>(w + cv.take(rows_b * (int64_t)r.n_max * 4));
+  a.ctl = reinterpret_cast<TopkCtl*>(w + kOffCtl);
+  a.hist = reinterpret_cast<uint32_t*>(w + kOffHist);
+  for (int r0 = 0; r0 < r.T; r0 += kMaxLongRows) {
+    const int nb = min(kMaxLongRows, r.T - r0);
+    TopkArgs b = a;
+    b.logits = k.logits + (int64_t)r0 * k.ld_logits;
+    b.row_len = r.row_len + r0;
+    b.indices = k.indices + (int64_t)r0 * k.ld_idx;
+    b.lens = k.lens + r0;
+    if (!hist_ready) {
+      dsa_status s = hip_status(launch_topk_hist(b, nb, st));
+      if (s != DSA_OK) return s;
+    }
+    dsa_status s = hip_status(launch_topk_filter(b, nb, st));
+    if (s != DSA_OK) return s;
+  }
+  return DSA_OK;
+}
+
+// ---------------------------------------------------------------- scores driver
+struct ScoreIn {
+  const void* q_idx;
+  int64_t ld_q_idx;
+  const float* w;
+  int64_t ld_w;
+  const dsa_key_cache* keys;
+  const dsa_rows* rows;
+  int32_t Hi, di;
+  float index_scale;
+  float* logits;
+  int64_t ld_logits;
+};
+
+dsa_status check_scores(const ScoreIn& s) {
+  dsa_status st = check_rows(s.rows);
+  if (st != DSA_OK) return st;
+  if (s.Hi < 1 || s.di < 1) return DSA_ERR_ARG;
+  if (s.Hi > 64 || (s.di != 64 && s.di != 128)) return DSA_ERR_UNSUPPORTED;
+  if (!std::isfinite(s.index_scale)) return DSA_ERR_ARG;
+  if (!s.keys) return DSA_ERR_ARG;
+  if (s.keys->dtype != DSA_KEY_BF16 && s.keys->dtype != DSA_KEY_FP8) return DSA_ERR_UNSUPPORTED;
+  if (!s.keys->data || !al16(s.keys->data)) return DSA_ERR_ARG;
+  if (s.keys->dtype == DSA_KEY_FP8 && (!s.keys->scale || !al4(s.keys->scale))) return DSA_ERR_ARG;
+  st = check_paging(s.keys->paging, s.keys->n_slots);
+  if (st != DSA_OK) return st;
+  if (s.rows->T == 0) return DSA_OK;
+  if (!s.q_idx || !al16(s.q_idx) || s.ld_q_idx < (int64_t)s.Hi * s.di || s.ld_q_idx % 8) return DSA_ERR_ARG;
+  if (!s.w || !al4(s.w) || s.ld_w < s.Hi) return DSA_ERR_ARG;
+  if (!s.logits || !al4(s.logits) || s.ld_logits < s.rows->n_max) return DSA_ERR_ARG;
+  return DSA_OK;
+}
+
+dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
+  const dsa_rows& r = *s.rows;
+  if (r.T == 0 || r.n_max == 0) return DSA_OK;
+  ScoreArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q_idx = static_cast<const uint16_t*>(s.q_idx);
+  a.ld_q = s.ld_q_idx;
+  a.w = s.w;
+  a.ld_w = s.ld_w;
+  a.keys = s.keys->data;
+  a.key_scale = s.keys->scale;
+  a.pg = make_paging(s.keys->paging, s.keys->n_slots);
+  a.row_req = r.row_req;
+  a.row_len = r.row_len;
+  a.n_max = r.n_max;
+  a.Hi = s.Hi;
+  a.index_scale = s.index_scale;
+  a.n_req = r.n_req;
+  a.logits = s.logits;
+  a.ld_logits = s.ld_logits;
+  a.hist = hist;
+  return hip_status(launch_index_scores(a, s.di, s.keys->dtype == DSA_KEY_FP8, hist != nullptr, r.T, st));
+}
+
+}  // namespace
+
+// ==================================================================== exported entry points
+extern "C" {
+
+int32_t dsa_abi_version(void) { return 1; }
+
+const char* dsa_status_string(int32_t status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_ARG: return "invalid argument (null pointer, bad shape, stride or alignment)";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape or format (outside the compiled envelope)";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small (see dsa_workspace_size)";
+    case DSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t dsa_workspace_size(int32_t entry, const dsa_problem* p) {
+  if (!p || p->T < 0 || p->n_max < 0 || p->topk < 0 || p->H < 0 || p->n_idx < 0) return SIZE_MAX;
+  switch (entry) {
+    case DSA_ENTRY_TOPK:
+      return (size_t)(kHeaderBytes + topk_ws_bytes(p->T, p->n_max));
+    case DSA_ENTRY_MLA_DECODE:
+      if (p->H % 16) return SIZE_MAX;
+      return (size_t)(kHeaderBytes + mla_ws_bytes(p->T, p->H, p->n_idx, true));
+    case DSA_ENTRY_MLA_PREFILL:
+      return 0;
+    case DSA_ENTRY_DECODE: {
+      if (p->H % 16) return SIZE_MAX;
+      const int64_t ld = logits_ld(p->n_max);
+      int64_t b = kHeaderBytes;
+      b = align256(b + (int64_t)p->T * ld * 4);                 // logits
+      b = align256(b + (int64_t)p->T * p->topk * 4);            // indices
+      b = align256(b + (int64_t)p->T * 4);                      // lens
+      b += topk_ws_bytes(p->T, p->n_max);
+      b = align256(b);
+      b += mla_ws_bytes(p->T, p->H, p->topk, p->T <= 1024);
+      return (size_t)b;
+    }
+    default:
+      return SIZE_MAX;
+  }
+}
+
+dsa_status dsa_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace || !al16(workspace)) return DSA_ERR_ARG;
+  if ((int64_t)ws_bytes < kHeaderBytes) return DSA_ERR_WORKSPACE;
+  return hip_status(launch_fill_zero(workspace, ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status dsa_index_scores(const void* q_idx, int64_t ld_q_idx, const float* w, int64_t ld_w,
+                            const dsa_key_cache* keys, const dsa_rows* rows, int32_t Hi,
+                            int32_t di, float index_scale, float* logits, int64_t ld_logits,
+                            void* stream) {
+  ScoreIn s{q_idx, ld_q_idx, w, ld_w, keys, rows, Hi, di, index_scale, logits, ld_logits};
+  dsa_status st = check_scores(s);
+  if (st != DSA_OK) return st;
+  return run_scores(s, nullptr, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_topk(const float* logits, int64_t ld_logits, const dsa_rows* rows, int32_t topk,
+                    int32_t* indices, int64_t ld_idx, int32_t* lens, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  TopkIn k{logits, ld_logits, rows, topk, indices, ld_idx, lens};
+  dsa_status st = check_topk(k);
+  if (st != DSA_OK) return st;
+  return run_topk(k, false, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_sparse_mla_decode(const void* q, int64_t ld_q, const dsa_kv_cache* kv,
+                                 const int32_t* idx, int64_t ld_idx, int32_t n_idx,
+                                 const dsa_kv_cache* extra_kv, const int32_t* extra_idx,
+                                 int64_t ld_extra, int32_t n_extra, int32_t B, int32_t H,
+                                 int32_t d_qk, int32_t d_v, float softmax_scale, void* out,
+                                 int64_t ld_out, float* lse, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  MlaIn m{q, ld_q, kv, idx, ld_idx, n_idx, extra_kv, extra_idx, ld_extra, n_extra, B, nullptr,
+          B, H, d_qk, d_v, softmax_scale, out, ld_out, lse};
+  dsa_status st = check_mla(m);
+  if (st != DSA_OK) return st;
+  return run_mla(m, true, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cache* kv,
+                                  const int32_t* idx, int64_t ld_idx, int32_t n_idx,
+                                  const dsa_kv_cache* extra_kv, const int32_t* extra_idx,
+                                  int64_t ld_extra, int32_t n_extra, const dsa_rows* rows,
+                                  int32_t H, int32_t d_qk, int32_t d_v, float softmax_scale,
+                                  void* out, int64_t ld_out, float* lse, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  MlaIn m{q, ld_q, kv, idx, ld_idx, n_idx, extra_kv, extra_idx, ld_extra, n_extra, rows->T,
+          rows->row_req, rows->n_req, H, d_qk, d_v, softmax_scale, out, ld_out, lse};
+  st = check_mla(m);
+  if (st != DSA_OK) return st;
+  return run_mla(m, false, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld_q_idx,
+                      const float* w, int64_t ld_w, const dsa_key_cache* keys,
+                      const dsa_kv_cache* kv, const dsa_rows* rows, int32_t H, int32_t d_qk,
+                      int32_t d_v, int32_t Hi, int32_t di, int32_t topk, float index_scale,
+                      float softmax_scale, void* out, int64_t ld_out, float* lse,
+                      int32_t* idx_out, int64_t ld_idx_out, int32_t* lens_out,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  dsa_status s = check_rows(rows);
+  if (s != DSA_OK) return s;
+  if (topk < 1) return DSA_ERR_ARG;
+  if (topk > 65536) return DSA_ERR_UNSUPPORTED;
+  if (idx_out && (!al4(idx_out) || ld_idx_out < topk)) return DSA_ERR_ARG;
+  if (lens_out && !al4(lens_out)) return DSA_ERR_ARG;
+  const int T = rows->T;
+  const int64_t ld = logits_ld(rows->n_max);
+  // validate all three steps before enqueueing anything (logits/indices are workspace-backed)
+  float* const dummy_f = reinterpret_cast<float*>(uintptr_t(256));
+  ScoreIn sc{q_idx, ld_q_idx, w, ld_w, keys, rows, Hi, di, index_scale, dummy_f, ld};
+  s = check_scores(sc);
+  if (s != DSA_OK) return s;
+  MlaIn m{q, ld_q, kv, reinterpret_cast<const int32_t*>(uintptr_t(256)), topk, topk, nullptr, nullptr,
+          0, 0, T, rows->row_req, rows->n_req, H, d_qk, d_v, softmax_scale, out, ld_out, lse};
+  s = check_mla(m);
+  if (s != DSA_OK) return s;
+  if (T == 0) return DSA_OK;
+  dsa_problem pr{T, rows->n_max, topk, H, topk, 0};
+  const size_t need = dsa_workspace_size(DSA_ENTRY_DECODE, &pr);
+  if (!workspace || !al16(workspace) || ws_bytes < need) return DSA_ERR_WORKSPACE;
+
+  uint8_t* wsb = static_cast<uint8_t*>(workspace);
+  Carve cv;
+  float* logits = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * ld * 4));
+  int32_t* idx_ws = reinterpret_cast<int32_t*>(wsb + cv.take((int64_t)T * topk * 4));
+  int32_t* lens_ws = reinterpret_cast<int32_t*>(wsb + cv.take((int64_t)T * 4));
+  int32_t* idx = idx_out ? idx_out : idx_ws;
+  const int64_t ld_idx = idx_out ? ld_idx_out : topk;
+  int32_t* lens = lens_out ? lens_out : lens_ws;
+
+  // step 1 (+ the first top-k digit when the long-row path will run and fits one batch)
+  const bool long_rows = rows->n_max > kTopkLdsMax;
+  const bool fuse_hist = long_rows && T <= kMaxLongRows;
+  sc.logits = logits;
+  s = run_scores(sc, fuse_hist ? reinterpret_cast<uint32_t*>(wsb + kOffHist) : nullptr, st);
+  if (s != DSA_OK) return s;
+  // step 2: top-k; its candidate lists are carved after the regions above
+  TopkIn tk{logits, ld, rows, topk, idx, ld_idx, lens};
+  {
+    TopkArgs a;
+    memset(&a, 0, sizeof(a));
+    if (!long_rows) {
+      s = run_topk(tk, false, nullptr, 0, st);
+    } else {
+      a.logits = logits;
+      a.ld_logits = ld;
+      a.row_len = rows->row_len;
+      a.n_max = rows->n_max;
+      a.topk = topk;
+      a.indices = idx;
+      a.ld_idx = ld_idx;
+      a.lens = lens;
+      const int64_t rows_b = min(T, kMaxLongRows);
+      a.cand_key = reinterpret_cast<uint32_t*>(wsb + cv.take(rows_b * (int64_t)rows->n_max * 4));
+      a.cand_pos = reinterpret_cast<int32_t*>(wsb + cv.take(rows_b * (int64_t)rows->n_max * 4));
+      a.ctl = reinterpret_cast<TopkCtl*>(wsb + kOffCtl);
+      a.hist = reinterpret_cast<uint32_t*>(wsb + kOffHist);
+      for (int r0 = 0; r0 < T && s == DSA_OK; r0 += kMaxLongRows) {
+        const int nb = min(kMaxLongRows, T - r0);
+        TopkArgs b = a;
+        b.logits = logits + (int64_t)r0 * ld;
+        b.row_len = rows->row_len + r0;
+        b.indices = idx + (int64_t)r0 * ld_idx;
+        b.lens = lens + r0;
+        if (!fuse_hist) s = hip_status(launch_topk_hist(b, nb, st));
+        if (s == DSA_OK) s = hip_status(launch_topk_filter(b, nb, st));
+      }
+    }
+    if (s != DSA_OK) return s;
+  }
+  // step 3: attention over the selection; split partials after our regions
+  const bool decode = T <= 1024;
+  const MlaPlan p = plan_mla(T, H, topk, decode);
+  MlaArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.ld_q = ld_q;
+  a.kv[0] = make_kv(kv);
+  a.kv[1] = a.kv[0];
+  a.idx[0] = idx;
+  a.idx[1] = idx;
+  a.ld_idx[0] = ld_idx;
+  a.ld_idx[1] = ld_idx;
+  a.n_idx[0] = topk;
+  a.n_idx[1] = 0;
+  a.row_req = rows->row_req;
+  a.n_req = rows->n_req;
+  a.H = H;
+  a.n_split = p.n_split;
+  a.rows_per_split = p.rows_per_split;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.out = static_cast<uint16_t*>(out);
+  a.ld_out = ld_out;
+  a.lse = lse;
+  if (p.n_split > 1) {
+    a.part_o = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * H * p.n_split * 512 * 4));
+    a.part_ml = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * H * p.n_split * 8));
+    a.counters = reinterpret_cast<uint32_t*>(wsb + kOffCtr);
+    if ((size_t)cv.off > ws_bytes) return DSA_ERR_WORKSPACE;
+  }
+  const int fmt = kv->format == DSA_KV_BF16 ? kFmtBf16 : (kv->format == DSA_KV_FP8_UNIFORM ? kFmtUniform : kFmtDsMla);
+  return hip_status(launch_sparse_mla(a, fmt, d_qk, p.ht, T, st));
+}
+
+}  // extern "C"

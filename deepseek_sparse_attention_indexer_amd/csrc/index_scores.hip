@@ -1,0 +1,168 @@
+// Lightning-indexer scores on gfx950 MFMA.
+//
+//   I(t, s) = index_scale * sum_j w[t, j] * max(0, q_idx[t, j, :] . k[slot(b, s), :])
+//
+// (scoring stage of tokenspeed PR 627 "Add gluon kernel for DSA"; keys are the paged
+// index_k_cache of the decode top-k wrapper in that PR's review, bf16, or fp8 e4m3 with an
+// fp32 per-token scale.)
+//
+// A wave owns one tile of 64 consecutive candidate positions of one query row. The row's
+// query heads are the MFMA A operand (M = 16 heads per tile, held in registers for the whole
+// wave), the 64 keys are four B operands of 16 keys each (K = 32 dims per MFMA), loaded
+// straight from HBM into registers: lane l reads 16 (bf16) or 8 (fp8) contiguous bytes of key
+// l%16, so each load instruction covers 64 contiguous bytes of 16 rows and a tile is one
+// contiguous 16 KiB (bf16, page 64) or 8 KiB (fp8) burst. The epilogue applies ReLU and the
+// head weights in fp32 on the accumulators, reduces the four lane groups with a 3-shuffle
+// reduce-scatter so lane l ends up with candidate s0 + l, and stores one coalesced 256-byte
+// row segment. Optionally the same pass counts a 4096-bin histogram of the top 12 bits of
+// the order-preserving key of each score (first radix digit of the top-k select).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+
+template <int DI, int MT, bool FP8, bool HIST>
+__global__ __launch_bounds__(256) void k_index_scores(ScoreArgs a) {
+  constexpr int KB = DI / 32;
+  __shared__ uint32_t s_hist[HIST ? kHistBins : 1];
+
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;       // lane group 0..3
+  const int c = lane & 15;       // column within a 16-wide tile
+  const int b = min(max(a.row_req ? a.row_req[t] : t, 0), a.n_req - 1);
+  int n = a.row_len[t];
+  n = min(max(n, 0), a.n_max);
+  const int ntiles = (n + 63) >> 6;
+
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < kHistBins; i += 256) s_hist[i] = 0;
+    __syncthreads();
+  }
+
+  // Query heads as A operands: qa[mt][kb] = q_idx[t, 16 mt + c, 32 kb + 8 g .. +7].
+  u32x4_t qa[MT][KB];
+  float wv[MT][4];
+  {
+    const uint16_t* qrow = a.q_idx + (int64_t)t * a.ld_q;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int head = 16 * mt + c;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if (head < a.Hi)
+          qa[mt][kb] = *reinterpret_cast<const u32x4_t*>(qrow + head * DI + 32 * kb + 8 * g);
+        else
+          qa[mt][kb] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hr = 16 * mt + 4 * g + r;   // head of accumulator row r
+        wv[mt][r] = hr < a.Hi ? a.w[(int64_t)t * a.ld_w + hr] * a.index_scale : 0.0f;
+      }
+    }
+  }
+
+  for (int tile = blockIdx.x * 4 + wave; tile < ntiles; tile += gridDim.x * 4) {
+    const int s0 = tile << 6;
+    u32x4_t kbv[4][KB];
+    float ksc[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int pos = min(s0 + 16 * st + c, n - 1);
+      const int64_t slot = slot_of(a.pg, b, pos);
+      if constexpr (!FP8) {
+        const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.keys) + slot * DI + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) kbv[st][kb] = *reinterpret_cast<const u32x4_t*>(kp + 32 * kb);
+        ksc[st] = 1.0f;
+      } else {
+        const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.keys) + slot * DI + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          kbv[st][kb] = fp8x8_to_bf16x8(*reinterpret_cast<const u32x2_t*>(kp + 32 * kb));
+        ksc[st] = a.key_scale[slot];
+      }
+    }
+    float part[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      f32x4_t acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16_16x16x32(qa[mt][kb], kbv[st][kb], acc[mt]);
+      float p = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[mt][r];
+          if constexpr (FP8) x *= ksc[st];
+          p = fmaf(wv[mt][r], fmaxf(x, 0.0f), p);
+        }
+      part[st] = p;
+    }
+    // reduce-scatter over the 4 lane groups: group g keeps the full sum of sub-tile st = g
+    const bool hi2 = lane & 32;
+    float k0 = hi2 ? part[2] : part[0];
+    float k1 = hi2 ? part[3] : part[1];
+    k0 += __shfl_xor(hi2 ? part[0] : part[2], 32);
+    k1 += __shfl_xor(hi2 ? part[1] : part[3], 32);
+    const bool hi1 = lane & 16;
+    float total = (hi1 ? k1 : k0) + __shfl_xor(hi1 ? k0 : k1, 16);
+
+    const int s = s0 + lane;
+    if (s < n) {
+      a.logits[(int64_t)t * a.ld_logits + s] = total;
+      if constexpr (HIST) atomicAdd(&s_hist[float_key(total) >> (32 - kHistBits)], 1u);
+    }
+  }
+
+  if constexpr (HIST) {
+    __syncthreads();
+    if (ntiles > 0) {
+      uint32_t* gh = a.hist + ((int64_t)t * kHistSlices + (blockIdx.x % kHistSlices)) * kHistBins;
+      for (int i = threadIdx.x; i < kHistBins; i += 256) {
+        const uint32_t v = s_hist[i];
+        if (v) atomicAdd(gh + i, v);
+      }
+    }
+  }
+}
+
+template <int DI, int MT, bool FP8, bool HIST>
+static hipError_t launch_t(const ScoreArgs& a, int T, hipStream_t st) {
+  const int ntiles = (a.n_max + 63) / 64;
+  int gx = (ntiles + 3) / 4;
+  // bound the grid: very long rows loop inside the waves, many rows keep x small
+  const int cap = T > 1 ? max(1, 16384 / T) : 1024;
+  gx = max(1, min(gx, cap));
+  hipLaunchKernelGGL((k_index_scores<DI, MT, FP8, HIST>), dim3(gx, T), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DI, bool FP8, bool HIST>
+static hipError_t launch_mt(const ScoreArgs& a, int T, hipStream_t st) {
+  if (a.Hi <= 16) return launch_t<DI, 1, FP8, HIST>(a, T, st);
+  if (a.Hi <= 32) return launch_t<DI, 2, FP8, HIST>(a, T, st);
+  return launch_t<DI, 4, FP8, HIST>(a, T, st);
+}
+
+template <bool FP8, bool HIST>
+static hipError_t launch_di(const ScoreArgs& a, int di, int T, hipStream_t st) {
+  if (di == 64) return launch_mt<64, FP8, HIST>(a, T, st);
+  return launch_mt<128, FP8, HIST>(a, T, st);
+}
+
+hipError_t launch_index_scores(const ScoreArgs& a, int di, bool fp8, bool hist, int T,
+                               hipStream_t st) {
+  if (T <= 0 || a.n_max <= 0) return hipSuccess;
+  if (fp8) return hist ? launch_di<true, true>(a, di, T, st) : launch_di<true, false>(a, di, T, st);
+  return hist ? launch_di<false, true>(a, di, T, st) : launch_di<false, false>(a, di, T, st);
+}
+
+}  // namespace dsa

@@ -141,11 +141,12 @@ def kv_rows(pool, b: int, positions: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------- the three steps
 
 
-def index_scores_row(prob, t: int) -> np.ndarray:
-    """I(t, s) for s in [0, n_t), float64."""
+def index_scores_row(prob, t: int, positions: np.ndarray | None = None) -> np.ndarray:
+    """I(t, s) for s in [0, n_t) (or for the given positions only), float64."""
     b = int(prob.row_req[t])
     n = int(prob.row_len[t])
-    keys = key_rows(prob.kpool, b, np.arange(n))               # [n, di]
+    pos = np.arange(n) if positions is None else np.asarray(positions, dtype=np.int64)
+    keys = key_rows(prob.kpool, b, pos)                         # [n, di]
     q = bf16_to_f64(prob.q_idx[t])                              # [Hi, di]
     w = prob.w[t].astype(np.float64)                            # [Hi]
     dots = q @ keys.T                                           # [Hi, n]

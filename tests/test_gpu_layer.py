@@ -1,0 +1,93 @@
+"""The whole layer on the GPU: the fused dsa_decode entry, and the prefill chain
+dsa_index_scores -> dsa_topk -> dsa_sparse_mla_prefill, against the oracle.
+
+Top-k is checked with rule T against the oracle's fp64 scores; attention is checked against
+the oracle run on the GPU's own selection (so near-tie choices do not leak into it)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.compare import attention_ok, scores_ok, topk_ok
+from dev import dsa, need_gpu, run_decode, run_scores, say, upload, workload
+
+pytestmark = [pytest.mark.gpu, need_gpu]
+
+DECODE = [
+    ("tiny", "tiny_decode", dict()),
+    ("ragged_b3", "glm_decode", dict(n_ctx=3000, B=3, ctx_lens=(3000, 1, 777), topk=256)),
+    ("glm_32k", "glm_decode", dict(n_ctx=32768)),
+    ("glm_128k", "glm_decode", dict(n_ctx=131072)),
+    ("long_1m_fp8_keys", "long_decode", dict()),
+    ("b4_20k_long_rows", "glm_decode", dict(n_ctx=20000, B=4, ctx_lens=(20000, 17000, 100, 19999), H=16)),
+]
+
+
+@pytest.mark.parametrize("label,name,kw", DECODE, ids=[d[0] for d in DECODE])
+def test_fused_decode(label, name, kw):
+    prob = workload(name, **kw)
+    say("decode", label)
+    out, lse, idx, lens = run_decode(prob)
+    for t in range(prob.T):
+        scores = oracle.index_scores_row(prob, t)
+        ok, msg = topk_ok(scores, prob.topk, idx[t], lens[t])
+        assert ok, f"row {t}: top-k {msg}"
+        o_ref, l_ref = oracle.attention_row(prob, t, idx[t])
+        ok, msg = attention_ok(out[t], lse[t], o_ref, l_ref, prob.kv.fmt)
+        assert ok, f"row {t}: attention {msg}"
+
+
+def _prefill_chain(prob):
+    m = dsa()
+    d = upload(prob)
+    logits = run_scores(prob, d, ld_pad=0)
+    idx = torch.full((prob.T, prob.topk), -7, dtype=torch.int32, device="cuda")
+    lens = torch.full((prob.T,), -7, dtype=torch.int32, device="cuda")
+    ws = m.Workspace(m.dsa_workspace_size(m.ENTRY_TOPK, T=prob.T, n_max=prob.n_max, topk=prob.topk))
+    m.dsa_topk(logits, d.rows, prob.topk, idx, lens, ws)
+    out = torch.full((prob.T, prob.H, prob.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((prob.T, prob.H), float("nan"), device="cuda")
+    m.dsa_sparse_mla_prefill(d.q, d.kv, idx, None, None, d.rows, prob.H, prob.d_qk, prob.d_v,
+                             prob.softmax_scale, out, lse)
+    torch.cuda.synchronize()
+    return (logits.cpu().numpy(), idx.cpu().numpy(), lens.cpu().numpy(), out.float().cpu().numpy(),
+            lse.cpu().numpy())
+
+
+def _check_prefill_rows(prob, res, rows):
+    logits, idx, lens, out, lse = res
+    for t in rows:
+        n = int(prob.row_len[t])
+        scores = oracle.index_scores_row(prob, t)
+        ok, msg = scores_ok(logits[t, :n], scores)
+        assert ok, f"row {t}: scores {msg}"
+        ok, msg = topk_ok(scores, prob.topk, idx[t], lens[t])
+        assert ok, f"row {t}: top-k {msg}"
+        o_ref, l_ref = oracle.attention_row(prob, t, idx[t])
+        ok, msg = attention_ok(out[t], lse[t], o_ref, l_ref, "bf16")
+        assert ok, f"row {t}: attention {msg}"
+
+
+def test_prefill_chain_small_all_rows():
+    prob = workload("causal_prefill", seg_lens=(300, 1, 45), topk=64, H=32)
+    say("prefill chain small")
+    _check_prefill_rows(prob, _prefill_chain(prob), range(prob.T))
+
+
+def test_prefill_chain_full_size_sampled_rows():
+    """One 8192-token segment plus a 1-token segment, topk 2048 with -1 padding for the first
+    2047 rows; sampled rows are compared whole, every row's top-k shape is checked."""
+    prob = workload("causal_prefill", seg_lens=(8192, 1))
+    say("prefill chain 8193 rows")
+    res = _prefill_chain(prob)
+    _, idx, lens, out, _ = res
+    exp_lens = np.minimum(prob.row_len, prob.topk)
+    assert np.array_equal(lens, exp_lens)
+    for t in range(prob.T):
+        m = int(exp_lens[t])
+        assert np.all(idx[t, m:] == -1) and np.all(idx[t, :m] >= 0) and np.all(idx[t, :m] < prob.row_len[t])
+    assert np.isfinite(out).all()
+    _check_prefill_rows(prob, res, [0, 1, 2, 2046, 2047, 2048, 5000, 8191, 8192])
+    # the 1-token segment attends to its own row only
+    row = oracle.kv_rows(prob.kv, 1, np.array([0]))[0]
+    assert np.abs(out[8192] - row[None, :512]).max() < 2e-2

@@ -1,0 +1,87 @@
+"""Top-k on the GPU (dsa_topk) against the oracle on the same fp32 scores.
+
+Given identical fp32 inputs the selection is integer work, so the GPU's SET must equal the
+oracle's exactly (both break ties toward the smaller position); order inside the set is free.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dev import need_gpu, run_topk, say
+
+pytestmark = [pytest.mark.gpu, need_gpu]
+
+
+def _check(logits_np, row_len, k, idx, lens):
+    for t, n in enumerate(row_len):
+        n = int(n)
+        ref_idx, m = oracle.topk_row(logits_np[t, :n].astype(np.float64), k)
+        assert int(lens[t]) == m, f"row {t}: lens {lens[t]} != {m}"
+        got = idx[t, :m]
+        assert np.all(idx[t, m:k] == -1), f"row {t}: padding"
+        assert np.unique(got).size == m, f"row {t}: duplicates"
+        assert set(got.tolist()) == set(ref_idx[:m].tolist()), f"row {t}: set differs"
+
+
+def _logits(rng, T, ld, quant=None, dist="normal"):
+    x = rng.standard_normal((T, ld)).astype(np.float32) if dist == "normal" else \
+        rng.uniform(-1, 1, (T, ld)).astype(np.float32)
+    if quant:
+        x = (np.round(x * quant) / quant).astype(np.float32)
+    return x
+
+
+CASES = [
+    # (name, T, row_len, k, quant)
+    ("lds_mixed", 5, [16384, 2048, 2047, 2049, 0], 2048, 64),
+    ("lds_small", 3, [512, 100, 513], 128, None),
+    ("lds_heavy_ties", 2, [8192, 8000], 2048, 4),
+    ("long_128k", 2, [131072, 20000], 2048, 256),
+    ("long_short_row", 3, [17000, 1500, 16385], 2048, None),
+    ("long_batches", 70, [17000] * 70, 256, 32),
+    ("long_1m", 1, [1 << 20], 2048, None),
+]
+
+
+@pytest.mark.parametrize("name,T,row_len,k,quant", CASES, ids=[c[0] for c in CASES])
+def test_topk_sets(name, T, row_len, k, quant):
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    ld = max(row_len) + 5
+    x = _logits(rng, T, ld, quant)
+    say("topk", name)
+    idx, lens = run_topk(torch.from_numpy(x).cuda(), row_len, T, k)
+    _check(x, row_len, k, idx, lens)
+
+
+@pytest.mark.parametrize("n", [3000, 100000])
+def test_topk_all_ties_and_signed_zero(n):
+    """Every score equal (zeros of both signs): the k smallest positions win."""
+    x = np.zeros((1, n), np.float32)
+    x[0, 1::3] = -0.0
+    idx, lens = run_topk(torch.from_numpy(x).cuda(), [n], 1, 2048)
+    assert int(lens[0]) == 2048 and set(idx[0].tolist()) == set(range(2048))
+
+
+def test_topk_negative_and_tie_at_threshold():
+    rng = np.random.default_rng(3)
+    n = 50000
+    x = -np.abs(rng.standard_normal((1, n))).astype(np.float32)
+    x[0, :4096] = -0.5            # a block of exact ties straddling the k-th value
+    x[0, 10000:10100] = 3.0
+    idx, lens = run_topk(torch.from_numpy(x).cuda(), [n], 1, 2048)
+    _check(x, [n], 2048, idx, lens)
+
+
+def test_topk_workspace_reuse_is_clean():
+    """Back-to-back calls on one workspace (long rows) give identical, correct sets: every call
+    returns its control words to zero."""
+    import deepseek_sparse_attention_indexer_amd as m
+    rng = np.random.default_rng(9)
+    ws = m.Workspace(m.dsa_workspace_size(m.ENTRY_TOPK, T=2, n_max=40000, topk=512))
+    for rep in range(3):
+        x = _logits(rng, 2, 40000, 16)
+        idx, lens = run_topk(torch.from_numpy(x).cuda(), [40000, 39000], 2, 512, ws=ws)
+        _check(x, [40000, 39000], 512, idx, lens)

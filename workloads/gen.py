@@ -230,9 +230,10 @@ def glm_decode(n_ctx: int = 32768, B: int = 1, H: int = 64, Hi: int = 64, di: in
                topk: int = 2048, page_size: int = 64, d_nope: int = 512, d_rope: int = 64,
                key_dtype: str = "bf16", kv_fmt: str = "bf16", shuffled: bool = True,
                seed: int = 0, ctx_lens=None, w_low: float = 0.0, index_scale: float = 1.0,
-               name: Optional[str] = None) -> DSAProblem:
+               make_kv: bool = True, name: Optional[str] = None) -> DSAProblem:
     """GLM-style decode: B requests, one query token each, n_ctx cached tokens per request
-    (or per-request ctx_lens), MLA 512+64 latent rows, indexer Hi x di, weights ~U(w_low, 1)."""
+    (or per-request ctx_lens), MLA 512+64 latent rows, indexer Hi x di, weights ~U(w_low, 1).
+    make_kv=False replaces the latent cache by one page of data (for indexer-only uses)."""
     ctx = np.full(B, n_ctx, dtype=np.int64) if ctx_lens is None else np.asarray(ctx_lens, np.int64)
     D = d_nope + d_rope
     ppr = (ctx + page_size - 1) // page_size
@@ -256,7 +257,11 @@ def glm_decode(n_ctx: int = 32768, B: int = 1, H: int = 64, Hi: int = 64, di: in
         k8, ks = quant_rows(kraw)
         kpool = KeyPool("fp8", k8, ks, page_size, bt, None)
     del kraw
-    kv = _make_kv(seed, _T_KV, kv_fmt, slots, d_nope, d_rope, page_size, bt, None)
+    if make_kv:
+        kv = _make_kv(seed, _T_KV, kv_fmt, slots, d_nope, d_rope, page_size, bt, None)
+    else:
+        kv = _make_kv(seed, _T_KV, kv_fmt, page_size, d_nope, d_rope, page_size,
+                      np.zeros_like(bt), None)
     return DSAProblem(
         name=name or f"glm_decode_{n_ctx}", T=B, H=H, d_qk=D, d_v=d_nope, topk=topk, q=q, kv=kv,
         row_req=np.arange(B, dtype=np.int32), row_len=ctx.astype(np.int32), n_req=B,
