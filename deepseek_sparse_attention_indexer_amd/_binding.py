@@ -11,13 +11,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libdsa.so")
+    """The in-tree build, or the library named by DSA_LIBRARY (for alternative builds)."""
+    return os.environ.get("DSA_LIBRARY") or os.path.join(_HERE, "libdsa.so")
 
 
 if not os.path.exists(lib_path()):
     raise ImportError(
         f"{lib_path()} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
-        "or python -m deepseek_sparse_attention_indexer_amd.build)")
+        "or python deepseek_sparse_attention_indexer_amd/build.py)")
 
 _lib = C.CDLL(lib_path())
 
@@ -85,6 +86,17 @@ _lib.dsa_abi_version.argtypes = []
 _lib.dsa_abi_version.restype = _I32
 
 
+class _KernelTime(C.Structure):
+    _fields_ = [("name", C.c_char * 40), ("count", C.c_int32), ("total_ms", C.c_float),
+                ("min_ms", C.c_float), ("max_ms", C.c_float)]
+
+
+_lib.dsa_profile_enable.argtypes = [_I32]
+_lib.dsa_profile_enable.restype = _I32
+_lib.dsa_profile_collect.argtypes = [C.POINTER(_KernelTime), _I32]
+_lib.dsa_profile_collect.restype = _I32
+
+
 class DSAError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -97,6 +109,21 @@ def dsa_status_string(status: int) -> str:
 
 def dsa_abi_version() -> int:
     return int(_lib.dsa_abi_version())
+
+
+def dsa_profile_enable(on: bool):
+    _check(_lib.dsa_profile_enable(1 if on else 0), "dsa_profile_enable")
+
+
+def dsa_profile_collect(max_entries: int = 32) -> dict:
+    """{kernel name: {"count", "total_ms", "min_ms", "max_ms"}} of the launches recorded while
+    profiling was enabled (waits for them)."""
+    buf = (_KernelTime * max_entries)()
+    n = _lib.dsa_profile_collect(buf, max_entries)
+    if n < 0:
+        raise DSAError(n, "dsa_profile_collect")
+    return {buf[i].name.decode(): {"count": buf[i].count, "total_ms": buf[i].total_ms,
+                                   "min_ms": buf[i].min_ms, "max_ms": buf[i].max_ms} for i in range(n)}
 
 
 def _check(status: int, where: str):

@@ -1,4 +1,4 @@
-"""Build libdsa.so in-tree with hipcc for gfx950 (python -m deepseek_sparse_attention_indexer_amd.build)."""
+"""Build libdsa.so in-tree with hipcc for gfx950 (python deepseek_sparse_attention_indexer_amd/build.py)."""
 from __future__ import annotations
 
 import glob

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <stdint.h>
 #include <string.h>
+#include <vector>
 
 #include "dsa.h"
 #include "kernels.hpp"
@@ -17,12 +18,9 @@ namespace {
 // kernel ends). It has a fixed size, so data regions of one problem never overlap control
 // words of another and one workspace can serve every entry and problem size.
 constexpr int kMaxLongRows = 64;                  // long-row top-k rows per launch batch
-constexpr int64_t kMaxCounters = 1 << 16;         // split-merge tickets per launch
 constexpr int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
-constexpr int64_t kOffCtl = 0;
-constexpr int64_t kOffHist = align256(kOffCtl + kMaxLongRows * (int64_t)sizeof(TopkCtl));
-constexpr int64_t kOffCtr = align256(kOffHist + (int64_t)kMaxLongRows * kHistSlices * kHistBins * 4);
-constexpr int64_t kHeaderBytes = align256(kOffCtr + kMaxCounters * 4);
+constexpr int64_t kOffHist = 0;
+constexpr int64_t kHeaderBytes = align256(kOffHist + (int64_t)kMaxLongRows * kHistSlices * kHistBins * 4);
 
 struct Carve {
   int64_t off = kHeaderBytes;
@@ -77,6 +75,38 @@ dsa_status check_rows(const dsa_rows* r) {
 
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+// ---------------------------------------------------------------- kernel timing
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Run one kernel launch, bracketed by events when profiling is on.
+template <class F>
+hipError_t timed(const char* name, hipStream_t st, F&& launch) {
+  if (!g_prof) return launch();
+  ProfRec r{name, pool_event(), pool_event()};
+  if (r.a) (void)hipEventRecord(r.a, st);
+  const hipError_t e = launch();
+  if (r.b) (void)hipEventRecord(r.b, st);
+  if (r.a && r.b) g_recs.push_back(r);
+  return e;
+}
+
 // ---------------------------------------------------------------- attention policy
 struct MlaPlan {
   int ht;          // head tiles per workgroup
@@ -85,26 +115,25 @@ struct MlaPlan {
 };
 
 MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
+  // A CU sustains only ~25 GB/s of gathers and a lone wave far less, so decode spreads rows
+  // AND partial outputs over every CU: one 16-head tile per 4-wave workgroup (the waves split
+  // the value columns) and about one workgroup per CU. Prefill rows have no split; all heads
+  // of a row share each gathered block.
   MlaPlan p;
   const int tiles = H / 16;
-  if (!decode) {
+  const int nblk = std::max(1, (ntot + 31) / 32);
+  int s = 1;
+  if (decode) {
+    p.ht = 1;
+    const int64_t base = (int64_t)T * tiles;
+    s = (int)std::min<int64_t>((256 + base - 1) / base, nblk);
+    s = std::max(1, s);
+  } else {
     p.ht = tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1);
-    p.n_split = 1;
-    p.rows_per_split = ((ntot + 31) / 32) * 32;
-    return p;
   }
-  p.ht = 1;   // decode: one head tile per workgroup, four row streams
-  const int64_t base = (int64_t)T * tiles;
-  const int max_split = max(1, (ntot + 127) / 128);
-  int s = (int)std::max<int64_t>(1, (512 + base - 1) / base);
-  s = min(s, max_split);
-  if (base * s > kMaxCounters) s = 1;
-  int rps = (ntot + s - 1) / s;
-  rps = ((rps + 31) / 32) * 32;
-  if (rps < 32) rps = 32;
-  p.rows_per_split = rps;
-  p.n_split = max(1, (ntot + rps - 1) / rps);
-  if (p.n_split == 1) p.rows_per_split = max(32, ((ntot + 31) / 32) * 32);
+  const int bps = (nblk + s - 1) / s;           // blocks per split
+  p.rows_per_split = bps * 32;
+  p.n_split = (nblk + bps - 1) / bps;
   return p;
 }
 
@@ -114,10 +143,25 @@ int64_t mla_ws_bytes(int T, int H, int ntot, bool decode) {
   return align256((int64_t)T * H * p.n_split * 512 * 4) + align256((int64_t)T * H * p.n_split * 8);
 }
 
+int topk_chunks_of(int n_max) { return std::max(1, (n_max + kTopkChunk - 1) / kTopkChunk); }
+
 int64_t topk_ws_bytes(int T, int n_max) {
   if (n_max <= kTopkLdsMax) return 0;
-  const int64_t rows = min(T, kMaxLongRows);
-  return 2 * align256(rows * (int64_t)n_max * 4);
+  const int64_t rows = std::min(T, kMaxLongRows);
+  const int64_t per = rows * topk_chunks_of(n_max) * (int64_t)kTopkChunk * 4;
+  return 2 * align256(per) + align256(rows * topk_chunks_of(n_max) * 8) + align256(rows * 8);
+}
+
+// carve the long-row top-k data regions (after the header) and the header's histograms
+void carve_topk(TopkArgs& a, Carve& cv, uint8_t* w, int T, int n_max) {
+  const int64_t rows = std::min(T, kMaxLongRows);
+  a.n_chunks = topk_chunks_of(n_max);
+  const int64_t per = rows * a.n_chunks * (int64_t)kTopkChunk * 4;
+  a.cand_key = reinterpret_cast<uint32_t*>(w + cv.take(per));
+  a.cand_pos = reinterpret_cast<int32_t*>(w + cv.take(per));
+  a.counts = reinterpret_cast<uint32_t*>(w + cv.take(rows * a.n_chunks * 8));
+  a.thr1 = reinterpret_cast<uint32_t*>(w + cv.take(rows * 8));
+  a.hist = reinterpret_cast<uint32_t*>(w + kOffHist);
 }
 
 int logits_ld(int n_max) { return ((max(n_max, 1) + 63) / 64) * 64; }
@@ -229,10 +273,12 @@ dsa_status run_mla(const MlaIn& m, bool decode, void* ws, size_t ws_bytes, hipSt
     Carve cv;
     a.part_o = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * m.H * p.n_split * 512 * 4));
     a.part_ml = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * m.H * p.n_split * 8));
-    a.counters = reinterpret_cast<uint32_t*>(w + kOffCtr);
   }
   int fmt = m.kv->format == DSA_KV_BF16 ? kFmtBf16 : (m.kv->format == DSA_KV_FP8_UNIFORM ? kFmtUniform : kFmtDsMla);
-  return hip_status(launch_sparse_mla(a, fmt, m.d_qk, p.ht, m.T, st));
+  dsa_status s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, m.d_qk, p.ht, m.T, st); }));
+  if (s == DSA_OK && p.n_split > 1)
+    s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, m.T, st); }));
+  return s;
 }
 
 // ---------------------------------------------------------------- top-k driver
@@ -251,9 +297,28 @@ dsa_status check_topk(const TopkIn& k) {
   if (s != DSA_OK) return s;
   if (k.topk < 1) return DSA_ERR_ARG;
   if (k.topk > 65536) return DSA_ERR_UNSUPPORTED;
+  if (k.rows->n_max > kMaxChunks * kTopkChunk) return DSA_ERR_UNSUPPORTED;
   if (k.rows->T == 0) return DSA_OK;
   if (!k.logits || !al4(k.logits) || k.ld_logits < k.rows->n_max) return DSA_ERR_ARG;
   if (!k.indices || !al4(k.indices) || k.ld_idx < k.topk || !k.lens || !al4(k.lens)) return DSA_ERR_ARG;
+  return DSA_OK;
+}
+
+// Long rows, in batches of kMaxLongRows rows: [first-digit histogram] -> filter -> finalize.
+dsa_status run_topk_long(const TopkArgs& a, const dsa_rows& r, bool hist_ready, hipStream_t st) {
+  for (int r0 = 0; r0 < r.T; r0 += kMaxLongRows) {
+    const int nb = std::min(kMaxLongRows, r.T - r0);
+    TopkArgs b = a;
+    b.logits = a.logits + (int64_t)r0 * a.ld_logits;
+    b.row_len = r.row_len + r0;
+    b.indices = a.indices + (int64_t)r0 * a.ld_idx;
+    b.lens = a.lens + r0;
+    dsa_status s = DSA_OK;
+    if (!hist_ready) s = hip_status(timed("topk_hist", st, [&] { return launch_topk_hist(b, nb, st); }));
+    if (s == DSA_OK) s = hip_status(timed("topk_filter", st, [&] { return launch_topk_filter(b, nb, st); }));
+    if (s == DSA_OK) s = hip_status(timed("topk_finalize", st, [&] { return launch_topk_finalize(b, nb, st); }));
+    if (s != DSA_OK) return s;
+  }
   return DSA_OK;
 }
 
@@ -272,31 +337,13 @@ dsa_status run_topk(const TopkIn& k, bool hist_ready, void* ws, size_t ws_bytes,
   a.indices = k.indices;
   a.ld_idx = k.ld_idx;
   a.lens = k.lens;
-  if (r.n_max <= kTopkLdsMax) return hip_status(launch_topk_lds(a, r.T, st));
+  if (r.n_max <= kTopkLdsMax)
+    return hip_status(timed("topk_lds", st, [&] { return launch_topk_lds(a, r.T, st); }));
   const int64_t need = kHeaderBytes + topk_ws_bytes(r.T, r.n_max);
   if (!ws || (int64_t)ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
-  uint8_t* w = static_cast<uint8_t*>(ws);
   Carve cv;
-  const int64_t rows_b = min(r.T, kMaxLongRows);
-  a.cand_key = reinterpret_cast<uint32_t*>(w + cv.take(rows_b * (int64_t)r.n_max * 4));
-  a.cand_pos = reinterpret_cast<int32_t*>(w + cv.take(rows_b * (int64_t)r.n_max * 4));
-  a.ctl = reinterpret_cast<TopkCtl*>(w + kOffCtl);
-  a.hist = reinterpret_cast<uint32_t*>(w + kOffHist);
-  for (int r0 = 0; r0 < r.T; r0 += kMaxLongRows) {
-    const int nb = min(kMaxLongRows, r.T - r0);
-    TopkArgs b = a;
-    b.logits = k.logits + (int64_t)r0 * k.ld_logits;
-    b.row_len = r.row_len + r0;
-    b.indices = k.indices + (int64_t)r0 * k.ld_idx;
-    b.lens = k.lens + r0;
-    if (!hist_ready) {
-      dsa_status s = hip_status(launch_topk_hist(b, nb, st));
-      if (s != DSA_OK) return s;
-    }
-    dsa_status s = hip_status(launch_topk_filter(b, nb, st));
-    if (s != DSA_OK) return s;
-  }
-  return DSA_OK;
+  carve_topk(a, cv, static_cast<uint8_t*>(ws), r.T, r.n_max);
+  return run_topk_long(a, r, hist_ready, st);
 }
 
 // ---------------------------------------------------------------- scores driver
@@ -353,7 +400,9 @@ dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
   a.logits = s.logits;
   a.ld_logits = s.ld_logits;
   a.hist = hist;
-  return hip_status(launch_index_scores(a, s.di, s.keys->dtype == DSA_KEY_FP8, hist != nullptr, r.T, st));
+  return hip_status(timed(hist ? "index_scores_hist" : "index_scores", st, [&] {
+    return launch_index_scores(a, s.di, s.keys->dtype == DSA_KEY_FP8, hist != nullptr, r.T, st);
+  }));
 }
 
 }  // namespace
@@ -467,7 +516,7 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
   dsa_status s = check_rows(rows);
   if (s != DSA_OK) return s;
   if (topk < 1) return DSA_ERR_ARG;
-  if (topk > 65536) return DSA_ERR_UNSUPPORTED;
+  if (topk > 65536 || rows->n_max > kMaxChunks * kTopkChunk) return DSA_ERR_UNSUPPORTED;
   if (idx_out && (!al4(idx_out) || ld_idx_out < topk)) return DSA_ERR_ARG;
   if (lens_out && !al4(lens_out)) return DSA_ERR_ARG;
   const int T = rows->T;
@@ -517,21 +566,8 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
       a.indices = idx;
       a.ld_idx = ld_idx;
       a.lens = lens;
-      const int64_t rows_b = min(T, kMaxLongRows);
-      a.cand_key = reinterpret_cast<uint32_t*>(wsb + cv.take(rows_b * (int64_t)rows->n_max * 4));
-      a.cand_pos = reinterpret_cast<int32_t*>(wsb + cv.take(rows_b * (int64_t)rows->n_max * 4));
-      a.ctl = reinterpret_cast<TopkCtl*>(wsb + kOffCtl);
-      a.hist = reinterpret_cast<uint32_t*>(wsb + kOffHist);
-      for (int r0 = 0; r0 < T && s == DSA_OK; r0 += kMaxLongRows) {
-        const int nb = min(kMaxLongRows, T - r0);
-        TopkArgs b = a;
-        b.logits = logits + (int64_t)r0 * ld;
-        b.row_len = rows->row_len + r0;
-        b.indices = idx + (int64_t)r0 * ld_idx;
-        b.lens = lens + r0;
-        if (!fuse_hist) s = hip_status(launch_topk_hist(b, nb, st));
-        if (s == DSA_OK) s = hip_status(launch_topk_filter(b, nb, st));
-      }
+      carve_topk(a, cv, wsb, T, rows->n_max);
+      s = run_topk_long(a, *rows, fuse_hist, st);
     }
     if (s != DSA_OK) return s;
   }
@@ -562,11 +598,50 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
   if (p.n_split > 1) {
     a.part_o = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * H * p.n_split * 512 * 4));
     a.part_ml = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * H * p.n_split * 8));
-    a.counters = reinterpret_cast<uint32_t*>(wsb + kOffCtr);
     if ((size_t)cv.off > ws_bytes) return DSA_ERR_WORKSPACE;
   }
   const int fmt = kv->format == DSA_KV_BF16 ? kFmtBf16 : (kv->format == DSA_KV_FP8_UNIFORM ? kFmtUniform : kFmtDsMla);
-  return hip_status(launch_sparse_mla(a, fmt, d_qk, p.ht, T, st));
+  s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, d_qk, p.ht, T, st); }));
+  if (s == DSA_OK && p.n_split > 1)
+    s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, T, st); }));
+  return s;
+}
+
+dsa_status dsa_profile_enable(int32_t on) {
+  g_prof = on != 0;
+  return DSA_OK;
+}
+
+int32_t dsa_profile_collect(dsa_kernel_time* out, int32_t max_entries) {
+  if (!out || max_entries < 0) return DSA_ERR_ARG;
+  int32_t n = 0;
+  dsa_status st = DSA_OK;
+  for (const ProfRec& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = DSA_ERR_HIP;
+    } else {
+      int32_t i = 0;
+      while (i < n && strncmp(out[i].name, r.name, sizeof(out[i].name)) != 0) ++i;
+      if (i == n && n < max_entries) {
+        memset(&out[n], 0, sizeof(out[n]));
+        strncpy(out[n].name, r.name, sizeof(out[n].name) - 1);
+        out[n].min_ms = ms;
+        out[n].max_ms = ms;
+        ++n;
+      }
+      if (i < n) {
+        out[i].count += 1;
+        out[i].total_ms += ms;
+        out[i].min_ms = std::min(out[i].min_ms, ms);
+        out[i].max_ms = std::max(out[i].max_ms, ms);
+      }
+    }
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return st == DSA_OK ? n : (int32_t)st;
 }
 
 }  // extern "C"

@@ -6,12 +6,16 @@
 // index_k_cache of the decode top-k wrapper in that PR's review, bf16, or fp8 e4m3 with an
 // fp32 per-token scale.)
 //
-// A wave owns one tile of 64 consecutive candidate positions of one query row. The row's
-// query heads are the MFMA A operand (M = 16 heads per tile, held in registers for the whole
-// wave), the 64 keys are four B operands of 16 keys each (K = 32 dims per MFMA), loaded
-// straight from HBM into registers: lane l reads 16 (bf16) or 8 (fp8) contiguous bytes of key
-// l%16, so each load instruction covers 64 contiguous bytes of 16 rows and a tile is one
-// contiguous 16 KiB (bf16, page 64) or 8 KiB (fp8) burst. The epilogue applies ReLU and the
+// A CU sustains only ~25 GB/s of HBM reads, so the stream is spread as one 8-wave workgroup
+// per CU and the row's query heads are fetched once per workgroup. A wave owns tiles of 64
+// consecutive candidate positions of one query row. The row's query
+// heads are the MFMA A operand (M = 16 heads per tile; staged once per workgroup through LDS,
+// then held in registers), the 64 keys are four B operands of 16 keys each (K = 32 dims per
+// MFMA), loaded straight from HBM into registers: lane l reads 16 (bf16) or 8 (fp8)
+// contiguous bytes of key l%16, so each load instruction covers 64 contiguous bytes of 16 rows
+// and a tile is one contiguous 16 KiB (bf16, page 64) or 8 KiB (fp8) burst. The query heads
+// are requested first (every MFMA waits on them), the first tile's keys right after, and
+// every later tile is prefetched one step ahead. The epilogue applies ReLU and the
 // head weights in fp32 on the accumulators, reduces the four lane groups with a 3-shuffle
 // reduce-scatter so lane l ends up with candidate s0 + l, and stores one coalesced 256-byte
 // row segment. Optionally the same pass counts a 4096-bin histogram of the top 12 bits of
@@ -21,9 +25,54 @@
 
 namespace dsa {
 
+// Keys of one 64-candidate tile as four B operands (16 keys each); fp8 keys are widened to
+// bf16 (exact) and their per-token scale kept for the epilogue.
+template <int DI, bool FP8>
+struct KeyTile {
+  static constexpr int KB = DI / 32;
+  u32x4_t b[4][KB];
+  float sc[4];
+
+  __device__ __forceinline__ void load(const ScoreArgs& a, int b_req, int s0, int n, int g, int c) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int pos = min(s0 + 16 * st + c, n - 1);
+      const int64_t slot = slot_of(a.pg, b_req, pos);
+      if constexpr (!FP8) {
+        const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.keys) + slot * DI + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) b[st][kb] = *reinterpret_cast<const u32x4_t*>(kp + 32 * kb);
+        sc[st] = 1.0f;
+      } else {
+        const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.keys) + slot * DI + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x2_t raw = *reinterpret_cast<const u32x2_t*>(kp + 32 * kb);
+          b[st][kb] = u32x4_t{raw[0], raw[1], 0u, 0u};   // widened after the loads land
+        }
+        sc[st] = a.key_scale[slot];
+      }
+    }
+  }
+
+  __device__ __forceinline__ void widen() {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) b[st][kb] = fp8x8_to_bf16x8(u32x2_t{b[st][kb][0], b[st][kb][1]});
+    }
+  }
+};
+
+constexpr int kScoreWaves = 8;   // one 512-thread workgroup per CU: the query heads load once per CU
+constexpr int kScoreThreads = 64 * kScoreWaves;
+
 template <int DI, int MT, bool FP8, bool HIST>
-__global__ __launch_bounds__(256) void k_index_scores(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
   constexpr int KB = DI / 32;
+  constexpr int QB = 64 * DI * 2;   // bytes of the (padded) query heads of one row
+  __shared__ __align__(16) uint8_t s_q[QB];
   __shared__ uint32_t s_hist[HIST ? kHistBins : 1];
 
   const int t = blockIdx.y;
@@ -35,56 +84,54 @@ __global__ __launch_bounds__(256) void k_index_scores(ScoreArgs a) {
   int n = a.row_len[t];
   n = min(max(n, 0), a.n_max);
   const int ntiles = (n + 63) >> 6;
+  const int stride = gridDim.x * kScoreWaves;
+  int tile = blockIdx.x * kScoreWaves + wave;
 
-  if constexpr (HIST) {
-    for (int i = threadIdx.x; i < kHistBins; i += 256) s_hist[i] = 0;
-    __syncthreads();
-  }
-
-  // Query heads as A operands: qa[mt][kb] = q_idx[t, 16 mt + c, 32 kb + 8 g .. +7].
-  u32x4_t qa[MT][KB];
-  float wv[MT][4];
+  // 1. the row's query heads (everything waits on them), then 2. the first tile's keys; q is
+  // staged once per workgroup in LDS, zero-padded to 16 * MT heads
+  constexpr int QPT = (16 * MT * DI * 2 + kScoreThreads * 16 - 1) / (kScoreThreads * 16);
+  u32x4_t qv[QPT];
   {
-    const uint16_t* qrow = a.q_idx + (int64_t)t * a.ld_q;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q_idx + (int64_t)t * a.ld_q);
+    const int qbytes = a.Hi * DI * 2;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int head = 16 * mt + c;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        if (head < a.Hi)
-          qa[mt][kb] = *reinterpret_cast<const u32x4_t*>(qrow + head * DI + 32 * kb + 8 * g);
-        else
-          qa[mt][kb] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int hr = 16 * mt + 4 * g + r;   // head of accumulator row r
-        wv[mt][r] = hr < a.Hi ? a.w[(int64_t)t * a.ld_w + hr] * a.index_scale : 0.0f;
-      }
+    for (int i = 0; i < QPT; ++i) {
+      const int o = (threadIdx.x + i * kScoreThreads) * 16;
+      qv[i] = o < qbytes ? *reinterpret_cast<const u32x4_t*>(qrow + o) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-
-  for (int tile = blockIdx.x * 4 + wave; tile < ntiles; tile += gridDim.x * 4) {
-    const int s0 = tile << 6;
-    u32x4_t kbv[4][KB];
-    float ksc[4];
+  KeyTile<DI, FP8> cur;
+  if (tile < ntiles) cur.load(a, b, tile << 6, n, g, c);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int pos = min(s0 + 16 * st + c, n - 1);
-      const int64_t slot = slot_of(a.pg, b, pos);
-      if constexpr (!FP8) {
-        const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.keys) + slot * DI + 8 * g;
+  for (int i = 0; i < QPT; ++i) {
+    const int o = (threadIdx.x + i * kScoreThreads) * 16;
+    if (o < 16 * MT * DI * 2) *reinterpret_cast<u32x4_t*>(s_q + o) = qv[i];
+  }
+  float wv[MT][4];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kbv[st][kb] = *reinterpret_cast<const u32x4_t*>(kp + 32 * kb);
-        ksc[st] = 1.0f;
-      } else {
-        const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.keys) + slot * DI + 8 * g;
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          kbv[st][kb] = fp8x8_to_bf16x8(*reinterpret_cast<const u32x2_t*>(kp + 32 * kb));
-        ksc[st] = a.key_scale[slot];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int hr = 16 * mt + 4 * g + r;   // head of accumulator row r
+      wv[mt][r] = hr < a.Hi ? a.w[(int64_t)t * a.ld_w + hr] * a.index_scale : 0.0f;
     }
+  if constexpr (HIST)
+    for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) s_hist[i] = 0;
+  __syncthreads();
+  // A operands: qa[mt][kb] = q_idx[t, 16 mt + c, 32 kb + 8 g .. +7]
+  u32x4_t qa[MT][KB];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qa[mt][kb] = *reinterpret_cast<const u32x4_t*>(s_q + ((16 * mt + c) * DI + 32 * kb + 8 * g) * 2);
+
+  while (tile < ntiles) {
+    const int s0 = tile << 6;
+    const int next = tile + stride;
+    KeyTile<DI, FP8> nxt;
+    if (next < ntiles) nxt.load(a, b, next << 6, n, g, c);   // prefetch
+    cur.widen();
     float part[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -94,14 +141,14 @@ __global__ __launch_bounds__(256) void k_index_scores(ScoreArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16_16x16x32(qa[mt][kb], kbv[st][kb], acc[mt]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16_16x16x32(qa[mt][kb], cur.b[st][kb], acc[mt]);
       float p = 0.f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float x = acc[mt][r];
-          if constexpr (FP8) x *= ksc[st];
+          if constexpr (FP8) x *= cur.sc[st];
           p = fmaf(wv[mt][r], fmaxf(x, 0.0f), p);
         }
       part[st] = p;
@@ -113,20 +160,22 @@ __global__ __launch_bounds__(256) void k_index_scores(ScoreArgs a) {
     k0 += __shfl_xor(hi2 ? part[0] : part[2], 32);
     k1 += __shfl_xor(hi2 ? part[1] : part[3], 32);
     const bool hi1 = lane & 16;
-    float total = (hi1 ? k1 : k0) + __shfl_xor(hi1 ? k0 : k1, 16);
+    const float total = (hi1 ? k1 : k0) + __shfl_xor(hi1 ? k0 : k1, 16);
 
     const int s = s0 + lane;
     if (s < n) {
       a.logits[(int64_t)t * a.ld_logits + s] = total;
       if constexpr (HIST) atomicAdd(&s_hist[float_key(total) >> (32 - kHistBits)], 1u);
     }
+    cur = nxt;
+    tile = next;
   }
 
   if constexpr (HIST) {
     __syncthreads();
     if (ntiles > 0) {
       uint32_t* gh = a.hist + ((int64_t)t * kHistSlices + (blockIdx.x % kHistSlices)) * kHistBins;
-      for (int i = threadIdx.x; i < kHistBins; i += 256) {
+      for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
         const uint32_t v = s_hist[i];
         if (v) atomicAdd(gh + i, v);
       }
@@ -137,11 +186,11 @@ __global__ __launch_bounds__(256) void k_index_scores(ScoreArgs a) {
 template <int DI, int MT, bool FP8, bool HIST>
 static hipError_t launch_t(const ScoreArgs& a, int T, hipStream_t st) {
   const int ntiles = (a.n_max + 63) / 64;
-  int gx = (ntiles + 3) / 4;
-  // bound the grid: very long rows loop inside the waves, many rows keep x small
-  const int cap = T > 1 ? max(1, 16384 / T) : 1024;
+  int gx = (ntiles + kScoreWaves - 1) / kScoreWaves;
+  // about one workgroup per CU in total: longer rows loop (with prefetch) inside the waves
+  const int cap = max(1, 256 / T);
   gx = max(1, min(gx, cap));
-  hipLaunchKernelGGL((k_index_scores<DI, MT, FP8, HIST>), dim3(gx, T), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_index_scores<DI, MT, FP8, HIST>), dim3(gx, T), dim3(kScoreThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -10,13 +10,20 @@ namespace dsa {
 // top-k radix: first digit = top 12 bits of the order-preserving key
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
-// copies of each row's global first-digit histogram, spread over workgroups to thin out
-// same-address atomics
-constexpr int kHistSlices = 4;
+// copies of each row's global first-digit histogram (more copies thin out same-address
+// atomics in the score kernel but cost every filter workgroup a longer read)
+constexpr int kHistSlices = 1;
 // rows with at most this many candidates are selected by one workgroup entirely in LDS
 constexpr int kTopkLdsMax = 16384;
 // candidates per workgroup in the multi-workgroup (long row) select
 constexpr int kTopkChunk = 4096;
+// the finalize step keeps the threshold bin's candidates in LDS when there are at most this
+// many (else it streams them from the workspace)
+constexpr int kTopkCandLds = 8192;
+// the threshold sub-bin it resolves in LDS holds at most this many keys (else streamed)
+constexpr int kTopkSubLds = 2048;
+// chunks per row (long rows up to kMaxChunks * kTopkChunk = 4M candidates)
+constexpr int kMaxChunks = 1024;
 
 struct ScoreArgs {
   const uint16_t* q_idx;   // bf16 [T, Hi, di]
@@ -40,14 +47,6 @@ struct ScoreArgs {
 hipError_t launch_index_scores(const ScoreArgs& a, int di, bool fp8, bool hist, int T,
                                hipStream_t st);
 
-// Per-row control words of the long-row select (zero at rest).
-struct TopkCtl {
-  uint32_t sel;     // selected so far (first-digit bins above the threshold bin)
-  uint32_t cand;    // candidates in the threshold bin
-  uint32_t done;    // finished workgroups
-  uint32_t _pad;
-};
-
 struct TopkArgs {
   const float* logits;
   int64_t ld_logits;
@@ -57,16 +56,19 @@ struct TopkArgs {
   int32_t* indices;
   int64_t ld_idx;
   int32_t* lens;
-  // long-row path workspace
-  TopkCtl* ctl;            // [T]
-  uint32_t* hist;          // [T, kHistSlices, kHistBins]
-  uint32_t* cand_key;      // [T, n_max]
-  int32_t* cand_pos;       // [T, n_max]
+  // long-row path workspace (per row: n_chunks = ceil(n_max / kTopkChunk) chunk regions)
+  uint32_t* hist;          // [T, kHistSlices, kHistBins] first-digit histogram, zero at rest
+  uint32_t* thr1;          // [T, 2]: (first digit of the threshold, count above its bin)
+  uint32_t* cand_key;      // [T, n_chunks, kTopkChunk] threshold-bin candidates: keys
+  int32_t* cand_pos;       // and positions
+  uint32_t* counts;        // [T, n_chunks, 2]: (above the bin, in the bin) per chunk
+  int32_t n_chunks;
 };
 
 hipError_t launch_topk_lds(const TopkArgs& a, int T, hipStream_t st);
 hipError_t launch_topk_hist(const TopkArgs& a, int T, hipStream_t st);
 hipError_t launch_topk_filter(const TopkArgs& a, int T, hipStream_t st);
+hipError_t launch_topk_finalize(const TopkArgs& a, int T, hipStream_t st);
 
 enum KvFmt { kFmtBf16 = 0, kFmtUniform = 1, kFmtDsMla = 2 };
 
@@ -94,10 +96,10 @@ struct MlaArgs {
   float* lse;              // [T, H] or nullptr
   float* part_o;           // [T, H, n_split, 512]
   float* part_ml;          // [T, H, n_split, 2]
-  uint32_t* counters;      // [T, H / (16 * HT)]
 };
 
 hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T, hipStream_t st);
+hipError_t launch_mla_combine(const MlaArgs& a, int T, hipStream_t st);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 

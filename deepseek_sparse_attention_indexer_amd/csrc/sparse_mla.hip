@@ -9,19 +9,22 @@
 // original list while their rows are never read (radixark/miles PR 3608, "What", padding).
 // A second list (extra) into a second cache shares the softmax (PR 4382, two-loop layout).
 //
-// Workgroup = 4 waves. A wave owns 16 heads; HT head tiles share each gathered block, and the
-// remaining 4/HT waves form independent row streams that are merged through LDS at the end.
-// Per 32-row block a stream gathers its rows into LDS as bf16 (fp8 dequantised on the way),
-// then each wave computes
+// Workgroup = HT x WD waves sharing each gathered 32-row block: a wave owns 16 heads (one of
+// HT head tiles) and 512 / WD value columns (decode runs one head tile with WD = 4, so four
+// waves issue the gather and the PV product and the score product is repeated per wave).
+// Blocks are double-buffered in LDS: while a block is computed, the next block's list
+// entries are resolved to cache offsets and its rows stream in (bf16 rows by direct
+// global->LDS loads with every load of the block in flight; fp8 rows staged in registers and
+// dequantised to bf16 on the way). Each wave computes
 //   S^T[32 rows x 16 heads] = K Q^T   (A = rows from LDS, B = q held in registers),
 // an online softmax in base 2, and
 //   O^T[512 x 16 heads] += V^T P^T   (A = V^T read from LDS and transposed 8x8 in registers,
 //                                      B = P^T straight from S^T's accumulator layout).
 // With the 16x16x32 layout, S^T's accumulator rows (4 per lane group, two 16-row tiles) are
 // exactly the k-slots of P^T as a B operand, so P never crosses lanes.
-// Splits (decode): each workgroup covers rows_per_split entries of the row's list, writes an
-// un-normalised partial (o, m, l), and the last workgroup of the (row, head group) merges
-// them (split-KV + LSE merge of PR 664).
+// The softmax runs in base 2 with a lazily rescaled running max. Splits (decode): each
+// workgroup covers rows_per_split entries of the row's list and writes an un-normalised
+// partial (o, m, l); k_mla_combine merges them (split-KV + LSE merge of PR 664).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,365 +40,419 @@ struct RowGeom {
   static constexpr int kUnits = FMT == kFmtBf16 ? DQK / 8 : (FMT == kFmtUniform ? DQK / 16 : 36);
 };
 
-// One unit of a gathered row: global -> (dequant) -> LDS bf16.
+// fp8 rows: one 16-byte unit of a row is loaded (with its scale) into registers first, then
+// dequantised to bf16 and stored to LDS, so that every load of a block is in flight at once.
+struct RawUnit {
+  u32x4_t v;
+  float sc;
+};
+
+// Byte offsets of a cache row, resolved once per row: the data (and for fp8 the scales).
+struct RowOff {
+  int64_t data;
+  int64_t scale;
+};
+
 template <int FMT, int DQK>
-__device__ __forceinline__ void stage_unit(const KvDev& kv, int64_t slot, bool valid, int u,
-                                           uint16_t* lrow) {
+__device__ __forceinline__ RowOff row_offsets(const KvDev& kv, int64_t slot) {
+  RowOff o;
   if constexpr (FMT == kFmtBf16) {
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (valid) v = *reinterpret_cast<const u32x4_t*>(kv.data + (slot * DQK + 8 * u) * 2);
-    *reinterpret_cast<u32x4_t*>(lrow + 8 * u) = v;
+    o.data = slot * DQK * 2;
+    o.scale = 0;
   } else if constexpr (FMT == kFmtUniform) {
-    u32x4_t lo = u32x4_t{0u, 0u, 0u, 0u}, hi = lo;
-    if (valid) {
-      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kv.data + slot * DQK + 16 * u);
-      const float sc = kv.scales[slot * (DQK / 64) + (16 * u) / 64];
-      float f[16];
-      fp8x4_to_f32(raw[0], f);
-      fp8x4_to_f32(raw[1], f + 4);
-      fp8x4_to_f32(raw[2], f + 8);
-      fp8x4_to_f32(raw[3], f + 12);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = pack_bf16_rne(f[2 * i] * sc, f[2 * i + 1] * sc);
-        hi[i] = pack_bf16_rne(f[8 + 2 * i] * sc, f[8 + 2 * i + 1] * sc);
-      }
-    }
-    *reinterpret_cast<u32x4_t*>(lrow + 16 * u) = lo;
-    *reinterpret_cast<u32x4_t*>(lrow + 16 * u + 8) = hi;
-  } else {  // fp8_ds_mla
+    o.data = slot * DQK;
+    o.scale = slot * (DQK / 64) * 4;
+  } else {  // fp8_ds_mla: page-planar layout
     const int P = kv.pg.page;
     int64_t page, pos;
     if (kv.pg.page_shift >= 0) { page = slot >> kv.pg.page_shift; pos = slot & (P - 1); }
     else { page = slot / P; pos = slot - page * P; }
-    const uint8_t* pbase = kv.data + page * (int64_t)P * 584;
-    const uint8_t* tok = pbase + pos * 576;
-    if (u < 28) {
-      u32x4_t lo = u32x4_t{0u, 0u, 0u, 0u}, hi = lo;
-      if (valid) {
-        const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(tok + 16 * u);
-        const float sc = ue8m0_scale(pbase[(int64_t)P * 576 + pos * 8 + (u >> 2)]);
-        float f[16];
-        fp8x4_to_f32(raw[0], f);
-        fp8x4_to_f32(raw[1], f + 4);
-        fp8x4_to_f32(raw[2], f + 8);
-        fp8x4_to_f32(raw[3], f + 12);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo[i] = pack_bf16_exact(f[2 * i] * sc, f[2 * i + 1] * sc);
-          hi[i] = pack_bf16_exact(f[8 + 2 * i] * sc, f[8 + 2 * i + 1] * sc);
-        }
-      }
-      *reinterpret_cast<u32x4_t*>(lrow + 16 * u) = lo;
-      *reinterpret_cast<u32x4_t*>(lrow + 16 * u + 8) = hi;
-    } else {
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (valid) v = *reinterpret_cast<const u32x4_t*>(tok + 448 + 16 * (u - 28));
-      *reinterpret_cast<u32x4_t*>(lrow + 448 + 8 * (u - 28)) = v;
-    }
+    const int64_t pbase = page * (int64_t)P * 584;
+    o.data = pbase + pos * 576;
+    o.scale = pbase + (int64_t)P * 576 + pos * 8;
   }
+  return o;
 }
 
-template <int FMT, int DQK, int HT, bool SPLIT>
-__global__ __launch_bounds__(256) void k_sparse_mla(MlaArgs a) {
-  constexpr int RS = 4 / HT;
+template <int FMT, int DQK>
+__device__ __forceinline__ RawUnit load_unit(const uint8_t* data, const uint8_t* scales, RowOff off,
+                                             bool valid, int u) {
+  RawUnit r;
+  r.v = u32x4_t{0u, 0u, 0u, 0u};
+  r.sc = 0.f;
+  if (!valid) return r;
+  if constexpr (FMT == kFmtUniform) {
+    r.v = *reinterpret_cast<const u32x4_t*>(data + off.data + 16 * u);
+    r.sc = *reinterpret_cast<const float*>(scales + off.scale + (u / 4) * 4);
+  } else {  // fp8_ds_mla
+    if (u < 28) {
+      r.v = *reinterpret_cast<const u32x4_t*>(data + off.data + 16 * u);
+      r.sc = ue8m0_scale(data[off.scale + (u >> 2)]);
+    } else {
+      r.v = *reinterpret_cast<const u32x4_t*>(data + off.data + 448 + 16 * (u - 28));
+    }
+  }
+  return r;
+}
+
+template <int FMT, int DQK>
+__device__ __forceinline__ void store_unit(const RawUnit& r, int u, uint16_t* lrow) {
+  const bool rope = FMT == kFmtDsMla && u >= 28;
+  if (rope) {   // RoPE columns of fp8_ds_mla rows are bf16 already
+    *reinterpret_cast<u32x4_t*>(lrow + 448 + 8 * (u - 28)) = r.v;
+    return;
+  }
+  float f[16];
+  fp8x4_to_f32(r.v[0], f);
+  fp8x4_to_f32(r.v[1], f + 4);
+  fp8x4_to_f32(r.v[2], f + 8);
+  fp8x4_to_f32(r.v[3], f + 12);
+  u32x4_t lo, hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (FMT == kFmtUniform) {   // arbitrary fp32 scale: round to bf16
+      lo[i] = pack_bf16_rne(f[2 * i] * r.sc, f[2 * i + 1] * r.sc);
+      hi[i] = pack_bf16_rne(f[8 + 2 * i] * r.sc, f[8 + 2 * i + 1] * r.sc);
+    } else {                              // power-of-two scale: exact in bf16
+      lo[i] = pack_bf16_exact(f[2 * i] * r.sc, f[2 * i + 1] * r.sc);
+      hi[i] = pack_bf16_exact(f[8 + 2 * i] * r.sc, f[8 + 2 * i + 1] * r.sc);
+    }
+  }
+  *reinterpret_cast<u32x4_t*>(lrow + 16 * u) = lo;
+  *reinterpret_cast<u32x4_t*>(lrow + 16 * u + 8) = hi;
+}
+
+template <int FMT, int DQK, int HT, int WD, bool SPLIT>
+__global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
+  constexpr int NW = HT * WD;                 // waves: HT head tiles x WD value-column slices
+  constexpr int NT = 64 * NW;
+  constexpr int GD = 4 / WD;                  // 128-column groups of the value a wave owns
   constexpr int KS = DQK / 32;
   constexpr int RE = RowGeom<FMT, DQK>::kElems;
   constexpr int UN = RowGeom<FMT, DQK>::kUnits;
-  constexpr int NLANE = 64 * HT;                 // lanes that gather one stream's block
-  __shared__ __align__(16) uint16_t s_rows[RS][kNB][RE];
-  __shared__ int64_t s_slot[RS][kNB];
-  __shared__ int32_t s_info[RS][kNB];            // bit0: valid, bit1: extra list
-  __shared__ uint32_t s_flag;
+  __shared__ __align__(16) uint16_t s_rows[2][kNB][RE];   // double-buffered gathered block
+  __shared__ int64_t s_off[2][kNB];                        // byte offset of each row's data
+  __shared__ int64_t s_soff[2][kNB];                       // and of its scales (fp8)
+  __shared__ int32_t s_info[2][kNB];                       // bit0: valid, bit1: extra list
 
   const int t = blockIdx.z;
   const int hg = blockIdx.y;
   const int split = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int ht = wave % HT;
-  const int rs = wave / HT;
+  const int ht = wave % HT;                   // head tile of this wave
+  const int gd0 = (wave / HT) * GD;           // first 128-column group of this wave
   const int g = lane >> 4;
   const int c = lane & 15;
   const int b = min(max(a.row_req ? a.row_req[t] : t, 0), a.n_req - 1);
   const int head0 = (hg * HT + ht) * 16;
+  // The kernel-argument arrays are never indexed with a per-lane value (that becomes a
+  // vector load from kernarg memory plus a full vmcnt wait, serialising the gathers).
+  const KvDev kv0 = a.kv[0], kv1 = a.kv[1];
+  const int32_t* const idx0 = a.idx[0];
+  const int32_t* const idx1 = a.idx[1];
+  const int64_t ld0 = a.ld_idx[0], ld1 = a.ld_idx[1];
   const int n0 = a.n_idx[0];
   const int ntot = n0 + a.n_idx[1];
   const int u_begin = split * a.rows_per_split;
   const int u_end = min(ntot, u_begin + a.rows_per_split);
   const int nblk = u_end > u_begin ? (u_end - u_begin + kNB - 1) / kNB : 0;
-  const int iters = (nblk + RS - 1) / RS;
 
-  u32x4_t qb[KS];
-  {
-    const uint16_t* qp = a.q + (int64_t)t * a.ld_q + (int64_t)(head0 + c) * DQK + 8 * g;
-#pragma unroll
-    for (int kb = 0; kb < KS; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(qp + 32 * kb);
-  }
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4_t o[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[i][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int it = 0; it < iters; ++it) {
-    const int blk = it * RS + rs;
-    const bool active = blk < nblk;
-    const int sl = ht * 64 + lane;
-    // ---- phase A: resolve the block's list entries to cache slots
-    if (active && sl < kNB) {
-      const int uu = u_begin + blk * kNB + sl;
+  // resolve block `blk`'s list entries to row offsets (threads 0..31)
+  auto resolve = [&](int blk, int buf) {
+    if (threadIdx.x < kNB) {
+      const int uu = u_begin + blk * kNB + threadIdx.x;
       int info = 0;
-      int64_t slot = 0;
+      RowOff off{0, 0};       // masked rows read row 0 (finite data) and are masked later
       if (uu < u_end) {
-        const int li = uu < n0 ? 0 : 1;
-        const int j = uu - (li ? n0 : 0);
-        const int e = a.idx[li][(int64_t)t * a.ld_idx[li] + j];
+        const bool li = uu >= n0;
+        const int e = li ? idx1[(int64_t)t * ld1 + (uu - n0)] : idx0[(int64_t)t * ld0 + uu];
         if (e >= 0) {
-          slot = slot_of(a.kv[li].pg, b, e);
-          info = 1 | (li << 1);
+          off = li ? row_offsets<FMT, DQK>(kv1, slot_of(kv1.pg, b, e))
+                   : row_offsets<FMT, DQK>(kv0, slot_of(kv0.pg, b, e));
+          info = 1 | ((int)li << 1);
         }
       }
-      s_slot[rs][sl] = slot;
-      s_info[rs][sl] = info;
+      s_off[buf][threadIdx.x] = off.data;
+      s_soff[buf][threadIdx.x] = off.scale;
+      s_info[buf][threadIdx.x] = info;
     }
-    __syncthreads();
-    // ---- phase B: gather + dequantise into LDS
-    if (active) {
+  };
+  // gather block rows into LDS: bf16 by direct global->LDS loads (asynchronous, completes at
+  // the next vmcnt wait), fp8 staged through registers and dequantised (synchronous)
+  auto gather = [&](int buf) {
+    if constexpr (FMT == kFmtBf16) {
+      // lane l of instruction ins fills 16-byte slot 64 * ins + l of the padded block; the pad
+      // slot of each row re-reads the row's first 16 bytes
+      constexpr int RW = DQK / 8 + 1;
+      constexpr int SLOTS = kNB * RW;
+      constexpr int NINS = (SLOTS + 63) / 64;
+      auto* lbase = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(
+          reinterpret_cast<uintptr_t>(&s_rows[buf][0][0]) & 0xffffffffu);
+      for (int ins = wave; ins < NINS; ins += NW) {
+        const int j = ins * 64 + lane;
+        if (j < SLOTS) {
+          const int r = j / RW;
+          int cc = j - r * RW;
+          cc = cc == RW - 1 ? 0 : cc;
+          const uint8_t* src = ((s_info[buf][r] & 2) ? kv1.data : kv0.data) + s_off[buf][r] + 16 * cc;
+          __builtin_amdgcn_global_load_lds(src, lbase + ins * 1024, 16, 0, 0);
+        }
+      }
+    } else {
       constexpr int TOT = kNB * UN;
-      constexpr int BATCH = 4;
-      for (int u0 = sl; u0 < TOT; u0 += NLANE * BATCH) {
+      constexpr int QN = (TOT + NT - 1) / NT;          // units per thread
+      constexpr int NBAT = (QN + 5) / 6;               // at most 6 units in flight (registers)
+      constexpr int QB = (QN + NBAT - 1) / NBAT;
+#pragma unroll 1
+      for (int bt = 0; bt < NBAT; ++bt) {
+        RawUnit raw[QB];
 #pragma unroll
-        for (int q = 0; q < BATCH; ++q) {
-          const int uid = u0 + q * NLANE;
-          if (uid < TOT) {
+        for (int q = 0; q < QB; ++q) {
+          const int uid = threadIdx.x + (bt * QB + q) * NT;
+          if (bt * QB + q < QN && uid < TOT) {
             const int r = uid / UN;
-            const int u = uid - r * UN;
-            const int info = s_info[rs][r];
-            stage_unit<FMT, DQK>(a.kv[(info >> 1) & 1], s_slot[rs][r], info & 1, u, &s_rows[rs][r][0]);
+            const int info = s_info[buf][r];
+            const bool x = info & 2;
+            raw[q] = load_unit<FMT, DQK>(x ? kv1.data : kv0.data,
+                                         reinterpret_cast<const uint8_t*>(x ? kv1.scales : kv0.scales),
+                                         RowOff{s_off[buf][r], s_soff[buf][r]}, info & 1, uid - r * UN);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const int uid = threadIdx.x + (bt * QB + q) * NT;
+          if (bt * QB + q < QN && uid < TOT) {
+            const int r = uid / UN;
+            store_unit<FMT, DQK>(raw[q], uid - r * UN, &s_rows[buf][r][0]);
           }
         }
       }
     }
+  };
+
+  // the first block's list entries go out before anything else (longest dependent chain),
+  // then the query heads, once per workgroup, through the row buffers (not yet in use)
+  if (nblk > 0) resolve(0, 0);
+  static_assert(HT * 16 * DQK * 2 <= (int)sizeof(s_rows), "q staging");
+  {
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)t * a.ld_q + (int64_t)(hg * HT * 16) * DQK);
+    uint8_t* qdst = reinterpret_cast<uint8_t*>(&s_rows[0][0][0]);
+    for (int o = threadIdx.x * 16; o < HT * 16 * DQK * 2; o += NT * 16)
+      *reinterpret_cast<u32x4_t*>(qdst + o) = *reinterpret_cast<const u32x4_t*>(qsrc + o);
+  }
+  __syncthreads();
+  u32x4_t qb[KS];
+  {
+    const uint16_t* qp = &s_rows[0][0][0] + (ht * 16 + c) * DQK + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(qp + 32 * kb);
+  }
+  float m_run = -INFINITY;   // running max (base-2 units) of head c; rescaled lazily
+  float l_run = 0.f;         // lane-partial sum of exp2(s - m_run)
+  f32x4_t o[GD][8];
+#pragma unroll
+  for (int i = 0; i < GD; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[i][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  __syncthreads();   // q is in registers before the first rows land in the buffers
+  if (nblk > 0) gather(0);
+  for (int it = 0; it < nblk; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < nblk) resolve(it + 1, cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);      // this block's rows (and the next block's offsets)
     __syncthreads();
-    // ---- phase C: S^T = K Q^T, online softmax, O^T += V^T P^T
-    if (active) {
-      f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-      const uint16_t* r0 = &s_rows[rs][c][8 * g];
-      const uint16_t* r1 = &s_rows[rs][16 + c][8 * g];
+    if (it + 1 < nblk) gather(cur ^ 1);  // overlaps the compute below (bf16)
+
+    // ---- S^T = K Q^T
+    f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    const uint16_t* r0 = &s_rows[cur][c][8 * g];
+    const uint16_t* r1 = &s_rows[cur][16 + c][8 * g];
 #pragma unroll
-      for (int kb = 0; kb < KS; ++kb) {
-        s0 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r0 + 32 * kb), qb[kb], s0);
-        s1 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r1 + 32 * kb), qb[kb], s1);
-      }
-      float p[8];
-      float mx = -INFINITY;
+    for (int kb = 0; kb < KS; ++kb) {
+      s0 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r0 + 32 * kb), qb[kb], s0);
+      s1 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r1 + 32 * kb), qb[kb], s1);
+    }
+    // ---- online softmax (base 2); the accumulators are rescaled only when some head's max
+    // grows by more than 2^8, so exp2(s - m_run) stays <= 256
+    float p[8];
+    float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x0 = (s_info[rs][4 * g + r] & 1) ? s0[r] * a.scale_log2 : -INFINITY;
-        const float x1 = (s_info[rs][16 + 4 * g + r] & 1) ? s1[r] * a.scale_log2 : -INFINITY;
-        p[r] = x0;
-        p[4 + r] = x1;
-        mx = fmaxf(mx, fmaxf(x0, x1));
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = (s_info[cur][4 * g + r] & 1) ? s0[r] * a.scale_log2 : -INFINITY;
+      const float x1 = (s_info[cur][16 + 4 * g + r] & 1) ? s1[r] * a.scale_log2 : -INFINITY;
+      p[r] = x0;
+      p[4 + r] = x1;
+      mx = fmaxf(mx, fmaxf(x0, x1));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run + 8.f)) {
       const float m_new = fmaxf(m_run, mx);
-      const bool none = m_new == -INFINITY;
-      const float alpha = none ? 1.f : exp2f(m_run - m_new);
-      float psum = 0.f;
+      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      if (m_run != -INFINITY || __any(l_run != 0.f)) {   // nothing to rescale before the first rows
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = none ? 0.f : exp2f(p[i] - m_new);
-        psum += p[i];
+        for (int i = 0; i < GD; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[i][e] *= alpha;
       }
-      l_run = l_run * alpha + psum;
       m_run = m_new;
+    }
+    const bool none = m_run == -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) {
+      p[i] = none ? 0.f : exp2f(p[i] - m_run);
+      l_run += p[i];
+    }
+    u32x4_t pb;
+    pb[0] = pack_bf16_rne(p[0], p[1]);
+    pb[1] = pack_bf16_rne(p[2], p[3]);
+    pb[2] = pack_bf16_rne(p[4], p[5]);
+    pb[3] = pack_bf16_rne(p[6], p[7]);
+    // ---- O^T += V^T P^T over this wave's value columns; V^T tiles come from 8 rows x 8
+    // consecutive columns, transposed in registers
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[i][e] *= alpha;
-      u32x4_t pb;
-      pb[0] = pack_bf16_rne(p[0], p[1]);
-      pb[1] = pack_bf16_rne(p[2], p[3]);
-      pb[2] = pack_bf16_rne(p[4], p[5]);
-      pb[3] = pack_bf16_rne(p[6], p[7]);
+    for (int i = 0; i < GD; ++i) {
+      const int gd = gd0 + i;
+      u32x4_t vr[8];
 #pragma unroll
-      for (int gd = 0; gd < 4; ++gd) {
-        u32x4_t vr[8];
+      for (int j = 0; j < 4; ++j) {
+        vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * gd + 8 * c]);
+        vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * gd + 8 * c]);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[rs][4 * g + j][128 * gd + 8 * c]);
-          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[rs][16 + 4 * g + j][128 * gd + 8 * c]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t av;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          u32x4_t av;
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) av[pp] = __builtin_amdgcn_perm(vr[2 * pp + 1][w], vr[2 * pp][w], sel);
-          o[gd][e] = mfma_bf16_16x16x32(av, pb, o[gd][e]);
-        }
+        for (int pp = 0; pp < 4; ++pp) av[pp] = __builtin_amdgcn_perm(vr[2 * pp + 1][w], vr[2 * pp][w], sel);
+        o[i][e] = mfma_bf16_16x16x32(av, pb, o[i][e]);
       }
     }
-    __syncthreads();
+    __syncthreads();   // block `cur` is refilled two iterations from now
   }
 
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
-  // ---- merge the row streams of each head tile (LDS, reusing the row buffers)
-  if constexpr (RS > 1) {
-    constexpr int STRIDE = 4 * 8 * 4 * 64 + 32;
-    static_assert((RS - 1) * HT * STRIDE * 4 <= (int)sizeof(s_rows), "merge scratch");
-    float* scratch = reinterpret_cast<float*>(&s_rows[0][0][0]);
-    if (rs > 0) {
-      float* dst = scratch + ((rs - 1) * HT + ht) * STRIDE;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[((i * 8 + e) * 4 + r) * 64 + lane] = o[i][e][r];
-      if (g == 0) {
-        dst[8192 + c] = m_run;
-        dst[8192 + 16 + c] = l_run;
-      }
-    }
-    __syncthreads();
-    if (rs == 0) {
-#pragma unroll 1
-      for (int q = 1; q < RS; ++q) {
-        const float* src = scratch + ((q - 1) * HT + ht) * STRIDE;
-        const float mq = src[8192 + c];
-        const float lq = src[8192 + 16 + c];
-        const float m_new = fmaxf(m_run, mq);
-        const bool none = m_new == -INFINITY;
-        const float a0 = none ? 0.f : exp2f(m_run - m_new);
-        const float aq = none ? 0.f : exp2f(mq - m_new);
-        l_run = l_run * a0 + lq * aq;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              o[i][e][r] = o[i][e][r] * a0 + src[((i * 8 + e) * 4 + r) * 64 + lane] * aq;
-      }
-    }
-  }
-
   const int head = head0 + c;
   if constexpr (!SPLIT) {
-    if (rs == 0) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)head * kDV;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)head * kDV;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < GD; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          u32x4_t v;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2)
-            v[e2] = pack_bf16_rne(o[i][2 * e2][r] * inv, o[i][2 * e2 + 1][r] * inv);
-          *reinterpret_cast<u32x4_t*>(op + 128 * i + 32 * g + 8 * r) = v;
-        }
-      if (a.lse && g == 0)
-        a.lse[(int64_t)t * a.H + head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
-    }
-  } else {
-    if (rs == 0) {
-      float* po = a.part_o + (((int64_t)t * a.H + head) * a.n_split + split) * kDV;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          f32x4_t v0, v1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { v0[e] = o[i][e][r]; v1[e] = o[i][4 + e][r]; }
-          float* d = po + 128 * i + 32 * g + 8 * r;
-          *reinterpret_cast<f32x4_t*>(d) = v0;
-          *reinterpret_cast<f32x4_t*>(d + 4) = v1;
-        }
-      if (g == 0) {
-        float* pml = a.part_ml + (((int64_t)t * a.H + head) * a.n_split + split) * 2;
-        pml[0] = m_run;
-        pml[1] = l_run;
-      }
-    }
-    // last workgroup of this (row, head group) merges the splits
-    __threadfence();
-    __syncthreads();
-    uint32_t* ctr = a.counters + (int64_t)t * gridDim.y + hg;
-    if (threadIdx.x == 0) s_flag = (atomicAdd(ctr, 1u) == (uint32_t)a.n_split - 1) ? 1u : 0u;
-    __syncthreads();
-    if (!s_flag) return;
-    __threadfence();
-    constexpr int NH = HT * 16;
-    // 256 threads: 16 per head, each 32 consecutive columns
-    for (int hh = threadIdx.x / 16; hh < NH; hh += 16) {
-      const int hd = hg * NH + hh;
-      const int d0 = (threadIdx.x % 16) * 32;
-      const float* pml = a.part_ml + ((int64_t)t * a.H + hd) * a.n_split * 2;
-      const float* po = a.part_o + ((int64_t)t * a.H + hd) * a.n_split * kDV + d0;
-      float ms = -INFINITY;
-      for (int s = 0; s < a.n_split; ++s) ms = fmaxf(ms, pml[2 * s]);
-      float acc[32];
-#pragma unroll
-      for (int d = 0; d < 32; ++d) acc[d] = 0.f;
-      float ls = 0.f;
-      if (ms != -INFINITY) {
-        for (int s = 0; s < a.n_split; ++s) {
-          const float wgt = exp2f(pml[2 * s] - ms);
-          ls += wgt * pml[2 * s + 1];
-          const f32x4_t* src = reinterpret_cast<const f32x4_t*>(po + (int64_t)s * kDV);
-#pragma unroll
-          for (int d = 0; d < 8; ++d) {
-            const f32x4_t v = src[d];
-            acc[4 * d] += wgt * v[0];
-            acc[4 * d + 1] += wgt * v[1];
-            acc[4 * d + 2] += wgt * v[2];
-            acc[4 * d + 3] += wgt * v[3];
-          }
-        }
-      }
-      const float inv = ls > 0.f ? 1.f / ls : 0.f;
-      uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)hd * kDV + d0;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      for (int r = 0; r < 4; ++r) {
         u32x4_t v;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2)
-          v[e2] = pack_bf16_rne(acc[8 * d + 2 * e2] * inv, acc[8 * d + 2 * e2 + 1] * inv);
-        *reinterpret_cast<u32x4_t*>(op + 8 * d) = v;
+          v[e2] = pack_bf16_rne(o[i][2 * e2][r] * inv, o[i][2 * e2 + 1][r] * inv);
+        *reinterpret_cast<u32x4_t*>(op + 128 * (gd0 + i) + 32 * g + 8 * r) = v;
       }
-      if (a.lse && (threadIdx.x % 16) == 0)
-        a.lse[(int64_t)t * a.H + hd] = ls > 0.f ? (ms + __log2f(ls)) * kLn2 : -INFINITY;
+    if (a.lse && g == 0 && gd0 == 0)
+      a.lse[(int64_t)t * a.H + head] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  } else {
+    // un-normalised partial (o, m, l) of this split; k_mla_combine merges them
+    float* po = a.part_o + (((int64_t)t * a.H + head) * a.n_split + split) * kDV;
+#pragma unroll
+    for (int i = 0; i < GD; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4_t v0, v1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v0[e] = o[i][e][r]; v1[e] = o[i][4 + e][r]; }
+        float* d = po + 128 * (gd0 + i) + 32 * g + 8 * r;
+        *reinterpret_cast<f32x4_t*>(d) = v0;
+        *reinterpret_cast<f32x4_t*>(d + 4) = v1;
+      }
+    if (g == 0 && gd0 == 0) {
+      float* pml = a.part_ml + (((int64_t)t * a.H + head) * a.n_split + split) * 2;
+      pml[0] = m_run;
+      pml[1] = l_run;
     }
-    if (threadIdx.x == 0) *ctr = 0u;
   }
 }
 
-template <int FMT, int DQK, int HT>
+// Merge the split partials of each (row, head): o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s
+// (the LSE merge of PR 664). One 256-thread workgroup per (row, head, 128-column quarter):
+// eight groups of 32 threads take every eighth split (4 columns per thread), so each thread
+// keeps several splits of loads in flight and the work spreads over many CUs; the groups'
+// sums meet in LDS.
+__global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
+  constexpr int NG = 8;
+  __shared__ f32x4_t s_acc[NG][32];
+  __shared__ float s_l[NG];
+  const int t = blockIdx.z;
+  const int head = blockIdx.y;
+  const int sg = threadIdx.x >> 5;                 // split group
+  const int d0 = blockIdx.x * 128 + (threadIdx.x & 31) * 4;
+  const int S = a.n_split;
+  const float* pml = a.part_ml + ((int64_t)t * a.H + head) * S * 2;
+  const float* po = a.part_o + ((int64_t)t * a.H + head) * S * kDV + d0;
+  float ms = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) ms = fmaxf(ms, pml[2 * sp]);
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float ls = 0.f;
+  if (ms != -INFINITY) {
+    for (int sp0 = sg; sp0 < S; sp0 += NG * 8) {
+      f32x4_t v[8];
+      float m[8], l[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sp = min(sp0 + u * NG, S - 1);
+        v[u] = *reinterpret_cast<const f32x4_t*>(po + (int64_t)sp * kDV);
+        m[u] = sp0 + u * NG < S ? pml[2 * sp] : -INFINITY;
+        l[u] = pml[2 * sp + 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wgt = m[u] == -INFINITY ? 0.f : exp2f(m[u] - ms);
+        ls += wgt * l[u];
+        acc += wgt * v[u];
+      }
+    }
+  }
+  s_acc[sg][threadIdx.x & 31] = acc;
+  if ((threadIdx.x & 31) == 0) s_l[sg] = ls;
+  __syncthreads();
+  if (sg != 0) return;
+  const int ci = threadIdx.x & 31;
+  f32x4_t tot = s_acc[0][ci];
+  float lt = s_l[0];
+#pragma unroll
+  for (int q = 1; q < NG; ++q) {
+    tot += s_acc[q][ci];
+    lt += s_l[q];
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)head * kDV + d0;
+  u32x2_t vv;
+  vv[0] = pack_bf16_rne(tot[0] * inv, tot[1] * inv);
+  vv[1] = pack_bf16_rne(tot[2] * inv, tot[3] * inv);
+  *reinterpret_cast<u32x2_t*>(op) = vv;
+  if (a.lse && blockIdx.x == 0 && ci == 0)
+    a.lse[(int64_t)t * a.H + head] = lt > 0.f ? (ms + log2f(lt)) * kLn2 : -INFINITY;
+}
+
+template <int FMT, int DQK, int HT, int WD>
 static hipError_t launch_h(const MlaArgs& a, int T, hipStream_t st) {
   dim3 grid(a.n_split, a.H / (16 * HT), T);
   if (a.n_split > 1)
-    hipLaunchKernelGGL((k_sparse_mla<FMT, DQK, HT, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_sparse_mla<FMT, DQK, HT, WD, true>), grid, dim3(64 * HT * WD), 0, st, a);
   else
-    hipLaunchKernelGGL((k_sparse_mla<FMT, DQK, HT, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_sparse_mla<FMT, DQK, HT, WD, false>), grid, dim3(64 * HT * WD), 0, st, a);
   return hipGetLastError();
 }
 
+// ht head tiles per workgroup; ht == 1 splits the value columns over 4 waves instead
 template <int FMT, int DQK>
 static hipError_t launch_d(const MlaArgs& a, int ht, int T, hipStream_t st) {
-  if (ht == 4) return launch_h<FMT, DQK, 4>(a, T, st);
-  if (ht == 2) return launch_h<FMT, DQK, 2>(a, T, st);
-  return launch_h<FMT, DQK, 1>(a, T, st);
+  if (ht == 4) return launch_h<FMT, DQK, 4, 1>(a, T, st);
+  if (ht == 2) return launch_h<FMT, DQK, 2, 2>(a, T, st);
+  return launch_h<FMT, DQK, 1, 4>(a, T, st);
 }
 
 hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T, hipStream_t st) {
@@ -409,6 +466,12 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T,
     return launch_d<kFmtUniform, 512>(a, ht, T, st);
   }
   return launch_d<kFmtDsMla, 512>(a, ht, T, st);
+}
+
+hipError_t launch_mla_combine(const MlaArgs& a, int T, hipStream_t st) {
+  if (T <= 0 || a.n_split <= 1) return hipSuccess;
+  hipLaunchKernelGGL(k_mla_combine, dim3(kDV / 128, a.H, T), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace dsa

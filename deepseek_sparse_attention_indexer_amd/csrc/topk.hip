@@ -13,16 +13,31 @@
 //
 //  * k_topk_lds: one 512-thread workgroup per row, the row's keys held in LDS (<= 16K).
 //  * long rows: the first-digit histogram is built per chunk (k_topk_hist, or fused into
-//    the score kernel), k_topk_filter's workgroups each emit their chunk's candidates above
-//    the threshold bin and append the threshold bin's candidates to a list, and the last
-//    workgroup to finish (atomic ticket) resolves that list exactly and clears the row's
-//    control words and histogram for the next call.
+//    the score kernel). k_topk_filter's workgroups (one per chunk) find the threshold bin and
+//    write their chunk's threshold-bin candidates and counts. k_topk_finalize's workgroups
+//    (one per chunk again) each repeat the same exact resolution of the bin from the
+//    candidates (second digit, then the sub-bin in LDS), derive every chunk's output offsets
+//    and write their own chunk's selections. Kernel boundaries replace device-scope fences,
+//    returning atomics and single-workgroup tails, which cost microseconds each on this part.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dsa {
 
 constexpr int kNT = 512;   // threads of the select workgroups
+
+// Reserve one output slot per lane with `pred` set: one LDS atomic per wave (ballot +
+// popcount) instead of one per element, which serialises on a single address.
+__device__ __forceinline__ uint32_t wave_reserve(bool pred, uint32_t* counter) {
+  const uint64_t m = __ballot(pred);
+  if (m == 0) return 0u;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
+  base = __shfl(base, leader);
+  return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+}
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   const int lane = threadIdx.x & 63;
@@ -149,13 +164,12 @@ __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
     pos_thr = radix_select_desc(n, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
   }
   const bool all_ties = eq <= need;
-  for (int i = threadIdx.x; i < n; i += kNT) {
-    const uint32_t key = s_key[i];
-    const bool sel = key > thr || (key == thr && (all_ties || ~(uint32_t)i >= pos_thr));
-    if (sel) {
-      const uint32_t o = atomicAdd(&s_res[2], 1u);
-      if (o < (uint32_t)k) out[o] = i;
-    }
+  for (int i0 = 0; i0 < n; i0 += kNT) {       // uniform trip count: wave_reserve needs all lanes
+    const int i = i0 + threadIdx.x;
+    const uint32_t key = i < n ? s_key[i] : 0u;
+    const bool sel = i < n && (key > thr || (key == thr && (all_ties || ~(uint32_t)i >= pos_thr)));
+    const uint32_t o = wave_reserve(sel, &s_res[2]);
+    if (sel && o < (uint32_t)k) out[o] = i;
   }
   if (threadIdx.x == 0) a.lens[t] = k;
 }
@@ -182,122 +196,306 @@ __global__ __launch_bounds__(kNT) void k_topk_hist(TopkArgs a) {
   }
 }
 
+// One workgroup per (row, chunk of kTopkChunk candidates). From the row's first-digit
+// histogram it finds the threshold bin, then writes this chunk's threshold-bin candidates
+// (key, position) into the chunk's own region and the chunk's counts (above the bin, in it).
+// No returning atomics and no fences: the kernel boundary publishes everything.
 __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_w[kNT / 64];
   __shared__ uint32_t s_res[8];
 
+  constexpr int D1 = 32 - kHistBits;          // shift of the first digit
+  constexpr int per = kTopkChunk / kNT;
   const int t = blockIdx.y;
   const int k = a.topk;
   int n = a.row_len[t];
   n = min(max(n, 0), a.n_max);
-  int32_t* out = a.indices + (int64_t)t * a.ld_idx;
-  TopkCtl* ctl = a.ctl + t;
-  uint32_t* gh = a.hist + (int64_t)t * kHistSlices * kHistBins;
-  const float* row = a.logits + (int64_t)t * a.ld_logits;
   const int s0 = blockIdx.x * kTopkChunk;
   const int s1 = min(n, s0 + kTopkChunk);
-  const int per = kTopkChunk / kNT;
-
-  uint32_t d1 = 0, above1 = 0;
-  if (n <= k) {
+  int32_t* out = a.indices + (int64_t)t * a.ld_idx;
+  if (n <= k) {                                // every position is selected
     for (int s = s0 + threadIdx.x; s < s1; s += kNT) out[s] = s;
-  } else {
-    // first digit of the threshold from the row's histogram
-    for (int i = threadIdx.x; i < kHistBins; i += kNT) {
-      uint32_t v = 0;
+    return;
+  }
+  if (s0 >= n) return;
+  // this chunk's scores go out first; the histogram read overlaps them
+  uint32_t keys[per];
+  const float* row = a.logits + (int64_t)t * a.ld_logits;
 #pragma unroll
-      for (int sl = 0; sl < kHistSlices; ++sl) v += gh[sl * kHistBins + i];
-      s_hist[i] = v;
-    }
-    __syncthreads();
-    find_digit_desc(s_hist, kHistBins, (uint32_t)k, s_w, s_res);
-    d1 = s_res[0];
-    above1 = s_res[1];
-    // this chunk: emit keys above the threshold bin, append the threshold bin to the list
-    uint32_t keys[kTopkChunk / kNT];
-    uint32_t n_gt = 0, n_eq = 0;
+  for (int j = 0; j < per; ++j) {
+    const int s = s0 + j * kNT + threadIdx.x;
+    keys[j] = s < s1 ? float_key(row[s]) : 0u;
+  }
+  const uint32_t* gh = a.hist + (int64_t)t * kHistSlices * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += kNT) {
+    uint32_t v = 0;
 #pragma unroll
-    for (int j = 0; j < per; ++j) {
-      const int s = s0 + j * kNT + threadIdx.x;
-      uint32_t key = 0;
-      if (s < s1) {
-        key = float_key(row[s]);
-        const uint32_t dg = key >> (32 - kHistBits);
-        n_gt += dg > d1;
-        n_eq += dg == d1;
-      }
-      keys[j] = key;
-    }
-    uint32_t tot_gt, tot_eq;
-    const uint32_t inc_gt = block_incl_scan(n_gt, s_w, &tot_gt);
-    __syncthreads();
-    const uint32_t inc_eq = block_incl_scan(n_eq, s_w, &tot_eq);
-    if (threadIdx.x == 0) {
-      s_res[4] = tot_gt ? atomicAdd(&ctl->sel, tot_gt) : 0u;
-      s_res[5] = tot_eq ? atomicAdd(&ctl->cand, tot_eq) : 0u;
-    }
-    __syncthreads();
-    uint32_t o_gt = s_res[4] + inc_gt - n_gt;
-    uint32_t o_eq = s_res[5] + inc_eq - n_eq;
-    uint32_t* ck = a.cand_key + (int64_t)t * a.n_max;
-    int32_t* cp = a.cand_pos + (int64_t)t * a.n_max;
+    for (int sl = 0; sl < kHistSlices; ++sl) v += gh[sl * kHistBins + i];
+    s_hist[i] = v;
+  }
+  __syncthreads();
+  find_digit_desc(s_hist, kHistBins, (uint32_t)k, s_w, s_res);
+  const uint32_t d1 = s_res[0];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.thr1[2 * t] = d1;
+    a.thr1[2 * t + 1] = s_res[1];
+  }
+  uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
-    for (int j = 0; j < per; ++j) {
-      const int s = s0 + j * kNT + threadIdx.x;
-      if (s < s1) {
-        const uint32_t dg = keys[j] >> (32 - kHistBits);
-        // the guards only matter if the histogram disagrees with the scores (a caller that
-        // skipped dsa_workspace_init); they keep every store inside the row's buffers
-        if (dg > d1) { if (o_gt < (uint32_t)k) out[o_gt] = s; ++o_gt; }
-        else if (dg == d1) { if (o_eq < (uint32_t)a.n_max) { ck[o_eq] = keys[j]; cp[o_eq] = s; } ++o_eq; }
+  for (int j = 0; j < per; ++j) {
+    const int s = s0 + j * kNT + threadIdx.x;
+    if (s < s1) {
+      const uint32_t dg = keys[j] >> D1;
+      n_gt += dg > d1;
+      n_eq += dg == d1;
+    }
+  }
+  uint32_t tot_gt, tot_eq;
+  block_incl_scan(n_gt, s_w, &tot_gt);
+  const uint32_t inc_eq = block_incl_scan(n_eq, s_w, &tot_eq);
+  uint32_t o_eq = inc_eq - n_eq;
+  const int64_t region = ((int64_t)t * a.n_chunks + blockIdx.x) * kTopkChunk;
+  uint32_t* ck = a.cand_key + region;
+  int32_t* cp = a.cand_pos + region;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    const int s = s0 + j * kNT + threadIdx.x;
+    if (s < s1 && (keys[j] >> D1) == d1) {
+      ck[o_eq] = keys[j];
+      cp[o_eq] = s;
+      ++o_eq;
+    }
+  }
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = a.counts + ((int64_t)t * a.n_chunks + blockIdx.x) * 2;
+    cnt[0] = tot_gt;
+    cnt[1] = tot_eq;
+  }
+}
+
+// One workgroup per (row, chunk). Every workgroup of a row repeats the same exact resolution
+// of the threshold bin (so they agree without talking): the second digit from the bin's
+// candidates, then the threshold sub-bin's last 8 bits and ties (smaller position first).
+// From the candidate list it also derives every chunk's count of selected keys, so it can
+// place its own chunk's selections: [keys above the bin, chunk order] [bin keys above the
+// sub-bin, chunk order] [selected sub-bin keys, chunk order]. It re-reads its own chunk's
+// scores to write them.
+__global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_w[kNT / 64];
+  __shared__ uint32_t s_res[8];
+  __shared__ uint32_t s_off[3][kMaxChunks + 1];  // per-chunk counts -> exclusive prefixes
+  __shared__ uint32_t s_ck[kTopkCandLds];        // the row's threshold-bin candidates (keys)
+  __shared__ uint32_t s_sk[kTopkSubLds];         // the threshold sub-bin: keys
+  __shared__ int32_t s_sp[kTopkSubLds];          // and positions
+
+  constexpr int D1 = 32 - kHistBits;
+  constexpr int D2 = D1 - kHistBits;
+  constexpr int per = kTopkChunk / kNT;
+  const int t = blockIdx.y;
+  const int c_me = blockIdx.x;
+  const int k = a.topk;
+  int n = a.row_len[t];
+  n = min(max(n, 0), a.n_max);
+  int32_t* out = a.indices + (int64_t)t * a.ld_idx;
+  if (c_me == 0) {   // no workgroup of this kernel reads the first-digit histogram
+    uint32_t* gh = a.hist + (int64_t)t * kHistSlices * kHistBins;
+    for (int i = threadIdx.x; i < kHistSlices * kHistBins; i += kNT) gh[i] = 0;
+    if (threadIdx.x == 0) a.lens[t] = min(n, k);
+    if (n <= k)
+      for (int i = n + threadIdx.x; i < k; i += kNT) out[i] = -1;
+  }
+  const int s0 = c_me * kTopkChunk;
+  if (n <= k || s0 >= n) return;
+  const int s1 = min(n, s0 + kTopkChunk);
+  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+
+  // own chunk's scores (written at the end), the threshold's first digit, per-chunk counts
+  uint32_t keys[per];
+  const float* row = a.logits + (int64_t)t * a.ld_logits;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    const int s = s0 + j * kNT + threadIdx.x;
+    keys[j] = s < s1 ? float_key(row[s]) : 0u;
+  }
+  const uint32_t d1 = a.thr1[2 * t];
+  const uint32_t above1 = a.thr1[2 * t + 1];
+  const uint32_t* cnt = a.counts + (int64_t)t * a.n_chunks * 2;
+  for (int c = threadIdx.x; c < nch; c += kNT) {
+    s_off[0][c] = cnt[2 * c];
+    s_off[1][c] = cnt[2 * c + 1];
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
+  __syncthreads();
+  // exclusive prefixes of the per-chunk counts: thread i owns chunks 2i and 2i + 1
+  static_assert(kMaxChunks <= 2 * kNT, "chunk prefix");
+  auto chunk_prefix = [&](int x) {
+    const int c0 = 2 * threadIdx.x;
+    const uint32_t v0 = c0 < nch ? s_off[x][c0] : 0u;
+    const uint32_t v1 = c0 + 1 < nch ? s_off[x][c0 + 1] : 0u;
+    uint32_t total;
+    const uint32_t incl = block_incl_scan(v0 + v1, s_w, &total);
+    __syncthreads();
+    if (c0 < nch) s_off[x][c0] = incl - v0 - v1;
+    if (c0 + 1 < nch) s_off[x][c0 + 1] = incl - v1;
+    if (threadIdx.x == 0) s_off[x][nch] = total;
+    __syncthreads();
+  };
+  chunk_prefix(0);
+  chunk_prefix(1);
+  const uint32_t n_cand = s_off[1][nch];
+  const bool cand_lds = n_cand <= (uint32_t)kTopkCandLds;
+  // candidate i of the row lives in chunk c at offset i - prefix[c]
+  auto chunk_of = [&](uint32_t i) {
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[1][mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto cand_at = [&](uint32_t i, int& c) -> int64_t {
+    c = chunk_of(i);
+    return ((int64_t)t * a.n_chunks + c) * kTopkChunk + (i - s_off[1][c]);
+  };
+  // 1. the candidates' second digit (and the keys kept in LDS when they fit)
+  for (uint32_t i0 = 0; i0 < n_cand; i0 += 8 * kNT) {
+    uint32_t kk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = i0 + u * kNT + threadIdx.x;
+      int c;
+      kk[u] = i < n_cand ? a.cand_key[cand_at(i, c)] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = i0 + u * kNT + threadIdx.x;
+      if (i < n_cand) {
+        if (cand_lds) s_ck[i] = kk[u];
+        atomicAdd(&s_hist[(kk[u] >> D2) & (kHistBins - 1)], 1u);
       }
     }
   }
-
-  // last workgroup of the row resolves the threshold bin
-  __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) s_res[6] = (atomicAdd(&ctl->done, 1u) == gridDim.x - 1) ? 1u : 0u;
+  const uint32_t need1 = (uint32_t)k - above1;
+  find_digit_desc(s_hist, kHistBins, need1, s_w, s_res);
+  const uint32_t d2 = s_res[0];
+  const uint32_t above2 = s_res[1];
+  const uint32_t n_sub = s_hist[d2];
+  const uint32_t pre = (d1 << kHistBits) | d2;          // top 24 bits of the threshold
+  // 2. per chunk: candidates above the sub-bin; gather the sub-bin itself
+  for (int c = threadIdx.x; c <= nch; c += kNT) s_off[2][c] = 0;
+  if (threadIdx.x == 0) s_res[5] = 0;
   __syncthreads();
-  if (!s_res[6]) return;
-  __threadfence();
-
-  if (n <= k) {
-    for (int i = n + threadIdx.x; i < k; i += kNT) out[i] = -1;
-  } else {
-    const int cnt = min((int)__hip_atomic_load(&ctl->cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), a.n_max);
-    const uint32_t* ck = a.cand_key + (int64_t)t * a.n_max;
-    const int32_t* cp = a.cand_pos + (int64_t)t * a.n_max;
-    uint32_t need = (uint32_t)k - above1, eq = 0;
-    auto get_key = [&](int i, uint32_t& key) { key = ck[i]; return true; };
-    const uint32_t hi_mask = ~0u << (32 - kHistBits);
-    const uint32_t thr = radix_select_desc(cnt, get_key, d1 << (32 - kHistBits), hi_mask,
-                                           32 - kHistBits, need, &eq, s_hist, s_w, s_res);
-    uint32_t pos_thr = 0u;
+  const bool sub_lds = n_sub <= (uint32_t)kTopkSubLds;
+  for (uint32_t i0 = 0; i0 < n_cand; i0 += kNT) {
+    const uint32_t i = i0 + threadIdx.x;
+    uint32_t key = 0u;
+    int c = 0;
+    int64_t at = 0;
+    if (i < n_cand) {
+      at = cand_at(i, c);
+      key = cand_lds ? s_ck[i] : a.cand_key[at];
+    }
+    const uint32_t hi = key >> D2;
+    if (i < n_cand && hi > pre) atomicAdd(&s_off[2][c], 1u);
+    const bool sub = i < n_cand && hi == pre && sub_lds;
+    const uint32_t j = wave_reserve(sub, &s_res[5]);
+    if (sub && j < (uint32_t)kTopkSubLds) { s_sk[j] = key; s_sp[j] = a.cand_pos[at]; }
+  }
+  __syncthreads();
+  // 3. the sub-bin: last 8 bits, then ties by position
+  uint32_t need = need1 - above2, eq = 0, thr = 0, pos_thr = 0;
+  bool all_ties = true;
+  if (sub_lds) {
+    const int m = (int)n_sub;
+    auto get_key = [&](int i, uint32_t& key) { key = s_sk[i]; return true; };
+    thr = radix_select_desc(m, get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
     if (eq > need) {
       uint32_t need2 = need, eq2 = 0;
-      auto get_tie = [&](int i, uint32_t& key) { key = ~(uint32_t)cp[i]; return ck[i] == thr; };
-      pos_thr = radix_select_desc(cnt, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
+      auto get_tie = [&](int i, uint32_t& key) { key = ~(uint32_t)s_sp[i]; return s_sk[i] == thr; };
+      pos_thr = radix_select_desc(m, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
     }
-    const bool all_ties = eq <= need;
-    if (threadIdx.x == 0) s_res[7] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < cnt; i += kNT) {
-      const uint32_t key = ck[i];
-      const bool sel = key > thr || (key == thr && (all_ties || ~(uint32_t)cp[i] >= pos_thr));
-      if (sel) {
-        const uint32_t o = above1 + atomicAdd(&s_res[7], 1u);
-        if (o < (uint32_t)k) out[o] = cp[i];
-      }
+  } else {   // a huge sub-bin (mass ties): stream it from the candidate regions
+    auto get_key = [&](int i, uint32_t& key) {
+      int c;
+      key = cand_lds ? s_ck[i] : a.cand_key[cand_at((uint32_t)i, c)];
+      return (key >> D2) == pre;
+    };
+    thr = radix_select_desc((int)n_cand, get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
+    if (eq > need) {
+      uint32_t need2 = need, eq2 = 0;
+      auto get_tie = [&](int i, uint32_t& key) {
+        int c;
+        const int64_t at = cand_at((uint32_t)i, c);
+        key = ~(uint32_t)a.cand_pos[at];
+        return (cand_lds ? s_ck[i] : a.cand_key[at]) == thr;
+      };
+      pos_thr = radix_select_desc((int)n_cand, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
     }
   }
-  for (int i = threadIdx.x; i < kHistSlices * kHistBins; i += kNT) gh[i] = 0;
-  if (threadIdx.x == 0) {
-    a.lens[t] = min(n, k);
-    ctl->sel = 0;
-    ctl->cand = 0;
-    ctl->done = 0;
+  all_ties = eq <= need;
+  auto in_sub_sel = [&](uint32_t key, int32_t pos) {
+    return (key >> D2) == pre && (key > thr || (key == thr && (all_ties || ~(uint32_t)pos >= pos_thr)));
+  };
+  // 4. per chunk: selected sub-bin keys
+  if (sub_lds) {
+    // the sub-bin is small: count its selected keys per chunk
+    for (int c = threadIdx.x; c <= nch; c += kNT) s_off[1][c] = 0;   // reuse: per-chunk sub counts
+    __syncthreads();
+    for (int i = threadIdx.x; i < (int)n_sub; i += kNT)
+      if (in_sub_sel(s_sk[i], s_sp[i])) {
+        const int32_t pos = s_sp[i];
+        atomicAdd(&s_off[1][pos / kTopkChunk], 1u);
+      }
+  } else {
+    // re-derive the chunk of every candidate: prefixes of the bin counts are still needed,
+    // so count into a fresh array
+    for (int c = threadIdx.x; c <= nch; c += kNT) s_hist[c] = 0;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) {
+      int c;
+      const int64_t at = cand_at(i, c);
+      const uint32_t key = cand_lds ? s_ck[i] : a.cand_key[at];
+      if (in_sub_sel(key, a.cand_pos[at])) atomicAdd(&s_hist[c], 1u);
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c <= nch; c += kNT) s_off[1][c] = s_hist[c];
+  }
+  __syncthreads();
+  chunk_prefix(1);   // selected sub-bin keys per chunk
+  chunk_prefix(2);   // bin keys above the sub-bin per chunk
+  // 5. this chunk's selections, thread-major within each class (deterministic)
+  uint32_t cls = 0, n12 = 0, n3 = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    const int s = s0 + j * kNT + threadIdx.x;
+    const uint32_t key = keys[j];
+    const uint32_t dg = key >> D1;
+    uint32_t c = 0;
+    if (s < s1) {
+      if (dg > d1) c = 1;
+      else if (dg == d1 && (key >> D2) > pre) c = 2;
+      else if (in_sub_sel(key, s)) c = 3;
+    }
+    cls |= c << (2 * j);
+    n12 += c == 1 ? 1u : (c == 2 ? 0x10000u : 0u);   // chunk totals stay below 2^16
+    n3 += c == 3;
+  }
+  uint32_t tot;
+  const uint32_t e12 = block_incl_scan(n12, s_w, &tot) - n12;
+  const uint32_t e3 = block_incl_scan(n3, s_w, &tot) - n3;
+  uint32_t o1 = s_off[0][c_me] + (e12 & 0xffffu);
+  uint32_t o2 = above1 + s_off[2][c_me] + (e12 >> 16);
+  uint32_t o3 = above1 + above2 + s_off[1][c_me] + e3;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    const int s = s0 + j * kNT + threadIdx.x;
+    const uint32_t c = (cls >> (2 * j)) & 3u;
+    if (c == 0) continue;
+    const uint32_t o = c == 1 ? o1++ : (c == 2 ? o2++ : o3++);
+    if (o < (uint32_t)k) out[o] = s;
   }
 }
 
@@ -318,6 +516,12 @@ hipError_t launch_topk_hist(const TopkArgs& a, int T, hipStream_t st) {
 hipError_t launch_topk_filter(const TopkArgs& a, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_topk_filter, dim3(topk_chunks(a), T), dim3(kNT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_finalize(const TopkArgs& a, int T, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_topk_finalize, dim3(topk_chunks(a), T), dim3(kNT), 0, st, a);
   return hipGetLastError();
 }
 

@@ -118,7 +118,7 @@ typedef struct dsa_rows {
 /* ---------------------------------------------------------------- step 1: indexer scores
  * q_idx: bf16 [T, Hi, di], row stride ld_q_idx elements (>= Hi*di, multiple of 8).
  * w:     fp32 [T, Hi], row stride ld_w (>= Hi); any sign.
- * logits: fp32 [T, ld_logits], ld_logits >= n_max (multiple of 4); writes logits[t, 0:n_t],
+ * logits: fp32 [T, ld_logits], ld_logits >= n_max; writes logits[t, 0:n_t],
  *         leaves [n_t, ld_logits) untouched.
  * Envelope: 1 <= Hi <= 64, di in {64, 128}. */
 dsa_status dsa_index_scores(const void* q_idx, int64_t ld_q_idx, const float* w, int64_t ld_w,
@@ -204,6 +204,25 @@ const char* dsa_status_string(int32_t status);
 
 /* ABI version (bumped on any signature or struct change). */
 int32_t dsa_abi_version(void);
+
+/* ---------------------------------------------------------------- kernel timing
+ * Profiling aid (the per-stage timings the pages report, e.g. the scores / top-k / sparse
+ * attention columns of PR 627's benchmark tables). While enabled, every kernel the library
+ * launches is bracketed by two HIP events on the caller's stream (host-side event objects
+ * from a pool; no device memory). dsa_profile_collect() waits for the recorded events,
+ * aggregates them by kernel name into `out` (at most max_entries rows), clears the record
+ * and returns the number of rows written (or a negative dsa_status). Not thread-safe;
+ * disabled by default; enabling adds event packets between the kernels of a call. */
+typedef struct dsa_kernel_time {
+  char name[40];
+  int32_t count;
+  float total_ms;
+  float min_ms;
+  float max_ms;
+} dsa_kernel_time;
+
+dsa_status dsa_profile_enable(int32_t on);
+int32_t dsa_profile_collect(dsa_kernel_time* out, int32_t max_entries);
 
 #ifdef __cplusplus
 }
