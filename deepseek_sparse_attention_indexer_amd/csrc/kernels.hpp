@@ -18,10 +18,8 @@ constexpr int kTopkLdsMax = 16384;
 // candidates per workgroup in the multi-workgroup (long row) select
 constexpr int kTopkChunk = 4096;
 // the finalize step keeps the threshold bin's candidates in LDS when there are at most this
-// many (else it streams them from the workspace)
+// many (else it re-reads them from the workspace)
 constexpr int kTopkCandLds = 8192;
-// the threshold sub-bin it resolves in LDS holds at most this many keys (else streamed)
-constexpr int kTopkSubLds = 2048;
 // chunks per row (long rows up to kMaxChunks * kTopkChunk = 4M candidates)
 constexpr int kMaxChunks = 1024;
 

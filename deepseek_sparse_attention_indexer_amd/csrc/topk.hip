@@ -14,11 +14,11 @@
 //  * k_topk_lds: one 512-thread workgroup per row, the row's keys held in LDS (<= 16K).
 //  * long rows: the first-digit histogram is built per chunk (k_topk_hist, or fused into
 //    the score kernel). k_topk_filter's workgroups (one per chunk) find the threshold bin and
-//    write their chunk's threshold-bin candidates and counts. k_topk_finalize's workgroups
-//    (one per chunk again) each repeat the same exact resolution of the bin from the
-//    candidates (second digit, then the sub-bin in LDS), derive every chunk's output offsets
-//    and write their own chunk's selections. Kernel boundaries replace device-scope fences,
-//    returning atomics and single-workgroup tails, which cost microseconds each on this part.
+//    write their chunk's threshold-bin candidates and counts. In k_topk_finalize one
+//    workgroup per chunk writes the chunk's keys above the bin while one more workgroup per
+//    row resolves the bin from its candidates (usually a few thousand, held in LDS). Kernel
+//    boundaries replace device-scope fences and returning atomics, which cost microseconds
+//    each on this part.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -274,105 +274,131 @@ __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
   }
 }
 
-// One workgroup per (row, chunk). Every workgroup of a row repeats the same exact resolution
-// of the threshold bin (so they agree without talking): the second digit from the bin's
-// candidates, then the threshold sub-bin's last 8 bits and ties (smaller position first).
-// From the candidate list it also derives every chunk's count of selected keys, so it can
-// place its own chunk's selections: [keys above the bin, chunk order] [bin keys above the
-// sub-bin, chunk order] [selected sub-bin keys, chunk order]. It re-reads its own chunk's
-// scores to write them.
+// Per row: one workgroup per chunk writes the chunk's keys above the threshold bin, and one
+// more workgroup (x == n_chunks) resolves the bin. Output layout: [keys above the bin, chunk
+// by chunk] then [the bin's selected keys, in candidate order]; both orders are fixed, so the
+// list is deterministic.
+//  * chunk workgroups: offset = sum of the earlier chunks' counts above the bin, then a
+//    thread-major scan of the chunk's own scores;
+//  * the resolver: gathers the bin's candidates (kept in LDS when there are at most
+//    kTopkCandLds, else re-read from the workspace), takes the second digit and the
+//    threshold sub-bin's last 8 bits by histogram, breaks ties at the threshold key toward
+//    the smaller position, then writes the selected candidates. It also returns the
+//    first-digit histogram to zero, writes lens and pads short rows with -1.
 __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_w[kNT / 64];
   __shared__ uint32_t s_res[8];
-  __shared__ uint32_t s_off[3][kMaxChunks + 1];  // per-chunk counts -> exclusive prefixes
-  __shared__ uint32_t s_ck[kTopkCandLds];        // the row's threshold-bin candidates (keys)
-  __shared__ uint32_t s_sk[kTopkSubLds];         // the threshold sub-bin: keys
-  __shared__ int32_t s_sp[kTopkSubLds];          // and positions
+  __shared__ uint32_t s_off[kMaxChunks + 1];   // the bin's candidates per chunk -> prefixes
+  __shared__ uint32_t s_ck[kTopkCandLds];      // candidate keys
+  __shared__ int32_t s_cp[kTopkCandLds];       // and positions
 
   constexpr int D1 = 32 - kHistBits;
   constexpr int D2 = D1 - kHistBits;
   constexpr int per = kTopkChunk / kNT;
   const int t = blockIdx.y;
-  const int c_me = blockIdx.x;
   const int k = a.topk;
   int n = a.row_len[t];
   n = min(max(n, 0), a.n_max);
   int32_t* out = a.indices + (int64_t)t * a.ld_idx;
-  if (c_me == 0) {   // no workgroup of this kernel reads the first-digit histogram
+  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+  const uint32_t* cnt = a.counts + (int64_t)t * a.n_chunks * 2;
+
+  if ((int)blockIdx.x < a.n_chunks) {
+    // ---- chunk workgroup: keys above the threshold bin
+    const int c_me = blockIdx.x;
+    const int s0 = c_me * kTopkChunk;
+    if (n <= k || c_me >= nch) return;
+    const int s1 = min(n, s0 + kTopkChunk);
+    const uint32_t d1 = a.thr1[2 * t];
+    uint32_t before = 0;                       // counts of the earlier chunks
+    for (int c = threadIdx.x; c < c_me; c += kNT) before += cnt[2 * c];
+    uint32_t keys[per];
+    const float* row = a.logits + (int64_t)t * a.ld_logits;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      const int s = s0 + j * kNT + threadIdx.x;
+      keys[j] = s < s1 ? float_key(row[s]) : 0u;
+    }
+    uint32_t base;
+    block_incl_scan(before, s_w, &base);
+    uint32_t sel = 0, m = 0;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      const int s = s0 + j * kNT + threadIdx.x;
+      const bool x = s < s1 && (keys[j] >> D1) > d1;
+      sel |= (uint32_t)x << j;
+      m += x;
+    }
+    uint32_t tot;
+    uint32_t o = base + block_incl_scan(m, s_w, &tot) - m;
+#pragma unroll
+    for (int j = 0; j < per; ++j)
+      if (sel >> j & 1u) {
+        if (o < (uint32_t)k) out[o] = s0 + j * kNT + threadIdx.x;
+        ++o;
+      }
+    return;
+  }
+
+  // ---- the resolver
+  if (threadIdx.x == 0) a.lens[t] = min(n, k);
+  {
     uint32_t* gh = a.hist + (int64_t)t * kHistSlices * kHistBins;
     for (int i = threadIdx.x; i < kHistSlices * kHistBins; i += kNT) gh[i] = 0;
-    if (threadIdx.x == 0) a.lens[t] = min(n, k);
-    if (n <= k)
-      for (int i = n + threadIdx.x; i < k; i += kNT) out[i] = -1;
   }
-  const int s0 = c_me * kTopkChunk;
-  if (n <= k || s0 >= n) return;
-  const int s1 = min(n, s0 + kTopkChunk);
-  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
-
-  // own chunk's scores (written at the end), the threshold's first digit, per-chunk counts
-  uint32_t keys[per];
-  const float* row = a.logits + (int64_t)t * a.ld_logits;
-#pragma unroll
-  for (int j = 0; j < per; ++j) {
-    const int s = s0 + j * kNT + threadIdx.x;
-    keys[j] = s < s1 ? float_key(row[s]) : 0u;
+  if (n <= k) {
+    for (int i = n + threadIdx.x; i < k; i += kNT) out[i] = -1;
+    return;
   }
   const uint32_t d1 = a.thr1[2 * t];
   const uint32_t above1 = a.thr1[2 * t + 1];
-  const uint32_t* cnt = a.counts + (int64_t)t * a.n_chunks * 2;
-  for (int c = threadIdx.x; c < nch; c += kNT) {
-    s_off[0][c] = cnt[2 * c];
-    s_off[1][c] = cnt[2 * c + 1];
-  }
-  for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
-  __syncthreads();
-  // exclusive prefixes of the per-chunk counts: thread i owns chunks 2i and 2i + 1
-  static_assert(kMaxChunks <= 2 * kNT, "chunk prefix");
-  auto chunk_prefix = [&](int x) {
+  {
+    // exclusive prefixes of the per-chunk candidate counts: thread i owns chunks 2i, 2i + 1
     const int c0 = 2 * threadIdx.x;
-    const uint32_t v0 = c0 < nch ? s_off[x][c0] : 0u;
-    const uint32_t v1 = c0 + 1 < nch ? s_off[x][c0 + 1] : 0u;
+    const uint32_t v0 = c0 < nch ? cnt[2 * c0 + 1] : 0u;
+    const uint32_t v1 = c0 + 1 < nch ? cnt[2 * c0 + 3] : 0u;
+    for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
     uint32_t total;
     const uint32_t incl = block_incl_scan(v0 + v1, s_w, &total);
+    if (c0 < nch) s_off[c0] = incl - v0 - v1;
+    if (c0 + 1 < nch) s_off[c0 + 1] = incl - v1;
+    if (threadIdx.x == 0) s_off[nch] = total;
     __syncthreads();
-    if (c0 < nch) s_off[x][c0] = incl - v0 - v1;
-    if (c0 + 1 < nch) s_off[x][c0 + 1] = incl - v1;
-    if (threadIdx.x == 0) s_off[x][nch] = total;
-    __syncthreads();
-  };
-  chunk_prefix(0);
-  chunk_prefix(1);
-  const uint32_t n_cand = s_off[1][nch];
-  const bool cand_lds = n_cand <= (uint32_t)kTopkCandLds;
-  // candidate i of the row lives in chunk c at offset i - prefix[c]
-  auto chunk_of = [&](uint32_t i) {
+  }
+  const uint32_t n_cand = s_off[nch];
+  const bool in_lds = n_cand <= (uint32_t)kTopkCandLds;
+  // workspace address of candidate i (candidates are numbered chunk by chunk)
+  auto cand_at = [&](uint32_t i) -> int64_t {
     int lo = 0, hi = nch - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_off[1][mid] <= i) lo = mid; else hi = mid - 1;
+      if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    return lo;
+    return ((int64_t)t * a.n_chunks + lo) * kTopkChunk + (i - s_off[lo]);
   };
-  auto cand_at = [&](uint32_t i, int& c) -> int64_t {
-    c = chunk_of(i);
-    return ((int64_t)t * a.n_chunks + c) * kTopkChunk + (i - s_off[1][c]);
-  };
-  // 1. the candidates' second digit (and the keys kept in LDS when they fit)
+  auto key_of = [&](uint32_t i) { return in_lds ? s_ck[i] : a.cand_key[cand_at(i)]; };
+  auto pos_of = [&](uint32_t i) { return in_lds ? s_cp[i] : a.cand_pos[cand_at(i)]; };
+  // 1. gather the candidates; histogram of their second digit
   for (uint32_t i0 = 0; i0 < n_cand; i0 += 8 * kNT) {
     uint32_t kk[8];
+    int32_t pp[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const uint32_t i = i0 + u * kNT + threadIdx.x;
-      int c;
-      kk[u] = i < n_cand ? a.cand_key[cand_at(i, c)] : 0u;
+      kk[u] = 0u;
+      pp[u] = 0;
+      if (i < n_cand) {
+        const int64_t at = cand_at(i);
+        kk[u] = a.cand_key[at];
+        if (in_lds) pp[u] = a.cand_pos[at];
+      }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const uint32_t i = i0 + u * kNT + threadIdx.x;
       if (i < n_cand) {
-        if (cand_lds) s_ck[i] = kk[u];
+        if (in_lds) { s_ck[i] = kk[u]; s_cp[i] = pp[u]; }
         atomicAdd(&s_hist[(kk[u] >> D2) & (kHistBins - 1)], 1u);
       }
     }
@@ -380,122 +406,37 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   __syncthreads();
   const uint32_t need1 = (uint32_t)k - above1;
   find_digit_desc(s_hist, kHistBins, need1, s_w, s_res);
-  const uint32_t d2 = s_res[0];
-  const uint32_t above2 = s_res[1];
-  const uint32_t n_sub = s_hist[d2];
-  const uint32_t pre = (d1 << kHistBits) | d2;          // top 24 bits of the threshold
-  // 2. per chunk: candidates above the sub-bin; gather the sub-bin itself
-  for (int c = threadIdx.x; c <= nch; c += kNT) s_off[2][c] = 0;
-  if (threadIdx.x == 0) s_res[5] = 0;
+  const uint32_t pre = (d1 << kHistBits) | s_res[0];     // top 24 bits of the threshold key
+  uint32_t need = need1 - s_res[1], eq = 0, pos_thr = 0;
   __syncthreads();
-  const bool sub_lds = n_sub <= (uint32_t)kTopkSubLds;
-  for (uint32_t i0 = 0; i0 < n_cand; i0 += kNT) {
-    const uint32_t i = i0 + threadIdx.x;
-    uint32_t key = 0u;
-    int c = 0;
-    int64_t at = 0;
-    if (i < n_cand) {
-      at = cand_at(i, c);
-      key = cand_lds ? s_ck[i] : a.cand_key[at];
-    }
-    const uint32_t hi = key >> D2;
-    if (i < n_cand && hi > pre) atomicAdd(&s_off[2][c], 1u);
-    const bool sub = i < n_cand && hi == pre && sub_lds;
-    const uint32_t j = wave_reserve(sub, &s_res[5]);
-    if (sub && j < (uint32_t)kTopkSubLds) { s_sk[j] = key; s_sp[j] = a.cand_pos[at]; }
-  }
-  __syncthreads();
-  // 3. the sub-bin: last 8 bits, then ties by position
-  uint32_t need = need1 - above2, eq = 0, thr = 0, pos_thr = 0;
-  bool all_ties = true;
-  if (sub_lds) {
-    const int m = (int)n_sub;
-    auto get_key = [&](int i, uint32_t& key) { key = s_sk[i]; return true; };
-    thr = radix_select_desc(m, get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
-    if (eq > need) {
-      uint32_t need2 = need, eq2 = 0;
-      auto get_tie = [&](int i, uint32_t& key) { key = ~(uint32_t)s_sp[i]; return s_sk[i] == thr; };
-      pos_thr = radix_select_desc(m, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
-    }
-  } else {   // a huge sub-bin (mass ties): stream it from the candidate regions
-    auto get_key = [&](int i, uint32_t& key) {
-      int c;
-      key = cand_lds ? s_ck[i] : a.cand_key[cand_at((uint32_t)i, c)];
-      return (key >> D2) == pre;
+  // 2. the threshold sub-bin: its last 8 bits, then ties toward the smaller position
+  auto get_key = [&](int i, uint32_t& key) { key = key_of((uint32_t)i); return true; };
+  const uint32_t thr =
+      radix_select_desc((int)n_cand, get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
+  if (eq > need) {
+    uint32_t need2 = need, eq2 = 0;
+    auto get_tie = [&](int i, uint32_t& key) {
+      key = ~(uint32_t)pos_of((uint32_t)i);
+      return key_of((uint32_t)i) == thr;
     };
-    thr = radix_select_desc((int)n_cand, get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
-    if (eq > need) {
-      uint32_t need2 = need, eq2 = 0;
-      auto get_tie = [&](int i, uint32_t& key) {
-        int c;
-        const int64_t at = cand_at((uint32_t)i, c);
-        key = ~(uint32_t)a.cand_pos[at];
-        return (cand_lds ? s_ck[i] : a.cand_key[at]) == thr;
-      };
-      pos_thr = radix_select_desc((int)n_cand, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
-    }
+    pos_thr = radix_select_desc((int)n_cand, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
   }
-  all_ties = eq <= need;
-  auto in_sub_sel = [&](uint32_t key, int32_t pos) {
-    return (key >> D2) == pre && (key > thr || (key == thr && (all_ties || ~(uint32_t)pos >= pos_thr)));
+  const bool all_ties = eq <= need;
+  auto selected = [&](uint32_t key, int32_t pos) {
+    const uint32_t hi = key >> D2;
+    return hi > pre || (hi == pre && (key > thr || (key == thr && (all_ties || ~(uint32_t)pos >= pos_thr))));
   };
-  // 4. per chunk: selected sub-bin keys
-  if (sub_lds) {
-    // the sub-bin is small: count its selected keys per chunk
-    for (int c = threadIdx.x; c <= nch; c += kNT) s_off[1][c] = 0;   // reuse: per-chunk sub counts
-    __syncthreads();
-    for (int i = threadIdx.x; i < (int)n_sub; i += kNT)
-      if (in_sub_sel(s_sk[i], s_sp[i])) {
-        const int32_t pos = s_sp[i];
-        atomicAdd(&s_off[1][pos / kTopkChunk], 1u);
-      }
-  } else {
-    // re-derive the chunk of every candidate: prefixes of the bin counts are still needed,
-    // so count into a fresh array
-    for (int c = threadIdx.x; c <= nch; c += kNT) s_hist[c] = 0;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) {
-      int c;
-      const int64_t at = cand_at(i, c);
-      const uint32_t key = cand_lds ? s_ck[i] : a.cand_key[at];
-      if (in_sub_sel(key, a.cand_pos[at])) atomicAdd(&s_hist[c], 1u);
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c <= nch; c += kNT) s_off[1][c] = s_hist[c];
-  }
-  __syncthreads();
-  chunk_prefix(1);   // selected sub-bin keys per chunk
-  chunk_prefix(2);   // bin keys above the sub-bin per chunk
-  // 5. this chunk's selections, thread-major within each class (deterministic)
-  uint32_t cls = 0, n12 = 0, n3 = 0;
-#pragma unroll
-  for (int j = 0; j < per; ++j) {
-    const int s = s0 + j * kNT + threadIdx.x;
-    const uint32_t key = keys[j];
-    const uint32_t dg = key >> D1;
-    uint32_t c = 0;
-    if (s < s1) {
-      if (dg > d1) c = 1;
-      else if (dg == d1 && (key >> D2) > pre) c = 2;
-      else if (in_sub_sel(key, s)) c = 3;
-    }
-    cls |= c << (2 * j);
-    n12 += c == 1 ? 1u : (c == 2 ? 0x10000u : 0u);   // chunk totals stay below 2^16
-    n3 += c == 3;
-  }
+  // 3. write the selected candidates after the keys above the bin, thread-major
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) m += selected(key_of(i), pos_of(i));
   uint32_t tot;
-  const uint32_t e12 = block_incl_scan(n12, s_w, &tot) - n12;
-  const uint32_t e3 = block_incl_scan(n3, s_w, &tot) - n3;
-  uint32_t o1 = s_off[0][c_me] + (e12 & 0xffffu);
-  uint32_t o2 = above1 + s_off[2][c_me] + (e12 >> 16);
-  uint32_t o3 = above1 + above2 + s_off[1][c_me] + e3;
-#pragma unroll
-  for (int j = 0; j < per; ++j) {
-    const int s = s0 + j * kNT + threadIdx.x;
-    const uint32_t c = (cls >> (2 * j)) & 3u;
-    if (c == 0) continue;
-    const uint32_t o = c == 1 ? o1++ : (c == 2 ? o2++ : o3++);
-    if (o < (uint32_t)k) out[o] = s;
+  uint32_t o = above1 + block_incl_scan(m, s_w, &tot) - m;
+  for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) {
+    const int32_t pos = pos_of(i);
+    if (selected(key_of(i), pos)) {
+      if (o < (uint32_t)k) out[o] = pos;
+      ++o;
+    }
   }
 }
 
@@ -521,7 +462,7 @@ hipError_t launch_topk_filter(const TopkArgs& a, int T, hipStream_t st) {
 
 hipError_t launch_topk_finalize(const TopkArgs& a, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk_finalize, dim3(topk_chunks(a), T), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL(k_topk_finalize, dim3(a.n_chunks + 1, T), dim3(kNT), 0, st, a);
   return hipGetLastError();
 }
 
