@@ -42,28 +42,42 @@ def algorithmic_bytes(prob):
     return {"keys": keys, "gathered_rows": gathered, "q_out_idx": qio, "total": keys + gathered + qio}
 
 
-def scores_kernel_bytes(prob):
-    """Per launch of the score kernel: every key read once, every score written once, the
-    query heads, weights and page-table entries read once."""
-    n = int(prob.row_len.sum())
-    key_b = 2 if prob.kpool.dtype == "bf16" else 1
-    per_cand = prob.di * key_b + 4 + (4 if prob.kpool.dtype == "fp8" else 0)
-    pages = (n + prob.kpool.page_size - 1) // prob.kpool.page_size
-    return n * per_cand + prob.T * (prob.Hi * prob.di * 2 + prob.Hi * 4) + pages * 4
+def kernel_bytes(prob, kernel):
+    """Algorithmic bytes one launch of `kernel` must move (decode, one row per request):
+    what the step reads and writes by definition, not what the implementation adds."""
+    T, n = prob.T, int(prob.row_len.sum())
+    topk = prob.topk
+    if kernel.startswith("index_scores"):
+        # every key (and fp8 scale) read once, every score written once, the query heads,
+        # weights and page-table entries read once
+        key_b = 2 if prob.kpool.dtype == "bf16" else 1
+        per_cand = prob.di * key_b + 4 + (4 if prob.kpool.dtype == "fp8" else 0)
+        pages = (n + prob.kpool.page_size - 1) // prob.kpool.page_size
+        return n * per_cand + T * (prob.Hi * prob.di * 2 + prob.Hi * 4) + pages * 4
+    if kernel.startswith("topk"):
+        # the scores read once, the index list written once
+        return n * 4 + T * topk * 4
+    if kernel == "sparse_mla":
+        row_b = {"bf16": 2 * prob.d_qk, "fp8_uniform": prob.d_qk + 4 * prob.d_qk // 64,
+                 "fp8_ds_mla": 584}[prob.kv.fmt]
+        rows = sum(min(topk, int(x)) for x in prob.row_len)
+        return rows * row_b + rows * 4 + T * prob.H * prob.d_qk * 2
+    return None
 
 
-def kernel_source_digest():
+def source_digest():
     h = hashlib.sha256()
-    for f in ("index_scores.hip", "common.hpp", "kernels.hpp"):
-        with open(os.path.join(ROOT, "deepseek_sparse_attention_indexer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "deepseek_sparse_attention_indexer_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
-    """HBM bytes per launch of the score kernel from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"index_scores_{workload}_traffic.txt")
+def read_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -71,7 +85,7 @@ def read_traffic(workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_digest") != kernel_source_digest():
+    if kv.get("source_digest") != source_digest():
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -179,11 +193,11 @@ def main():
     prof = dsa.dsa_profile_collect()
     dsa.dsa_profile_enable(False)
     per_kernel = {k: round(v["total_ms"] / v["count"] * 1e3, 2) for k, v in prof.items()}
-    dom = max(prof, key=lambda k: prof[k]["total_ms"])
+    dom = max(prof, key=lambda k: prof[k]["total_ms"] / prof[k]["count"])
     dom_us = prof[dom]["total_ms"] / prof[dom]["count"] * 1e3
-    sk_bytes = scores_kernel_bytes(prob)
-    achieved = sk_bytes / (dom_us * 1e-6) / 1e9 if dom.startswith("index_scores") else None
-    traffic = read_traffic(args.workload) if dom.startswith("index_scores") else None
+    dom_bytes = kernel_bytes(prob, dom)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9 if dom_bytes else None
+    traffic = read_traffic(dom, args.workload)
 
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
@@ -214,7 +228,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1) if achieved else None,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                     "traffic": traffic, "algorithmic_bytes": sk_bytes, "avg_us": round(dom_us, 2)},
+                     "traffic": traffic, "kernel_algorithmic_bytes": dom_bytes, "avg_us": round(dom_us, 2),
+                     "timing": "HIP events around each launch on the launch stream, cold steps"},
         "layer": {"algorithmic_bytes": ab, "hbm_roofline_frac": round(layer_frac, 4),
                   "warm_us": round(warm, 2), "cold_us_p10_p90": [round(sorted(cold_us)[K // 10], 2),
                                                                   round(sorted(cold_us)[(9 * K) // 10], 2)],

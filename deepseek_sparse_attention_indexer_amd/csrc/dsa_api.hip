@@ -9,6 +9,10 @@
 #include "dsa.h"
 #include "kernels.hpp"
 
+namespace dsa {
+thread_local LaunchEvents t_launch_events;
+}  // namespace dsa
+
 using namespace dsa;
 
 namespace {
@@ -95,15 +99,24 @@ hipEvent_t pool_event() {
   return e;
 }
 
-// Run one kernel launch, bracketed by events when profiling is on.
+// Run one kernel launch; in timing mode the launch records a pair of events at its kernel's
+// start and end (launch_kernel), on the stream it runs on.
 template <class F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
+  (void)st;
   if (!g_prof) return launch();
   ProfRec r{name, pool_event(), pool_event()};
-  if (r.a) (void)hipEventRecord(r.a, st);
+  if (!r.a || !r.b) return launch();
+  t_launch_events = LaunchEvents{r.a, r.b};
   const hipError_t e = launch();
-  if (r.b) (void)hipEventRecord(r.b, st);
-  if (r.a && r.b) g_recs.push_back(r);
+  const bool launched = t_launch_events.start == nullptr;
+  t_launch_events = LaunchEvents{};
+  if (launched && e == hipSuccess) {
+    g_recs.push_back(r);
+  } else {
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
   return e;
 }
 

@@ -190,7 +190,7 @@ static hipError_t launch_t(const ScoreArgs& a, int T, hipStream_t st) {
   // about one workgroup per CU in total: longer rows loop (with prefetch) inside the waves
   const int cap = max(1, 256 / T);
   gx = max(1, min(gx, cap));
-  hipLaunchKernelGGL((k_index_scores<DI, MT, FP8, HIST>), dim3(gx, T), dim3(kScoreThreads), 0, st, a);
+  launch_kernel(k_index_scores<DI, MT, FP8, HIST>, dim3(gx, T), dim3(kScoreThreads), st, a);
   return hipGetLastError();
 }
 

@@ -1,11 +1,28 @@
 // Kernel argument blocks and host launchers of the DSA library (internal).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "common.hpp"
 
 namespace dsa {
+
+// Kernel timing. In the library's timing mode the wrapper around a launch sets these events;
+// the launch records them from its own dispatch packet (kernel start and end: the interval a
+// kernel-trace profiler reports) and clears them.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+extern thread_local LaunchEvents t_launch_events;
+
+template <class... P, class... A>
+inline void launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, A... args) {
+  const LaunchEvents ev = t_launch_events;
+  t_launch_events = LaunchEvents{};
+  hipExtLaunchKernelGGL(k, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+}
 
 // top-k radix: first digit = top 12 bits of the order-preserving key
 constexpr int kHistBits = 12;

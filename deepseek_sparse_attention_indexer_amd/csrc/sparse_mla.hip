@@ -441,9 +441,9 @@ template <int FMT, int DQK, int HT, int WD>
 static hipError_t launch_h(const MlaArgs& a, int T, hipStream_t st) {
   dim3 grid(a.n_split, a.H / (16 * HT), T);
   if (a.n_split > 1)
-    hipLaunchKernelGGL((k_sparse_mla<FMT, DQK, HT, WD, true>), grid, dim3(64 * HT * WD), 0, st, a);
+    launch_kernel(k_sparse_mla<FMT, DQK, HT, WD, true>, grid, dim3(64 * HT * WD), st, a);
   else
-    hipLaunchKernelGGL((k_sparse_mla<FMT, DQK, HT, WD, false>), grid, dim3(64 * HT * WD), 0, st, a);
+    launch_kernel(k_sparse_mla<FMT, DQK, HT, WD, false>, grid, dim3(64 * HT * WD), st, a);
   return hipGetLastError();
 }
 
@@ -470,7 +470,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T,
 
 hipError_t launch_mla_combine(const MlaArgs& a, int T, hipStream_t st) {
   if (T <= 0 || a.n_split <= 1) return hipSuccess;
-  hipLaunchKernelGGL(k_mla_combine, dim3(kDV / 128, a.H, T), dim3(256), 0, st, a);
+  launch_kernel(k_mla_combine, dim3(kDV / 128, a.H, T), dim3(256), st, a);
   return hipGetLastError();
 }
 

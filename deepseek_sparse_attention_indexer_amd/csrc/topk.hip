@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
 
 hipError_t launch_topk_lds(const TopkArgs& a, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk_lds, dim3(T), dim3(kNT), 0, st, a);
+  launch_kernel(k_topk_lds, dim3(T), dim3(kNT), st, a);
   return hipGetLastError();
 }
 
@@ -450,19 +450,19 @@ static int topk_chunks(const TopkArgs& a) { return max(1, (a.n_max + kTopkChunk 
 
 hipError_t launch_topk_hist(const TopkArgs& a, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk_hist, dim3(topk_chunks(a), T), dim3(kNT), 0, st, a);
+  launch_kernel(k_topk_hist, dim3(topk_chunks(a), T), dim3(kNT), st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_filter(const TopkArgs& a, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk_filter, dim3(topk_chunks(a), T), dim3(kNT), 0, st, a);
+  launch_kernel(k_topk_filter, dim3(topk_chunks(a), T), dim3(kNT), st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_finalize(const TopkArgs& a, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk_finalize, dim3(a.n_chunks + 1, T), dim3(kNT), 0, st, a);
+  launch_kernel(k_topk_finalize, dim3(a.n_chunks + 1, T), dim3(kNT), st, a);
   return hipGetLastError();
 }
 

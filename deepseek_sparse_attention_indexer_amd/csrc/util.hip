@@ -19,7 +19,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   if (bytes == 0) return hipSuccess;
   const size_t blocks = (bytes / 16 + 255) / 256;
   const unsigned grid = (unsigned)(blocks < 4096 ? (blocks ? blocks : 1) : 4096);
-  hipLaunchKernelGGL(k_fill_zero, dim3(grid), dim3(256), 0, st, static_cast<uint8_t*>(p), bytes);
+  launch_kernel(k_fill_zero, dim3(grid), dim3(256), st, static_cast<uint8_t*>(p), bytes);
   return hipGetLastError();
 }
 

@@ -208,11 +208,12 @@ int32_t dsa_abi_version(void);
 /* ---------------------------------------------------------------- kernel timing
  * Profiling aid (the per-stage timings the pages report, e.g. the scores / top-k / sparse
  * attention columns of PR 627's benchmark tables). While enabled, every kernel the library
- * launches is bracketed by two HIP events on the caller's stream (host-side event objects
- * from a pool; no device memory). dsa_profile_collect() waits for the recorded events,
+ * launches records two HIP events from its own dispatch on the caller's stream, at the
+ * kernel's start and end (host-side event objects from a pool; no device memory), so a
+ * duration is the kernel's alone. dsa_profile_collect() waits for the recorded events,
  * aggregates them by kernel name into `out` (at most max_entries rows), clears the record
  * and returns the number of rows written (or a negative dsa_status). Not thread-safe;
- * disabled by default; enabling adds event packets between the kernels of a call. */
+ * disabled by default. */
 typedef struct dsa_kernel_time {
   char name[40];
   int32_t count;
