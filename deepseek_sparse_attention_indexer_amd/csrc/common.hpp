@@ -49,6 +49,14 @@ __device__ __forceinline__ int64_t slot_of(const Paging& p, int b, int s) {
   return sl < 0 ? 0 : (sl >= p.n_slots ? p.n_slots - 1 : sl);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, then the
+// barrier. __syncthreads() also waits for every outstanding global load of the wave (vmcnt 0),
+// which would turn a prefetch issued before the barrier into a stall. Not for data written to
+// LDS by direct global->LDS loads (those complete on vmcnt).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 and +0 share a key.
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -33,11 +33,48 @@ struct KeyTile {
   u32x4_t b[4][KB];
   float sc[4];
 
-  __device__ __forceinline__ void load(const ScoreArgs& a, int b_req, int s0, int n, int g, int c) {
+  // Addressing of the tile's four 16-key sub-tiles for this lane's key c, in two halves so
+  // that the page-table reads of two tiles go out together and well before their key loads:
+  // table() issues the reads (raw entries + in-page offsets; packed caches: the positions),
+  // finish() turns them into clamped slots.
+  struct Addr {
+    int pg[4];
+    int off[4];
+  };
+  // Branch-free (a merge after a conditional read would force a wait right after it): a
+  // paged cache reads its block-table entry, a packed cache reads req_base[b] through the same
+  // load.
+  __device__ __forceinline__ static void table(const ScoreArgs& a, int b_req, int s0, int n, int c,
+                                               Addr& ad) {
+    const Paging& p = a.pg;
+    const bool paged = p.bt != nullptr;
+    const int32_t* tb = paged ? p.bt : p.req_base;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int pos = min(s0 + 16 * st + c, n - 1);
-      const int64_t slot = slot_of(a.pg, b_req, pos);
+      const int q = p.page_shift >= 0 ? (pos >> p.page_shift) : pos / p.page;
+      const int lp = min(max(q, 0), max((int)p.bt_stride - 1, 0));
+      ad.off[st] = paged ? pos - q * p.page : pos;
+      const int64_t at = paged ? (int64_t)b_req * p.bt_stride + lp : (int64_t)b_req;
+      ad.pg[st] = tb[at];
+    }
+  }
+  __device__ __forceinline__ static void finish(const ScoreArgs& a, const Addr& ad, int64_t* sl) {
+    const Paging& p = a.pg;
+    const bool paged = p.bt != nullptr;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int64_t in_page = (int64_t)min(max(ad.pg[st], 0), p.n_pages - 1) * p.page + ad.off[st];
+      const int64_t v = (int64_t)ad.pg[st] + ad.off[st];
+      const int64_t packed = v < 0 ? 0 : (v >= p.n_slots ? p.n_slots - 1 : v);
+      sl[st] = paged ? in_page : packed;
+    }
+  }
+
+  __device__ __forceinline__ void load(const ScoreArgs& a, const int64_t* sl, int g) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int64_t slot = sl[st];
       if constexpr (!FP8) {
         const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.keys) + slot * DI + 8 * g;
 #pragma unroll
@@ -73,6 +110,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
   constexpr int KB = DI / 32;
   constexpr int QB = 64 * DI * 2;   // bytes of the (padded) query heads of one row
   __shared__ __align__(16) uint8_t s_q[QB];
+  __shared__ float s_w[16 * MT];
   __shared__ uint32_t s_hist[HIST ? kHistBins : 1];
 
   const int t = blockIdx.y;
@@ -87,8 +125,14 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
   const int stride = gridDim.x * kScoreWaves;
   int tile = blockIdx.x * kScoreWaves + wave;
 
-  // 1. the row's query heads (everything waits on them), then 2. the first tile's keys; q is
-  // staged once per workgroup in LDS, zero-padded to 16 * MT heads
+  // 1. page-table entries of this wave's first two tiles, 2. the row's query heads and head
+  // weights (staged once per workgroup in LDS, zero-padded to 16 * MT heads), 3. the first
+  // tile's 16 key loads back to back. Loads complete in issue order, so each wait below only
+  // covers what it needs.
+  using Tile = KeyTile<DI, FP8>;
+  typename Tile::Addr ad_cur, ad_nxt;
+  if (tile < ntiles) Tile::table(a, b, tile << 6, n, c, ad_cur);
+  if (tile + stride < ntiles) Tile::table(a, b, (tile + stride) << 6, n, c, ad_nxt);
   constexpr int QPT = (16 * MT * DI * 2 + kScoreThreads * 16 - 1) / (kScoreThreads * 16);
   u32x4_t qv[QPT];
   {
@@ -100,37 +144,48 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
       qv[i] = o < qbytes ? *reinterpret_cast<const u32x4_t*>(qrow + o) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  KeyTile<DI, FP8> cur;
-  if (tile < ntiles) cur.load(a, b, tile << 6, n, g, c);
+  const float wraw = threadIdx.x < a.Hi ? a.w[(int64_t)t * a.ld_w + threadIdx.x] : 0.0f;
+  // q and w arrive with the table entries; staging them first keeps the key loads below clear
+  // of any wait
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int o = (threadIdx.x + i * kScoreThreads) * 16;
     if (o < 16 * MT * DI * 2) *reinterpret_cast<u32x4_t*>(s_q + o) = qv[i];
   }
-  float wv[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hr = 16 * mt + 4 * g + r;   // head of accumulator row r
-      wv[mt][r] = hr < a.Hi ? a.w[(int64_t)t * a.ld_w + hr] * a.index_scale : 0.0f;
-    }
+  if (threadIdx.x < 16 * MT) s_w[threadIdx.x] = wraw * a.index_scale;
   if constexpr (HIST)
     for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) s_hist[i] = 0;
-  __syncthreads();
-  // A operands: qa[mt][kb] = q_idx[t, 16 mt + c, 32 kb + 8 g .. +7]
+  Tile cur;
+  if (tile < ntiles) {
+    int64_t sl[4];
+    Tile::finish(a, ad_cur, sl);
+    cur.load(a, sl, g);
+  }
+  lds_barrier();   // not __syncthreads(): the first tile's key loads stay in flight
+  // A operands: qa[mt][kb] = q_idx[t, 16 mt + c, 32 kb + 8 g .. +7]; weights of the
+  // accumulator rows this lane holds (row r of head tile mt is head 16 mt + 4 g + r)
   u32x4_t qa[MT][KB];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
       qa[mt][kb] = *reinterpret_cast<const u32x4_t*>(s_q + ((16 * mt + c) * DI + 32 * kb + 8 * g) * 2);
+  float wv[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[mt][r] = s_w[16 * mt + 4 * g + r];
 
   while (tile < ntiles) {
     const int s0 = tile << 6;
     const int next = tile + stride;
-    KeyTile<DI, FP8> nxt;
-    if (next < ntiles) nxt.load(a, b, next << 6, n, g, c);   // prefetch
+    Tile nxt;
+    if (next < ntiles) {                                       // prefetch the next tile
+      int64_t sl[4];
+      Tile::finish(a, ad_nxt, sl);
+      nxt.load(a, sl, g);
+    }
+    if (next + stride < ntiles) Tile::table(a, b, (next + stride) << 6, n, c, ad_nxt);
     cur.widen();
     float part[4];
 #pragma unroll
@@ -172,7 +227,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
   }
 
   if constexpr (HIST) {
-    __syncthreads();
+    lds_barrier();
     if (ntiles > 0) {
       uint32_t* gh = a.hist + ((int64_t)t * kHistSlices + (blockIdx.x % kHistSlices)) * kHistBins;
       for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
