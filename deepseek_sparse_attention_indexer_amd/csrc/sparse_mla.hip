@@ -231,15 +231,29 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
     }
   };
 
-  // the first block's list entries go out before anything else (longest dependent chain),
-  // then the query heads, once per workgroup, through the row buffers (not yet in use)
-  if (nblk > 0) resolve(0, 0);
-  static_assert(HT * 16 * DQK * 2 <= (int)sizeof(s_rows), "q staging");
+  // The query heads (once per workgroup) are requested first, then the first block's list
+  // entries and table reads (the longest dependent chain), so both round trips overlap; q is
+  // staged through the row buffers (not yet in use).
+  constexpr int QBYTES = HT * 16 * DQK * 2;
+  constexpr int QIT = (QBYTES + NT * 16 - 1) / (NT * 16);
+  static_assert(QBYTES <= (int)sizeof(s_rows), "q staging");
+  u32x4_t qreg[QIT];
   {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)t * a.ld_q + (int64_t)(hg * HT * 16) * DQK);
+#pragma unroll
+    for (int i = 0; i < QIT; ++i) {
+      const int o = (threadIdx.x + i * NT) * 16;
+      qreg[i] = o < QBYTES ? *reinterpret_cast<const u32x4_t*>(qsrc + o) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  if (nblk > 0) resolve(0, 0);
+  {
     uint8_t* qdst = reinterpret_cast<uint8_t*>(&s_rows[0][0][0]);
-    for (int o = threadIdx.x * 16; o < HT * 16 * DQK * 2; o += NT * 16)
-      *reinterpret_cast<u32x4_t*>(qdst + o) = *reinterpret_cast<const u32x4_t*>(qsrc + o);
+#pragma unroll
+    for (int i = 0; i < QIT; ++i) {
+      const int o = (threadIdx.x + i * NT) * 16;
+      if (o < QBYTES) *reinterpret_cast<u32x4_t*>(qdst + o) = qreg[i];
+    }
   }
   __syncthreads();
   u32x4_t qb[KS];
@@ -382,50 +396,70 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
 // keeps several splits of loads in flight and the work spreads over many CUs; the groups'
 // sums meet in LDS.
 __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
-  constexpr int NG = 8;
+  constexpr int NG = 8;                            // split groups of 32 threads
   __shared__ f32x4_t s_acc[NG][32];
   __shared__ float s_l[NG];
+  __shared__ float s_m[NG];
   const int t = blockIdx.z;
   const int head = blockIdx.y;
-  const int sg = threadIdx.x >> 5;                 // split group
-  const int d0 = blockIdx.x * 128 + (threadIdx.x & 31) * 4;
+  const int sg = threadIdx.x >> 5;
+  const int ci = threadIdx.x & 31;
+  const int d0 = blockIdx.x * 128 + ci * 4;
   const int S = a.n_split;
   const float* pml = a.part_ml + ((int64_t)t * a.H + head) * S * 2;
   const float* po = a.part_o + ((int64_t)t * a.H + head) * S * kDV + d0;
-  float ms = -INFINITY;
-  for (int sp = 0; sp < S; ++sp) ms = fmaxf(ms, pml[2 * sp]);
+  // one pass: every partial (o, m, l) of this group's splits is requested at once and merged
+  // online in registers (base-2 maxima); no separate pass for the global maximum
+  float mg = -INFINITY, lg = 0.f;
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float ls = 0.f;
-  if (ms != -INFINITY) {
-    for (int sp0 = sg; sp0 < S; sp0 += NG * 8) {
-      f32x4_t v[8];
-      float m[8], l[8];
+  for (int sp0 = sg; sp0 < S; sp0 += NG * 8) {
+    f32x4_t v[8];
+    float m[8], l[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = min(sp0 + u * NG, S - 1);
+      v[u] = *reinterpret_cast<const f32x4_t*>(po + (int64_t)sp * kDV);
+      m[u] = pml[2 * sp];
+      l[u] = pml[2 * sp + 1];
+    }
+    float mx = mg;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (sp0 + u * NG >= S) m[u] = -INFINITY;
+      mx = fmaxf(mx, m[u]);
+    }
+    if (mx != -INFINITY) {
+      const float alpha = mg == -INFINITY ? 0.f : exp2f(mg - mx);
+      acc *= alpha;
+      lg *= alpha;
+      mg = mx;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int sp = min(sp0 + u * NG, S - 1);
-        v[u] = *reinterpret_cast<const f32x4_t*>(po + (int64_t)sp * kDV);
-        m[u] = sp0 + u * NG < S ? pml[2 * sp] : -INFINITY;
-        l[u] = pml[2 * sp + 1];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wgt = m[u] == -INFINITY ? 0.f : exp2f(m[u] - ms);
-        ls += wgt * l[u];
+        const float wgt = m[u] == -INFINITY ? 0.f : exp2f(m[u] - mg);
+        lg += wgt * l[u];
         acc += wgt * v[u];
       }
     }
   }
-  s_acc[sg][threadIdx.x & 31] = acc;
-  if ((threadIdx.x & 31) == 0) s_l[sg] = ls;
-  __syncthreads();
+  s_acc[sg][ci] = acc;
+  if (ci == 0) {
+    s_l[sg] = lg;
+    s_m[sg] = mg;
+  }
+  lds_barrier();
   if (sg != 0) return;
-  const int ci = threadIdx.x & 31;
-  f32x4_t tot = s_acc[0][ci];
-  float lt = s_l[0];
+  float ms = -INFINITY;
 #pragma unroll
-  for (int q = 1; q < NG; ++q) {
-    tot += s_acc[q][ci];
-    lt += s_l[q];
+  for (int q = 0; q < NG; ++q) ms = fmaxf(ms, s_m[q]);
+  f32x4_t tot = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float lt = 0.f;
+  if (ms != -INFINITY) {
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const float wgt = s_m[q] == -INFINITY ? 0.f : exp2f(s_m[q] - ms);
+      tot += wgt * s_acc[q][ci];
+      lt += wgt * s_l[q];
+    }
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)head * kDV + d0;

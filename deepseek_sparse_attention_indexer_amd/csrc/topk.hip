@@ -39,13 +39,17 @@ __device__ __forceinline__ uint32_t wave_reserve(bool pred, uint32_t* counter) {
   return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
 }
 
+// Inclusive scan over the 64 lanes with DPP moves (a few cycles each) instead of LDS
+// permutes: shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the row totals carried
+// forward with the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (rows 2, 3).
+// Lanes without a source read 0 (bound_ctrl).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t u = __shfl_up(v, d);
-    if (lane >= d) v += u;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
@@ -55,9 +59,9 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* s_w, u
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(v);
-  __syncthreads();
+  lds_barrier();
   if (lane == 63) s_w[w] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t off = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
@@ -94,7 +98,7 @@ __device__ void find_digit_desc(const uint32_t* h, int nb, uint32_t need, uint32
       acc += cnt;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Radix select (descending) over items i < cnt for which get(i, key) is true and whose key
@@ -113,19 +117,19 @@ __device__ uint32_t radix_select_desc(int cnt, Get get, uint32_t prefix, uint32_
     const int nb = 1 << bits;
     const uint32_t dm = (uint32_t)(nb - 1);
     for (int i = threadIdx.x; i < nb; i += kNT) s_hist[i] = 0;
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < cnt; i += kNT) {
       uint32_t key;
       if (get(i, key) && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & dm], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     find_digit_desc(s_hist, nb, need, s_w, s_res);
     const uint32_t d = s_res[0];
     need -= s_res[1];
     last_eq = s_hist[d];
     prefix |= d << shift;
     pmask |= dm << shift;
-    __syncthreads();
+    lds_barrier();
   }
   *eq_count = last_eq;
   return prefix;
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
   const float* row = a.logits + (int64_t)t * a.ld_logits;
   for (int i = threadIdx.x; i < n; i += kNT) s_key[i] = float_key(row[i]);
   if (threadIdx.x == 0) s_res[2] = 0;
-  __syncthreads();
+  lds_barrier();
 
   uint32_t need = (uint32_t)k, eq = 0;
   auto get_key = [&](int i, uint32_t& key) { key = s_key[i]; return true; };
@@ -183,12 +187,12 @@ __global__ __launch_bounds__(kNT) void k_topk_hist(TopkArgs a) {
   const int s0 = blockIdx.x * kTopkChunk;
   if (s0 >= n) return;
   for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
-  __syncthreads();
+  lds_barrier();
   const float* row = a.logits + (int64_t)t * a.ld_logits;
   const int s1 = min(n, s0 + kTopkChunk);
   for (int s = s0 + threadIdx.x; s < s1; s += kNT)
     atomicAdd(&s_hist[float_key(row[s]) >> (32 - kHistBits)], 1u);
-  __syncthreads();
+  lds_barrier();
   uint32_t* gh = a.hist + ((int64_t)t * kHistSlices + (blockIdx.x % kHistSlices)) * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += kNT) {
     const uint32_t v = s_hist[i];
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
     for (int sl = 0; sl < kHistSlices; ++sl) v += gh[sl * kHistBins + i];
     s_hist[i] = v;
   }
-  __syncthreads();
+  lds_barrier();
   find_digit_desc(s_hist, kHistBins, (uint32_t)k, s_w, s_res);
   const uint32_t d1 = s_res[0];
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
     if (c0 < nch) s_off[c0] = incl - v0 - v1;
     if (c0 + 1 < nch) s_off[c0 + 1] = incl - v1;
     if (threadIdx.x == 0) s_off[nch] = total;
-    __syncthreads();
+    lds_barrier();
   }
   const uint32_t n_cand = s_off[nch];
   const bool in_lds = n_cand <= (uint32_t)kTopkCandLds;
@@ -403,12 +407,12 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t need1 = (uint32_t)k - above1;
   find_digit_desc(s_hist, kHistBins, need1, s_w, s_res);
   const uint32_t pre = (d1 << kHistBits) | s_res[0];     // top 24 bits of the threshold key
   uint32_t need = need1 - s_res[1], eq = 0, pos_thr = 0;
-  __syncthreads();
+  lds_barrier();
   // 2. the threshold sub-bin: its last 8 bits, then ties toward the smaller position
   auto get_key = [&](int i, uint32_t& key) { key = key_of((uint32_t)i); return true; };
   const uint32_t thr =
