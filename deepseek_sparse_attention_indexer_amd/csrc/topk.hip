@@ -135,6 +135,39 @@ __device__ uint32_t radix_select_desc(int cnt, Get get, uint32_t prefix, uint32_
   return prefix;
 }
 
+// The same radix select over items held in registers: item u (< U) of every thread, taken
+// when get(u, key) is true.
+template <int U, class Get>
+__device__ uint32_t radix_select_regs(Get get, uint32_t prefix, uint32_t pmask, int low_bits,
+                                      uint32_t& need, uint32_t* eq_count, uint32_t* s_hist,
+                                      uint32_t* s_w, uint32_t* s_res) {
+  int shift = low_bits;
+  uint32_t last_eq = 0;
+  while (shift > 0) {
+    const int bits = shift >= 12 ? 12 : shift;
+    shift -= bits;
+    const int nb = 1 << bits;
+    const uint32_t dm = (uint32_t)(nb - 1);
+    for (int i = threadIdx.x; i < nb; i += kNT) s_hist[i] = 0;
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t key;
+      if (get(u, key) && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & dm], 1u);
+    }
+    lds_barrier();
+    find_digit_desc(s_hist, nb, need, s_w, s_res);
+    const uint32_t d = s_res[0];
+    need -= s_res[1];
+    last_eq = s_hist[d];
+    prefix |= d << shift;
+    pmask |= dm << shift;
+    lds_barrier();
+  }
+  *eq_count = last_eq;
+  return prefix;
+}
+
 // ------------------------------------------------------------------ rows that fit in LDS
 __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
   __shared__ uint32_t s_key[kTopkLdsMax];
@@ -346,13 +379,14 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   }
 
   // ---- the resolver
-  if (threadIdx.x == 0) a.lens[t] = min(n, k);
-  {
+  auto clear_hist = [&]() {   // the first-digit histogram back to zero (no one here reads it)
     uint32_t* gh = a.hist + (int64_t)t * kHistSlices * kHistBins;
     for (int i = threadIdx.x; i < kHistSlices * kHistBins; i += kNT) gh[i] = 0;
-  }
+    if (threadIdx.x == 0) a.lens[t] = min(n, k);
+  };
   if (n <= k) {
     for (int i = n + threadIdx.x; i < k; i += kNT) out[i] = -1;
+    clear_hist();
     return;
   }
   const uint32_t d1 = a.thr1[2 * t];
@@ -372,37 +406,53 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   }
   const uint32_t n_cand = s_off[nch];
   const bool in_lds = n_cand <= (uint32_t)kTopkCandLds;
-  // workspace address of candidate i (candidates are numbered chunk by chunk)
+  // Chunk of candidate i (candidates are numbered chunk by chunk): the largest c < nch with
+  // prefix[c] <= i, by binary lifting with a uniform number of steps, so that several lookups
+  // interleave their LDS reads. prefix[nch] = n_cand > i stops every probe past the end.
+  const int steps = nch <= 1 ? 0 : 32 - __clz(nch - 1);
   auto cand_at = [&](uint32_t i) -> int64_t {
-    int lo = 0, hi = nch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
+    int lo = 0;
+    for (int r = steps - 1; r >= 0; --r) {
+      const int probe = lo + (1 << r);
+      if (s_off[min(probe, nch)] <= i) lo = probe;
     }
     return ((int64_t)t * a.n_chunks + lo) * kTopkChunk + (i - s_off[lo]);
   };
   auto key_of = [&](uint32_t i) { return in_lds ? s_ck[i] : a.cand_key[cand_at(i)]; };
   auto pos_of = [&](uint32_t i) { return in_lds ? s_cp[i] : a.cand_pos[cand_at(i)]; };
-  // 1. gather the candidates; histogram of their second digit
-  for (uint32_t i0 = 0; i0 < n_cand; i0 += 8 * kNT) {
-    uint32_t kk[8];
-    int32_t pp[8];
+  // 1. gather the candidates; histogram of their second digit. Up to RU * kNT candidates stay
+  // in registers (candidate u * kNT + thread) for every later step.
+  constexpr int RU = 8;
+  const bool in_regs = n_cand <= (uint32_t)(RU * kNT);
+  uint32_t kk[RU];
+  int32_t pp[RU];
+  for (uint32_t i0 = 0; i0 < n_cand; i0 += RU * kNT) {
+    // lanes past the end re-read the last candidate (n_cand >= 1: the bin holds the k-th key)
+    uint32_t ic[RU];
+    int lo[RU];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t i = i0 + u * kNT + threadIdx.x;
-      kk[u] = 0u;
-      pp[u] = 0;
-      if (i < n_cand) {
-        const int64_t at = cand_at(i);
-        kk[u] = a.cand_key[at];
-        if (in_lds) pp[u] = a.cand_pos[at];
+    for (int u = 0; u < RU; ++u) {
+      ic[u] = min(i0 + u * kNT + threadIdx.x, n_cand - 1);
+      lo[u] = 0;
+    }
+    for (int r = steps - 1; r >= 0; --r) {
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        const int probe = lo[u] + (1 << r);
+        if (s_off[min(probe, nch)] <= ic[u]) lo[u] = probe;
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < RU; ++u) {
+      const int64_t at = ((int64_t)t * a.n_chunks + lo[u]) * kTopkChunk + (ic[u] - s_off[lo[u]]);
+      kk[u] = a.cand_key[at];
+      pp[u] = a.cand_pos[at];
+    }
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
       const uint32_t i = i0 + u * kNT + threadIdx.x;
       if (i < n_cand) {
-        if (in_lds) { s_ck[i] = kk[u]; s_cp[i] = pp[u]; }
+        if (in_lds && !in_regs) { s_ck[i] = kk[u]; s_cp[i] = pp[u]; }
         atomicAdd(&s_hist[(kk[u] >> D2) & (kHistBins - 1)], 1u);
       }
     }
@@ -414,34 +464,69 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   uint32_t need = need1 - s_res[1], eq = 0, pos_thr = 0;
   lds_barrier();
   // 2. the threshold sub-bin: its last 8 bits, then ties toward the smaller position
-  auto get_key = [&](int i, uint32_t& key) { key = key_of((uint32_t)i); return true; };
-  const uint32_t thr =
-      radix_select_desc((int)n_cand, get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
-  if (eq > need) {
-    uint32_t need2 = need, eq2 = 0;
-    auto get_tie = [&](int i, uint32_t& key) {
-      key = ~(uint32_t)pos_of((uint32_t)i);
-      return key_of((uint32_t)i) == thr;
+  uint32_t thr;
+  if (in_regs) {
+    auto get_key = [&](int u, uint32_t& key) {
+      key = kk[u];
+      return u * kNT + threadIdx.x < n_cand;
     };
-    pos_thr = radix_select_desc((int)n_cand, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
+    thr = radix_select_regs<RU>(get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
+    if (eq > need) {
+      uint32_t need2 = need, eq2 = 0;
+      auto get_tie = [&](int u, uint32_t& key) {
+        key = ~(uint32_t)pp[u];
+        return u * kNT + threadIdx.x < n_cand && kk[u] == thr;
+      };
+      pos_thr = radix_select_regs<RU>(get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
+    }
+  } else {
+    auto get_key = [&](int i, uint32_t& key) { key = key_of((uint32_t)i); return true; };
+    thr = radix_select_desc((int)n_cand, get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
+    if (eq > need) {
+      uint32_t need2 = need, eq2 = 0;
+      auto get_tie = [&](int i, uint32_t& key) {
+        key = ~(uint32_t)pos_of((uint32_t)i);
+        return key_of((uint32_t)i) == thr;
+      };
+      pos_thr = radix_select_desc((int)n_cand, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
+    }
   }
   const bool all_ties = eq <= need;
   auto selected = [&](uint32_t key, int32_t pos) {
     const uint32_t hi = key >> D2;
     return hi > pre || (hi == pre && (key > thr || (key == thr && (all_ties || ~(uint32_t)pos >= pos_thr))));
   };
-  // 3. write the selected candidates after the keys above the bin, thread-major
-  uint32_t m = 0;
-  for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) m += selected(key_of(i), pos_of(i));
+  // 3. write the selected candidates after the keys above the bin, thread-major (candidate
+  // thread + j * kNT for j = 0, 1, ... in both forms)
   uint32_t tot;
-  uint32_t o = above1 + block_incl_scan(m, s_w, &tot) - m;
-  for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) {
-    const int32_t pos = pos_of(i);
-    if (selected(key_of(i), pos)) {
-      if (o < (uint32_t)k) out[o] = pos;
-      ++o;
+  if (in_regs) {
+    uint32_t sel = 0, m = 0;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const bool x = u * kNT + threadIdx.x < n_cand && selected(kk[u], pp[u]);
+      sel |= (uint32_t)x << u;
+      m += x;
+    }
+    uint32_t o = above1 + block_incl_scan(m, s_w, &tot) - m;
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+      if (sel >> u & 1u) {
+        if (o < (uint32_t)k) out[o] = pp[u];
+        ++o;
+      }
+  } else {
+    uint32_t m = 0;
+    for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) m += selected(key_of(i), pos_of(i));
+    uint32_t o = above1 + block_incl_scan(m, s_w, &tot) - m;
+    for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) {
+      const int32_t pos = pos_of(i);
+      if (selected(key_of(i), pos)) {
+        if (o < (uint32_t)k) out[o] = pos;
+        ++o;
+      }
     }
   }
+  clear_hist();   // last: stores in flight would hold up every wait above (vmcnt counts them)
 }
 
 hipError_t launch_topk_lds(const TopkArgs& a, int T, hipStream_t st) {
