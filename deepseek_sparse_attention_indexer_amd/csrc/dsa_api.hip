@@ -22,6 +22,7 @@ namespace {
 // kernel ends). It has a fixed size, so data regions of one problem never overlap control
 // words of another and one workspace can serve every entry and problem size.
 constexpr int kMaxLongRows = 64;                  // long-row top-k rows per launch batch
+constexpr int kPrefillMinRows = 64;               // rows from which the shared-key score kernel is used
 constexpr int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 constexpr int64_t kOffHist = 0;
 constexpr int64_t kHeaderBytes = align256(kOffHist + (int64_t)kMaxLongRows * kHistSlices * kHistBins * 4);
@@ -413,6 +414,12 @@ dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
   a.logits = s.logits;
   a.ld_logits = s.ld_logits;
   a.hist = hist;
+  // Rows that may share a request (a row table is given) and are many: the prefill kernel,
+  // whose workgroups share each key tile among 8 rows. Otherwise one row per workgroup.
+  const bool shared_rows = r.row_req != nullptr && r.T >= kPrefillMinRows && hist == nullptr &&
+                           s.keys->dtype == DSA_KEY_BF16 && s.keys->n_slots <= INT32_MAX;
+  if (shared_rows)
+    return hip_status(timed("index_scores_prefill", st, [&] { return launch_index_scores_prefill(a, s.di, r.T, st); }));
   return hip_status(timed(hist ? "index_scores_hist" : "index_scores", st, [&] {
     return launch_index_scores(a, s.di, s.keys->dtype == DSA_KEY_FP8, hist != nullptr, r.T, st);
   }));

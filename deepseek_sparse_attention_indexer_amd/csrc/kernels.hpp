@@ -61,6 +61,9 @@ struct ScoreArgs {
 
 hipError_t launch_index_scores(const ScoreArgs& a, int di, bool fp8, bool hist, int T,
                                hipStream_t st);
+// many rows sharing keys (prefill): 8 rows per workgroup share each key tile; bf16 keys,
+// slots < 2^31
+hipError_t launch_index_scores_prefill(const ScoreArgs& a, int di, int T, hipStream_t st);
 
 struct TopkArgs {
   const float* logits;
