@@ -93,6 +93,42 @@ def read_traffic(kernel, workload):
         return None
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def prefill_indexer(dsa, to_device, workloads, torch, dev, reps=5):
+    """The indexer's score kernel on the causal prefill (segments 8192 + 1, 64 x 128 indexer
+    heads): MFMA-equivalent rate over the dense bf16 peak."""
+    import numpy as np
+    prob = workloads.causal_prefill((8192, 1), make_attn=False, name="causal_prefill_8k")
+    d = to_device(prob, dev)
+    ld = ((prob.n_max + 63) // 64) * 64
+    logits = torch.empty(prob.T, ld, dtype=torch.float32, device=dev)
+    pairs = int(prob.row_len.astype(np.int64).sum())
+    flops = pairs * 2 * prob.Hi * prob.di
+
+    def run():
+        dsa.dsa_index_scores(d.q_idx, d.w, d.keys, d.rows, prob.Hi, prob.di, prob.index_scale, logits)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    dsa.dsa_profile_enable(True)
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    prof = dsa.dsa_profile_collect()
+    dsa.dsa_profile_enable(False)
+    name, rec = max(prof.items(), key=lambda kv: kv[1]["total_ms"])
+    us = rec["total_ms"] / rec["count"] * 1e3
+    achieved = flops / (us * 1e-6) / 1e12
+    return {"workload": "causal_prefill_8k", "kernel": name, "rows": int(prob.T), "score_pairs": pairs,
+            "gflop": round(flops / 1e9, 2), "avg_us": round(us, 1), "bound": "mfma",
+            "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "timing": "HIP events from each dispatch, inputs resident (8193 rows x 64 x 128 bf16)"}
+
+
 def cpu_baseline(prob, seconds):
     import numpy as np  # noqa: F401
     import oracle
@@ -123,6 +159,7 @@ def main():
     ap.add_argument("--workload", default="glm_decode_128k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -237,6 +274,9 @@ def main():
         "vs_baseline_note": "value / 411 us: the pages' Gluon 128k decode total (tokenspeed PR 627, "
                             "GFX9-class GPU, heads and precision unstated); context, not the target",
     }
+    if not args.no_prefill:
+        log("prefill indexer ...")
+        res["prefill_indexer"] = prefill_indexer(dsa, to_device, workloads, torch, dev)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)

@@ -57,6 +57,45 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// One of two pagings, field by field (selecting a reference would put both in scratch).
+__device__ __forceinline__ Paging pick_paging(bool x, const Paging& p1, const Paging& p0) {
+  Paging r;
+  r.bt = x ? p1.bt : p0.bt;
+  r.req_base = x ? p1.req_base : p0.req_base;
+  r.bt_stride = x ? p1.bt_stride : p0.bt_stride;
+  r.n_slots = x ? p1.n_slots : p0.n_slots;
+  r.page = x ? p1.page : p0.page;
+  r.page_shift = x ? p1.page_shift : p0.page_shift;
+  r.n_pages = x ? p1.n_pages : p0.n_pages;
+  r._pad = 0;
+  return r;
+}
+
+// The same mapping in two steps, so that many table reads are in flight before any is used
+// and no branch separates a read from its use (a merge after a conditional read makes the
+// compiler wait right there): slot_read issues the block-table read (a packed cache reads
+// req_base[b] through the same load), slot_done clamps into the cache. s >= 0.
+struct SlotRead {
+  int ent;
+  int off;
+};
+__device__ __forceinline__ SlotRead slot_read(const Paging& p, int b, int s) {
+  const bool paged = p.bt != nullptr;
+  const int q = p.page_shift >= 0 ? (s >> p.page_shift) : s / p.page;
+  const int lp = min(max(q, 0), max((int)p.bt_stride - 1, 0));
+  SlotRead r;
+  r.off = paged ? s - q * p.page : s;
+  const int32_t* tb = paged ? p.bt : p.req_base;
+  r.ent = tb[paged ? (int64_t)b * p.bt_stride + lp : (int64_t)b];
+  return r;
+}
+__device__ __forceinline__ int64_t slot_done(const Paging& p, SlotRead r) {
+  const int64_t in_page = (int64_t)min(max(r.ent, 0), p.n_pages - 1) * p.page + r.off;
+  const int64_t v = (int64_t)r.ent + r.off;
+  const int64_t packed = v < 0 ? 0 : (v >= p.n_slots ? p.n_slots - 1 : v);
+  return p.bt != nullptr ? in_page : packed;
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 and +0 share a key.
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

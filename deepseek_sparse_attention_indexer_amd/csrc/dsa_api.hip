@@ -131,7 +131,8 @@ struct MlaPlan {
 MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   // A CU sustains only ~25 GB/s of gathers and a lone wave far less, so decode spreads rows
   // AND partial outputs over every CU: one 16-head tile per 4-wave workgroup (the waves split
-  // the value columns) and about one workgroup per CU. Prefill rows have no split; all heads
+  // the value columns) and about two workgroups per CU, so two gathered blocks are in flight
+  // per CU (splits never go below one 32-row block). Prefill rows have no split; all heads
   // of a row share each gathered block.
   MlaPlan p;
   const int tiles = H / 16;
@@ -140,7 +141,7 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   if (decode) {
     p.ht = 1;
     const int64_t base = (int64_t)T * tiles;
-    s = (int)std::min<int64_t>((256 + base - 1) / base, nblk);
+    s = (int)std::min<int64_t>((512 + base - 1) / base, nblk);   // about two workgroups per CU
     s = std::max(1, s);
   } else {
     p.ht = tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1);
@@ -184,6 +185,7 @@ dsa_status check_kv(const dsa_kv_cache* kv, int d_qk) {
   if (!kv || !kv->data || !al16(kv->data)) return DSA_ERR_ARG;
   dsa_status s = check_paging(kv->paging, kv->n_slots);
   if (s != DSA_OK) return s;
+  if (kv->n_slots > (int64_t(1) << 30)) return DSA_ERR_UNSUPPORTED;   // slots travel in 30 bits
   if (kv->d_nope + kv->d_rope != d_qk) return DSA_ERR_ARG;
   switch (kv->format) {
     case DSA_KV_BF16:
@@ -393,6 +395,14 @@ dsa_status check_scores(const ScoreIn& s) {
   return DSA_OK;
 }
 
+// Many rows that share requests (more rows than requests: a prefill, an extend chunk,
+// speculative verification): scored by the kernel whose workgroups share each key tile among
+// 8 rows. Otherwise one row per workgroup.
+bool shared_key_rows(const dsa_rows& r, const dsa_key_cache& k) {
+  return r.row_req != nullptr && r.T >= kPrefillMinRows && r.T > r.n_req && k.dtype == DSA_KEY_BF16 &&
+         k.n_slots <= INT32_MAX;
+}
+
 dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
   const dsa_rows& r = *s.rows;
   if (r.T == 0 || r.n_max == 0) return DSA_OK;
@@ -414,11 +424,7 @@ dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
   a.logits = s.logits;
   a.ld_logits = s.ld_logits;
   a.hist = hist;
-  // Rows that may share a request (a row table is given) and are many: the prefill kernel,
-  // whose workgroups share each key tile among 8 rows. Otherwise one row per workgroup.
-  const bool shared_rows = r.row_req != nullptr && r.T >= kPrefillMinRows && hist == nullptr &&
-                           s.keys->dtype == DSA_KEY_BF16 && s.keys->n_slots <= INT32_MAX;
-  if (shared_rows)
+  if (hist == nullptr && shared_key_rows(r, *s.keys))
     return hip_status(timed("index_scores_prefill", st, [&] { return launch_index_scores_prefill(a, s.di, r.T, st); }));
   return hip_status(timed(hist ? "index_scores_hist" : "index_scores", st, [&] {
     return launch_index_scores(a, s.di, s.keys->dtype == DSA_KEY_FP8, hist != nullptr, r.T, st);
@@ -566,7 +572,8 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
 
   // step 1 (+ the first top-k digit when the long-row path will run and fits one batch)
   const bool long_rows = rows->n_max > kTopkLdsMax;
-  const bool fuse_hist = long_rows && T <= kMaxLongRows;
+  // (rows that share their keys are scored by the shared-key kernel, which has no histogram)
+  const bool fuse_hist = long_rows && T <= kMaxLongRows && !shared_key_rows(*rows, *keys);
   sc.logits = logits;
   s = run_scores(sc, fuse_hist ? reinterpret_cast<uint32_t*>(wsb + kOffHist) : nullptr, st);
   if (s != DSA_OK) return s;

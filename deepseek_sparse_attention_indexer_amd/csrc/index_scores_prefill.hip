@@ -10,7 +10,7 @@
 // head reduction. One query row per workgroup (the decode kernel) re-reads every key tile
 // for every row, which makes a long causal prefill L2-bandwidth bound. Here a workgroup
 // takes 8 consecutive rows (one per wave, all heads held in registers as MFMA A operands) and
-// a chunk of 4096 key positions; each 64-key tile is read from memory once into a
+// a chunk of up to 8192 key positions; each 64-key tile is read from memory once into a
 // double-buffered LDS tile and used by all 8 rows. The tile is stored XOR-swizzled (16-byte
 // chunk p of key row r at p ^ (r mod chunks-per-row)) so that the 16 lanes that read one
 // column of 16 key rows hit distinct banks. The epilogue is the decode kernel's: ReLU and the
@@ -28,10 +28,10 @@ namespace dsa {
 constexpr int kPfRows = 8;                      // query rows per workgroup, one per wave
 constexpr int kPfThreads = 64 * kPfRows;
 constexpr int kPfTile = 64;                     // keys per LDS tile
-constexpr int kPfChunk = 8192;                  // key positions per workgroup (grid x)
+constexpr int kPfChunkMax = 8192;               // key positions per workgroup (grid x), at most
 
 template <int DI, int MT>
-__global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArgs a, int T) {
+__global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArgs a, int T, int chunk) {
   constexpr int KB = DI / 32;                   // MFMA k-blocks of one key row
   constexpr int CPR = DI * 2 / 16;              // 16-byte chunks per key row
   constexpr int RB = DI * 2;                    // bytes per key row
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArg
   constexpr int LPT = TB / (16 * kPfThreads);   // 16-byte loads per thread per tile
   static_assert(LPT >= 1 && TB % (16 * kPfThreads) == 0, "tile staging");
   __shared__ __align__(16) uint8_t s_k[2][TB];
-  __shared__ int32_t s_slot[kPfChunk];
+  __shared__ int32_t s_slot[kPfChunkMax];
   __shared__ int32_t s_rowb[kPfRows];
   __shared__ int32_t s_rown[kPfRows];
 
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArg
   // starting the largest workgroups first keeps the end of the grid from waiting on them
   const int t = (gridDim.y - 1 - blockIdx.y) * kPfRows + wave;
   const bool row_ok = t < T;
-  const int c0 = blockIdx.x * kPfChunk;
+  const int c0 = blockIdx.x * chunk;
   int my_n = 0;
   if (lane == 0) {
     int b = -1;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArg
         nmax = max(nmax, s_rown[w]);
       }
     done |= grp;
-    const int kend = min(c0 + kPfChunk, nmax);
+    const int kend = min(c0 + chunk, nmax);
     if (kend <= c0) continue;
     const bool mine = grp >> wave & 1u;
     const int ntile = (kend - c0 + kPfTile - 1) / kPfTile;
@@ -126,23 +126,22 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArg
     // slots of this request's keys in the chunk: every table read of the thread goes out at
     // once (a paged cache reads its block table, a packed one req_base[b]); positions past
     // kend are clamped and not stored
-    {
-      constexpr int SPT = kPfChunk / kPfThreads;
+    for (int u0 = 0; u0 < kend - c0; u0 += 8 * kPfThreads) {
       const Paging& pg = a.pg;
       const bool paged = pg.bt != nullptr;
       const int32_t* tb = paged ? pg.bt : pg.req_base;
-      int ent[SPT], offs[SPT];
+      int ent[8], offs[8];
 #pragma unroll
-      for (int u = 0; u < SPT; ++u) {
-        const int pos = c0 + min(threadIdx.x + u * kPfThreads, kend - c0 - 1);
+      for (int u = 0; u < 8; ++u) {
+        const int pos = c0 + min(u0 + (int)threadIdx.x + u * kPfThreads, kend - c0 - 1);
         const int q = pg.page_shift >= 0 ? (pos >> pg.page_shift) : pos / pg.page;
         const int lp = min(max(q, 0), max((int)pg.bt_stride - 1, 0));
         offs[u] = paged ? pos - q * pg.page : pos;
         ent[u] = tb[paged ? (int64_t)b * pg.bt_stride + lp : (int64_t)b];
       }
 #pragma unroll
-      for (int u = 0; u < SPT; ++u) {
-        const int i = threadIdx.x + u * kPfThreads;
+      for (int u = 0; u < 8; ++u) {
+        const int i = u0 + threadIdx.x + u * kPfThreads;
         const int64_t in_page = (int64_t)min(max(ent[u], 0), pg.n_pages - 1) * pg.page + offs[u];
         const int64_t v = (int64_t)ent[u] + offs[u];
         const int64_t packed = v < 0 ? 0 : (v >= pg.n_slots ? pg.n_slots - 1 : v);
@@ -246,10 +245,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArg
 
 template <int DI>
 static hipError_t launch_prefill_di(const ScoreArgs& a, int T, hipStream_t st) {
-  const dim3 grid((a.n_max + kPfChunk - 1) / kPfChunk, (T + kPfRows - 1) / kPfRows);
-  if (a.Hi <= 16) launch_kernel(k_index_scores_prefill<DI, 1>, grid, dim3(kPfThreads), st, a, T);
-  else if (a.Hi <= 32) launch_kernel(k_index_scores_prefill<DI, 2>, grid, dim3(kPfThreads), st, a, T);
-  else launch_kernel(k_index_scores_prefill<DI, 4>, grid, dim3(kPfThreads), st, a, T);
+  // the largest chunk that still gives about two workgroups per CU (few row blocks, e.g. an
+  // extend chunk, need short chunks to fill the chip; a long prefill has rows enough)
+  const int nrb = (T + kPfRows - 1) / kPfRows;
+  int chunk = kPfChunkMax;
+  while (chunk > 1024 && (int64_t)nrb * ((a.n_max + chunk - 1) / chunk) < 512) chunk >>= 1;
+  const dim3 grid((a.n_max + chunk - 1) / chunk, nrb);
+  if (a.Hi <= 16) launch_kernel(k_index_scores_prefill<DI, 1>, grid, dim3(kPfThreads), st, a, T, chunk);
+  else if (a.Hi <= 32) launch_kernel(k_index_scores_prefill<DI, 2>, grid, dim3(kPfThreads), st, a, T, chunk);
+  else launch_kernel(k_index_scores_prefill<DI, 4>, grid, dim3(kPfThreads), st, a, T, chunk);
   return hipGetLastError();
 }
 

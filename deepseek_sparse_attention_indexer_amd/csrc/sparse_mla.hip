@@ -31,6 +31,7 @@
 namespace dsa {
 
 constexpr int kNB = 32;     // rows per block
+constexpr int kResolve = 1024;   // list entries resolved to slots per pass (multiple of kNB)
 constexpr int kDV = 512;    // value width
 
 template <int FMT, int DQK>
@@ -131,9 +132,8 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
   constexpr int RE = RowGeom<FMT, DQK>::kElems;
   constexpr int UN = RowGeom<FMT, DQK>::kUnits;
   __shared__ __align__(16) uint16_t s_rows[2][kNB][RE];   // double-buffered gathered block
-  __shared__ int64_t s_off[2][kNB];                        // byte offset of each row's data
-  __shared__ int64_t s_soff[2][kNB];                       // and of its scales (fp8)
-  __shared__ int32_t s_info[2][kNB];                       // bit0: valid, bit1: extra list
+  // list entries of the current pass resolved to cache slots: slot | list << 30, -1 = padding
+  __shared__ int32_t s_slot[kResolve];
 
   const int t = blockIdx.z;
   const int hg = blockIdx.y;
@@ -156,31 +156,45 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
   const int ntot = n0 + a.n_idx[1];
   const int u_begin = split * a.rows_per_split;
   const int u_end = min(ntot, u_begin + a.rows_per_split);
-  const int nblk = u_end > u_begin ? (u_end - u_begin + kNB - 1) / kNB : 0;
+  static_assert(kResolve % NT == 0 && kResolve % kNB == 0, "resolve pass");
+  int pass_n = 0;   // entries of the current pass (slot table rows at or past it are padding)
 
-  // resolve block `blk`'s list entries to row offsets (threads 0..31)
-  auto resolve = [&](int blk, int buf) {
-    if (threadIdx.x < kNB) {
-      const int uu = u_begin + blk * kNB + threadIdx.x;
-      int info = 0;
-      RowOff off{0, 0};       // masked rows read row 0 (finite data) and are masked later
-      if (uu < u_end) {
-        const bool li = uu >= n0;
-        const int e = li ? idx1[(int64_t)t * ld1 + (uu - n0)] : idx0[(int64_t)t * ld0 + uu];
-        if (e >= 0) {
-          off = li ? row_offsets<FMT, DQK>(kv1, slot_of(kv1.pg, b, e))
-                   : row_offsets<FMT, DQK>(kv0, slot_of(kv0.pg, b, e));
-          info = 1 | ((int)li << 1);
-        }
-      }
-      s_off[buf][threadIdx.x] = off.data;
-      s_soff[buf][threadIdx.x] = off.scale;
-      s_info[buf][threadIdx.x] = info;
+  // Entries [p0, p1) of the split (at most kResolve) to slots, all at once: every index read
+  // of the thread, then every table read, then the slots (two round trips per pass instead
+  // of two per block).
+  auto resolve_pass = [&](int p0, int p1) {
+    constexpr int RPT = kResolve / NT;
+    int e[RPT];
+    bool li[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int uu = min(p0 + (int)threadIdx.x + k * NT, p1 - 1);
+      li[k] = uu >= n0;
+      const int32_t* ip = li[k] ? idx1 + (int64_t)t * ld1 + (uu - n0) : idx0 + (int64_t)t * ld0 + uu;
+      e[k] = *ip;
     }
+    SlotRead sr[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) sr[k] = slot_read(pick_paging(li[k], kv1.pg, kv0.pg), b, max(e[k], 0));
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int j = threadIdx.x + k * NT;
+      const int64_t slot = slot_done(pick_paging(li[k], kv1.pg, kv0.pg), sr[k]);
+      if (j < p1 - p0) s_slot[j] = e[k] >= 0 ? (int32_t)slot | ((int32_t)li[k] << 30) : -1;
+    }
+  };
+  // cache row of pass entry j (a padding entry reads row 0 of the main cache: finite data,
+  // masked by the softmax)
+  auto slot_at = [&](int j) -> int32_t { return j < pass_n ? s_slot[j] : -1; };
+  auto row_of = [&](int j, bool& x) -> RowOff {
+    const int32_t v = slot_at(j);
+    x = v >= 0 && (v >> 30);
+    const int64_t slot = v >= 0 ? (v & 0x3fffffff) : 0;
+    return x ? row_offsets<FMT, DQK>(kv1, slot) : row_offsets<FMT, DQK>(kv0, slot);
   };
   // gather block rows into LDS: bf16 by direct global->LDS loads (asynchronous, completes at
   // the next vmcnt wait), fp8 staged through registers and dequantised (synchronous)
-  auto gather = [&](int buf) {
+  auto gather = [&](int buf, int jb) {   // jb: pass entry of the block's first row
     if constexpr (FMT == kFmtBf16) {
       // lane l of instruction ins fills 16-byte slot 64 * ins + l of the padded block; the pad
       // slot of each row re-reads the row's first 16 bytes
@@ -195,7 +209,9 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
           const int r = j / RW;
           int cc = j - r * RW;
           cc = cc == RW - 1 ? 0 : cc;
-          const uint8_t* src = ((s_info[buf][r] & 2) ? kv1.data : kv0.data) + s_off[buf][r] + 16 * cc;
+          bool x;
+          const RowOff off = row_of(jb + r, x);
+          const uint8_t* src = (x ? kv1.data : kv0.data) + off.data + 16 * cc;
           __builtin_amdgcn_global_load_lds(src, lbase + ins * 1024, 16, 0, 0);
         }
       }
@@ -212,11 +228,11 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
           const int uid = threadIdx.x + (bt * QB + q) * NT;
           if (bt * QB + q < QN && uid < TOT) {
             const int r = uid / UN;
-            const int info = s_info[buf][r];
-            const bool x = info & 2;
+            bool x;
+            const RowOff off = row_of(jb + r, x);
             raw[q] = load_unit<FMT, DQK>(x ? kv1.data : kv0.data,
                                          reinterpret_cast<const uint8_t*>(x ? kv1.scales : kv0.scales),
-                                         RowOff{s_off[buf][r], s_soff[buf][r]}, info & 1, uid - r * UN);
+                                         off, slot_at(jb + r) >= 0, uid - r * UN);
           }
         }
 #pragma unroll
@@ -231,9 +247,9 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
     }
   };
 
-  // The query heads (once per workgroup) are requested first, then the first block's list
-  // entries and table reads (the longest dependent chain), so both round trips overlap; q is
-  // staged through the row buffers (not yet in use).
+  // The query heads (once per workgroup) are requested first, then the first pass's list
+  // entries and table reads, so both round trips overlap; q is staged through the row
+  // buffers (not yet in use).
   constexpr int QBYTES = HT * 16 * DQK * 2;
   constexpr int QIT = (QBYTES + NT * 16 - 1) / (NT * 16);
   static_assert(QBYTES <= (int)sizeof(s_rows), "q staging");
@@ -246,7 +262,7 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
       qreg[i] = o < QBYTES ? *reinterpret_cast<const u32x4_t*>(qsrc + o) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  if (nblk > 0) resolve(0, 0);
+  if (u_end > u_begin) resolve_pass(u_begin, min(u_end, u_begin + kResolve));
   {
     uint8_t* qdst = reinterpret_cast<uint8_t*>(&s_rows[0][0][0]);
 #pragma unroll
@@ -271,13 +287,21 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
     for (int e = 0; e < 8; ++e) o[i][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   __syncthreads();   // q is in registers before the first rows land in the buffers
-  if (nblk > 0) gather(0);
-  for (int it = 0; it < nblk; ++it) {
+  for (int p0 = u_begin; p0 < u_end; p0 += kResolve) {
+    const int p1 = min(u_end, p0 + kResolve);
+    const int nb = (p1 - p0 + kNB - 1) / kNB;
+    pass_n = p1 - p0;
+    if (p0 != u_begin) {
+      resolve_pass(p0, p1);
+      __syncthreads();
+    }
+    gather(0, 0);
+  for (int it = 0; it < nb; ++it) {
     const int cur = it & 1;
-    if (it + 1 < nblk) resolve(it + 1, cur ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);      // this block's rows (and the next block's offsets)
+    const int jb = it * kNB;             // pass entry of this block's first row
+    __builtin_amdgcn_s_waitcnt(0);      // this block's rows
     __syncthreads();
-    if (it + 1 < nblk) gather(cur ^ 1);  // overlaps the compute below (bf16)
+    if (it + 1 < nb) gather(cur ^ 1, jb + kNB);   // overlaps the compute below (bf16)
 
     // ---- S^T = K Q^T
     f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -294,8 +318,10 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float x0 = (s_info[cur][4 * g + r] & 1) ? s0[r] * a.scale_log2 : -INFINITY;
-      const float x1 = (s_info[cur][16 + 4 * g + r] & 1) ? s1[r] * a.scale_log2 : -INFINITY;
+      const bool ok0 = slot_at(jb + 4 * g + r) >= 0;
+      const bool ok1 = slot_at(jb + 16 + 4 * g + r) >= 0;
+      const float x0 = ok0 ? s0[r] * a.scale_log2 : -INFINITY;
+      const float x1 = ok1 ? s1[r] * a.scale_log2 : -INFINITY;
       p[r] = x0;
       p[4 + r] = x1;
       mx = fmaxf(mx, fmaxf(x0, x1));
@@ -347,6 +373,7 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
       }
     }
     __syncthreads();   // block `cur` is refilled two iterations from now
+  }
   }
 
   l_run += __shfl_xor(l_run, 16);

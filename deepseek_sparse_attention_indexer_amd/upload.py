@@ -34,8 +34,8 @@ def _kv(pool, device) -> KVCache:
 
 def to_device(prob, device="cuda") -> SimpleNamespace:
     d = SimpleNamespace()
-    d.q = _t(prob.q.view(np.int16), device, torch.bfloat16)
-    d.kv = _kv(prob.kv, device)
+    d.q = _t(prob.q.view(np.int16), device, torch.bfloat16) if prob.q is not None else None
+    d.kv = _kv(prob.kv, device) if prob.kv is not None else None
     d.extra_kv = _kv(prob.extra_kv, device) if prob.extra_kv is not None else None
     d.row_len = _t(prob.row_len.astype(np.int32), device)
     d.row_req = _t(prob.row_req.astype(np.int32), device)

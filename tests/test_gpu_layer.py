@@ -20,6 +20,11 @@ DECODE = [
     ("glm_128k", "glm_decode", dict(n_ctx=131072)),
     ("long_1m_fp8_keys", "long_decode", dict()),
     ("b4_20k_long_rows", "glm_decode", dict(n_ctx=20000, B=4, ctx_lens=(20000, 17000, 100, 19999), H=16)),
+    # several query tokens per request (causal among themselves): speculative verification
+    # and an extend chunk; the 96-row case scores with the shared-key kernel
+    ("spec_b3_q4", "glm_decode", dict(n_ctx=20000, B=3, q_len=4, ctx_lens=(20000, 17001, 900), H=16)),
+    ("extend_64_20k", "glm_decode", dict(n_ctx=20000, q_len=64, H=16)),
+    ("spec_b24_q4", "glm_decode", dict(n_ctx=9000, B=24, q_len=4, H=16, topk=512)),
 ]
 
 

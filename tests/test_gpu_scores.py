@@ -17,6 +17,10 @@ SMALL = [
     ("glm_decode", dict(n_ctx=777, Hi=64, page_size=48, make_kv=False)),
     ("glm_decode", dict(n_ctx=640, Hi=16, di=64, key_dtype="fp8", make_kv=False)),
     ("causal_prefill", dict(seg_lens=(300, 1, 45))),
+    # 10 requests x 8 query tokens (80 rows > requests: the shared-key prefill kernel) on a
+    # paged cache with 48-token pages, rows crossing the 8192-position chunk boundary
+    ("glm_decode", dict(n_ctx=9000, B=10, q_len=8, page_size=48, make_kv=False,
+                        ctx_lens=(9000, 8, 8200, 100, 8193, 4097, 50, 8999, 2000, 9))),
 ]
 
 

@@ -230,9 +230,12 @@ def glm_decode(n_ctx: int = 32768, B: int = 1, H: int = 64, Hi: int = 64, di: in
                topk: int = 2048, page_size: int = 64, d_nope: int = 512, d_rope: int = 64,
                key_dtype: str = "bf16", kv_fmt: str = "bf16", shuffled: bool = True,
                seed: int = 0, ctx_lens=None, w_low: float = 0.0, index_scale: float = 1.0,
-               make_kv: bool = True, name: Optional[str] = None) -> DSAProblem:
-    """GLM-style decode: B requests, one query token each, n_ctx cached tokens per request
-    (or per-request ctx_lens), MLA 512+64 latent rows, indexer Hi x di, weights ~U(w_low, 1).
+               make_kv: bool = True, name: Optional[str] = None, q_len: int = 1) -> DSAProblem:
+    """GLM-style decode: B requests, q_len query tokens each (1: plain decode; more:
+    speculative verification or an extend chunk), n_ctx cached tokens per request (or
+    per-request ctx_lens) that include the new tokens, MLA 512+64 latent rows, indexer
+    Hi x di, weights ~U(w_low, 1). Rows are request-major; the i-th new token of a request
+    sees its ctx - q_len + 1 + i first positions (causal among the new tokens).
     make_kv=False replaces the latent cache by one page of data (for indexer-only uses)."""
     ctx = np.full(B, n_ctx, dtype=np.int64) if ctx_lens is None else np.asarray(ctx_lens, np.int64)
     D = d_nope + d_rope
@@ -247,9 +250,14 @@ def glm_decode(n_ctx: int = 32768, B: int = 1, H: int = 64, Hi: int = 64, di: in
             bt[b, :ppr[b]] = np.arange(o, o + ppr[b], dtype=np.int32)
             o += int(ppr[b])
     slots = n_pages * page_size
-    q = _bf16_normal(seed, _T_Q, (B, H, D))
-    q_idx = _bf16_normal(seed, _T_QIDX, (B, Hi, di))
-    w = _rng(seed, _T_W).uniform(w_low, 1.0, size=(B, Hi)).astype(np.float32)
+    T = B * q_len
+    if np.any(ctx < q_len):
+        raise ValueError("every context must hold the request's new tokens")
+    q = _bf16_normal(seed, _T_Q, (T, H, D))
+    q_idx = _bf16_normal(seed, _T_QIDX, (T, Hi, di))
+    w = _rng(seed, _T_W).uniform(w_low, 1.0, size=(T, Hi)).astype(np.float32)
+    row_req = np.repeat(np.arange(B, dtype=np.int32), q_len)
+    row_len = (np.repeat(ctx, q_len) - (q_len - 1) + np.tile(np.arange(q_len), B)).astype(np.int32)
     kraw = _normal(seed, _T_KIDX, (slots, di))
     if key_dtype == "bf16":
         kpool = KeyPool("bf16", to_bf16_bits(kraw), None, page_size, bt, None)
@@ -263,8 +271,8 @@ def glm_decode(n_ctx: int = 32768, B: int = 1, H: int = 64, Hi: int = 64, di: in
         kv = _make_kv(seed, _T_KV, kv_fmt, page_size, d_nope, d_rope, page_size,
                       np.zeros_like(bt), None)
     return DSAProblem(
-        name=name or f"glm_decode_{n_ctx}", T=B, H=H, d_qk=D, d_v=d_nope, topk=topk, q=q, kv=kv,
-        row_req=np.arange(B, dtype=np.int32), row_len=ctx.astype(np.int32), n_req=B,
+        name=name or f"glm_decode_{n_ctx}", T=T, H=H, d_qk=D, d_v=d_nope, topk=topk, q=q, kv=kv,
+        row_req=row_req, row_len=row_len, n_req=B,
         softmax_scale=1.0 / math.sqrt(D), Hi=Hi, di=di, q_idx=q_idx, w=w, kpool=kpool,
         index_scale=index_scale)
 
@@ -296,20 +304,21 @@ def tiny_decode(seed: int = 0, topk: int = 128) -> DSAProblem:
 
 def causal_prefill(seg_lens=(8192, 1), H: int = 64, Hi: int = 64, di: int = 128,
                    topk: int = 2048, d_nope: int = 512, d_rope: int = 64, seed: int = 0,
-                   name: Optional[str] = None) -> DSAProblem:
+                   name: Optional[str] = None, make_attn: bool = True) -> DSAProblem:
     """Packed causal prefill: segments laid out back to back in one contiguous cache
-    (req_base = segment offsets, no page table). Row at segment position p sees [0, p]."""
+    (req_base = segment offsets, no page table). Row at segment position p sees [0, p].
+    make_attn=False leaves out the attention inputs (q, latent cache): indexer only."""
     seg = np.asarray(seg_lens, dtype=np.int64)
     T = int(seg.sum())
     D = d_nope + d_rope
     base = np.concatenate([[0], np.cumsum(seg)[:-1]]).astype(np.int32)
     row_req = np.repeat(np.arange(len(seg), dtype=np.int32), seg)
     row_len = np.concatenate([np.arange(1, s + 1) for s in seg]).astype(np.int32)
-    q = _bf16_normal(seed, _T_Q, (T, H, D))
+    q = _bf16_normal(seed, _T_Q, (T, H, D)) if make_attn else None
     q_idx = _bf16_normal(seed, _T_QIDX, (T, Hi, di))
     w = _rng(seed, _T_W).uniform(0.0, 1.0, size=(T, Hi)).astype(np.float32)
     kpool = KeyPool("bf16", _bf16_normal(seed, _T_KIDX, (T, di)), None, 1, None, base)
-    kv = _make_kv(seed, _T_KV, "bf16", T, d_nope, d_rope, 1, None, base)
+    kv = _make_kv(seed, _T_KV, "bf16", T, d_nope, d_rope, 1, None, base) if make_attn else None
     return DSAProblem(
         name=name or "causal_prefill_" + "_".join(str(int(s)) for s in seg), T=T, H=H, d_qk=D,
         d_v=d_nope, topk=topk, q=q, kv=kv, row_req=row_req, row_len=row_len, n_req=len(seg),
@@ -434,6 +443,10 @@ WORKLOADS = {
     "causal_prefill_8k": lambda seed=0: causal_prefill((8192, 1), seed=seed, name="causal_prefill_8k"),
     "dsv4_fp8_decode": lambda seed=0: dsv4_fp8_decode(seed=seed),
     "long_decode_1m": lambda seed=0: long_decode(seed=seed, name="long_decode_1m"),
+    # several query tokens per request: speculative verification, and a 64-token extend chunk
+    "spec_decode_b16_q4_32k": lambda seed=0: glm_decode(n_ctx=32768, B=16, q_len=4, seed=seed,
+                                                        name="spec_decode_b16_q4_32k"),
+    "extend_64_128k": lambda seed=0: glm_decode(n_ctx=131072, q_len=64, seed=seed, name="extend_64_128k"),
 }
 
 
