@@ -73,6 +73,8 @@ _sigs = {
                    C.POINTER(_Rows), _I32, _I32, _I32, _I32, _I32, _I32, _F, _F, _P, _I64, _P, _P,
                    _I64, _P, _P, _SZ, _P],
     "dsa_workspace_init": [_P, _SZ, _P],
+    "dsa_kv_cache_write": [_P, _I64, _I32, _P, C.POINTER(_KVCache), _P],
+    "dsa_key_cache_write": [_P, _I64, _I32, _P, C.POINTER(_KeyCache), _I32, _P],
 }
 for _name, _args in _sigs.items():
     _fn = getattr(_lib, _name)
@@ -135,6 +137,19 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+def _ld(t) -> int:
+    """Row stride (elements) of a row-major [rows, ...] tensor. A single row's leading stride is
+    free in torch (e.g. a broadcast view gives 0); the library then gets one full row."""
+    if t is None:
+        return 0
+    if t.dim() >= 1 and t.shape[0] == 1:
+        row = 1
+        for d in t.shape[1:]:
+            row *= int(d)
+        return max(int(t.stride(0)), row)
+    return int(t.stride(0))
+
+
 def _stream(stream) -> C.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -149,7 +164,7 @@ def _dev(t: Optional[torch.Tensor], name: str):
 def _paging(page_size, block_table, req_base) -> _Paging:
     _dev(block_table, "block_table")
     _dev(req_base, "req_base")
-    stride = int(block_table.stride(0)) if block_table is not None else 0
+    stride = _ld(block_table) if block_table is not None else 0
     return _Paging(int(page_size), 0, _ptr(block_table), stride, _ptr(req_base))
 
 
@@ -232,17 +247,31 @@ class Workspace:
         return self.buf.numel()
 
 
+def dsa_kv_cache_write(src, slots, kv: KVCache, stream=None):
+    """Write bf16 rows src [n, D] (row stride src.stride(0)) into the latent cache at slots [n]
+    (int32 device; -1 skips), in the cache's format."""
+    _check(_lib.dsa_kv_cache_write(_ptr(src), _ld(src), int(src.shape[0]), _ptr(slots),
+                                   C.byref(kv.c), _stream(stream)), "dsa_kv_cache_write")
+
+
+def dsa_key_cache_write(src, slots, keys: KeyCache, di: int, stream=None):
+    """Write bf16 index keys src [n, di] into the key cache at slots [n] (bf16 copy, or fp8 with
+    one scale per token)."""
+    _check(_lib.dsa_key_cache_write(_ptr(src), _ld(src), int(src.shape[0]), _ptr(slots),
+                                    C.byref(keys.c), int(di), _stream(stream)), "dsa_key_cache_write")
+
+
 def dsa_index_scores(q_idx, w, keys: KeyCache, rows: Rows, Hi: int, di: int, index_scale: float,
                      logits, stream=None):
-    _check(_lib.dsa_index_scores(_ptr(q_idx), int(q_idx.stride(0)), _ptr(w), int(w.stride(0)),
+    _check(_lib.dsa_index_scores(_ptr(q_idx), _ld(q_idx), _ptr(w), _ld(w),
                                  C.byref(keys.c), C.byref(rows.c), int(Hi), int(di),
-                                 float(index_scale), _ptr(logits), int(logits.stride(0)),
+                                 float(index_scale), _ptr(logits), _ld(logits),
                                  _stream(stream)), "dsa_index_scores")
 
 
 def dsa_topk(logits, rows: Rows, topk: int, indices, lens, ws: Optional[Workspace], stream=None):
-    _check(_lib.dsa_topk(_ptr(logits), int(logits.stride(0)), C.byref(rows.c), int(topk),
-                         _ptr(indices), int(indices.stride(0)), _ptr(lens),
+    _check(_lib.dsa_topk(_ptr(logits), _ld(logits), C.byref(rows.c), int(topk),
+                         _ptr(indices), _ld(indices), _ptr(lens),
                          ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)),
            "dsa_topk")
 
@@ -253,10 +282,10 @@ def dsa_sparse_mla_decode(q, kv: KVCache, idx, extra_kv: Optional[KVCache], extr
     n_idx = int(idx.shape[1]) if idx is not None else 0
     n_extra = int(extra_idx.shape[1]) if extra_idx is not None else 0
     _check(_lib.dsa_sparse_mla_decode(
-        _ptr(q), int(q.stride(0)), C.byref(kv.c), _ptr(idx), int(idx.stride(0)) if idx is not None else 0,
+        _ptr(q), _ld(q), C.byref(kv.c), _ptr(idx), _ld(idx) if idx is not None else 0,
         n_idx, C.byref(extra_kv.c) if extra_kv else None, _ptr(extra_idx),
-        int(extra_idx.stride(0)) if extra_idx is not None else 0, n_extra, int(B), int(H), int(d_qk),
-        int(d_v), float(softmax_scale), _ptr(out), int(out.stride(0)), _ptr(lse),
+        _ld(extra_idx) if extra_idx is not None else 0, n_extra, int(B), int(H), int(d_qk),
+        int(d_v), float(softmax_scale), _ptr(out), _ld(out), _ptr(lse),
         ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)), "dsa_sparse_mla_decode")
 
 
@@ -266,10 +295,10 @@ def dsa_sparse_mla_prefill(q, kv: KVCache, idx, extra_kv: Optional[KVCache], ext
     n_idx = int(idx.shape[1]) if idx is not None else 0
     n_extra = int(extra_idx.shape[1]) if extra_idx is not None else 0
     _check(_lib.dsa_sparse_mla_prefill(
-        _ptr(q), int(q.stride(0)), C.byref(kv.c), _ptr(idx), int(idx.stride(0)) if idx is not None else 0,
+        _ptr(q), _ld(q), C.byref(kv.c), _ptr(idx), _ld(idx) if idx is not None else 0,
         n_idx, C.byref(extra_kv.c) if extra_kv else None, _ptr(extra_idx),
-        int(extra_idx.stride(0)) if extra_idx is not None else 0, n_extra, C.byref(rows.c), int(H),
-        int(d_qk), int(d_v), float(softmax_scale), _ptr(out), int(out.stride(0)), _ptr(lse),
+        _ld(extra_idx) if extra_idx is not None else 0, n_extra, C.byref(rows.c), int(H),
+        int(d_qk), int(d_v), float(softmax_scale), _ptr(out), _ld(out), _ptr(lse),
         ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)), "dsa_sparse_mla_prefill")
 
 
@@ -277,8 +306,8 @@ def dsa_decode(q, q_idx, w, keys: KeyCache, kv: KVCache, rows: Rows, H: int, d_q
                Hi: int, di: int, topk: int, index_scale: float, softmax_scale: float, out, lse,
                idx_out, lens_out, ws: Workspace, stream=None):
     _check(_lib.dsa_decode(
-        _ptr(q), int(q.stride(0)), _ptr(q_idx), int(q_idx.stride(0)), _ptr(w), int(w.stride(0)),
+        _ptr(q), _ld(q), _ptr(q_idx), _ld(q_idx), _ptr(w), _ld(w),
         C.byref(keys.c), C.byref(kv.c), C.byref(rows.c), int(H), int(d_qk), int(d_v), int(Hi), int(di),
-        int(topk), float(index_scale), float(softmax_scale), _ptr(out), int(out.stride(0)), _ptr(lse),
-        _ptr(idx_out), int(idx_out.stride(0)) if idx_out is not None else 0, _ptr(lens_out),
+        int(topk), float(index_scale), float(softmax_scale), _ptr(out), _ld(out), _ptr(lse),
+        _ptr(idx_out), _ld(idx_out) if idx_out is not None else 0, _ptr(lens_out),
         ws.ptr, ws.nbytes, _stream(stream)), "dsa_decode")

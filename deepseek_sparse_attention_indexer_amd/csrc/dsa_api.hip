@@ -436,7 +436,80 @@ dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
 // ==================================================================== exported entry points
 extern "C" {
 
-int32_t dsa_abi_version(void) { return 1; }
+int32_t dsa_abi_version(void) { return 2; }
+dsa_status dsa_kv_cache_write(const void* src, int64_t ld_src, int32_t n_tok, const int32_t* slots,
+                              const dsa_kv_cache* kv, void* stream) {
+  if (n_tok < 0 || !kv) return DSA_ERR_ARG;
+  if (n_tok == 0) return DSA_OK;
+  if (!src || !al16(src) || !slots || !al4(slots) || !kv->data || ld_src % 8) return DSA_ERR_ARG;
+  if (kv->n_slots < 1) return DSA_ERR_ARG;
+  CacheWriteArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src = static_cast<const uint16_t*>(src);
+  a.ld_src = ld_src;
+  a.n_tok = n_tok;
+  a.D = kv->d_nope + kv->d_rope;
+  a.slots = slots;
+  a.n_slots = kv->n_slots;
+  a.data = static_cast<uint8_t*>(const_cast<void*>(kv->data));
+  if (ld_src < a.D || kv->d_nope < 0 || kv->d_rope < 0) return DSA_ERR_ARG;
+  int kind;
+  switch (kv->format) {
+    case DSA_KV_BF16:
+      if (a.D % 8 || !al16(kv->data)) return DSA_ERR_ARG;
+      kind = kCwBf16;
+      break;
+    case DSA_KV_FP8_UNIFORM:
+      if (a.D % 64 || a.D > 4096) return DSA_ERR_UNSUPPORTED;
+      if (!kv->scales || !al4(kv->scales) || !al16(kv->data)) return DSA_ERR_ARG;
+      a.fscale = const_cast<float*>(kv->scales);
+      a.group = 64;
+      kind = kCwScaled;
+      break;
+    case DSA_KV_FP8_DS_MLA:
+      if (kv->d_nope != 448 || kv->d_rope != 64) return DSA_ERR_UNSUPPORTED;
+      if (kv->paging.page_size < 1 || kv->n_slots % kv->paging.page_size || !al16(kv->data)) return DSA_ERR_ARG;
+      a.page = kv->paging.page_size;
+      kind = kCwDsMla;
+      break;
+    default:
+      return DSA_ERR_ARG;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(timed("cache_write_kv", st, [&] { return launch_cache_write(a, kind, st); }));
+}
+
+dsa_status dsa_key_cache_write(const void* src, int64_t ld_src, int32_t n_tok, const int32_t* slots,
+                               const dsa_key_cache* keys, int32_t di, void* stream) {
+  if (n_tok < 0 || !keys) return DSA_ERR_ARG;
+  if (di != 64 && di != 128) return DSA_ERR_UNSUPPORTED;
+  if (n_tok == 0) return DSA_OK;
+  if (!src || !al16(src) || !slots || !al4(slots) || !keys->data || !al16(keys->data)) return DSA_ERR_ARG;
+  if (ld_src < di || ld_src % 8 || keys->n_slots < 1) return DSA_ERR_ARG;
+  CacheWriteArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src = static_cast<const uint16_t*>(src);
+  a.ld_src = ld_src;
+  a.n_tok = n_tok;
+  a.D = di;
+  a.slots = slots;
+  a.n_slots = keys->n_slots;
+  a.data = static_cast<uint8_t*>(const_cast<void*>(keys->data));
+  int kind;
+  if (keys->dtype == DSA_KEY_BF16) {
+    kind = kCwBf16;
+  } else if (keys->dtype == DSA_KEY_FP8) {
+    if (!keys->scale || !al4(keys->scale)) return DSA_ERR_ARG;
+    a.fscale = const_cast<float*>(keys->scale);
+    a.group = di;
+    kind = kCwScaled;
+  } else {
+    return DSA_ERR_ARG;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(timed("cache_write_keys", st, [&] { return launch_cache_write(a, kind, st); }));
+}
+
 
 const char* dsa_status_string(int32_t status) {
   switch (status) {

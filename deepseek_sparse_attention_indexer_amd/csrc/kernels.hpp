@@ -119,6 +119,22 @@ struct MlaArgs {
 hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T, hipStream_t st);
 hipError_t launch_mla_combine(const MlaArgs& a, int T, hipStream_t st);
 
+// cache writes: bf16 rows -> a cache format, one row per token at slots[token]
+enum { kCwBf16 = 0, kCwScaled = 1, kCwDsMla = 2 };
+struct CacheWriteArgs {
+  const uint16_t* src;     // bf16 [n_tok, ld_src]
+  int64_t ld_src;
+  int32_t n_tok;
+  int32_t D;               // channels per row
+  const int32_t* slots;    // [n_tok]; -1 or out of range: skipped
+  int64_t n_slots;
+  uint8_t* data;           // cache bytes (layout per kind)
+  float* fscale;           // kCwScaled: [n_slots, D / group]
+  int32_t group;           // kCwScaled: channels per fp32 scale
+  int32_t page;            // kCwDsMla: tokens per page
+};
+hipError_t launch_cache_write(const CacheWriteArgs& a, int kind, hipStream_t st);
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace dsa

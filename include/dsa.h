@@ -202,6 +202,33 @@ dsa_status dsa_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 /* Static message for a status code. */
 const char* dsa_status_string(int32_t status);
 
+/* ---------------------------------------------------------------- cache writes
+ * The step just before the layer: new tokens' rows enter the caches in the layer's formats
+ * (aiter PR 4382 "Paged Sparse Attention Gluon Kernel", section "Supported formats &
+ * dtypes": the uniform fp8 pool and the packed fp8_ds_mla token; and fp8 index keys with one
+ * fp32 scale per token).
+ * src:   bf16 rows [n_tok, ld_src], ld_src >= row width and a multiple of 8, 16-byte aligned.
+ * slots: device int32 [n_tok], the cache slot of each row (the caller's block-table mapping of
+ *        (request, position)); -1 or a slot outside [0, n_slots) skips that row.
+ * The cache's data (and scales) must be writable device memory (the descriptors' const is for
+ * the read path). Rows with distinct slots may be written by one call; two rows with the same
+ * slot race. Rounding (the pages give the layouts only): e4m3 to nearest even after
+ * saturating to +-448; fp32 scales = amax / 448 in fp32 (1 for an all-zero group), each value
+ * divided by its scale with IEEE division; fp8_ds_mla exponent byte = k + 127 for the smallest
+ * integer k with 448 * 2^k >= amax, clamped to [1, 254] (127 for an all-zero group), values
+ * multiplied by 2^-k exactly.
+ * dsa_kv_cache_write: DSA_KV_BF16 copies d_nope + d_rope channels; DSA_KV_FP8_UNIFORM takes
+ *   D = d_nope + d_rope (a multiple of 64) channels, one scale per 64; DSA_KV_FP8_DS_MLA needs
+ *   d_nope = 448, d_rope = 64 (exponent pad byte written 0).
+ * dsa_key_cache_write: di in {64, 128}; DSA_KEY_BF16 copies, DSA_KEY_FP8 writes e4m3 bytes and
+ *   one scale per token.
+ * Errors: DSA_ERR_ARG for null pointers, bad strides or alignment, n_tok < 0;
+ * DSA_ERR_UNSUPPORTED for shapes outside the list above. */
+dsa_status dsa_kv_cache_write(const void* src, int64_t ld_src, int32_t n_tok, const int32_t* slots,
+                              const dsa_kv_cache* kv, void* stream);
+dsa_status dsa_key_cache_write(const void* src, int64_t ld_src, int32_t n_tok, const int32_t* slots,
+                               const dsa_key_cache* keys, int32_t di, void* stream);
+
 /* ABI version (bumped on any signature or struct change). */
 int32_t dsa_abi_version(void);
 
