@@ -25,7 +25,7 @@ _lib = C.CDLL(lib_path())
 DSA_OK, DSA_ERR_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
 ENTRY_TOPK, ENTRY_MLA_DECODE, ENTRY_MLA_PREFILL, ENTRY_DECODE = 1, 2, 3, 4
 KEY_BF16, KEY_FP8 = 0, 1
-KV_BF16, KV_FP8_UNIFORM, KV_FP8_DS_MLA = 0, 1, 2
+KV_BF16, KV_FP8_UNIFORM, KV_FP8_DS_MLA, KV_FP8_UNIFORM_FNUZ = 0, 1, 2, 3
 
 
 class _Paging(C.Structure):
@@ -49,6 +49,10 @@ class _Rows(C.Structure):
                 ("row_len", C.c_void_p), ("n_max", C.c_int32), ("_pad0", C.c_int32)]
 
 
+class _AttnOpts(C.Structure):
+    _fields_ = [("sink", C.c_void_p), ("lse_log2", C.c_int32), ("_pad0", C.c_int32)]
+
+
 class _Problem(C.Structure):
     _fields_ = [("T", C.c_int32), ("n_max", C.c_int32), ("topk", C.c_int32), ("H", C.c_int32),
                 ("n_idx", C.c_int32), ("_pad0", C.c_int32)]
@@ -65,13 +69,14 @@ _sigs = {
                          _P, _I64, _P],
     "dsa_topk": [_P, _I64, C.POINTER(_Rows), _I32, _P, _I64, _P, _P, _SZ, _P],
     "dsa_sparse_mla_decode": [_P, _I64, C.POINTER(_KVCache), _P, _I64, _I32, C.POINTER(_KVCache), _P,
-                              _I64, _I32, _I32, _I32, _I32, _I32, _F, _P, _I64, _P, _P, _SZ, _P],
+                              _I64, _I32, _I32, _I32, _I32, _I32, _F, _P, _I64, _P,
+                              C.POINTER(_AttnOpts), _P, _SZ, _P],
     "dsa_sparse_mla_prefill": [_P, _I64, C.POINTER(_KVCache), _P, _I64, _I32, C.POINTER(_KVCache), _P,
-                               _I64, _I32, C.POINTER(_Rows), _I32, _I32, _I32, _F, _P, _I64, _P, _P,
-                               _SZ, _P],
+                               _I64, _I32, C.POINTER(_Rows), _I32, _I32, _I32, _F, _P, _I64, _P,
+                               C.POINTER(_AttnOpts), _P, _SZ, _P],
     "dsa_decode": [_P, _I64, _P, _I64, _P, _I64, C.POINTER(_KeyCache), C.POINTER(_KVCache),
-                   C.POINTER(_Rows), _I32, _I32, _I32, _I32, _I32, _I32, _F, _F, _P, _I64, _P, _P,
-                   _I64, _P, _P, _SZ, _P],
+                   C.POINTER(_Rows), _I32, _I32, _I32, _I32, _I32, _I32, _F, _F, _P, _I64, _P,
+                   C.POINTER(_AttnOpts), _P, _I64, _P, _P, _SZ, _P],
     "dsa_workspace_init": [_P, _SZ, _P],
     "dsa_kv_cache_write": [_P, _I64, _I32, _P, C.POINTER(_KVCache), _P],
     "dsa_key_cache_write": [_P, _I64, _I32, _P, C.POINTER(_KeyCache), _I32, _P],
@@ -86,6 +91,10 @@ _lib.dsa_status_string.argtypes = [_I32]
 _lib.dsa_status_string.restype = C.c_char_p
 _lib.dsa_abi_version.argtypes = []
 _lib.dsa_abi_version.restype = _I32
+ABI_VERSION = 3   # the signatures above
+if _lib.dsa_abi_version() != ABI_VERSION:
+    raise ImportError(f"{lib_path()} has ABI version {_lib.dsa_abi_version()}, this binding needs "
+                      f"{ABI_VERSION}: rebuild the library")
 
 
 class _KernelTime(C.Structure):
@@ -182,8 +191,9 @@ class KeyCache:
 
 
 class KVCache:
-    """Latent cache. fmt 'bf16': data [slots, D] bf16; 'fp8_uniform': uint8 [slots, D] + scales
-    [slots, D/64] fp32; 'fp8_ds_mla': uint8 [pages, page_size * 584]."""
+    """Latent cache. fmt 'bf16': data [slots, D] bf16; 'fp8_uniform' (OCP e4m3) and
+    'fp8_uniform_fnuz' (fnuz e4m3): uint8 [slots, D] + scales [slots, D/64] fp32; 'fp8_ds_mla':
+    uint8 [pages, page_size * 584]."""
 
     def __init__(self, fmt: str, data: torch.Tensor, d_nope: int, d_rope: int, page_size: int = 1,
                  block_table: Optional[torch.Tensor] = None, req_base: Optional[torch.Tensor] = None,
@@ -191,7 +201,8 @@ class KVCache:
         _dev(data, "data")
         _dev(scales, "scales")
         self.keep = (data, scales, block_table, req_base)
-        f = {"bf16": KV_BF16, "fp8_uniform": KV_FP8_UNIFORM, "fp8_ds_mla": KV_FP8_DS_MLA}[fmt]
+        f = {"bf16": KV_BF16, "fp8_uniform": KV_FP8_UNIFORM, "fp8_ds_mla": KV_FP8_DS_MLA,
+             "fp8_uniform_fnuz": KV_FP8_UNIFORM_FNUZ}[fmt]
         n_slots = int(data.shape[0]) * (page_size if fmt == "fp8_ds_mla" else 1)
         self.c = _KVCache(f, int(d_nope), int(d_rope), 0, _ptr(data), _ptr(scales), n_slots,
                           _paging(page_size, block_table, req_base))
@@ -207,6 +218,14 @@ class Rows:
         self.keep = (row_len, row_req)
         self.T = int(row_len.shape[0])
         self.c = _Rows(self.T, int(n_req), _ptr(row_req), _ptr(row_len), int(n_max), 0)
+
+
+def _opts(sink, lse_log2: bool):
+    """Attention options struct (None when both are defaults); sink: fp32 [H] device tensor."""
+    if sink is None and not lse_log2:
+        return None
+    _dev(sink, "sink")
+    return C.byref(_AttnOpts(_ptr(sink), 1 if lse_log2 else 0, 0))
 
 
 def dsa_workspace_size(entry: int, T: int = 0, n_max: int = 0, topk: int = 0, H: int = 0,
@@ -278,20 +297,21 @@ def dsa_topk(logits, rows: Rows, topk: int, indices, lens, ws: Optional[Workspac
 
 def dsa_sparse_mla_decode(q, kv: KVCache, idx, extra_kv: Optional[KVCache], extra_idx, B: int,
                           H: int, d_qk: int, d_v: int, softmax_scale: float, out, lse,
-                          ws: Optional[Workspace], stream=None):
+                          ws: Optional[Workspace], stream=None, sink=None, lse_log2: bool = False):
     n_idx = int(idx.shape[1]) if idx is not None else 0
     n_extra = int(extra_idx.shape[1]) if extra_idx is not None else 0
     _check(_lib.dsa_sparse_mla_decode(
         _ptr(q), _ld(q), C.byref(kv.c), _ptr(idx), _ld(idx) if idx is not None else 0,
         n_idx, C.byref(extra_kv.c) if extra_kv else None, _ptr(extra_idx),
         _ld(extra_idx) if extra_idx is not None else 0, n_extra, int(B), int(H), int(d_qk),
-        int(d_v), float(softmax_scale), _ptr(out), _ld(out), _ptr(lse),
+        int(d_v), float(softmax_scale), _ptr(out), _ld(out), _ptr(lse), _opts(sink, lse_log2),
         ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)), "dsa_sparse_mla_decode")
 
 
 def dsa_sparse_mla_prefill(q, kv: KVCache, idx, extra_kv: Optional[KVCache], extra_idx, rows: Rows,
                            H: int, d_qk: int, d_v: int, softmax_scale: float, out, lse,
-                           ws: Optional[Workspace] = None, stream=None):
+                           ws: Optional[Workspace] = None, stream=None, sink=None,
+                           lse_log2: bool = False):
     n_idx = int(idx.shape[1]) if idx is not None else 0
     n_extra = int(extra_idx.shape[1]) if extra_idx is not None else 0
     _check(_lib.dsa_sparse_mla_prefill(
@@ -299,15 +319,16 @@ def dsa_sparse_mla_prefill(q, kv: KVCache, idx, extra_kv: Optional[KVCache], ext
         n_idx, C.byref(extra_kv.c) if extra_kv else None, _ptr(extra_idx),
         _ld(extra_idx) if extra_idx is not None else 0, n_extra, C.byref(rows.c), int(H),
         int(d_qk), int(d_v), float(softmax_scale), _ptr(out), _ld(out), _ptr(lse),
-        ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)), "dsa_sparse_mla_prefill")
+        _opts(sink, lse_log2), ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)),
+        "dsa_sparse_mla_prefill")
 
 
 def dsa_decode(q, q_idx, w, keys: KeyCache, kv: KVCache, rows: Rows, H: int, d_qk: int, d_v: int,
                Hi: int, di: int, topk: int, index_scale: float, softmax_scale: float, out, lse,
-               idx_out, lens_out, ws: Workspace, stream=None):
+               idx_out, lens_out, ws: Workspace, stream=None, sink=None, lse_log2: bool = False):
     _check(_lib.dsa_decode(
         _ptr(q), _ld(q), _ptr(q_idx), _ld(q_idx), _ptr(w), _ld(w),
         C.byref(keys.c), C.byref(kv.c), C.byref(rows.c), int(H), int(d_qk), int(d_v), int(Hi), int(di),
         int(topk), float(index_scale), float(softmax_scale), _ptr(out), _ld(out), _ptr(lse),
-        _ptr(idx_out), _ld(idx_out) if idx_out is not None else 0, _ptr(lens_out),
+        _opts(sink, lse_log2), _ptr(idx_out), _ld(idx_out) if idx_out is not None else 0, _ptr(lens_out),
         ws.ptr, ws.nbytes, _stream(stream)), "dsa_decode")

@@ -1,13 +1,15 @@
 // Cache writes on gfx950: bf16 rows -> the formats the layer reads.
 //
 // Formats of aiter PR 4382 "Paged Sparse Attention Gluon Kernel" (section "Supported formats
-// & dtypes"): the uniform fp8 pool (e4m3 values, one fp32 scale per 64 channels), the packed
+// & dtypes"): the uniform fp8 pool (e4m3 values, one fp32 scale per 64 channels; OCP or, per
+// the section "fp8 flavors", fnuz bytes: bias 8, largest magnitude 240), the packed
 // fp8_ds_mla token (448 NoPE channels as e4m3 with one UE8M0 exponent per 64 channels, 64 RoPE
 // channels as bf16; page-planar, 584 bytes per token), and fp8 index keys with one fp32 scale
 // per token; plus plain bf16 copies. Rounding (the pages state the layouts only):
-//   * e4m3: round to nearest even after saturating to +-448 (gfx950's conversion);
-//   * fp32 scales: amax / 448 in fp32 (1 for an all-zero group), values divided by the scale
-//     with IEEE round-to-nearest division;
+//   * e4m3: round to nearest even after saturating to +-448 (gfx950's conversion); fnuz
+//     likewise after saturating to +-240, and zero is always 0x00 (0x80 is NaN there);
+//   * fp32 scales: amax / 448 (fnuz: amax / 240) in fp32 (1 for an all-zero group), values
+//     divided by the scale with IEEE round-to-nearest division;
 //   * UE8M0: the smallest k with 448 * 2^k >= amax, found exactly from amax's exponent and
 //     mantissa bits, stored as k + 127 in [1, 254] (127 for an all-zero group); the division
 //     by 2^k is an exact ldexp.
@@ -46,6 +48,28 @@ __device__ __forceinline__ u32x2_t f32x8_to_fp8(const float* f) {
 
 __device__ __forceinline__ float sat448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
 
+// 8 floats (already within +-240) -> 8 fnuz e4m3 bytes. A fnuz code's value is half that of
+// the OCP code with the same bits, on the same grid, so the OCP conversion of 2y gives the
+// fnuz byte of y except at the two ends: |y| in (232, 240] rounds to 240 (code 0x7F, NaN in
+// OCP): the conversion of the saturated 2y gives 0x7E and bit 0 is set; and values that round
+// to zero convert as +0 (OCP's -0 byte is fnuz's NaN).
+__device__ __forceinline__ u32x2_t f32x8_to_fnuz(const float* y) {
+  float f2[8];
+  uint32_t big[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = fabsf(y[i]);
+    float v = sat448(2.f * y[i]);
+    v = a <= 0x1p-11f ? 0.f : v;                 // |2y| <= 2^-10 rounds to zero
+    f2[i] = v;
+    if (a > 232.f) big[i >> 2] |= 1u << (8 * (i & 3));
+  }
+  u32x2_t r = f32x8_to_fp8(f2);
+  r[0] |= big[0];
+  r[1] |= big[1];
+  return r;
+}
+
 template <int KIND>
 __global__ __launch_bounds__(64 * kCwWaves) void k_cache_write(CacheWriteArgs a) {
   const int lane = threadIdx.x & 63;
@@ -60,8 +84,9 @@ __global__ __launch_bounds__(64 * kCwWaves) void k_cache_write(CacheWriteArgs a)
     uint16_t* dst = reinterpret_cast<uint16_t*>(a.data) + slot * a.D;
     for (int c = 8 * lane; c < a.D; c += 512)
       *reinterpret_cast<u32x4_t*>(dst + c) = *reinterpret_cast<const u32x4_t*>(src + c);
-  } else if constexpr (KIND == kCwScaled) {
+  } else if constexpr (KIND == kCwScaled || KIND == kCwScaledFnuz) {
     // e4m3 with one fp32 scale per `group` channels (uniform pool: 64; index keys: the row)
+    constexpr float kMax = KIND == kCwScaled ? 448.0f : 240.0f;
     const int lanes = a.group / 8;                          // lanes per group (8 or 16)
     uint8_t* dst = a.data + slot * a.D;
     for (int c0 = 0; c0 < a.D; c0 += 512) {                 // uniform over the wave
@@ -78,11 +103,11 @@ __global__ __launch_bounds__(64 * kCwWaves) void k_cache_write(CacheWriteArgs a)
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
       m = lanes_max(m, lanes);
-      const float scale = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+      const float scale = m > 0.f ? __fdiv_rn(m, kMax) : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = sat448(__fdiv_rn(f[i], scale));
+      for (int i = 0; i < 8; ++i) f[i] = fminf(fmaxf(__fdiv_rn(f[i], scale), -kMax), kMax);
       if (live) {
-        *reinterpret_cast<u32x2_t*>(dst + c) = f32x8_to_fp8(f);
+        *reinterpret_cast<u32x2_t*>(dst + c) = KIND == kCwScaled ? f32x8_to_fp8(f) : f32x8_to_fnuz(f);
         if ((c % a.group) == 0) a.fscale[slot * (a.D / a.group) + c / a.group] = scale;
       }
     }
@@ -131,6 +156,7 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, int kind, hipStream_t st)
   const dim3 grid((a.n_tok + kCwWaves - 1) / kCwWaves);
   if (kind == kCwBf16) launch_kernel(k_cache_write<kCwBf16>, grid, dim3(64 * kCwWaves), st, a);
   else if (kind == kCwScaled) launch_kernel(k_cache_write<kCwScaled>, grid, dim3(64 * kCwWaves), st, a);
+  else if (kind == kCwScaledFnuz) launch_kernel(k_cache_write<kCwScaledFnuz>, grid, dim3(64 * kCwWaves), st, a);
   else launch_kernel(k_cache_write<kCwDsMla>, grid, dim3(64 * kCwWaves), st, a);
   return hipGetLastError();
 }

@@ -137,6 +137,19 @@ __device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t raw) {
   return r;
 }
 
+// 4 fnuz e4m3 bytes (exponent bias 8, largest magnitude 240) -> fp32, exactly. Moving a
+// byte's sign to bit 31 and its exponent and mantissa fields to bits 30..20 gives an fp32 whose
+// value is the byte's times 2^-119 (subnormal codes land on fp32 denormals, which the build
+// preserves); the product with 2^119 is then exact. There is no native conversion of this
+// encoding on gfx950. Byte 0x80 (NaN in this encoding) decodes as -0.
+__device__ __forceinline__ void fnuz4_to_f32(uint32_t w, float* o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = (w >> (8 * i)) & 0xffu;
+    o[i] = __uint_as_float(((b & 0x80u) << 24) | ((b & 0x7fu) << 20)) * 0x1p119f;
+  }
+}
+
 // 2^(e-127) for a UE8M0 byte 1..254 (exact, built from the exponent field).
 __device__ __forceinline__ float ue8m0_scale(uint32_t e) { return __uint_as_float(e << 23); }
 

@@ -192,6 +192,7 @@ dsa_status check_kv(const dsa_kv_cache* kv, int d_qk) {
       if (d_qk != 576 && d_qk != 512) return DSA_ERR_UNSUPPORTED;
       break;
     case DSA_KV_FP8_UNIFORM:
+    case DSA_KV_FP8_UNIFORM_FNUZ:
       if (!kv->scales || !al4(kv->scales)) return DSA_ERR_ARG;
       if (d_qk != 576 && d_qk != 512) return DSA_ERR_UNSUPPORTED;
       break;
@@ -203,6 +204,28 @@ dsa_status check_kv(const dsa_kv_cache* kv, int d_qk) {
       return DSA_ERR_UNSUPPORTED;
   }
   return DSA_OK;
+}
+
+int kv_fmt(const dsa_kv_cache* kv) {
+  switch (kv->format) {
+    case DSA_KV_BF16: return kFmtBf16;
+    case DSA_KV_FP8_UNIFORM: return kFmtUniform;
+    case DSA_KV_FP8_UNIFORM_FNUZ: return kFmtFnuz;
+    default: return kFmtDsMla;
+  }
+}
+
+// attention options (NULL: no sink, natural-log lse)
+dsa_status check_opts(const dsa_attn_opts* o) {
+  if (!o) return DSA_OK;
+  if (o->sink && !al4(o->sink)) return DSA_ERR_ARG;
+  if (o->lse_log2 != 0 && o->lse_log2 != 1) return DSA_ERR_ARG;
+  return DSA_OK;
+}
+
+void apply_opts(MlaArgs& a, const dsa_attn_opts* o) {
+  a.sink = o ? o->sink : nullptr;
+  a.lse_log2 = o ? o->lse_log2 : 0;
 }
 
 KvDev make_kv(const dsa_kv_cache* kv) {
@@ -232,6 +255,7 @@ struct MlaIn {
   void* out;
   int64_t ld_out;
   float* lse;
+  const dsa_attn_opts* opts;
 };
 
 dsa_status check_mla(const MlaIn& m) {
@@ -245,7 +269,9 @@ dsa_status check_mla(const MlaIn& m) {
   if (!m.q || !al16(m.q) || m.ld_q < (int64_t)m.H * m.d_qk || m.ld_q % 8) return DSA_ERR_ARG;
   if (!m.out || !al16(m.out) || m.ld_out < (int64_t)m.H * m.d_v || m.ld_out % 8) return DSA_ERR_ARG;
   if (m.lse && !al4(m.lse)) return DSA_ERR_ARG;
-  dsa_status s = check_kv(m.kv, m.d_qk);
+  dsa_status s = check_opts(m.opts);
+  if (s != DSA_OK) return s;
+  s = check_kv(m.kv, m.d_qk);
   if (s != DSA_OK) return s;
   if (m.n_idx > 0 && (!m.idx || !al4(m.idx) || m.ld_idx < m.n_idx)) return DSA_ERR_ARG;
   if (m.n_extra > 0) {
@@ -282,6 +308,7 @@ dsa_status run_mla(const MlaIn& m, bool decode, void* ws, size_t ws_bytes, hipSt
   a.out = static_cast<uint16_t*>(m.out);
   a.ld_out = m.ld_out;
   a.lse = m.lse;
+  apply_opts(a, m.opts);
   if (p.n_split > 1) {
     const int64_t need = kHeaderBytes + mla_ws_bytes(m.T, m.H, ntot, decode);
     if (!ws || (int64_t)ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
@@ -290,7 +317,7 @@ dsa_status run_mla(const MlaIn& m, bool decode, void* ws, size_t ws_bytes, hipSt
     a.part_o = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * m.H * p.n_split * 512 * 4));
     a.part_ml = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * m.H * p.n_split * 8));
   }
-  int fmt = m.kv->format == DSA_KV_BF16 ? kFmtBf16 : (m.kv->format == DSA_KV_FP8_UNIFORM ? kFmtUniform : kFmtDsMla);
+  const int fmt = kv_fmt(m.kv);
   dsa_status s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, m.d_qk, p.ht, m.T, st); }));
   if (s == DSA_OK && p.n_split > 1)
     s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, m.T, st); }));
@@ -436,7 +463,7 @@ dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
 // ==================================================================== exported entry points
 extern "C" {
 
-int32_t dsa_abi_version(void) { return 2; }
+int32_t dsa_abi_version(void) { return 3; }
 dsa_status dsa_kv_cache_write(const void* src, int64_t ld_src, int32_t n_tok, const int32_t* slots,
                               const dsa_kv_cache* kv, void* stream) {
   if (n_tok < 0 || !kv) return DSA_ERR_ARG;
@@ -465,6 +492,13 @@ dsa_status dsa_kv_cache_write(const void* src, int64_t ld_src, int32_t n_tok, co
       a.fscale = const_cast<float*>(kv->scales);
       a.group = 64;
       kind = kCwScaled;
+      break;
+    case DSA_KV_FP8_UNIFORM_FNUZ:
+      if (a.D % 64 || a.D > 4096) return DSA_ERR_UNSUPPORTED;
+      if (!kv->scales || !al4(kv->scales) || !al16(kv->data)) return DSA_ERR_ARG;
+      a.fscale = const_cast<float*>(kv->scales);
+      a.group = 64;
+      kind = kCwScaledFnuz;
       break;
     case DSA_KV_FP8_DS_MLA:
       if (kv->d_nope != 448 || kv->d_rope != 64) return DSA_ERR_UNSUPPORTED;
@@ -579,10 +613,10 @@ dsa_status dsa_sparse_mla_decode(const void* q, int64_t ld_q, const dsa_kv_cache
                                  const dsa_kv_cache* extra_kv, const int32_t* extra_idx,
                                  int64_t ld_extra, int32_t n_extra, int32_t B, int32_t H,
                                  int32_t d_qk, int32_t d_v, float softmax_scale, void* out,
-                                 int64_t ld_out, float* lse, void* workspace, size_t ws_bytes,
-                                 void* stream) {
+                                 int64_t ld_out, float* lse, const dsa_attn_opts* opts,
+                                 void* workspace, size_t ws_bytes, void* stream) {
   MlaIn m{q, ld_q, kv, idx, ld_idx, n_idx, extra_kv, extra_idx, ld_extra, n_extra, B, nullptr,
-          B, H, d_qk, d_v, softmax_scale, out, ld_out, lse};
+          B, H, d_qk, d_v, softmax_scale, out, ld_out, lse, opts};
   dsa_status st = check_mla(m);
   if (st != DSA_OK) return st;
   return run_mla(m, true, workspace, ws_bytes, static_cast<hipStream_t>(stream));
@@ -593,12 +627,13 @@ dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cach
                                   const dsa_kv_cache* extra_kv, const int32_t* extra_idx,
                                   int64_t ld_extra, int32_t n_extra, const dsa_rows* rows,
                                   int32_t H, int32_t d_qk, int32_t d_v, float softmax_scale,
-                                  void* out, int64_t ld_out, float* lse, void* workspace,
-                                  size_t ws_bytes, void* stream) {
+                                  void* out, int64_t ld_out, float* lse,
+                                  const dsa_attn_opts* opts, void* workspace, size_t ws_bytes,
+                                  void* stream) {
   dsa_status st = check_rows(rows);
   if (st != DSA_OK) return st;
   MlaIn m{q, ld_q, kv, idx, ld_idx, n_idx, extra_kv, extra_idx, ld_extra, n_extra, rows->T,
-          rows->row_req, rows->n_req, H, d_qk, d_v, softmax_scale, out, ld_out, lse};
+          rows->row_req, rows->n_req, H, d_qk, d_v, softmax_scale, out, ld_out, lse, opts};
   st = check_mla(m);
   if (st != DSA_OK) return st;
   return run_mla(m, false, workspace, ws_bytes, static_cast<hipStream_t>(stream));
@@ -609,7 +644,8 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
                       const dsa_kv_cache* kv, const dsa_rows* rows, int32_t H, int32_t d_qk,
                       int32_t d_v, int32_t Hi, int32_t di, int32_t topk, float index_scale,
                       float softmax_scale, void* out, int64_t ld_out, float* lse,
-                      int32_t* idx_out, int64_t ld_idx_out, int32_t* lens_out,
+                      const dsa_attn_opts* opts, int32_t* idx_out, int64_t ld_idx_out,
+                      int32_t* lens_out,
                       void* workspace, size_t ws_bytes, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   dsa_status s = check_rows(rows);
@@ -626,7 +662,7 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
   s = check_scores(sc);
   if (s != DSA_OK) return s;
   MlaIn m{q, ld_q, kv, reinterpret_cast<const int32_t*>(uintptr_t(256)), topk, topk, nullptr, nullptr,
-          0, 0, T, rows->row_req, rows->n_req, H, d_qk, d_v, softmax_scale, out, ld_out, lse};
+          0, 0, T, rows->row_req, rows->n_req, H, d_qk, d_v, softmax_scale, out, ld_out, lse, opts};
   s = check_mla(m);
   if (s != DSA_OK) return s;
   if (T == 0) return DSA_OK;
@@ -695,12 +731,13 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
   a.out = static_cast<uint16_t*>(out);
   a.ld_out = ld_out;
   a.lse = lse;
+  apply_opts(a, opts);
   if (p.n_split > 1) {
     a.part_o = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * H * p.n_split * 512 * 4));
     a.part_ml = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * H * p.n_split * 8));
     if ((size_t)cv.off > ws_bytes) return DSA_ERR_WORKSPACE;
   }
-  const int fmt = kv->format == DSA_KV_BF16 ? kFmtBf16 : (kv->format == DSA_KV_FP8_UNIFORM ? kFmtUniform : kFmtDsMla);
+  const int fmt = kv_fmt(kv);
   s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, d_qk, p.ht, T, st); }));
   if (s == DSA_OK && p.n_split > 1)
     s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, T, st); }));

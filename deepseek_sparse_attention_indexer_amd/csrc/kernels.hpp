@@ -88,7 +88,10 @@ hipError_t launch_topk_hist(const TopkArgs& a, int T, hipStream_t st);
 hipError_t launch_topk_filter(const TopkArgs& a, int T, hipStream_t st);
 hipError_t launch_topk_finalize(const TopkArgs& a, int T, hipStream_t st);
 
-enum KvFmt { kFmtBf16 = 0, kFmtUniform = 1, kFmtDsMla = 2 };
+// uniform pools hold OCP e4m3 (kFmtUniform) or fnuz e4m3 (kFmtFnuz) bytes, same layout
+enum KvFmt { kFmtBf16 = 0, kFmtUniform = 1, kFmtDsMla = 2, kFmtFnuz = 3 };
+template <int FMT>
+constexpr bool kUniformFmt = FMT == kFmtUniform || FMT == kFmtFnuz;
 
 struct KvDev {
   const uint8_t* data;
@@ -112,6 +115,8 @@ struct MlaArgs {
   uint16_t* out;           // bf16 [T, H, 512]
   int64_t ld_out;
   float* lse;              // [T, H] or nullptr
+  const float* sink;       // [H] per-head sink logit (natural-log units) or nullptr
+  int32_t lse_log2;        // lse in base 2 instead of natural log
   float* part_o;           // [T, H, n_split, 512]
   float* part_ml;          // [T, H, n_split, 2]
 };
@@ -120,7 +125,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T,
 hipError_t launch_mla_combine(const MlaArgs& a, int T, hipStream_t st);
 
 // cache writes: bf16 rows -> a cache format, one row per token at slots[token]
-enum { kCwBf16 = 0, kCwScaled = 1, kCwDsMla = 2 };
+enum { kCwBf16 = 0, kCwScaled = 1, kCwDsMla = 2, kCwScaledFnuz = 3 };
 struct CacheWriteArgs {
   const uint16_t* src;     // bf16 [n_tok, ld_src]
   int64_t ld_src;
@@ -129,8 +134,8 @@ struct CacheWriteArgs {
   const int32_t* slots;    // [n_tok]; -1 or out of range: skipped
   int64_t n_slots;
   uint8_t* data;           // cache bytes (layout per kind)
-  float* fscale;           // kCwScaled: [n_slots, D / group]
-  int32_t group;           // kCwScaled: channels per fp32 scale
+  float* fscale;           // kCwScaled(Fnuz): [n_slots, D / group]
+  int32_t group;           // kCwScaled(Fnuz): channels per fp32 scale
   int32_t page;            // kCwDsMla: tokens per page
 };
 hipError_t launch_cache_write(const CacheWriteArgs& a, int kind, hipStream_t st);

@@ -4,7 +4,8 @@
 //   out[t,h] = sum_i softmax_i(softmax_scale * q[t,h] . c_i) * c_i[0:512],  lse = ln sum_i e^(.)
 // Rows are 512 latent + 64 RoPE bf16 (tokenspeed PR 664 "gfx950 Gluon bf16 MLA decode and
 // prefill kernels"), or fp8 rows of aiter PR 4382 "Paged Sparse Attention Gluon Kernel"
-// (uniform pool: fp8 * fp32 scale per 64 columns; fp8_ds_mla: 448 NoPE fp8 * 2^(e-127) per 64
+// (uniform pool: fp8 * fp32 scale per 64 columns, the bytes OCP or fnuz e4m3 (section "fp8
+// flavors"; fnuz has no native conversion and is decoded by bit placement); fp8_ds_mla: 448 NoPE fp8 * 2^(e-127) per 64
 // columns + 64 RoPE bf16, page-planar 584 bytes/token). -1 entries are masked from the
 // original list while their rows are never read (radixark/miles PR 3608, "What", padding).
 // A second list (extra) into a second cache shares the softmax (PR 4382, two-loop layout).
@@ -25,6 +26,9 @@
 // The softmax runs in base 2 with a lazily rescaled running max. Splits (decode): each
 // workgroup covers rows_per_split entries of the row's list and writes an un-normalised
 // partial (o, m, l); k_mla_combine merges them (split-KV + LSE merge of PR 664).
+// DeepSeek-V4 options (radixark/miles PR 3608, section "What", forward bullet: the lse the
+// backward takes is in base 2 with the sink folded in): a per-head sink logit joins the
+// softmax denominator only (it carries no value row), and the lse may be written in base 2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,7 +42,7 @@ template <int FMT, int DQK>
 struct RowGeom {
   static constexpr int kElems = DQK + 8;                       // padded bf16 row in LDS
   // 16-byte work units per row and what one unit produces
-  static constexpr int kUnits = FMT == kFmtBf16 ? DQK / 8 : (FMT == kFmtUniform ? DQK / 16 : 36);
+  static constexpr int kUnits = FMT == kFmtBf16 ? DQK / 8 : (kUniformFmt<FMT> ? DQK / 16 : 36);
 };
 
 // fp8 rows: one 16-byte unit of a row is loaded (with its scale) into registers first, then
@@ -60,7 +64,7 @@ __device__ __forceinline__ RowOff row_offsets(const KvDev& kv, int64_t slot) {
   if constexpr (FMT == kFmtBf16) {
     o.data = slot * DQK * 2;
     o.scale = 0;
-  } else if constexpr (FMT == kFmtUniform) {
+  } else if constexpr (kUniformFmt<FMT>) {
     o.data = slot * DQK;
     o.scale = slot * (DQK / 64) * 4;
   } else {  // fp8_ds_mla: page-planar layout
@@ -82,7 +86,7 @@ __device__ __forceinline__ RawUnit load_unit(const uint8_t* data, const uint8_t*
   r.v = u32x4_t{0u, 0u, 0u, 0u};
   r.sc = 0.f;
   if (!valid) return r;
-  if constexpr (FMT == kFmtUniform) {
+  if constexpr (kUniformFmt<FMT>) {
     r.v = *reinterpret_cast<const u32x4_t*>(data + off.data + 16 * u);
     r.sc = *reinterpret_cast<const float*>(scales + off.scale + (u / 4) * 4);
   } else {  // fp8_ds_mla
@@ -104,14 +108,15 @@ __device__ __forceinline__ void store_unit(const RawUnit& r, int u, uint16_t* lr
     return;
   }
   float f[16];
-  fp8x4_to_f32(r.v[0], f);
-  fp8x4_to_f32(r.v[1], f + 4);
-  fp8x4_to_f32(r.v[2], f + 8);
-  fp8x4_to_f32(r.v[3], f + 12);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (FMT == kFmtFnuz) fnuz4_to_f32(r.v[k], f + 4 * k);
+    else fp8x4_to_f32(r.v[k], f + 4 * k);
+  }
   u32x4_t lo, hi;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (FMT == kFmtUniform) {   // arbitrary fp32 scale: round to bf16
+    if constexpr (kUniformFmt<FMT>) {     // arbitrary fp32 scale: round to bf16
       lo[i] = pack_bf16_rne(f[2 * i] * r.sc, f[2 * i + 1] * r.sc);
       hi[i] = pack_bf16_rne(f[8 + 2 * i] * r.sc, f[8 + 2 * i + 1] * r.sc);
     } else {                              // power-of-two scale: exact in bf16
@@ -121,6 +126,31 @@ __device__ __forceinline__ void store_unit(const RawUnit& r, int u, uint16_t* lr
   }
   *reinterpret_cast<u32x4_t*>(lrow + 16 * u) = lo;
   *reinterpret_cast<u32x4_t*>(lrow + 16 * u + 8) = hi;
+}
+
+// Final normalisation of one (row, head) from its base-2 running max m and sum l (l = 0: no
+// listed row), with the optional sink logit (natural-log units) in the denominator:
+// returns the factor for the accumulated output, and the lse in the requested base.
+struct Finish {
+  float inv;
+  float lse;
+};
+__device__ __forceinline__ Finish finish_softmax(float m, float l, float sink, bool lse_log2) {
+  Finish f;
+  float lse2;
+  if (sink > -INFINITY) {
+    const float s2 = sink * kLog2e;
+    const float mm = fmaxf(m, s2);
+    const float wl = l > 0.f ? exp2f(m - mm) : 0.f;   // weight of the listed rows' terms
+    const float z = l * wl + exp2f(s2 - mm);
+    f.inv = wl / z;
+    lse2 = mm + log2f(z);
+  } else {
+    f.inv = l > 0.f ? 1.f / l : 0.f;
+    lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
+  }
+  f.lse = lse_log2 ? lse2 : lse2 * kLn2;
+  return f;
 }
 
 template <int FMT, int DQK, int HT, int WD, bool SPLIT>
@@ -381,7 +411,8 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
 
   const int head = head0 + c;
   if constexpr (!SPLIT) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const Finish fin = finish_softmax(m_run, l_run, a.sink ? a.sink[head] : -INFINITY, a.lse_log2);
+    const float inv = fin.inv;
     uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)head * kDV;
 #pragma unroll
     for (int i = 0; i < GD; ++i)
@@ -393,8 +424,7 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
           v[e2] = pack_bf16_rne(o[i][2 * e2][r] * inv, o[i][2 * e2 + 1][r] * inv);
         *reinterpret_cast<u32x4_t*>(op + 128 * (gd0 + i) + 32 * g + 8 * r) = v;
       }
-    if (a.lse && g == 0 && gd0 == 0)
-      a.lse[(int64_t)t * a.H + head] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    if (a.lse && g == 0 && gd0 == 0) a.lse[(int64_t)t * a.H + head] = fin.lse;
   } else {
     // un-normalised partial (o, m, l) of this split; k_mla_combine merges them
     float* po = a.part_o + (((int64_t)t * a.H + head) * a.n_split + split) * kDV;
@@ -488,14 +518,14 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
       lt += wgt * s_l[q];
     }
   }
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const Finish fin = finish_softmax(ms, lt, a.sink ? a.sink[head] : -INFINITY, a.lse_log2);
+  const float inv = fin.inv;
   uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)head * kDV + d0;
   u32x2_t vv;
   vv[0] = pack_bf16_rne(tot[0] * inv, tot[1] * inv);
   vv[1] = pack_bf16_rne(tot[2] * inv, tot[3] * inv);
   *reinterpret_cast<u32x2_t*>(op) = vv;
-  if (a.lse && blockIdx.x == 0 && ci == 0)
-    a.lse[(int64_t)t * a.H + head] = lt > 0.f ? (ms + log2f(lt)) * kLn2 : -INFINITY;
+  if (a.lse && blockIdx.x == 0 && ci == 0) a.lse[(int64_t)t * a.H + head] = fin.lse;
 }
 
 template <int FMT, int DQK, int HT, int WD>
@@ -525,6 +555,10 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T,
   if (fmt == kFmtUniform) {
     if (d_qk == 576) return launch_d<kFmtUniform, 576>(a, ht, T, st);
     return launch_d<kFmtUniform, 512>(a, ht, T, st);
+  }
+  if (fmt == kFmtFnuz) {
+    if (d_qk == 576) return launch_d<kFmtFnuz, 576>(a, ht, T, st);
+    return launch_d<kFmtFnuz, 512>(a, ht, T, st);
   }
   return launch_d<kFmtDsMla, 512>(a, ht, T, st);
 }

@@ -49,4 +49,7 @@ def to_device(prob, device="cuda") -> SimpleNamespace:
         d.w = _t(prob.w, device)
     d.idx_main = _t(prob.idx_main, device) if prob.idx_main is not None else None
     d.idx_extra = _t(prob.idx_extra, device) if prob.idx_extra is not None else None
+    sink = getattr(prob, "sink", None)
+    d.sink = _t(np.asarray(sink, dtype=np.float32), device) if sink is not None else None
+    d.lse_log2 = bool(getattr(prob, "lse_log2", False))
     return d

@@ -66,7 +66,11 @@ typedef enum dsa_kv_format {
   /* packed pages [n_slots/page_size, page_size * 584] bytes, block-planar: page_size x 576
      data bytes (448 NoPE fp8 + 64 RoPE bf16) then page_size x 8 scale bytes (7 UE8M0
      exponents + 1 pad); NoPE x = fp8 * 2^(e-127); PR 4382, "Packed fp8 fp8_ds_mla - 3D" */
-  DSA_KV_FP8_DS_MLA = 2
+  DSA_KV_FP8_DS_MLA = 2,
+  /* the uniform layout with fnuz e4m3 bytes (exponent bias 8, largest magnitude 240, 0x80 is
+     NaN and is never written); PR 4382, section "fp8 flavors": no native gfx950 conversion,
+     so the bytes are decoded by bit placement (exact) */
+  DSA_KV_FP8_UNIFORM_FNUZ = 3
 } dsa_kv_format;
 
 /* Logical position s of request b -> cache slot.
@@ -135,6 +139,20 @@ dsa_status dsa_topk(const float* logits, int64_t ld_logits, const dsa_rows* rows
                     int32_t* indices, int64_t ld_idx, int32_t* lens, void* workspace,
                     size_t ws_bytes, void* stream);
 
+/* Attention options (NULL everywhere means: no sink, natural-log lse). DeepSeek-V4's forward
+ * hands its backward an lse in base 2 with an attention sink folded in (radixark/miles PR
+ * 3608, section "What", forward bullet). The sink is one logit per head, in the units of
+ * softmax_scale * q . c, that joins the softmax denominator and carries no value row:
+ *   out[t,h] = sum_i e^(l_i) c_i[0:d_v] / (e^(sink[h]) + sum_i e^(l_i)),
+ *   lse[t,h] = ln(e^(sink[h]) + sum_i e^(l_i))   (a row with no listed entry: out 0, lse sink[h]).
+ * sink: device fp32 [H] or NULL (a -inf entry is no sink for that head).
+ * lse_log2: 0 = natural log, 1 = base 2 (lse / ln 2; -inf stays -inf). Other values: DSA_ERR_ARG. */
+typedef struct dsa_attn_opts {
+  const float* sink;
+  int32_t lse_log2;
+  int32_t _pad0;
+} dsa_attn_opts;
+
 /* ---------------------------------------------------------------- step 3: sparse MLA
  * q:   bf16 [T, H, d_qk], row stride ld_q (>= H*d_qk, multiple of 8).
  * idx: int32 [T, n_idx] positions (stride ld_idx) into `kv` for the row's request; -1 = none.
@@ -144,6 +162,7 @@ dsa_status dsa_topk(const float* logits, int64_t ld_logits, const dsa_rows* rows
  *      out[t,h] = sum_i softmax_i(softmax_scale * q[t,h] . c_i) * c_i[0:d_v]; rows with no
  *      listed entry give out = 0.
  * lse: fp32 [T, H] natural-log logsumexp of the scaled logits (-inf for empty rows); may be NULL.
+ * opts: sink and lse base (see dsa_attn_opts); may be NULL.
  * Envelope: H multiple of 16; d_qk = d_nope + d_rope in {512, 576}; d_v = 512; both caches
  * of the same format. The decode entry splits each row's list over workgroups and merges the
  * partials (PR 664 split-KV + LSE merge); the prefill entry gives each row one workgroup. */
@@ -152,16 +171,17 @@ dsa_status dsa_sparse_mla_decode(const void* q, int64_t ld_q, const dsa_kv_cache
                                  const dsa_kv_cache* extra_kv, const int32_t* extra_idx,
                                  int64_t ld_extra, int32_t n_extra, int32_t B, int32_t H,
                                  int32_t d_qk, int32_t d_v, float softmax_scale, void* out,
-                                 int64_t ld_out, float* lse, void* workspace, size_t ws_bytes,
-                                 void* stream);
+                                 int64_t ld_out, float* lse, const dsa_attn_opts* opts,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cache* kv,
                                   const int32_t* idx, int64_t ld_idx, int32_t n_idx,
                                   const dsa_kv_cache* extra_kv, const int32_t* extra_idx,
                                   int64_t ld_extra, int32_t n_extra, const dsa_rows* rows,
                                   int32_t H, int32_t d_qk, int32_t d_v, float softmax_scale,
-                                  void* out, int64_t ld_out, float* lse, void* workspace,
-                                  size_t ws_bytes, void* stream);
+                                  void* out, int64_t ld_out, float* lse,
+                                  const dsa_attn_opts* opts, void* workspace, size_t ws_bytes,
+                                  void* stream);
 
 /* ---------------------------------------------------------------- fused layer
  * Steps 1-3 on one stream with no host sync: scores into the workspace, top-k, attention
@@ -172,8 +192,8 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
                       const dsa_kv_cache* kv, const dsa_rows* rows, int32_t H, int32_t d_qk,
                       int32_t d_v, int32_t Hi, int32_t di, int32_t topk, float index_scale,
                       float softmax_scale, void* out, int64_t ld_out, float* lse,
-                      int32_t* idx_out, int64_t ld_idx_out, int32_t* lens_out,
-                      void* workspace, size_t ws_bytes, void* stream);
+                      const dsa_attn_opts* opts, int32_t* idx_out, int64_t ld_idx_out,
+                      int32_t* lens_out, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- workspace and errors */
 typedef enum dsa_entry {
@@ -214,11 +234,13 @@ const char* dsa_status_string(int32_t status);
  * the read path). Rows with distinct slots may be written by one call; two rows with the same
  * slot race. Rounding (the pages give the layouts only): e4m3 to nearest even after
  * saturating to +-448; fp32 scales = amax / 448 in fp32 (1 for an all-zero group), each value
- * divided by its scale with IEEE division; fp8_ds_mla exponent byte = k + 127 for the smallest
+ * divided by its scale with IEEE division (fnuz pool: 240 in place of 448, and zero of either
+ * sign is byte 0x00); fp8_ds_mla exponent byte = k + 127 for the smallest
  * integer k with 448 * 2^k >= amax, clamped to [1, 254] (127 for an all-zero group), values
  * multiplied by 2^-k exactly.
  * dsa_kv_cache_write: DSA_KV_BF16 copies d_nope + d_rope channels; DSA_KV_FP8_UNIFORM takes
- *   D = d_nope + d_rope (a multiple of 64) channels, one scale per 64; DSA_KV_FP8_DS_MLA needs
+ *   D = d_nope + d_rope (a multiple of 64) channels, one scale per 64 (DSA_KV_FP8_UNIFORM_FNUZ
+ *   likewise); DSA_KV_FP8_DS_MLA needs
  *   d_nope = 448, d_rope = 64 (exponent pad byte written 0).
  * dsa_key_cache_write: di in {64, 128}; DSA_KEY_BF16 copies, DSA_KEY_FP8 writes e4m3 bytes and
  *   one scale per token.

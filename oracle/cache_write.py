@@ -11,9 +11,11 @@ the data and exponents of a page stored apart); and the fp8 index keys with one 
 token. The pages give the layouts and the OCP e4m3 flavour, not the rounding of the scales;
 the readings taken here:
 
-* values are rounded to e4m3 to nearest, ties to even, after saturating to +-448;
-* fp32 scales: scale = amax / 448 in fp32 arithmetic (1.0 for an all-zero group), and each
-  value is divided by its scale in fp32 before rounding;
+* values are rounded to e4m3 to nearest, ties to even, after saturating to +-448; the fnuz
+  flavour of the uniform pool (section "fp8 flavors": bias 8) saturates to +-240, and zero of
+  either sign is byte 0x00 (0x80 is NaN there);
+* fp32 scales: scale = amax / 448 (fnuz: amax / 240) in fp32 arithmetic (1.0 for an all-zero
+  group), and each value is divided by its scale in fp32 before rounding;
 * UE8M0 exponents: the smallest integer k with 448 * 2^k >= amax (exact), stored as k + 127
   clamped to [1, 254]; an all-zero group stores 127 (scale 1). Dividing by 2^k is exact.
 
@@ -61,6 +63,33 @@ def fp8_e4m3fn_encode(x) -> np.ndarray:
     return np.where(sign, code | 0x80, code).astype(np.uint8)
 
 
+def _e4m3fnuz_finite_values() -> tuple[np.ndarray, np.ndarray]:
+    """Non-negative fnuz e4m3 values in increasing order with their codes (bias 8, exponent
+    field 0 is subnormal m/8 * 2^-7, every code 0x00..0x7F finite: the largest is 240)."""
+    vals = [(m / 8.0) * 2.0 ** -7 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 8)
+            for e, m in ((c >> 3, c & 7) for c in range(0x80))]
+    return np.asarray(vals, np.float64), np.arange(0x80, dtype=np.uint8)
+
+
+_FNUZ_VALS, _FNUZ_CODES = _e4m3fnuz_finite_values()
+FP8_FNUZ_MAX = 240.0
+
+
+def fp8_e4m3fnuz_encode(x) -> np.ndarray:
+    """float values -> fnuz e4m3 bytes: saturate to +-240, round to nearest, ties to the even
+    code; a value that rounds to zero is 0x00 whatever its sign (there is no negative zero)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), FP8_FNUZ_MAX)
+    hi = np.minimum(np.searchsorted(_FNUZ_VALS, a, side="left"), len(_FNUZ_VALS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _FNUZ_VALS[lo]
+    dhi = _FNUZ_VALS[hi] - a
+    pick_hi = (_FNUZ_VALS[hi] == a) | (dhi < dlo) | ((dhi == dlo) & ((_FNUZ_CODES[hi] & 1) == 0) & (hi != lo))
+    code = _FNUZ_CODES[np.where(pick_hi, hi, lo)].astype(np.uint8)
+    neg = np.signbit(x) & (code != 0)
+    return np.where(neg, code | 0x80, code).astype(np.uint8)
+
+
 def bf16_bits_to_f32(bits) -> np.ndarray:
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return u.view(np.float32)
@@ -80,21 +109,25 @@ def ue8m0_exponent(amax) -> np.ndarray:
     return np.clip(out, 1, 254)
 
 
-def quant_fp32_scaled(values_f32: np.ndarray, group: int):
+def quant_fp32_scaled(values_f32: np.ndarray, group: int, fnuz: bool = False):
     """float32 [n, D] -> (e4m3 bytes [n, D], float32 scales [n, D // group]) with one scale per
-    group of `group` channels: scale = amax / 448 (fp32), byte = e4m3(x / scale) (fp32 divide)."""
+    group of `group` channels: scale = amax / 448 (fp32), byte = e4m3(x / scale) (fp32 divide);
+    fnuz: amax / 240 and the fnuz encoding."""
     v = np.ascontiguousarray(values_f32, dtype=np.float32)
     n, D = v.shape
     g = v.reshape(n, D // group, group)
     amax = np.abs(g).max(axis=2)
-    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    fmax = np.float32(FP8_FNUZ_MAX if fnuz else FP8_MAX)
+    scale = np.where(amax > 0, amax / fmax, np.float32(1.0)).astype(np.float32)
     q = (g / scale[:, :, None]).astype(np.float32)          # IEEE float32 division
-    return fp8_e4m3fn_encode(q).reshape(n, D), scale
+    enc = fp8_e4m3fnuz_encode if fnuz else fp8_e4m3fn_encode
+    return enc(q).reshape(n, D), scale
 
 
-def write_uniform(src_bf16_bits: np.ndarray):
-    """bf16 rows [n, D] -> uniform pool rows: (fp8 bytes [n, D], fp32 scales [n, D / 64])."""
-    return quant_fp32_scaled(bf16_bits_to_f32(src_bf16_bits), 64)
+def write_uniform(src_bf16_bits: np.ndarray, fnuz: bool = False):
+    """bf16 rows [n, D] -> uniform pool rows: (fp8 bytes [n, D], fp32 scales [n, D / 64]),
+    OCP or fnuz bytes."""
+    return quant_fp32_scaled(bf16_bits_to_f32(src_bf16_bits), 64, fnuz)
 
 
 def write_index_keys(src_bf16_bits: np.ndarray):

@@ -25,6 +25,13 @@ What it computes, per query row t of request b that sees candidates s in [0, n_t
    An empty list gives out = 0 and lse = -inf. Two lists (main + extra, aiter PR 4382 "Paged
    Sparse Attention Gluon Kernel", section "Supported formats & dtypes", two-loop bullet) are
    one softmax over their union, each list read through its own cache.
+4. DeepSeek-V4 options of step 3 (radixark/miles PR 3608, section "What", forward bullet: the
+   backward takes an lse in base 2 with the sink folded in). The pages name the sink without
+   defining it; the reading taken: one logit per head, in the units of l_i, that joins the
+   softmax denominator and carries no value row:
+       out[t, h, :] = sum_i exp(l_i) c_i[:d_v] / (exp(sink_h) + sum_i exp(l_i)),
+       lse[t, h] = log(exp(sink_h) + sum_i exp(l_i))
+   (an empty list: out = 0, lse = sink_h). The base-2 lse is lse / ln 2.
 """
 from __future__ import annotations
 
@@ -62,6 +69,30 @@ def _fp8_e4m3fn_table() -> np.ndarray:
 
 
 FP8_E4M3FN = _fp8_e4m3fn_table()
+
+
+def _fp8_e4m3fnuz_table() -> np.ndarray:
+    """Value of every fnuz e4m3 byte (aiter PR 4382, section "fp8 flavors": float8_e4m3fnuz,
+    exponent bias 8).
+
+    Layout s.eeee.mmm: bias 8; e = 0 is subnormal (m / 8 * 2^-7); no infinities and no negative
+    zero: byte 0x80 is the only NaN, so S.1111.111 is finite, 1.875 * 2^7 = 240.
+    """
+    t = np.empty(256, dtype=np.float64)
+    for byte in range(256):
+        sign = -1.0 if byte & 0x80 else 1.0
+        e = (byte >> 3) & 0xF
+        m = byte & 0x7
+        if byte == 0x80:
+            t[byte] = math.nan
+        elif e == 0:
+            t[byte] = sign * (m / 8.0) * 2.0 ** (1 - 8)
+        else:
+            t[byte] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)
+    return t
+
+
+FP8_E4M3FNUZ = _fp8_e4m3fnuz_table()
 
 
 def ue8m0_to_f64(e: np.ndarray) -> np.ndarray:
@@ -107,7 +138,8 @@ def key_rows(kpool, b: int, positions: np.ndarray) -> np.ndarray:
 def kv_rows(pool, b: int, positions: np.ndarray) -> np.ndarray:
     """Latent rows of the given positions, dequantised to float64 [n, d_nope + d_rope].
 
-    fp8_uniform (PR 4382, "Uniform fp8 pool - 2D"): x = fp8(byte[slot, c]) * scale[slot, c // 64].
+    fp8_uniform (PR 4382, "Uniform fp8 pool - 2D"): x = fp8(byte[slot, c]) * scale[slot, c // 64];
+    fp8_uniform_fnuz: the same with the fnuz decoding of the bytes (section "fp8 flavors").
     fp8_ds_mla (PR 4382, "Packed fp8 fp8_ds_mla - 3D"): slot -> page = slot // block,
     pos = slot % block; the page holds block x 576 data bytes then block x 8 scale bytes;
     NoPE byte c of the token sits at pos * 576 + c and is scaled by 2^(e_g - 127) with
@@ -117,8 +149,13 @@ def kv_rows(pool, b: int, positions: np.ndarray) -> np.ndarray:
     slots = slots_of(pool, b, positions)
     if pool.fmt == "bf16":
         return bf16_to_f64(pool.data[slots])
-    if pool.fmt == "fp8_uniform":
-        vals = FP8_E4M3FN[pool.data[slots]]
+    if pool.fmt in ("fp8_uniform", "fp8_uniform_fnuz"):
+        if pool.fmt == "fp8_uniform":
+            vals = FP8_E4M3FN[pool.data[slots]]
+        else:
+            if np.any(pool.data[slots] == 0x80):
+                raise ValueError("fnuz NaN byte 0x80 in a cache row")
+            vals = FP8_E4M3FNUZ[pool.data[slots]]
         groups = np.arange(vals.shape[1]) // 64
         return vals * pool.scales[slots][:, groups].astype(np.float64)
     if pool.fmt == "fp8_ds_mla":
@@ -169,7 +206,10 @@ def topk_row(scores: np.ndarray, k: int) -> tuple[np.ndarray, int]:
 
 
 def attention_row(prob, t: int, idx_main: np.ndarray, idx_extra: np.ndarray | None = None):
-    """Sparse MLA attention of row t over the listed rows. Returns (out [H, d_v], lse [H])."""
+    """Sparse MLA attention of row t over the listed rows. Returns (out [H, d_v], lse [H]).
+
+    prob.sink (float32 [H] or None) and prob.lse_log2 (bool) are the DeepSeek-V4 options of
+    step 4 of the module description; absent attributes mean no sink and a natural-log lse."""
     b = int(prob.row_req[t])
     parts = []
     for pool, lst in ((prob.kv, idx_main), (prob.extra_kv, idx_extra)):
@@ -180,17 +220,20 @@ def attention_row(prob, t: int, idx_main: np.ndarray, idx_extra: np.ndarray | No
         if keep.size:
             parts.append(kv_rows(pool, b, keep))
     H, d_v = prob.H, prob.d_v
+    sink = getattr(prob, "sink", None)
+    sink = np.full(H, -np.inf) if sink is None else np.asarray(sink, dtype=np.float64)
+    base = math.log(2.0) if getattr(prob, "lse_log2", False) else 1.0
     if not parts:
-        return np.zeros((H, d_v)), np.full(H, -np.inf)
+        return np.zeros((H, d_v)), sink / base
     rows = np.concatenate(parts, axis=0)                        # [n, D]
     q = bf16_to_f64(prob.q[t])                                  # [H, d_qk]
     logits = float(prob.softmax_scale) * (q @ rows[:, :prob.d_qk].T)   # [H, n]
-    m = logits.max(axis=1, keepdims=True)
+    m = np.maximum(logits.max(axis=1), sink)[:, None]           # finite: there is a row
     e = np.exp(logits - m)
-    z = e.sum(axis=1, keepdims=True)
+    z = e.sum(axis=1, keepdims=True) + np.exp(sink[:, None] - m)
     out = (e @ rows[:, :d_v]) / z
     lse = (m + np.log(z))[:, 0]
-    return out, lse
+    return out, lse / base
 
 
 def layer_row(prob, t: int) -> dict:

@@ -74,10 +74,10 @@ def run_attention(prob, d=None, mode="decode", idx=None):
     if mode == "decode":
         ws = m.Workspace(m.dsa_workspace_size(m.ENTRY_MLA_DECODE, T=prob.T, H=prob.H, n_idx=n_idx))
         m.dsa_sparse_mla_decode(d.q, d.kv, idx_main, d.extra_kv, d.idx_extra, prob.T, prob.H, prob.d_qk,
-                                prob.d_v, prob.softmax_scale, out, lse, ws)
+                                prob.d_v, prob.softmax_scale, out, lse, ws, sink=d.sink, lse_log2=d.lse_log2)
     else:
         m.dsa_sparse_mla_prefill(d.q, d.kv, idx_main, d.extra_kv, d.idx_extra, d.rows, prob.H, prob.d_qk,
-                                 prob.d_v, prob.softmax_scale, out, lse)
+                                 prob.d_v, prob.softmax_scale, out, lse, sink=d.sink, lse_log2=d.lse_log2)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -92,6 +92,7 @@ def run_decode(prob, d=None):
     lens = torch.full((T,), -7, dtype=torch.int32, device="cuda")
     ws = m.Workspace(m.dsa_workspace_size(m.ENTRY_DECODE, T=T, n_max=prob.n_max, topk=prob.topk, H=H))
     m.dsa_decode(d.q, d.q_idx, d.w, d.keys, d.kv, d.rows, H, prob.d_qk, prob.d_v, prob.Hi, prob.di,
-                 prob.topk, prob.index_scale, prob.softmax_scale, out, lse, idx, lens, ws)
+                 prob.topk, prob.index_scale, prob.softmax_scale, out, lse, idx, lens, ws,
+                 sink=d.sink, lse_log2=d.lse_log2)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), lens.cpu().numpy()

@@ -118,13 +118,13 @@ def test_topk_rejects(kw, status):
 def mla(**kw):
     a = dict(q=FAKE, ld_q=16 * 576, kv=_kv(), idx=FAKE, ld_idx=128, n_idx=128, extra_kv=None,
              extra_idx=None, ld_extra=0, n_extra=0, B=1, H=16, d_qk=576, d_v=512, scale=0.04,
-             out=FAKE, ld_out=16 * 512, lse=None, ws=None, wsb=0)
+             out=FAKE, ld_out=16 * 512, lse=None, opts=None, ws=None, wsb=0)
     a.update(kw)
     return B._lib.dsa_sparse_mla_decode(
         a["q"], a["ld_q"], C.byref(a["kv"]), a["idx"], a["ld_idx"], a["n_idx"],
         C.byref(a["extra_kv"]) if a["extra_kv"] is not None else None, a["extra_idx"], a["ld_extra"],
         a["n_extra"], a["B"], a["H"], a["d_qk"], a["d_v"], a["scale"], a["out"], a["ld_out"], a["lse"],
-        a["ws"], a["wsb"], None)
+        C.byref(a["opts"]) if a["opts"] is not None else None, a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -146,6 +146,11 @@ def mla(**kw):
     (dict(n_extra=10, extra_idx=FAKE, ld_extra=10,
           extra_kv=_kv(fmt=B.KV_FP8_UNIFORM, scales=FAKE)), B.DSA_ERR_UNSUPPORTED),  # mixed formats
     (dict(scale=float("inf")), B.DSA_ERR_ARG),
+    (dict(kv=_kv(fmt=B.KV_FP8_UNIFORM_FNUZ)), B.DSA_ERR_ARG),    # fnuz pool without scales
+    (dict(n_extra=10, extra_idx=FAKE, ld_extra=10, kv=_kv(fmt=B.KV_FP8_UNIFORM, scales=FAKE),
+          extra_kv=_kv(fmt=B.KV_FP8_UNIFORM_FNUZ, scales=FAKE)), B.DSA_ERR_UNSUPPORTED),  # OCP + fnuz
+    (dict(opts=B._AttnOpts(None, 2, 0)), B.DSA_ERR_ARG),         # lse base flag is 0 or 1
+    (dict(opts=B._AttnOpts(C.c_void_p(0x10002), 0, 0)), B.DSA_ERR_ARG),   # misaligned sink
     # a 2048-entry list over 64 heads splits across workgroups and needs the workspace
     (dict(H=64, ld_q=64 * 576, ld_out=64 * 512, n_idx=2048, ld_idx=2048), B.DSA_ERR_WORKSPACE),
 ])

@@ -27,6 +27,19 @@ CASES = [
                               n_extra=300, pad="tail", n_pad=5)),
     ("ds_mla_h64_two_lists", dict(fmt="fp8_ds_mla", B=2, H=64, n_ctx=5000, n_idx=128, page_size=256,
                                   n_extra=1024, pad="shuffled", n_pad=30)),
+    # DeepSeek-V4 options: fnuz uniform pools, attention sinks, base-2 lse
+    ("fnuz_512", dict(fmt="fp8_uniform_fnuz", B=2, H=16, n_ctx=800, n_idx=200, pad="shuffled", n_pad=9)),
+    ("fnuz_576_two_lists", dict(fmt="fp8_uniform_fnuz", B=2, H=32, n_ctx=900, n_idx=64, n_extra=150,
+                                d_nope=512, d_v=512, n_pad=4)),
+    ("bf16_sink_log2", dict(fmt="bf16", B=3, H=16, n_ctx=700, n_idx=96, pad="tail", n_pad=10,
+                            sink=True, lse_log2=True)),
+    ("bf16_sink_h64_split", dict(fmt="bf16", B=2, H=64, n_ctx=3000, n_idx=2048, pad="shuffled",
+                                 n_pad=100, sink=True)),
+    ("bf16_all_padded_sink", dict(fmt="bf16", B=2, H=16, n_ctx=300, n_idx=64, pad="all", sink=True,
+                                  lse_log2=True)),
+    ("ds_mla_two_lists_sink_log2", dict(fmt="fp8_ds_mla", B=3, H=16, n_ctx=2000, n_idx=128,
+                                        page_size=256, n_extra=300, pad="tail", n_pad=5, sink=True,
+                                        lse_log2=True)),
 ]
 
 
@@ -46,6 +59,48 @@ def test_attention(name, kw, mode):
     say("attention", name, mode)
     out, lse = run_attention(prob, mode=mode)
     _check_all(prob, out, lse)
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_sink_edge_values(mode):
+    """Per-head sinks at the ends of the range: -inf (no sink for that head), far above every
+    logit (out -> 0, lse -> sink), and far below; the others ordinary."""
+    import dataclasses
+    base = workload("attention_case", fmt="bf16", B=2, H=16, n_ctx=700, n_idx=256, pad="shuffled",
+                    n_pad=20, sink=True)
+    sink = base.sink.copy()
+    sink[0], sink[1], sink[2], sink[3] = -np.inf, 80.0, -80.0, 0.0
+    for log2 in (False, True):
+        prob = dataclasses.replace(base, sink=sink, lse_log2=log2)
+        say("attention sink edges", mode, "log2" if log2 else "ln")
+        out, lse = run_attention(prob, mode=mode)
+        _check_all(prob, out, lse)
+
+
+def _fnuz_case(codes, scale):
+    import dataclasses
+    base = workload("attention_case", fmt="fp8_uniform_fnuz", B=2, H=16, n_ctx=500, n_idx=128,
+                    pad="shuffled", n_pad=8)
+    rng = np.random.default_rng(len(codes))
+    data = rng.choice(np.asarray(codes, np.uint8), size=base.kv.data.shape)
+    kv = dataclasses.replace(base.kv, data=data, scales=np.full_like(base.kv.scales, scale))
+    return dataclasses.replace(base, kv=kv)
+
+
+@pytest.mark.parametrize("which", ["subnormal", "ends"])
+def test_fnuz_extreme_codes(which):
+    """Every fnuz byte class decodes exactly: subnormal codes (m / 8 * 2^-7, decoded through fp32
+    denormals) scaled up to unit size, and +-240 (0x7F / 0xFF, NaN codes in OCP) beside zero."""
+    if which == "subnormal":
+        codes = [c | s for c in range(1, 8) for s in (0, 0x80)]
+        prob = _fnuz_case(codes, 256.0)
+    else:
+        codes = [0x7F, 0xFF, 0x00, 0x38, 0xB8]
+        prob = _fnuz_case(codes, 1.0 / 128)
+    say("attention fnuz codes", which)
+    out, lse = run_attention(prob, mode="decode")
+    _check_all(prob, out, lse)
+    assert np.abs(out).max() > 0.05        # the rows are not (wrongly) all zero
 
 
 def test_attention_dsv4_fp8_full_size():

@@ -40,20 +40,25 @@ def _src(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
 
 
+@pytest.mark.parametrize("fnuz", [False, True], ids=["ocp", "fnuz"])
 @pytest.mark.parametrize("D", [512, 576])
-def test_kv_uniform(D):
+def test_kv_uniform(D, fnuz):
     m = dsa()
-    rng = np.random.default_rng(D)
+    rng = np.random.default_rng(D + fnuz)
     n, n_slots = 300, 1000
     bits = _rows(rng, n, D)
+    if fnuz:   # values on the fnuz ties near the top (232 between 224 and 240) and tiny ones
+        x = np.array([240, 232, -232, 233, 224, 228, -240, 2.0 ** -11, -(2.0 ** -11), -1e-6,
+                      3 * 2.0 ** -12, 0, -0.0, 1, 100, 16] * 4, np.float32)
+        bits[6, :64] = to_bf16_bits(x)
     slots = _slots(rng, n, n_slots)
     data = torch.full((n_slots, D), SENT, dtype=torch.uint8, device="cuda")
     scales = torch.full((n_slots, D // 64), -7.0, dtype=torch.float32, device="cuda")
-    kv = m.KVCache("fp8_uniform", data, D - 64, 64, scales=scales)
-    say("cache write uniform", D)
+    kv = m.KVCache("fp8_uniform_fnuz" if fnuz else "fp8_uniform", data, D - 64, 64, scales=scales)
+    say("cache write uniform", D, "fnuz" if fnuz else "ocp")
     m.dsa_kv_cache_write(_src(bits), torch.from_numpy(slots).cuda(), kv)
     torch.cuda.synchronize()
-    q, s = CW.write_uniform(bits)
+    q, s = CW.write_uniform(bits, fnuz=fnuz)
     got, gs = data.cpu().numpy(), scales.cpu().numpy()
     ok = (slots >= 0) & (slots < n_slots)
     assert np.array_equal(got[slots[ok]], q[ok])

@@ -42,6 +42,22 @@ def test_fused_decode(label, name, kw):
         assert ok, f"row {t}: attention {msg}"
 
 
+@pytest.mark.parametrize("log2", [False, True], ids=["ln", "log2"])
+def test_fused_decode_with_sinks(log2):
+    """The fused entry with DeepSeek-V4's attention options: per-head sinks in the softmax
+    denominator and the lse in either base (split-KV path: 64 heads over 2048 rows)."""
+    import dataclasses
+    from workloads.gen import sinks
+    base = workload("glm_decode", n_ctx=20000, B=2, ctx_lens=(20000, 700), topk=2048)
+    prob = dataclasses.replace(base, sink=sinks(0, base.H), lse_log2=log2)
+    say("decode sinks", "log2" if log2 else "ln")
+    out, lse, idx, lens = run_decode(prob)
+    for t in range(prob.T):
+        o_ref, l_ref = oracle.attention_row(prob, t, idx[t])
+        ok, msg = attention_ok(out[t], lse[t], o_ref, l_ref, prob.kv.fmt)
+        assert ok, f"row {t}: attention {msg}"
+
+
 def _prefill_chain(prob):
     m = dsa()
     d = upload(prob)

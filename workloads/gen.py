@@ -12,7 +12,11 @@ and stored in the byte format the caches use:
   (448 NoPE fp8 + 64 RoPE bf16) followed by ``page_size`` x 8 scale bytes (7 UE8M0 exponents,
   one per 64 NoPE channels, and one pad byte);
 * the uniform fp8 pool of the same page's section "Uniform fp8 pool - 2D": ``[slots, D]`` fp8
-  with one fp32 scale per 64 channels.
+  with one fp32 scale per 64 channels, OCP bytes, or fnuz bytes (``float8_e4m3fnuz``, bias 8,
+  torch's cast after clamping to +-240; section "fp8 flavors");
+* DeepSeek-V4 attention sinks: one logit per head, drawn N(3, 2^2) (the pages give no
+  distribution; with unit-variance logits over ~100 rows this puts the sink's share of the
+  softmax mass anywhere from negligible to most of it).
 
 Page tables are random permutations of physical pages ("shuffled page table").
 Nothing here scores, selects, attends or dequantises.
@@ -27,6 +31,7 @@ import numpy as np
 import torch
 
 FP8_MAX = 448.0
+FP8_FNUZ_MAX = 240.0
 DS_MLA_NOPE = 448
 DS_MLA_ROPE = 64
 DS_MLA_DATA_BYTES = 576          # 448 fp8 + 64 * 2 bytes of bf16
@@ -62,6 +67,7 @@ class KVPool:
 
     fmt "bf16":        data uint16 [slots, D]            (D = d_nope + d_rope, e.g. 512 + 64)
     fmt "fp8_uniform": data uint8  [slots, D], scales float32 [slots, D // 64]
+    fmt "fp8_uniform_fnuz": the same with fnuz e4m3 bytes
     fmt "fp8_ds_mla":  data uint8  [pages, page_size * 584] (block-planar page layout)
     Addressing as for KeyPool (for fp8_ds_mla the slot splits into page = slot // page_size and
     in-page position = slot % page_size).
@@ -116,6 +122,8 @@ class DSAProblem:
     idx_main: Optional[np.ndarray] = None
     extra_kv: Optional[KVPool] = None
     idx_extra: Optional[np.ndarray] = None
+    sink: Optional[np.ndarray] = None       # float32 [H] per-head sink logit (DeepSeek-V4)
+    lse_log2: bool = False                  # lse in base 2
     meta: dict = field(default_factory=dict)
 
     @property
@@ -148,6 +156,12 @@ def to_fp8_bytes(x: np.ndarray) -> np.ndarray:
     """float32 -> OCP e4m3fn bytes (torch cast, RNE) after saturating to +-448."""
     x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -FP8_MAX, FP8_MAX)
     return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def to_fp8_fnuz_bytes(x: np.ndarray) -> np.ndarray:
+    """float32 -> fnuz e4m3 bytes (torch cast, RNE) after saturating to +-240."""
+    x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -FP8_FNUZ_MAX, FP8_FNUZ_MAX)
+    return torch.from_numpy(x).to(torch.float8_e4m3fnuz).view(torch.uint8).numpy()
 
 
 def _bf16_normal(seed, tid, shape):
@@ -203,15 +217,17 @@ def pack_ds_mla(values: np.ndarray, page_size: int) -> np.ndarray:
     return out
 
 
-def quant_uniform(values: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def quant_uniform(values: np.ndarray, fnuz: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """float32 [slots, D] -> (fp8 bytes [slots, D], float32 scales [slots, D // 64]),
-    scale = amax over 64 channels / 448."""
+    scale = amax over 64 channels / 448 (OCP bytes), or / 240 (fnuz bytes)."""
     slots, D = values.shape
     assert D % 64 == 0
     g = values.reshape(slots, D // 64, 64)
     amax = np.abs(g).max(axis=2)
-    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
-    return to_fp8_bytes((g / scale[:, :, None]).reshape(slots, D)), scale
+    fmax = np.float32(FP8_FNUZ_MAX if fnuz else FP8_MAX)
+    scale = np.where(amax > 0, amax / fmax, np.float32(1.0)).astype(np.float32)
+    enc = to_fp8_fnuz_bytes if fnuz else to_fp8_bytes
+    return enc((g / scale[:, :, None]).reshape(slots, D)), scale
 
 
 def quant_rows(values: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
@@ -223,7 +239,12 @@ def quant_rows(values: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 
 # --------------------------------------------------------------------------- workloads
 # tensor ids of the sub-streams
-_T_Q, _T_QIDX, _T_W, _T_KIDX, _T_KV, _T_BT, _T_EXTRA, _T_CTX, _T_LIST, _T_BT2, _T_KV2 = range(11)
+_T_Q, _T_QIDX, _T_W, _T_KIDX, _T_KV, _T_BT, _T_EXTRA, _T_CTX, _T_LIST, _T_BT2, _T_KV2, _T_SINK = range(12)
+
+
+def sinks(seed: int, H: int) -> np.ndarray:
+    """Per-head attention-sink logits, float32 [H] ~ N(3, 2^2)."""
+    return (3.0 + 2.0 * _rng(seed, _T_SINK).standard_normal(H)).astype(np.float32)
 
 
 def glm_decode(n_ctx: int = 32768, B: int = 1, H: int = 64, Hi: int = 64, di: int = 128,
@@ -283,9 +304,9 @@ def _make_kv(seed, tid, fmt, slots, d_nope, d_rope, page_size, bt, req_base) -> 
         return KVPool("bf16", _bf16_normal(seed, tid, (slots, D)), None, page_size, bt, req_base,
                       d_nope, d_rope)
     vals = _normal(seed, tid, (slots, D))
-    if fmt == "fp8_uniform":
-        data, sc = quant_uniform(vals)
-        return KVPool("fp8_uniform", data, sc, page_size, bt, req_base, d_nope, d_rope)
+    if fmt in ("fp8_uniform", "fp8_uniform_fnuz"):
+        data, sc = quant_uniform(vals, fnuz=fmt == "fp8_uniform_fnuz")
+        return KVPool(fmt, data, sc, page_size, bt, req_base, d_nope, d_rope)
     if fmt == "fp8_ds_mla":
         assert d_nope == DS_MLA_NOPE and d_rope == DS_MLA_ROPE
         return KVPool("fp8_ds_mla", pack_ds_mla(vals, page_size), None, page_size, bt, req_base,
@@ -387,14 +408,16 @@ def dsv4_fp8_decode(B: int = 64, H: int = 16, window: int = 128, n_extra: int = 
 def attention_case(fmt: str = "bf16", B: int = 2, H: int = 16, n_ctx: int = 700, n_idx: int = 96,
                    pad: str = "tail", n_pad: int = 10, page_size: int = 64, seed: int = 0,
                    n_extra: int = 0, extra_fmt: Optional[str] = None, d_nope: Optional[int] = None,
-                   d_rope: int = 64, d_v: Optional[int] = None, name: Optional[str] = None) -> DSAProblem:
+                   d_rope: int = 64, d_v: Optional[int] = None, name: Optional[str] = None,
+                   sink: bool = False, lse_log2: bool = False) -> DSAProblem:
     """Attention-only case with explicit index lists.
 
     Each request b has n_ctx cached tokens; its list holds n_idx distinct positions drawn at
     random, with n_pad of them replaced by -1 ("tail": the last n_pad entries; "shuffled":
     random places; "all": every entry). fmt chooses the pool format. bf16 defaults to the GLM
     row (512 latent + 64 RoPE, value = the 512 latent columns); the fp8 formats default to the
-    DeepSeek-V4 row (448 NoPE + 64 RoPE, value = the whole 512-wide row)."""
+    DeepSeek-V4 row (448 NoPE + 64 RoPE, value = the whole 512-wide row). sink draws per-head
+    sink logits; lse_log2 asks for the base-2 lse."""
     if d_nope is None:
         d_nope = 512 if fmt == "bf16" else DS_MLA_NOPE
     if fmt == "fp8_ds_mla" or extra_fmt == "fp8_ds_mla":
@@ -432,7 +455,8 @@ def attention_case(fmt: str = "bf16", B: int = 2, H: int = 16, n_ctx: int = 700,
         name=name or f"attn_{fmt}_{B}x{H}_{n_idx}_{pad}", T=B, H=H, d_qk=D,
         d_v=d_v, topk=n_idx, q=q, kv=kv,
         row_req=np.arange(B, dtype=np.int32), row_len=ctx.astype(np.int32), n_req=B,
-        softmax_scale=1.0 / math.sqrt(D), idx_main=idx_main, extra_kv=extra, idx_extra=idx_extra)
+        softmax_scale=1.0 / math.sqrt(D), idx_main=idx_main, extra_kv=extra, idx_extra=idx_extra,
+        sink=sinks(seed, H) if sink else None, lse_log2=lse_log2)
 
 
 # Named workloads (the five the measurement plan covers, plus the 128k headline shape).
