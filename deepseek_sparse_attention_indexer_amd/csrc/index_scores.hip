@@ -118,21 +118,29 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;       // lane group 0..3
   const int c = lane & 15;       // column within a 16-wide tile
-  const int b = min(max(a.row_req ? a.row_req[t] : t, 0), a.n_req - 1);
-  int n = a.row_len[t];
-  n = min(max(n, 0), a.n_max);
-  const int ntiles = (n + 63) >> 6;
   const int stride = gridDim.x * kScoreWaves;
   int tile = blockIdx.x * kScoreWaves + wave;
 
   // 1. page-table entries of this wave's first two tiles, 2. the row's query heads and head
   // weights (staged once per workgroup in LDS, zero-padded to 16 * MT heads), 3. the first
   // tile's 16 key loads back to back. Loads complete in issue order, so each wait below only
-  // covers what it needs.
+  // covers what it needs. The table reads do not wait for the row's request and length: they
+  // go out for request t (a decode row is its own request) and the longest row, both kept
+  // inside the table, and are re-issued only if the row belongs to another request.
   using Tile = KeyTile<DI, FP8>;
   typename Tile::Addr ad_cur, ad_nxt;
-  if (tile < ntiles) Tile::table(a, b, tile << 6, n, c, ad_cur);
-  if (tile + stride < ntiles) Tile::table(a, b, (tile + stride) << 6, n, c, ad_nxt);
+  const int b_spec = min(t, a.n_req - 1);
+  const int ntiles_max = (a.n_max + 63) >> 6;
+  if (tile < ntiles_max) Tile::table(a, b_spec, tile << 6, a.n_max, c, ad_cur);
+  if (tile + stride < ntiles_max) Tile::table(a, b_spec, (tile + stride) << 6, a.n_max, c, ad_nxt);
+  const int b = min(max(a.row_req ? a.row_req[t] : t, 0), a.n_req - 1);
+  int n = a.row_len[t];
+  n = min(max(n, 0), a.n_max);
+  const int ntiles = (n + 63) >> 6;
+  if (b != b_spec) {   // uniform: the whole workgroup serves row t
+    if (tile < ntiles) Tile::table(a, b, tile << 6, n, c, ad_cur);
+    if (tile + stride < ntiles) Tile::table(a, b, (tile + stride) << 6, n, c, ad_nxt);
+  }
   constexpr int QPT = (16 * MT * DI * 2 + kScoreThreads * 16 - 1) / (kScoreThreads * 16);
   u32x4_t qv[QPT];
   {

@@ -27,9 +27,10 @@ inline void launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st
 // top-k radix: first digit = top 12 bits of the order-preserving key
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
-// copies of each row's global first-digit histogram (more copies thin out same-address
-// atomics in the score kernel but cost every filter workgroup a longer read)
-constexpr int kHistSlices = 1;
+// copies of each row's global first-digit histogram, written by alternate workgroups: the
+// score kernel's atomics on the few busy bins serialise per address, so more copies shorten
+// that tail, at the price of a longer histogram read in every filter workgroup
+constexpr int kHistSlices = 2;
 // rows with at most this many candidates are selected by one workgroup entirely in LDS
 constexpr int kTopkLdsMax = 16384;
 // candidates per workgroup in the multi-workgroup (long row) select

@@ -246,9 +246,21 @@ __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
   constexpr int per = kTopkChunk / kNT;
   const int t = blockIdx.y;
   const int k = a.topk;
+  const int s0 = blockIdx.x * kTopkChunk;
+  // this chunk's scores go out first, before the row length is known (positions below the
+  // longest row stay inside the logits row); the histogram read overlaps them
+  uint32_t keys[per];
+  const float* row = a.logits + (int64_t)t * a.ld_logits;
+  {
+    const int s1_max = min(a.n_max, s0 + kTopkChunk);
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      const int s = s0 + j * kNT + threadIdx.x;
+      keys[j] = s < s1_max ? float_key(row[s]) : 0u;
+    }
+  }
   int n = a.row_len[t];
   n = min(max(n, 0), a.n_max);
-  const int s0 = blockIdx.x * kTopkChunk;
   const int s1 = min(n, s0 + kTopkChunk);
   int32_t* out = a.indices + (int64_t)t * a.ld_idx;
   if (n <= k) {                                // every position is selected
@@ -256,20 +268,22 @@ __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
     return;
   }
   if (s0 >= n) return;
-  // this chunk's scores go out first; the histogram read overlaps them
-  uint32_t keys[per];
-  const float* row = a.logits + (int64_t)t * a.ld_logits;
-#pragma unroll
-  for (int j = 0; j < per; ++j) {
-    const int s = s0 + j * kNT + threadIdx.x;
-    keys[j] = s < s1 ? float_key(row[s]) : 0u;
-  }
   const uint32_t* gh = a.hist + (int64_t)t * kHistSlices * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += kNT) {
-    uint32_t v = 0;
+  {
+    // every slice of every bin this thread sums is in flight at once (one round trip)
+    constexpr int HB = kHistBins / kNT;
+    uint32_t v[HB][kHistSlices];
 #pragma unroll
-    for (int sl = 0; sl < kHistSlices; ++sl) v += gh[sl * kHistBins + i];
-    s_hist[i] = v;
+    for (int h = 0; h < HB; ++h)
+#pragma unroll
+      for (int sl = 0; sl < kHistSlices; ++sl) v[h][sl] = gh[sl * kHistBins + h * kNT + threadIdx.x];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int sl = 0; sl < kHistSlices; ++sl) x += v[h][sl];
+      s_hist[h * kNT + threadIdx.x] = x;
+    }
   }
   lds_barrier();
   find_digit_desc(s_hist, kHistBins, (uint32_t)k, s_w, s_res);
@@ -335,28 +349,41 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   constexpr int per = kTopkChunk / kNT;
   const int t = blockIdx.y;
   const int k = a.topk;
-  int n = a.row_len[t];
-  n = min(max(n, 0), a.n_max);
   int32_t* out = a.indices + (int64_t)t * a.ld_idx;
-  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
   const uint32_t* cnt = a.counts + (int64_t)t * a.n_chunks * 2;
 
   if ((int)blockIdx.x < a.n_chunks) {
-    // ---- chunk workgroup: keys above the threshold bin
+    // ---- chunk workgroup: keys above the threshold bin. Its loads go out before the row
+    // length is known (chunks past the row's end then simply return). Every chunk workgroup
+    // first returns its share of the row's first-digit histogram to zero (all readers of it
+    // ran in the previous kernel).
     const int c_me = blockIdx.x;
     const int s0 = c_me * kTopkChunk;
-    if (n <= k || c_me >= nch) return;
-    const int s1 = min(n, s0 + kTopkChunk);
-    const uint32_t d1 = a.thr1[2 * t];
+    {
+      constexpr int HW = kHistSlices * kHistBins;
+      const int share = (HW + a.n_chunks - 1) / a.n_chunks;
+      uint32_t* gh = a.hist + (int64_t)t * HW;
+      const int h1 = min(HW, (c_me + 1) * share);
+      for (int i = c_me * share + threadIdx.x; i < h1; i += kNT) gh[i] = 0;
+    }
     uint32_t before = 0;                       // counts of the earlier chunks
     for (int c = threadIdx.x; c < c_me; c += kNT) before += cnt[2 * c];
     uint32_t keys[per];
     const float* row = a.logits + (int64_t)t * a.ld_logits;
+    {
+      const int s1_max = min(a.n_max, s0 + kTopkChunk);
 #pragma unroll
-    for (int j = 0; j < per; ++j) {
-      const int s = s0 + j * kNT + threadIdx.x;
-      keys[j] = s < s1 ? float_key(row[s]) : 0u;
+      for (int j = 0; j < per; ++j) {
+        const int s = s0 + j * kNT + threadIdx.x;
+        keys[j] = s < s1_max ? float_key(row[s]) : 0u;
+      }
     }
+    const uint32_t d1 = a.thr1[2 * t];
+    int n = a.row_len[t];
+    n = min(max(n, 0), a.n_max);
+    const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+    if (n <= k || c_me >= nch) return;
+    const int s1 = min(n, s0 + kTopkChunk);
     uint32_t base;
     block_incl_scan(before, s_w, &base);
     uint32_t sel = 0, m = 0;
@@ -378,10 +405,14 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
     return;
   }
 
-  // ---- the resolver
-  auto clear_hist = [&]() {   // the first-digit histogram back to zero (no one here reads it)
-    uint32_t* gh = a.hist + (int64_t)t * kHistSlices * kHistBins;
-    for (int i = threadIdx.x; i < kHistSlices * kHistBins; i += kNT) gh[i] = 0;
+  // ---- the resolver: the per-chunk counts go out before the row length is known
+  const int c0 = 2 * threadIdx.x;
+  const uint32_t r0 = c0 < a.n_chunks ? cnt[2 * c0 + 1] : 0u;
+  const uint32_t r1 = c0 + 1 < a.n_chunks ? cnt[2 * c0 + 3] : 0u;
+  int n = a.row_len[t];
+  n = min(max(n, 0), a.n_max);
+  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+  auto clear_hist = [&]() {   // lens (the chunk workgroups return the histogram to zero)
     if (threadIdx.x == 0) a.lens[t] = min(n, k);
   };
   if (n <= k) {
@@ -393,9 +424,8 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   const uint32_t above1 = a.thr1[2 * t + 1];
   {
     // exclusive prefixes of the per-chunk candidate counts: thread i owns chunks 2i, 2i + 1
-    const int c0 = 2 * threadIdx.x;
-    const uint32_t v0 = c0 < nch ? cnt[2 * c0 + 1] : 0u;
-    const uint32_t v1 = c0 + 1 < nch ? cnt[2 * c0 + 3] : 0u;
+    const uint32_t v0 = c0 < nch ? r0 : 0u;
+    const uint32_t v1 = c0 + 1 < nch ? r1 : 0u;
     for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
     uint32_t total;
     const uint32_t incl = block_incl_scan(v0 + v1, s_w, &total);
