@@ -96,6 +96,13 @@ __device__ __forceinline__ int64_t slot_done(const Paging& p, SlotRead r) {
   return p.bt != nullptr ? in_page : packed;
 }
 
+// max(0, x) for any fp32 x in one integer max: a float with the sign bit clear is a
+// non-negative int32 and keeps its bits; every negative float (and -0) is a negative int32 and
+// becomes +0. fmaxf would first canonicalise an MFMA result (a second instruction).
+__device__ __forceinline__ float relu_f32(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 and +0 share a key.
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
         for (int r = 0; r < 4; ++r) {
           float x = acc[mt][r];
           if constexpr (FP8) x *= cur.sc[st];
-          p = fmaf(wv[mt][r], fmaxf(x, 0.0f), p);
+          p = fmaf(wv[mt][r], relu_f32(x), p);
         }
       part[st] = p;
     }

@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArg
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) pp = fmaf(wv[mt][rr], fmaxf(acc[mt][rr], 0.0f), pp);
+            for (int rr = 0; rr < 4; ++rr) pp = fmaf(wv[mt][rr], relu_f32(acc[mt][rr]), pp);
           return pp;
         };
         float part[4];
