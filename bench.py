@@ -129,6 +129,57 @@ def prefill_indexer(dsa, to_device, workloads, torch, dev, reps=5):
             "timing": "HIP events from each dispatch, inputs resident (8193 rows x 64 x 128 bf16)"}
 
 
+def other_configs(dsa, to_device, workloads, torch, dev, flush, names, reps=15):
+    """Cold per-call latency of the other single-GPU workloads (context beside the headline):
+    the fused layer for decode shapes, the attention stage alone for the DSv4 fp8 case."""
+    res = {}
+    for name in names:
+        prob = workloads.make_workload(name)
+        d = to_device(prob, dev)
+        T, H = prob.T, prob.H
+        out = torch.empty(T, H, prob.d_v, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(T, H, dtype=torch.float32, device=dev)
+        if prob.kpool is not None:
+            idx = torch.empty(T, prob.topk, dtype=torch.int32, device=dev)
+            lens = torch.empty(T, dtype=torch.int32, device=dev)
+            ws = dsa.Workspace(dsa.dsa_workspace_size(dsa.ENTRY_DECODE, T=T, n_max=prob.n_max, topk=prob.topk,
+                                                      H=H), dev)
+
+            def step():
+                dsa.dsa_decode(d.q, d.q_idx, d.w, d.keys, d.kv, d.rows, H, prob.d_qk, prob.d_v, prob.Hi, prob.di,
+                               prob.topk, prob.index_scale, prob.softmax_scale, out, lse, idx, lens, ws)
+            stage = "layer (scores + top-k + sparse attention)"
+            ab = algorithmic_bytes(prob)["total"]
+        else:
+            n_main = d.idx_main.shape[1]
+            n_extra = d.idx_extra.shape[1] if d.idx_extra is not None else 0
+            ws = dsa.Workspace(dsa.dsa_workspace_size(dsa.ENTRY_MLA_DECODE, T=T, H=H, n_idx=n_main + n_extra), dev)
+
+            def step():
+                dsa.dsa_sparse_mla_decode(d.q, d.kv, d.idx_main, d.extra_kv, d.idx_extra, T, H, prob.d_qk,
+                                          prob.d_v, prob.softmax_scale, out, lse, ws)
+            stage = "sparse attention over main + extra lists (the stage this case specifies)"
+            row_b = {"bf16": 2 * prob.d_qk, "fp8_uniform": prob.d_qk + 4 * prob.d_qk // 64, "fp8_ds_mla": 584}[prob.kv.fmt]
+            ab = T * (n_main + n_extra) * (row_b + 4) + T * H * (prob.d_qk * 2 + prob.d_v * 2 + 4)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            flush.sum()
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        us = statistics.median([a.elapsed_time(b) * 1e3 for a, b in evs])
+        res[name] = {"stage": stage, "rows": int(T), "context_max": int(prob.n_max), "cold_us": round(us, 2),
+                     "algorithmic_bytes": int(ab), "hbm_roofline_frac": round(ab / (HBM_PEAK_GBS * 1e9) / (us * 1e-6), 4)}
+        del d, out, lse, ws
+        torch.cuda.empty_cache()
+        log(f"  {name}: {us:.2f} us cold")
+    return res
+
+
 def cpu_baseline(prob, seconds):
     import numpy as np  # noqa: F401
     import oracle
@@ -160,6 +211,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (32k, 1M fp8-key decode, DSv4 fp8 attention, multi-token)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -277,6 +330,11 @@ def main():
     if not args.no_prefill:
         log("prefill indexer ...")
         res["prefill_indexer"] = prefill_indexer(dsa, to_device, workloads, torch, dev)
+    if not args.no_configs:
+        log("other workloads ...")
+        res["other_configs"] = other_configs(dsa, to_device, workloads, torch, dev, flush,
+                                             ["glm_decode_32k", "long_decode_1m", "dsv4_fp8_decode",
+                                              "spec_decode_b16_q4_32k", "extend_64_128k"])
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)

@@ -45,8 +45,16 @@ struct RowGeom {
   static constexpr int kUnits = FMT == kFmtBf16 ? DQK / 8 : (kUniformFmt<FMT> ? DQK / 16 : 36);
 };
 
-// fp8 rows: one 16-byte unit of a row is loaded (with its scale) into registers first, then
-// dequantised to bf16 and stored to LDS, so that every load of a block is in flight at once.
+// fp8 rows travel as raw bytes: data bytes per row (fp8_ds_mla: 448 fp8 + 64 bf16 RoPE; uniform
+// pools: one byte per channel) and scale bytes per row (fp8_ds_mla: 7 UE8M0 + 1 pad; uniform:
+// one fp32 per 64 channels)
+template <int FMT, int DQK>
+struct RawGeom {
+  static constexpr int kData = FMT == kFmtDsMla ? 576 : DQK;
+  static constexpr int kScale = FMT == kFmtDsMla ? 8 : (DQK / 64) * 4;
+};
+
+// One 16-byte unit of an fp8 row and its scale, on the way to bf16.
 struct RawUnit {
   u32x4_t v;
   float sc;
@@ -77,27 +85,6 @@ __device__ __forceinline__ RowOff row_offsets(const KvDev& kv, int64_t slot) {
     o.scale = pbase + (int64_t)P * 576 + pos * 8;
   }
   return o;
-}
-
-template <int FMT, int DQK>
-__device__ __forceinline__ RawUnit load_unit(const uint8_t* data, const uint8_t* scales, RowOff off,
-                                             bool valid, int u) {
-  RawUnit r;
-  r.v = u32x4_t{0u, 0u, 0u, 0u};
-  r.sc = 0.f;
-  if (!valid) return r;
-  if constexpr (kUniformFmt<FMT>) {
-    r.v = *reinterpret_cast<const u32x4_t*>(data + off.data + 16 * u);
-    r.sc = *reinterpret_cast<const float*>(scales + off.scale + (u / 4) * 4);
-  } else {  // fp8_ds_mla
-    if (u < 28) {
-      r.v = *reinterpret_cast<const u32x4_t*>(data + off.data + 16 * u);
-      r.sc = ue8m0_scale(data[off.scale + (u >> 2)]);
-    } else {
-      r.v = *reinterpret_cast<const u32x4_t*>(data + off.data + 448 + 16 * (u - 28));
-    }
-  }
-  return r;
 }
 
 template <int FMT, int DQK>
@@ -161,7 +148,17 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
   constexpr int KS = DQK / 32;
   constexpr int RE = RowGeom<FMT, DQK>::kElems;
   constexpr int UN = RowGeom<FMT, DQK>::kUnits;
-  __shared__ __align__(16) uint16_t s_rows[2][kNB][RE];   // double-buffered gathered block
+  // bf16 rows: two gathered blocks in LDS (double buffer). fp8 rows: one bf16 block, plus two
+  // raw blocks (bytes as stored, data then scales) that the direct loads fill a block ahead
+  constexpr bool kRaw = FMT != kFmtBf16;
+  constexpr int BB = kNB * RE * 2;                            // bytes of one bf16 block
+  constexpr int RDB = RawGeom<FMT, DQK>::kData;
+  constexpr int RSB = RawGeom<FMT, DQK>::kScale;
+  constexpr int RAWB = kNB * (RDB + RSB);                     // bytes of one raw block
+  constexpr int LDSB = kRaw ? BB + 2 * RAWB : 2 * BB;
+  static_assert(RDB % 16 == 0 && RSB % 4 == 0 && (kNB * RDB) % 1024 == 0, "raw staging");
+  __shared__ __align__(16) uint8_t s_lds[LDSB];
+  uint16_t (*const s_rows)[kNB][RE] = reinterpret_cast<uint16_t (*)[kNB][RE]>(s_lds);
   // list entries of the current pass resolved to cache slots: slot | list << 30, -1 = padding
   __shared__ int32_t s_slot[kResolve];
 
@@ -222,8 +219,8 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
     const int64_t slot = v >= 0 ? (v & 0x3fffffff) : 0;
     return x ? row_offsets<FMT, DQK>(kv1, slot) : row_offsets<FMT, DQK>(kv0, slot);
   };
-  // gather block rows into LDS: bf16 by direct global->LDS loads (asynchronous, completes at
-  // the next vmcnt wait), fp8 staged through registers and dequantised (synchronous)
+  // bf16 rows into LDS by direct global->LDS loads (asynchronous, completes at the next vmcnt
+  // wait)
   auto gather = [&](int buf, int jb) {   // jb: pass entry of the block's first row
     if constexpr (FMT == kFmtBf16) {
       // lane l of instruction ins fills 16-byte slot 64 * ins + l of the padded block; the pad
@@ -245,35 +242,61 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
           __builtin_amdgcn_global_load_lds(src, lbase + ins * 1024, 16, 0, 0);
         }
       }
-    } else {
-      constexpr int TOT = kNB * UN;
-      constexpr int QN = (TOT + NT - 1) / NT;          // units per thread
-      constexpr int NBAT = (QN + 5) / 6;               // at most 6 units in flight (registers)
-      constexpr int QB = (QN + NBAT - 1) / NBAT;
-#pragma unroll 1
-      for (int bt = 0; bt < NBAT; ++bt) {
-        RawUnit raw[QB];
-#pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          const int uid = threadIdx.x + (bt * QB + q) * NT;
-          if (bt * QB + q < QN && uid < TOT) {
-            const int r = uid / UN;
-            bool x;
-            const RowOff off = row_of(jb + r, x);
-            raw[q] = load_unit<FMT, DQK>(x ? kv1.data : kv0.data,
-                                         reinterpret_cast<const uint8_t*>(x ? kv1.scales : kv0.scales),
-                                         off, slot_at(jb + r) >= 0, uid - r * UN);
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          const int uid = threadIdx.x + (bt * QB + q) * NT;
-          if (bt * QB + q < QN && uid < TOT) {
-            const int r = uid / UN;
-            store_unit<FMT, DQK>(raw[q], uid - r * UN, &s_rows[buf][r][0]);
-          }
-        }
+    }
+  };
+
+  // fp8 rows: the block's raw bytes go into raw buffer `buf` by direct global->LDS loads
+  // (asynchronous; instruction ins of the data fills bytes [1024 ins, +1024), lane l at +16 l,
+  // i.e. 16-byte chunk q = 64 ins + l = row q / (RDB / 16), chunk q % (RDB / 16); the scales
+  // follow as dwords), one block ahead of its use
+  auto gather_raw = [&](int buf, int jb) {
+    uint8_t* rb = s_lds + BB + buf * RAWB;
+    auto* lds_d = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(reinterpret_cast<uintptr_t>(rb) & 0xffffffffu);
+    auto* lds_s = lds_d + kNB * RDB;
+    constexpr int CPR = RDB / 16;                    // 16-byte chunks per row
+    constexpr int NID = kNB * RDB / 1024;            // data instructions per block
+    for (int ins = wave; ins < NID; ins += NW) {
+      const int q = ins * 64 + lane;
+      const int r = q / CPR;
+      bool x;
+      const RowOff off = row_of(jb + r, x);
+      __builtin_amdgcn_global_load_lds((x ? kv1.data : kv0.data) + off.data + 16 * (q - r * CPR), lds_d + ins * 1024, 16, 0, 0);
+    }
+    constexpr int SPR = RSB / 4;                     // scale dwords per row
+    constexpr int NIS = (kNB * SPR + 63) / 64;       // scale instructions per block
+    for (int ins = wave; ins < NIS; ins += NW) {
+      const int q = ins * 64 + lane;
+      if (q < kNB * SPR) {
+        const int r = q / SPR;
+        bool x;
+        const RowOff off = row_of(jb + r, x);
+        const uint8_t* sb = FMT == kFmtDsMla ? (x ? kv1.data : kv0.data)
+                                             : reinterpret_cast<const uint8_t*>(x ? kv1.scales : kv0.scales);
+        __builtin_amdgcn_global_load_lds(sb + off.scale + 4 * (q - r * SPR), lds_s + ins * 256, 4, 0, 0);
       }
+    }
+  };
+  // raw buffer `buf` -> the bf16 block (LDS to LDS); list padding becomes zero rows
+  auto dequant = [&](int buf, int jb) {
+    const uint8_t* rb = s_lds + BB + buf * RAWB;
+    for (int uid = threadIdx.x; uid < kNB * UN; uid += NT) {
+      const int r = uid / UN;
+      const int u = uid - r * UN;
+      const uint8_t* rd = rb + r * RDB;
+      const uint8_t* rs = rb + kNB * RDB + r * RSB;
+      RawUnit ru;
+      if constexpr (FMT == kFmtDsMla) {
+        ru.v = *reinterpret_cast<const u32x4_t*>(rd + (u < 28 ? 16 * u : 448 + 16 * (u - 28)));
+        ru.sc = u < 28 ? ue8m0_scale(rs[u >> 2]) : 0.f;
+      } else {
+        ru.v = *reinterpret_cast<const u32x4_t*>(rd + 16 * u);
+        ru.sc = *reinterpret_cast<const float*>(rs + (u / 4) * 4);
+      }
+      if (slot_at(jb + r) < 0) {
+        ru.v = u32x4_t{0u, 0u, 0u, 0u};
+        ru.sc = 0.f;
+      }
+      store_unit<FMT, DQK>(ru, u, &s_rows[0][r][0]);
     }
   };
 
@@ -282,7 +305,7 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
   // buffers (not yet in use).
   constexpr int QBYTES = HT * 16 * DQK * 2;
   constexpr int QIT = (QBYTES + NT * 16 - 1) / (NT * 16);
-  static_assert(QBYTES <= (int)sizeof(s_rows), "q staging");
+  static_assert(QBYTES <= LDSB, "q staging");
   u32x4_t qreg[QIT];
   {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)t * a.ld_q + (int64_t)(hg * HT * 16) * DQK);
@@ -325,13 +348,21 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
       resolve_pass(p0, p1);
       __syncthreads();
     }
-    gather(0, 0);
+    if constexpr (kRaw) gather_raw(0, 0);
+    else gather(0, 0);
   for (int it = 0; it < nb; ++it) {
-    const int cur = it & 1;
+    const int cur = kRaw ? 0 : (it & 1);
     const int jb = it * kNB;             // pass entry of this block's first row
-    __builtin_amdgcn_s_waitcnt(0);      // this block's rows
+    __builtin_amdgcn_s_waitcnt(0);      // this block's rows (raw bytes for fp8)
     __syncthreads();
-    if (it + 1 < nb) gather(cur ^ 1, jb + kNB);   // overlaps the compute below (bf16)
+    if constexpr (kRaw) {
+      // the next block's raw bytes stream in during this block's dequantisation and compute
+      if (it + 1 < nb) gather_raw((it + 1) & 1, jb + kNB);
+      dequant(it & 1, jb);
+      lds_barrier();                     // bf16 rows complete; the loads just issued stay in flight
+    } else {
+      if (it + 1 < nb) gather(cur ^ 1, jb + kNB);   // overlaps the compute below
+    }
 
     // ---- S^T = K Q^T
     f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
