@@ -30,10 +30,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def keys_read(prob):
+    """Index keys the method must read: rows of one request share its keys, so each request
+    counts its longest row once."""
+    import numpy as np
+    req = np.asarray(prob.row_req)
+    lens = np.asarray(prob.row_len)
+    return int(sum(int(lens[req == b].max()) for b in np.unique(req)))
+
+
 def algorithmic_bytes(prob):
     """What the method must move per layer (decode, one row per request)."""
     T, H, topk = prob.T, prob.H, prob.topk
-    n = int(prob.row_len.sum())
+    n = keys_read(prob)
     key_b = 2 if prob.kpool.dtype == "bf16" else 1
     keys = n * prob.di * key_b + (n * 4 if prob.kpool.dtype == "fp8" else 0)
     row_b = {"bf16": 2 * prob.d_qk, "fp8_uniform": prob.d_qk + 4 * prob.d_qk // 64, "fp8_ds_mla": 584}[prob.kv.fmt]
@@ -45,7 +54,7 @@ def algorithmic_bytes(prob):
 def kernel_bytes(prob, kernel):
     """Algorithmic bytes one launch of `kernel` must move (decode, one row per request):
     what the step reads and writes by definition, not what the implementation adds."""
-    T, n = prob.T, int(prob.row_len.sum())
+    T, n = prob.T, keys_read(prob)
     topk = prob.topk
     if kernel.startswith("index_scores"):
         # every key (and fp8 scale) read once, every score written once, the query heads,

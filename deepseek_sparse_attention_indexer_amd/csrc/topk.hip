@@ -21,152 +21,11 @@
 //    each on this part.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace dsa {
 
 constexpr int kNT = 512;   // threads of the select workgroups
-
-// Reserve one output slot per lane with `pred` set: one LDS atomic per wave (ballot +
-// popcount) instead of one per element, which serialises on a single address.
-__device__ __forceinline__ uint32_t wave_reserve(bool pred, uint32_t* counter) {
-  const uint64_t m = __ballot(pred);
-  if (m == 0) return 0u;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)m) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-  base = __shfl(base, leader);
-  return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-}
-
-// Inclusive scan over the 64 lanes with DPP moves (a few cycles each) instead of LDS
-// permutes: shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the row totals carried
-// forward with the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (rows 2, 3).
-// Lanes without a source read 0 (bound_ctrl).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return v;
-}
-
-// Inclusive scan over the workgroup (thread order). s_w: kNT/64 words of LDS.
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* s_w, uint32_t* total) {
-  constexpr int NW = kNT / 64;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const uint32_t x = wave_incl_scan(v);
-  lds_barrier();
-  if (lane == 63) s_w[w] = x;
-  lds_barrier();
-  uint32_t off = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t y = s_w[i];
-    off += (i < w) ? y : 0u;
-    tot += y;
-  }
-  if (total) *total = tot;
-  return x + off;
-}
-
-// Digit d (0..nb-1) of a histogram such that (count of digits > d) < need <= (count >= d).
-// Writes s_res[0] = d, s_res[1] = count of digits > d. Requires sum(h) >= need >= 1.
-__device__ void find_digit_desc(const uint32_t* h, int nb, uint32_t need, uint32_t* s_w,
-                                uint32_t* s_res) {
-  const int per = nb >= kNT ? nb / kNT : 1;
-  const int act = nb / per;
-  const int tid = threadIdx.x;
-  uint32_t local = 0;
-  if (tid < act)
-    for (int i = 0; i < per; ++i) local += h[nb - 1 - (tid * per + i)];
-  const uint32_t incl = block_incl_scan(local, s_w, nullptr);
-  const uint32_t excl = incl - local;
-  if (tid < act && excl < need && need <= incl) {
-    uint32_t acc = excl;
-    for (int i = 0; i < per; ++i) {
-      const int bin = nb - 1 - (tid * per + i);
-      const uint32_t cnt = h[bin];
-      if (acc + cnt >= need) {
-        s_res[0] = (uint32_t)bin;
-        s_res[1] = acc;
-        break;
-      }
-      acc += cnt;
-    }
-  }
-  lds_barrier();
-}
-
-// Radix select (descending) over items i < cnt for which get(i, key) is true and whose key
-// matches `prefix` under `pmask`. Resolves the low `low_bits` bits in 12-bit digits; on
-// return `need` is the number still to take among keys equal to the returned threshold and
-// *eq_count the number of such keys.
-template <class Get>
-__device__ uint32_t radix_select_desc(int cnt, Get get, uint32_t prefix, uint32_t pmask,
-                                      int low_bits, uint32_t& need, uint32_t* eq_count,
-                                      uint32_t* s_hist, uint32_t* s_w, uint32_t* s_res) {
-  int shift = low_bits;
-  uint32_t last_eq = 0;
-  while (shift > 0) {
-    const int bits = shift >= 12 ? 12 : shift;
-    shift -= bits;
-    const int nb = 1 << bits;
-    const uint32_t dm = (uint32_t)(nb - 1);
-    for (int i = threadIdx.x; i < nb; i += kNT) s_hist[i] = 0;
-    lds_barrier();
-    for (int i = threadIdx.x; i < cnt; i += kNT) {
-      uint32_t key;
-      if (get(i, key) && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & dm], 1u);
-    }
-    lds_barrier();
-    find_digit_desc(s_hist, nb, need, s_w, s_res);
-    const uint32_t d = s_res[0];
-    need -= s_res[1];
-    last_eq = s_hist[d];
-    prefix |= d << shift;
-    pmask |= dm << shift;
-    lds_barrier();
-  }
-  *eq_count = last_eq;
-  return prefix;
-}
-
-// The same radix select over items held in registers: item u (< U) of every thread, taken
-// when get(u, key) is true.
-template <int U, class Get>
-__device__ uint32_t radix_select_regs(Get get, uint32_t prefix, uint32_t pmask, int low_bits,
-                                      uint32_t& need, uint32_t* eq_count, uint32_t* s_hist,
-                                      uint32_t* s_w, uint32_t* s_res) {
-  int shift = low_bits;
-  uint32_t last_eq = 0;
-  while (shift > 0) {
-    const int bits = shift >= 12 ? 12 : shift;
-    shift -= bits;
-    const int nb = 1 << bits;
-    const uint32_t dm = (uint32_t)(nb - 1);
-    for (int i = threadIdx.x; i < nb; i += kNT) s_hist[i] = 0;
-    lds_barrier();
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t key;
-      if (get(u, key) && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & dm], 1u);
-    }
-    lds_barrier();
-    find_digit_desc(s_hist, nb, need, s_w, s_res);
-    const uint32_t d = s_res[0];
-    need -= s_res[1];
-    last_eq = s_hist[d];
-    prefix |= d << shift;
-    pmask |= dm << shift;
-    lds_barrier();
-  }
-  *eq_count = last_eq;
-  return prefix;
-}
 
 // ------------------------------------------------------------------ rows that fit in LDS
 __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
@@ -192,13 +51,13 @@ __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
 
   uint32_t need = (uint32_t)k, eq = 0;
   auto get_key = [&](int i, uint32_t& key) { key = s_key[i]; return true; };
-  const uint32_t thr = radix_select_desc(n, get_key, 0u, 0u, 32, need, &eq, s_hist, s_w, s_res);
+  const uint32_t thr = radix_select_desc<kNT>(n, get_key, 0u, 0u, 32, need, &eq, s_hist, s_w, s_res);
   // ties at thr: keep the `need` smallest positions (largest complemented positions)
   uint32_t pos_thr = 0u;
   if (eq > need) {
     uint32_t need2 = need, eq2 = 0;
     auto get_tie = [&](int i, uint32_t& key) { key = ~(uint32_t)i; return s_key[i] == thr; };
-    pos_thr = radix_select_desc(n, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
+    pos_thr = radix_select_desc<kNT>(n, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
   }
   const bool all_ties = eq <= need;
   for (int i0 = 0; i0 < n; i0 += kNT) {       // uniform trip count: wave_reserve needs all lanes
@@ -286,7 +145,7 @@ __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
     }
   }
   lds_barrier();
-  find_digit_desc(s_hist, kHistBins, (uint32_t)k, s_w, s_res);
+  find_digit_desc<kNT>(s_hist, kHistBins, (uint32_t)k, s_w, s_res);
   const uint32_t d1 = s_res[0];
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.thr1[2 * t] = d1;
@@ -303,8 +162,8 @@ __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
     }
   }
   uint32_t tot_gt, tot_eq;
-  block_incl_scan(n_gt, s_w, &tot_gt);
-  const uint32_t inc_eq = block_incl_scan(n_eq, s_w, &tot_eq);
+  block_incl_scan<kNT>(n_gt, s_w, &tot_gt);
+  const uint32_t inc_eq = block_incl_scan<kNT>(n_eq, s_w, &tot_eq);
   uint32_t o_eq = inc_eq - n_eq;
   const int64_t region = ((int64_t)t * a.n_chunks + blockIdx.x) * kTopkChunk;
   uint32_t* ck = a.cand_key + region;
@@ -385,7 +244,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
     if (n <= k || c_me >= nch) return;
     const int s1 = min(n, s0 + kTopkChunk);
     uint32_t base;
-    block_incl_scan(before, s_w, &base);
+    block_incl_scan<kNT>(before, s_w, &base);
     uint32_t sel = 0, m = 0;
 #pragma unroll
     for (int j = 0; j < per; ++j) {
@@ -395,7 +254,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
       m += x;
     }
     uint32_t tot;
-    uint32_t o = base + block_incl_scan(m, s_w, &tot) - m;
+    uint32_t o = base + block_incl_scan<kNT>(m, s_w, &tot) - m;
 #pragma unroll
     for (int j = 0; j < per; ++j)
       if (sel >> j & 1u) {
@@ -428,7 +287,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
     const uint32_t v1 = c0 + 1 < nch ? r1 : 0u;
     for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
     uint32_t total;
-    const uint32_t incl = block_incl_scan(v0 + v1, s_w, &total);
+    const uint32_t incl = block_incl_scan<kNT>(v0 + v1, s_w, &total);
     if (c0 < nch) s_off[c0] = incl - v0 - v1;
     if (c0 + 1 < nch) s_off[c0 + 1] = incl - v1;
     if (threadIdx.x == 0) s_off[nch] = total;
@@ -489,7 +348,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   }
   lds_barrier();
   const uint32_t need1 = (uint32_t)k - above1;
-  find_digit_desc(s_hist, kHistBins, need1, s_w, s_res);
+  find_digit_desc<kNT>(s_hist, kHistBins, need1, s_w, s_res);
   const uint32_t pre = (d1 << kHistBits) | s_res[0];     // top 24 bits of the threshold key
   uint32_t need = need1 - s_res[1], eq = 0, pos_thr = 0;
   lds_barrier();
@@ -500,25 +359,25 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
       key = kk[u];
       return u * kNT + threadIdx.x < n_cand;
     };
-    thr = radix_select_regs<RU>(get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
+    thr = radix_select_regs<kNT, RU>(get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
     if (eq > need) {
       uint32_t need2 = need, eq2 = 0;
       auto get_tie = [&](int u, uint32_t& key) {
         key = ~(uint32_t)pp[u];
         return u * kNT + threadIdx.x < n_cand && kk[u] == thr;
       };
-      pos_thr = radix_select_regs<RU>(get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
+      pos_thr = radix_select_regs<kNT, RU>(get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
     }
   } else {
     auto get_key = [&](int i, uint32_t& key) { key = key_of((uint32_t)i); return true; };
-    thr = radix_select_desc((int)n_cand, get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
+    thr = radix_select_desc<kNT>((int)n_cand, get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
     if (eq > need) {
       uint32_t need2 = need, eq2 = 0;
       auto get_tie = [&](int i, uint32_t& key) {
         key = ~(uint32_t)pos_of((uint32_t)i);
         return key_of((uint32_t)i) == thr;
       };
-      pos_thr = radix_select_desc((int)n_cand, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
+      pos_thr = radix_select_desc<kNT>((int)n_cand, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
     }
   }
   const bool all_ties = eq <= need;
@@ -537,7 +396,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
       sel |= (uint32_t)x << u;
       m += x;
     }
-    uint32_t o = above1 + block_incl_scan(m, s_w, &tot) - m;
+    uint32_t o = above1 + block_incl_scan<kNT>(m, s_w, &tot) - m;
 #pragma unroll
     for (int u = 0; u < RU; ++u)
       if (sel >> u & 1u) {
@@ -547,7 +406,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   } else {
     uint32_t m = 0;
     for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) m += selected(key_of(i), pos_of(i));
-    uint32_t o = above1 + block_incl_scan(m, s_w, &tot) - m;
+    uint32_t o = above1 + block_incl_scan<kNT>(m, s_w, &tot) - m;
     for (uint32_t i = threadIdx.x; i < n_cand; i += kNT) {
       const int32_t pos = pos_of(i);
       if (selected(key_of(i), pos)) {
