@@ -108,8 +108,10 @@ constexpr int kScoreThreads = 64 * kScoreWaves;
 template <int DI, int MT, bool FP8, bool HIST>
 __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
   constexpr int KB = DI / 32;
-  constexpr int QB = 64 * DI * 2;   // bytes of the (padded) query heads of one row
-  __shared__ __align__(16) uint8_t s_q[QB];
+  // the row's query heads in LDS, one head per QS bytes: the 16 bytes of padding put the 16
+  // heads that one A-operand read touches in distinct banks
+  constexpr int QS = DI * 2 + 16;
+  __shared__ __align__(16) uint8_t s_q[64 * QS];
   __shared__ float s_w[16 * MT];
   __shared__ uint32_t s_hist[HIST ? kHistBins : 1];
 
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int o = (threadIdx.x + i * kScoreThreads) * 16;
-    if (o < 16 * MT * DI * 2) *reinterpret_cast<u32x4_t*>(s_q + o) = qv[i];
+    if (o < 16 * MT * DI * 2) *reinterpret_cast<u32x4_t*>(s_q + (o / (DI * 2)) * QS + o % (DI * 2)) = qv[i];
   }
   if (threadIdx.x < 16 * MT) s_w[threadIdx.x] = wraw * a.index_scale;
   if constexpr (HIST)
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-      qa[mt][kb] = *reinterpret_cast<const u32x4_t*>(s_q + ((16 * mt + c) * DI + 32 * kb + 8 * g) * 2);
+      qa[mt][kb] = *reinterpret_cast<const u32x4_t*>(s_q + (16 * mt + c) * QS + (32 * kb + 8 * g) * 2);
   float wv[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)

@@ -305,7 +305,9 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
   // buffers (not yet in use).
   constexpr int QBYTES = HT * 16 * DQK * 2;
   constexpr int QIT = (QBYTES + NT * 16 - 1) / (NT * 16);
-  static_assert(QBYTES <= LDSB, "q staging");
+  // staged one head per padded row (RE elements): the 16 heads of one B-operand read then sit
+  // in distinct LDS banks
+  static_assert(HT * 16 * RE * 2 <= LDSB, "q staging");
   u32x4_t qreg[QIT];
   {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)t * a.ld_q + (int64_t)(hg * HT * 16) * DQK);
@@ -321,13 +323,13 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
 #pragma unroll
     for (int i = 0; i < QIT; ++i) {
       const int o = (threadIdx.x + i * NT) * 16;
-      if (o < QBYTES) *reinterpret_cast<u32x4_t*>(qdst + o) = qreg[i];
+      if (o < QBYTES) *reinterpret_cast<u32x4_t*>(qdst + (o / (DQK * 2)) * (RE * 2) + o % (DQK * 2)) = qreg[i];
     }
   }
   __syncthreads();
   u32x4_t qb[KS];
   {
-    const uint16_t* qp = &s_rows[0][0][0] + (ht * 16 + c) * DQK + 8 * g;
+    const uint16_t* qp = &s_rows[0][0][0] + (ht * 16 + c) * RE + 8 * g;
 #pragma unroll
     for (int kb = 0; kb < KS; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(qp + 32 * kb);
   }
