@@ -459,19 +459,46 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
       }
     if (a.lse && g == 0 && gd0 == 0) a.lse[(int64_t)t * a.H + head] = fin.lse;
   } else {
-    // un-normalised partial (o, m, l) of this split; k_mla_combine merges them
-    float* po = a.part_o + (((int64_t)t * a.H + head) * a.n_split + split) * kDV;
+    // un-normalised partial (o, m, l) of this split; k_mla_combine merges them. A lane holds
+    // 128 contiguous bytes of one head's row, so direct stores would spread every instruction
+    // over 64 cache lines; the block is staged in LDS (free now: the last iteration ended
+    // with a barrier) and written back one head row at a time, 1 KiB per instruction.
+    constexpr int PS = kDV + 4;                       // padded fp32 row of one head in LDS
+    if constexpr (HT * 16 * PS * 4 <= LDSB) {
+      float* s_po = reinterpret_cast<float*>(s_lds);
 #pragma unroll
-    for (int i = 0; i < GD; ++i)
+      for (int i = 0; i < GD; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        f32x4_t v0, v1;
+        for (int r = 0; r < 4; ++r) {
+          f32x4_t v0, v1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { v0[e] = o[i][e][r]; v1[e] = o[i][4 + e][r]; }
-        float* d = po + 128 * (gd0 + i) + 32 * g + 8 * r;
-        *reinterpret_cast<f32x4_t*>(d) = v0;
-        *reinterpret_cast<f32x4_t*>(d + 4) = v1;
+          for (int e = 0; e < 4; ++e) { v0[e] = o[i][e][r]; v1[e] = o[i][4 + e][r]; }
+          float* d = s_po + (ht * 16 + c) * PS + 128 * (gd0 + i) + 32 * g + 8 * r;
+          *reinterpret_cast<f32x4_t*>(d) = v0;
+          *reinterpret_cast<f32x4_t*>(d + 4) = v1;
+        }
+      lds_barrier();
+      float* po = a.part_o + ((int64_t)t * a.H + hg * HT * 16) * a.n_split * kDV + (int64_t)split * kDV;
+      for (int q = threadIdx.x * 4; q < HT * 16 * kDV; q += NT * 4) {
+        const int hl = q / kDV;
+        const int col = q - hl * kDV;
+        *reinterpret_cast<f32x4_t*>(po + (int64_t)hl * a.n_split * kDV + col) =
+            *reinterpret_cast<const f32x4_t*>(s_po + hl * PS + col);
       }
+    } else {                                          // too many heads to stage: direct stores
+      float* po = a.part_o + (((int64_t)t * a.H + head) * a.n_split + split) * kDV;
+#pragma unroll
+      for (int i = 0; i < GD; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          f32x4_t v0, v1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { v0[e] = o[i][e][r]; v1[e] = o[i][4 + e][r]; }
+          float* d = po + 128 * (gd0 + i) + 32 * g + 8 * r;
+          *reinterpret_cast<f32x4_t*>(d) = v0;
+          *reinterpret_cast<f32x4_t*>(d + 4) = v1;
+        }
+    }
     if (g == 0 && gd0 == 0) {
       float* pml = a.part_ml + (((int64_t)t * a.H + head) * a.n_split + split) * 2;
       pml[0] = m_run;
