@@ -141,7 +141,7 @@ __device__ __forceinline__ Finish finish_softmax(float m, float l, float sink, b
 }
 
 template <int FMT, int DQK, int HT, int WD, bool SPLIT>
-__global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
+__global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(MlaArgs a) {
   constexpr int NW = HT * WD;                 // waves: HT head tiles x WD value-column slices
   constexpr int NT = 64 * NW;
   constexpr int GD = 4 / WD;                  // 128-column groups of the value a wave owns
@@ -249,54 +249,81 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
   // (asynchronous; instruction ins of the data fills bytes [1024 ins, +1024), lane l at +16 l,
   // i.e. 16-byte chunk q = 64 ins + l = row q / (RDB / 16), chunk q % (RDB / 16); the scales
   // follow as dwords), one block ahead of its use
+  __shared__ const uint8_t* s_raddr[2][kNB];        // a raw block's row data / scale addresses
   auto gather_raw = [&](int buf, int jb) {
+    // each row's addresses once (the page arithmetic of one row per lane), then the loads
+    if (threadIdx.x < kNB) {
+      bool x;
+      const RowOff off = row_of(jb + threadIdx.x, x);
+      s_raddr[0][threadIdx.x] = (x ? kv1.data : kv0.data) + off.data;
+      s_raddr[1][threadIdx.x] = (FMT == kFmtDsMla ? (x ? kv1.data : kv0.data)
+                                                  : reinterpret_cast<const uint8_t*>(x ? kv1.scales : kv0.scales)) + off.scale;
+    }
+    lds_barrier();
     uint8_t* rb = s_lds + BB + buf * RAWB;
     auto* lds_d = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(reinterpret_cast<uintptr_t>(rb) & 0xffffffffu);
     auto* lds_s = lds_d + kNB * RDB;
     constexpr int CPR = RDB / 16;                    // 16-byte chunks per row
     constexpr int NID = kNB * RDB / 1024;            // data instructions per block
-    for (int ins = wave; ins < NID; ins += NW) {
-      const int q = ins * 64 + lane;
-      const int r = q / CPR;
-      bool x;
-      const RowOff off = row_of(jb + r, x);
-      __builtin_amdgcn_global_load_lds((x ? kv1.data : kv0.data) + off.data + 16 * (q - r * CPR), lds_d + ins * 1024, 16, 0, 0);
+#pragma unroll
+    for (int k = 0; k < (NID + NW - 1) / NW; ++k) {
+      const int ins = wave + k * NW;
+      if (ins < NID) {
+        const int q = ins * 64 + lane;
+        const int r = q / CPR;
+        __builtin_amdgcn_global_load_lds(s_raddr[0][r] + 16 * (q - r * CPR), lds_d + ins * 1024, 16, 0, 0);
+      }
     }
     constexpr int SPR = RSB / 4;                     // scale dwords per row
     constexpr int NIS = (kNB * SPR + 63) / 64;       // scale instructions per block
-    for (int ins = wave; ins < NIS; ins += NW) {
+#pragma unroll
+    for (int k = 0; k < (NIS + NW - 1) / NW; ++k) {
+      const int ins = wave + k * NW;
       const int q = ins * 64 + lane;
-      if (q < kNB * SPR) {
+      if (ins < NIS && q < kNB * SPR) {
         const int r = q / SPR;
-        bool x;
-        const RowOff off = row_of(jb + r, x);
-        const uint8_t* sb = FMT == kFmtDsMla ? (x ? kv1.data : kv0.data)
-                                             : reinterpret_cast<const uint8_t*>(x ? kv1.scales : kv0.scales);
-        __builtin_amdgcn_global_load_lds(sb + off.scale + 4 * (q - r * SPR), lds_s + ins * 256, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(s_raddr[1][r] + 4 * (q - r * SPR), lds_s + ins * 256, 4, 0, 0);
       }
     }
   };
   // raw buffer `buf` -> the bf16 block (LDS to LDS); list padding becomes zero rows
+  // (the LDS reads of a batch of units go out before its first conversion; batches of three
+  // keep the kernel at two waves per SIMD)
   auto dequant = [&](int buf, int jb) {
     const uint8_t* rb = s_lds + BB + buf * RAWB;
-    for (int uid = threadIdx.x; uid < kNB * UN; uid += NT) {
-      const int r = uid / UN;
-      const int u = uid - r * UN;
-      const uint8_t* rd = rb + r * RDB;
-      const uint8_t* rs = rb + kNB * RDB + r * RSB;
-      RawUnit ru;
-      if constexpr (FMT == kFmtDsMla) {
-        ru.v = *reinterpret_cast<const u32x4_t*>(rd + (u < 28 ? 16 * u : 448 + 16 * (u - 28)));
-        ru.sc = u < 28 ? ue8m0_scale(rs[u >> 2]) : 0.f;
-      } else {
-        ru.v = *reinterpret_cast<const u32x4_t*>(rd + 16 * u);
-        ru.sc = *reinterpret_cast<const float*>(rs + (u / 4) * 4);
+    constexpr int QN = (kNB * UN + NT - 1) / NT;     // units per thread
+    constexpr int QB = 3;                            // units per batch
+#pragma unroll
+    for (int q0 = 0; q0 < QN; q0 += QB) {
+      RawUnit ru[QB];
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const int uid = min((int)threadIdx.x + (q0 + q) * NT, kNB * UN - 1);
+        const int r = uid / UN;
+        const int u = uid - r * UN;
+        const uint8_t* rd = rb + r * RDB;
+        const uint8_t* rs = rb + kNB * RDB + r * RSB;
+        if constexpr (FMT == kFmtDsMla) {
+          ru[q].v = *reinterpret_cast<const u32x4_t*>(rd + (u < 28 ? 16 * u : 448 + 16 * (u - 28)));
+          ru[q].sc = u < 28 ? ue8m0_scale(rs[u >> 2]) : 0.f;
+        } else {
+          ru[q].v = *reinterpret_cast<const u32x4_t*>(rd + 16 * u);
+          ru[q].sc = *reinterpret_cast<const float*>(rs + (u / 4) * 4);
+        }
       }
-      if (slot_at(jb + r) < 0) {
-        ru.v = u32x4_t{0u, 0u, 0u, 0u};
-        ru.sc = 0.f;
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const int uid = threadIdx.x + (q0 + q) * NT;
+        if (q0 + q < QN && uid < kNB * UN) {
+          const int r = uid / UN;
+          const int u = uid - r * UN;
+          if (slot_at(jb + r) < 0) {
+            ru[q].v = u32x4_t{0u, 0u, 0u, 0u};
+            ru[q].sc = 0.f;
+          }
+          store_unit<FMT, DQK>(ru[q], u, &s_rows[0][r][0]);
+        }
       }
-      store_unit<FMT, DQK>(ru, u, &s_rows[0][r][0]);
     }
   };
 
@@ -327,11 +354,18 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
     }
   }
   __syncthreads();
-  u32x4_t qb[KS];
+  // One head tile and four waves (decode): the waves split the score product instead of each
+  // computing all of it, two per 16-row half of the block, each over half of the head
+  // dimension; the four 16 x 16 partials meet in LDS. Every wave then holds the whole S^T.
+  constexpr bool kSplitK = HT == 1 && WD == 4 && KS % 2 == 0;
+  constexpr int KQ = kSplitK ? KS / 2 : KS;          // k-steps of the score product per wave
+  const int kq0 = kSplitK ? (wave & 1) * KQ : 0;     // this wave's first k-step
+  __shared__ f32x4_t s_sp[kSplitK ? 4 : 1][64];      // the partials
+  u32x4_t qb[KQ];
   {
     const uint16_t* qp = &s_rows[0][0][0] + (ht * 16 + c) * RE + 8 * g;
 #pragma unroll
-    for (int kb = 0; kb < KS; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(qp + 32 * kb);
+    for (int kb = 0; kb < KQ; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(qp + 32 * (kq0 + kb));
   }
   float m_run = -INFINITY;   // running max (base-2 units) of head c; rescaled lazily
   float l_run = 0.f;         // lane-partial sum of exp2(s - m_run)
@@ -368,12 +402,23 @@ __global__ __launch_bounds__(64 * HT * WD) void k_sparse_mla(MlaArgs a) {
 
     // ---- S^T = K Q^T
     f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-    const uint16_t* r0 = &s_rows[cur][c][8 * g];
-    const uint16_t* r1 = &s_rows[cur][16 + c][8 * g];
+    if constexpr (kSplitK) {
+      const uint16_t* rp = &s_rows[cur][16 * (wave >> 1) + c][8 * g + 32 * kq0];
+      f32x4_t sp = s0;
 #pragma unroll
-    for (int kb = 0; kb < KS; ++kb) {
-      s0 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r0 + 32 * kb), qb[kb], s0);
-      s1 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r1 + 32 * kb), qb[kb], s1);
+      for (int kb = 0; kb < KQ; ++kb) sp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 32 * kb), qb[kb], sp);
+      s_sp[wave][lane] = sp;
+      lds_barrier();
+      s0 = s_sp[0][lane] + s_sp[1][lane];
+      s1 = s_sp[2][lane] + s_sp[3][lane];
+    } else {
+      const uint16_t* r0 = &s_rows[cur][c][8 * g];
+      const uint16_t* r1 = &s_rows[cur][16 + c][8 * g];
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) {
+        s0 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r0 + 32 * kb), qb[kb], s0);
+        s1 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r1 + 32 * kb), qb[kb], s1);
+      }
     }
     // ---- online softmax (base 2); the accumulators are rescaled only when some head's max
     // grows by more than 2^8, so exp2(s - m_run) stays <= 256
