@@ -553,20 +553,23 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
 }
 
 // Merge the split partials of each (row, head): o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s
-// (the LSE merge of PR 664). One 256-thread workgroup per (row, head, 128-column quarter):
-// eight groups of 32 threads take every eighth split (4 columns per thread), so each thread
-// keeps several splits of loads in flight and the work spreads over many CUs; the groups'
-// sums meet in LDS.
+// (the LSE merge of PR 664). One 256-thread workgroup per (row, head, QW x 128 columns):
+// groups of 32 QW threads (4 columns each) take every NG-th split, so each thread keeps
+// several splits of loads in flight; the groups' sums meet in LDS. Many splits (a long row):
+// QW = 1, eight groups, the work spread over many CUs. Few splits (many rows): QW = 4, a
+// whole head per workgroup (a quarter-row workgroup would have one split per group).
+template <int QW>
 __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
-  constexpr int NG = 8;                            // split groups of 32 threads
-  __shared__ f32x4_t s_acc[NG][32];
+  constexpr int TPG = 32 * QW;                     // threads per split group
+  constexpr int NG = 256 / TPG;                    // split groups
+  __shared__ f32x4_t s_acc[NG][TPG];
   __shared__ float s_l[NG];
   __shared__ float s_m[NG];
   const int t = blockIdx.z;
   const int head = blockIdx.y;
-  const int sg = threadIdx.x >> 5;
-  const int ci = threadIdx.x & 31;
-  const int d0 = blockIdx.x * 128 + ci * 4;
+  const int sg = threadIdx.x / TPG;
+  const int ci = threadIdx.x % TPG;
+  const int d0 = blockIdx.x * 128 * QW + ci * 4;
   const int S = a.n_split;
   const float* pml = a.part_ml + ((int64_t)t * a.H + head) * S * 2;
   const float* po = a.part_o + ((int64_t)t * a.H + head) * S * kDV + d0;
@@ -670,7 +673,10 @@ hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T,
 
 hipError_t launch_mla_combine(const MlaArgs& a, int T, hipStream_t st) {
   if (T <= 0 || a.n_split <= 1) return hipSuccess;
-  launch_kernel(k_mla_combine, dim3(kDV / 128, a.H, T), dim3(256), st, a);
+  if (a.n_split <= 16)
+    launch_kernel(k_mla_combine<4>, dim3(kDV / 512, a.H, T), dim3(256), st, a);
+  else
+    launch_kernel(k_mla_combine<1>, dim3(kDV / 128, a.H, T), dim3(256), st, a);
   return hipGetLastError();
 }
 
