@@ -50,7 +50,9 @@ def build(verbose: bool = False, src_dir: str | None = None, out: str | None = N
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(compile_one, srcs))
     tmp = out + ".tmp"
-    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: a symbol left undefined (e.g. a kernel whose host stub was not emitted) fails
+    # the link here instead of the first load of the library
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -57,6 +57,24 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt fields at their maxima: not waited on)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// the same for a wave-uniform count in [LO, HI], by a binary search of scalar branches
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) wait_vmcnt_dyn<LO, MID>(n);
+    else wait_vmcnt_dyn<MID + 1, HI>(n);
+  }
+}
+
 // One of two pagings, field by field (selecting a reference would put both in scratch).
 __device__ __forceinline__ Paging pick_paging(bool x, const Paging& p1, const Paging& p0) {
   Paging r;

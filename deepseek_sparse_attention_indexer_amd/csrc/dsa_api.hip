@@ -124,31 +124,41 @@ hipError_t timed(const char* name, hipStream_t st, F&& launch) {
 // ---------------------------------------------------------------- attention policy
 struct MlaPlan {
   int ht;          // head tiles per workgroup
+  int nbuf;        // depth of the block ring in LDS
   int n_split;
   int rows_per_split;
 };
 
 MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
-  // A CU sustains only ~25 GB/s of gathers and a lone wave far less, so decode spreads rows
-  // AND partial outputs over every CU: one 16-head tile per 4-wave workgroup (the waves split
-  // the value columns) and about two workgroups per CU, so two gathered blocks are in flight
-  // per CU (splits never go below one 32-row block). Prefill rows have no split; all heads
-  // of a row share each gathered block.
+  // A CU sustains only ~25 GB/s of gathers and a lone wave far less, so a decode step with
+  // few rows spreads rows AND partial outputs over every CU: one 16-head tile per 4-wave
+  // workgroup (the waves split the value columns) and about two workgroups per CU, so two
+  // gathered blocks are in flight per CU (splits never go below one 32-row block). With many
+  // rows (16 or more) there is enough parallelism to share each gathered block among 64
+  // heads instead (a quarter of the gathers), one workgroup per CU, splits only to reach
+  // one workgroup per CU. Prefill rows have no split; all heads of a row share each block.
+  // A workgroup that walks more than two blocks keeps three in flight (ring of four) when it
+  // holds all of a CU anyway (64 heads: the registers allow one workgroup per CU).
   MlaPlan p;
   const int tiles = H / 16;
   const int nblk = std::max(1, (ntot + 31) / 32);
   int s = 1;
-  if (decode) {
+  if (decode && !(T >= 16 && tiles % 4 == 0)) {
     p.ht = 1;
     const int64_t base = (int64_t)T * tiles;
     s = (int)std::min<int64_t>((512 + base - 1) / base, nblk);   // about two workgroups per CU
-    s = std::max(1, s);
   } else {
     p.ht = tiles % 4 == 0 ? 4 : (tiles % 2 == 0 ? 2 : 1);
+    if (decode) {
+      const int64_t base = (int64_t)T * (tiles / p.ht);
+      s = (int)std::min<int64_t>((256 + base - 1) / base, nblk);  // about one workgroup per CU
+    }
   }
+  s = std::max(1, s);
   const int bps = (nblk + s - 1) / s;           // blocks per split
   p.rows_per_split = bps * 32;
   p.n_split = (nblk + bps - 1) / bps;
+  p.nbuf = (p.ht == 4 && bps > 2) ? 4 : 2;
   return p;
 }
 
@@ -318,7 +328,7 @@ dsa_status run_mla(const MlaIn& m, bool decode, void* ws, size_t ws_bytes, hipSt
     a.part_ml = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * m.H * p.n_split * 8));
   }
   const int fmt = kv_fmt(m.kv);
-  dsa_status s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, m.d_qk, p.ht, m.T, st); }));
+  dsa_status s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, m.d_qk, p.ht, p.nbuf, m.T, st); }));
   if (s == DSA_OK && p.n_split > 1)
     s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, m.T, st); }));
   return s;
@@ -738,7 +748,7 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
     if ((size_t)cv.off > ws_bytes) return DSA_ERR_WORKSPACE;
   }
   const int fmt = kv_fmt(kv);
-  s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, d_qk, p.ht, T, st); }));
+  s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, d_qk, p.ht, p.nbuf, T, st); }));
   if (s == DSA_OK && p.n_split > 1)
     s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, T, st); }));
   return s;

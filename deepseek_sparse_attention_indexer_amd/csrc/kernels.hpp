@@ -122,7 +122,7 @@ struct MlaArgs {
   float* part_ml;          // [T, H, n_split, 2]
 };
 
-hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T, hipStream_t st);
+hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int nbuf, int T, hipStream_t st);
 hipError_t launch_mla_combine(const MlaArgs& a, int T, hipStream_t st);
 
 // cache writes: bf16 rows -> a cache format, one row per token at slots[token]

@@ -13,10 +13,12 @@
 // Workgroup = HT x WD waves sharing each gathered 32-row block: a wave owns 16 heads (one of
 // HT head tiles) and 512 / WD value columns (decode runs one head tile with WD = 4, so four
 // waves issue the gather and the PV product and the score product is repeated per wave).
-// Blocks are double-buffered in LDS: while a block is computed, the next block's list
-// entries are resolved to cache offsets and its rows stream in (bf16 rows by direct
-// global->LDS loads with every load of the block in flight; fp8 rows staged in registers and
-// dequantised to bf16 on the way). Each wave computes
+// Blocks stream through a ring of NBUF buffers in LDS: while a block is computed, the next
+// NBUF - 1 blocks' rows are in flight (direct global->LDS loads; bf16 rows land in place, fp8
+// rows land as raw bytes and are dequantised to one bf16 block just before use). Each wave
+// waits only for its own loads of the block it needs (vmcnt = the loads of the later blocks),
+// so the barriers never drain the ring. A workgroup with one or two blocks to cover takes
+// NBUF = 2; many blocks per workgroup take a deeper ring. Each wave computes
 //   S^T[32 rows x 16 heads] = K Q^T   (A = rows from LDS, B = q held in registers),
 // an online softmax in base 2, and
 //   O^T[512 x 16 heads] += V^T P^T   (A = V^T read from LDS and transposed 8x8 in registers,
@@ -140,27 +142,28 @@ __device__ __forceinline__ Finish finish_softmax(float m, float l, float sink, b
   return f;
 }
 
-template <int FMT, int DQK, int HT, int WD, bool SPLIT>
+template <int FMT, int DQK, int HT, int WD, bool SPLIT, int NBUF>
 __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(MlaArgs a) {
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
   constexpr int NW = HT * WD;                 // waves: HT head tiles x WD value-column slices
   constexpr int NT = 64 * NW;
   constexpr int GD = 4 / WD;                  // 128-column groups of the value a wave owns
   constexpr int KS = DQK / 32;
   constexpr int RE = RowGeom<FMT, DQK>::kElems;
   constexpr int UN = RowGeom<FMT, DQK>::kUnits;
-  // bf16 rows: two gathered blocks in LDS (double buffer). fp8 rows: one bf16 block, plus two
-  // raw blocks (bytes as stored, data then scales) that the direct loads fill a block ahead
+  // bf16 rows: NBUF gathered blocks in LDS. fp8 rows: one bf16 block, plus NBUF raw blocks
+  // (bytes as stored, data then scales) that the direct loads fill ahead of use
   constexpr bool kRaw = FMT != kFmtBf16;
   constexpr int BB = kNB * RE * 2;                            // bytes of one bf16 block
   constexpr int RDB = RawGeom<FMT, DQK>::kData;
   constexpr int RSB = RawGeom<FMT, DQK>::kScale;
   constexpr int RAWB = kNB * (RDB + RSB);                     // bytes of one raw block
-  constexpr int LDSB = kRaw ? BB + 2 * RAWB : 2 * BB;
+  constexpr int LDSB = kRaw ? BB + NBUF * RAWB : NBUF * BB;
   static_assert(RDB % 16 == 0 && RSB % 4 == 0 && (kNB * RDB) % 1024 == 0, "raw staging");
   __shared__ __align__(16) uint8_t s_lds[LDSB];
   uint16_t (*const s_rows)[kNB][RE] = reinterpret_cast<uint16_t (*)[kNB][RE]>(s_lds);
   // list entries of the current pass resolved to cache slots: slot | list << 30, -1 = padding
-  __shared__ int32_t s_slot[kResolve];
+  __shared__ __align__(16) int32_t s_slot[kResolve];
 
   const int t = blockIdx.z;
   const int hg = blockIdx.y;
@@ -212,34 +215,60 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   };
   // cache row of pass entry j (a padding entry reads row 0 of the main cache: finite data,
   // masked by the softmax)
-  auto slot_at = [&](int j) -> int32_t { return j < pass_n ? s_slot[j] : -1; };
+  // (j stays below kResolve: the read is unconditional, so that a thread's reads go out together
+  // instead of one branch and one wait each)
+  auto slot_at = [&](int j) -> int32_t {
+    const int32_t v = s_slot[j];
+    return j < pass_n ? v : -1;
+  };
   auto row_of = [&](int j, bool& x) -> RowOff {
     const int32_t v = slot_at(j);
     x = v >= 0 && (v >> 30);
     const int64_t slot = v >= 0 ? (v & 0x3fffffff) : 0;
     return x ? row_offsets<FMT, DQK>(kv1, slot) : row_offsets<FMT, DQK>(kv0, slot);
   };
+  // Source addresses of each row of the blocks in the ring (row data; fp8 scales), one slot
+  // per ring buffer: computed once per row (one lane per row) an iteration before the
+  // block's loads go out, so that the loads themselves need one LDS read and an add.
+  __shared__ const uint8_t* s_ra[NBUF][kRaw ? 2 : 1][kNB];
+  auto row_addrs = [&](int rs, int jb, int r) {    // row r of the block at pass entry jb
+    bool x;
+    const RowOff off = row_of(jb + r, x);
+    const uint8_t* base = x ? kv1.data : kv0.data;
+    s_ra[rs][0][r] = base + off.data;
+    if constexpr (kRaw)
+      s_ra[rs][1][r] = (FMT == kFmtDsMla ? base : reinterpret_cast<const uint8_t*>(x ? kv1.scales : kv0.scales)) + off.scale;
+  };
   // bf16 rows into LDS by direct global->LDS loads (asynchronous, completes at the next vmcnt
   // wait)
-  auto gather = [&](int buf, int jb) {   // jb: pass entry of the block's first row
+  auto gather = [&](int buf) {   // the block in ring slot buf (addresses in s_ra[buf])
     if constexpr (FMT == kFmtBf16) {
       // lane l of instruction ins fills 16-byte slot 64 * ins + l of the padded block; the pad
       // slot of each row re-reads the row's first 16 bytes
       constexpr int RW = DQK / 8 + 1;
       constexpr int SLOTS = kNB * RW;
       constexpr int NINS = (SLOTS + 63) / 64;
+      constexpr int PER = (NINS + NW - 1) / NW;        // instructions of a wave (at most)
       auto* lbase = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(
           reinterpret_cast<uintptr_t>(&s_rows[buf][0][0]) & 0xffffffffu);
-      for (int ins = wave; ins < NINS; ins += NW) {
-        const int j = ins * 64 + lane;
-        if (j < SLOTS) {
-          const int r = j / RW;
-          int cc = j - r * RW;
-          cc = cc == RW - 1 ? 0 : cc;
-          bool x;
-          const RowOff off = row_of(jb + r, x);
-          const uint8_t* src = (x ? kv1.data : kv0.data) + off.data + 16 * cc;
-          __builtin_amdgcn_global_load_lds(src, lbase + ins * 1024, 16, 0, 0);
+      // every address read of the wave first (one LDS round trip), then the loads
+      const uint8_t* src[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int j = min((wave + k * NW) * 64 + lane, SLOTS - 1);
+        const int r = j / RW;
+        int cc = j - r * RW;
+        cc = cc == RW - 1 ? 0 : cc;
+        src[k] = s_ra[buf][0][r] + 16 * cc;
+      }
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int ins = wave + k * NW;
+        if (ins < NINS && ins * 64 + lane < SLOTS) {
+          // the builtin takes a named local: given an array element (or an expression over the
+          // template-shaped address array) the host compilation silently drops the kernel
+          const uint8_t* sp = src[k];
+          __builtin_amdgcn_global_load_lds(sp, lbase + ins * 1024, 16, 0, 0);
         }
       }
     }
@@ -249,17 +278,7 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   // (asynchronous; instruction ins of the data fills bytes [1024 ins, +1024), lane l at +16 l,
   // i.e. 16-byte chunk q = 64 ins + l = row q / (RDB / 16), chunk q % (RDB / 16); the scales
   // follow as dwords), one block ahead of its use
-  __shared__ const uint8_t* s_raddr[2][kNB];        // a raw block's row data / scale addresses
-  auto gather_raw = [&](int buf, int jb) {
-    // each row's addresses once (the page arithmetic of one row per lane), then the loads
-    if (threadIdx.x < kNB) {
-      bool x;
-      const RowOff off = row_of(jb + threadIdx.x, x);
-      s_raddr[0][threadIdx.x] = (x ? kv1.data : kv0.data) + off.data;
-      s_raddr[1][threadIdx.x] = (FMT == kFmtDsMla ? (x ? kv1.data : kv0.data)
-                                                  : reinterpret_cast<const uint8_t*>(x ? kv1.scales : kv0.scales)) + off.scale;
-    }
-    lds_barrier();
+  auto gather_raw = [&](int buf) {   // the block in ring slot buf (addresses in s_ra[buf])
     uint8_t* rb = s_lds + BB + buf * RAWB;
     auto* lds_d = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(reinterpret_cast<uintptr_t>(rb) & 0xffffffffu);
     auto* lds_s = lds_d + kNB * RDB;
@@ -271,7 +290,8 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
       if (ins < NID) {
         const int q = ins * 64 + lane;
         const int r = q / CPR;
-        __builtin_amdgcn_global_load_lds(s_raddr[0][r] + 16 * (q - r * CPR), lds_d + ins * 1024, 16, 0, 0);
+        const uint8_t* sp = s_ra[buf][0][r] + 16 * (q - r * CPR);
+        __builtin_amdgcn_global_load_lds(sp, lds_d + ins * 1024, 16, 0, 0);
       }
     }
     constexpr int SPR = RSB / 4;                     // scale dwords per row
@@ -282,7 +302,8 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
       const int q = ins * 64 + lane;
       if (ins < NIS && q < kNB * SPR) {
         const int r = q / SPR;
-        __builtin_amdgcn_global_load_lds(s_raddr[1][r] + 4 * (q - r * SPR), lds_s + ins * 256, 4, 0, 0);
+        const uint8_t* sp = s_ra[buf][kRaw ? 1 : 0][r] + 4 * (q - r * SPR);
+        __builtin_amdgcn_global_load_lds(sp, lds_s + ins * 256, 4, 0, 0);
       }
     }
   };
@@ -376,29 +397,62 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
     for (int e = 0; e < 8; ++e) o[i][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   __syncthreads();   // q is in registers before the first rows land in the buffers
+  // loads this wave issues per block (instructions of a block are dealt round-robin to the
+  // waves; every one of them has at least one active lane, so each counts once on vmcnt)
+  constexpr int NID = kNB * RDB / 1024;                      // raw data instructions
+  constexpr int NIS = (kNB * (RSB / 4) + 63) / 64;           // raw scale instructions
+  constexpr int NINS = (kNB * (DQK / 8 + 1) + 63) / 64;      // bf16 instructions
+  constexpr int PB_MAX = kRaw ? (NID + NW - 1) / NW + (NIS + NW - 1) / NW : (NINS + NW - 1) / NW;
+  static_assert((NBUF - 2) * PB_MAX < 64, "vmcnt range");
+  const int w_u = __builtin_amdgcn_readfirstlane(wave);
+  const int per_block = kRaw ? (NID - w_u + NW - 1) / NW + (NIS - w_u + NW - 1) / NW
+                             : (NINS - w_u + NW - 1) / NW;
   for (int p0 = u_begin; p0 < u_end; p0 += kResolve) {
     const int p1 = min(u_end, p0 + kResolve);
     const int nb = (p1 - p0 + kNB - 1) / kNB;
-    pass_n = p1 - p0;
     if (p0 != u_begin) {
+      __syncthreads();                   // every wave is done with the previous pass's slots
+      pass_n = p1 - p0;
       resolve_pass(p0, p1);
       __syncthreads();
-    }
-    if constexpr (kRaw) gather_raw(0, 0);
-    else gather(0, 0);
-  for (int it = 0; it < nb; ++it) {
-    const int cur = kRaw ? 0 : (it & 1);
-    const int jb = it * kNB;             // pass entry of this block's first row
-    __builtin_amdgcn_s_waitcnt(0);      // this block's rows (raw bytes for fp8)
-    __syncthreads();
-    if constexpr (kRaw) {
-      // the next block's raw bytes stream in during this block's dequantisation and compute
-      if (it + 1 < nb) gather_raw((it + 1) & 1, jb + kNB);
-      dequant(it & 1, jb);
-      lds_barrier();                     // bf16 rows complete; the loads just issued stay in flight
     } else {
-      if (it + 1 < nb) gather(cur ^ 1, jb + kNB);   // overlaps the compute below
+      pass_n = p1 - p0;
     }
+    // the addresses of the first NBUF blocks (one thread per row), then the first NBUF - 1
+    // blocks' loads
+    for (int t = threadIdx.x; t < NBUF * kNB && t < nb * kNB; t += NT) row_addrs(t / kNB, (t / kNB) * kNB, t % kNB);
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k) {
+      if (k < nb) {
+        if constexpr (kRaw) gather_raw(k);
+        else gather(k);
+      }
+    }
+  for (int it = 0; it < nb; ++it) {
+    const int cur = kRaw ? 0 : it % NBUF;
+    const int jb = it * kNB;             // pass entry of this block's first row
+    // this block's rows (raw bytes for fp8) are in: the later blocks' loads stay in flight
+    const int later = min(NBUF - 2, nb - 1 - it);
+    wait_vmcnt_dyn<0, (NBUF - 2) * PB_MAX>(later * per_block);
+    lds_barrier();                       // ... for every wave; and the buffer refilled below is free
+    if (it + NBUF - 1 < nb) {
+      if constexpr (kRaw) gather_raw((it + NBUF - 1) % NBUF);
+      else gather((it + NBUF - 1) % NBUF);
+    }
+    // the addresses of the block after it, into the slot this block's loads used (read by
+    // the next iteration's loads, after its barrier)
+    if (it + NBUF < nb && threadIdx.x < kNB) row_addrs(it % NBUF, jb + NBUF * kNB, threadIdx.x);
+    if constexpr (kRaw) {
+      dequant(it % NBUF, jb);
+      lds_barrier();                     // bf16 rows complete; the loads just issued stay in flight
+    }
+
+    // the block's row validity for the softmax (rows 4g..4g+3 and 16+4g..16+4g+3 of this lane),
+    // read before the score product so the reads overlap it
+    const int jm = jb + 4 * g;
+    const u32x4_t sl0 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm]);
+    const u32x4_t sl1 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm + 16]);
 
     // ---- S^T = K Q^T
     f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -426,8 +480,8 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok0 = slot_at(jb + 4 * g + r) >= 0;
-      const bool ok1 = slot_at(jb + 16 + 4 * g + r) >= 0;
+      const bool ok0 = jm + r < pass_n && (int32_t)sl0[r] >= 0;
+      const bool ok1 = jm + 16 + r < pass_n && (int32_t)sl1[r] >= 0;
       const float x0 = ok0 ? s0[r] * a.scale_log2 : -INFINITY;
       const float x1 = ok1 ? s1[r] * a.scale_log2 : -INFINITY;
       p[r] = x0;
@@ -480,7 +534,6 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
         o[i][e] = mfma_bf16_16x16x32(av, pb, o[i][e]);
       }
     }
-    __syncthreads();   // block `cur` is refilled two iterations from now
   }
   }
 
@@ -506,11 +559,12 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   } else {
     // un-normalised partial (o, m, l) of this split; k_mla_combine merges them. A lane holds
     // 128 contiguous bytes of one head's row, so direct stores would spread every instruction
-    // over 64 cache lines; the block is staged in LDS (free now: the last iteration ended
-    // with a barrier) and written back one head row at a time, 1 KiB per instruction.
+    // over 64 cache lines; the block is staged in LDS (free once every wave is past its last
+    // block) and written back one head row at a time, 1 KiB per instruction.
     constexpr int PS = kDV + 4;                       // padded fp32 row of one head in LDS
     if constexpr (HT * 16 * PS * 4 <= LDSB) {
       float* s_po = reinterpret_cast<float*>(s_lds);
+      lds_barrier();
 #pragma unroll
       for (int i = 0; i < GD; ++i)
 #pragma unroll
@@ -636,39 +690,45 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
   if (a.lse && blockIdx.x == 0 && ci == 0) a.lse[(int64_t)t * a.H + head] = fin.lse;
 }
 
-template <int FMT, int DQK, int HT, int WD>
+template <int FMT, int DQK, int HT, int WD, int NBUF>
 static hipError_t launch_h(const MlaArgs& a, int T, hipStream_t st) {
   dim3 grid(a.n_split, a.H / (16 * HT), T);
   if (a.n_split > 1)
-    launch_kernel(k_sparse_mla<FMT, DQK, HT, WD, true>, grid, dim3(64 * HT * WD), st, a);
+    launch_kernel(k_sparse_mla<FMT, DQK, HT, WD, true, NBUF>, grid, dim3(64 * HT * WD), st, a);
   else
-    launch_kernel(k_sparse_mla<FMT, DQK, HT, WD, false>, grid, dim3(64 * HT * WD), st, a);
+    launch_kernel(k_sparse_mla<FMT, DQK, HT, WD, false, NBUF>, grid, dim3(64 * HT * WD), st, a);
   return hipGetLastError();
 }
 
-// ht head tiles per workgroup; ht == 1 splits the value columns over 4 waves instead
+// ht head tiles per workgroup (ht == 1 splits the value columns over 4 waves instead); a ring
+// of 2 or 4 blocks
 template <int FMT, int DQK>
-static hipError_t launch_d(const MlaArgs& a, int ht, int T, hipStream_t st) {
-  if (ht == 4) return launch_h<FMT, DQK, 4, 1>(a, T, st);
-  if (ht == 2) return launch_h<FMT, DQK, 2, 2>(a, T, st);
-  return launch_h<FMT, DQK, 1, 4>(a, T, st);
+static hipError_t launch_d(const MlaArgs& a, int ht, int nbuf, int T, hipStream_t st) {
+  if (nbuf > 2) {
+    if (ht == 4) return launch_h<FMT, DQK, 4, 1, 4>(a, T, st);
+    if (ht == 2) return launch_h<FMT, DQK, 2, 2, 4>(a, T, st);
+    return launch_h<FMT, DQK, 1, 4, 4>(a, T, st);
+  }
+  if (ht == 4) return launch_h<FMT, DQK, 4, 1, 2>(a, T, st);
+  if (ht == 2) return launch_h<FMT, DQK, 2, 2, 2>(a, T, st);
+  return launch_h<FMT, DQK, 1, 4, 2>(a, T, st);
 }
 
-hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int T, hipStream_t st) {
+hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int nbuf, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (fmt == kFmtBf16) {
-    if (d_qk == 576) return launch_d<kFmtBf16, 576>(a, ht, T, st);
-    return launch_d<kFmtBf16, 512>(a, ht, T, st);
+    if (d_qk == 576) return launch_d<kFmtBf16, 576>(a, ht, nbuf, T, st);
+    return launch_d<kFmtBf16, 512>(a, ht, nbuf, T, st);
   }
   if (fmt == kFmtUniform) {
-    if (d_qk == 576) return launch_d<kFmtUniform, 576>(a, ht, T, st);
-    return launch_d<kFmtUniform, 512>(a, ht, T, st);
+    if (d_qk == 576) return launch_d<kFmtUniform, 576>(a, ht, nbuf, T, st);
+    return launch_d<kFmtUniform, 512>(a, ht, nbuf, T, st);
   }
   if (fmt == kFmtFnuz) {
-    if (d_qk == 576) return launch_d<kFmtFnuz, 576>(a, ht, T, st);
-    return launch_d<kFmtFnuz, 512>(a, ht, T, st);
+    if (d_qk == 576) return launch_d<kFmtFnuz, 576>(a, ht, nbuf, T, st);
+    return launch_d<kFmtFnuz, 512>(a, ht, nbuf, T, st);
   }
-  return launch_d<kFmtDsMla, 512>(a, ht, T, st);
+  return launch_d<kFmtDsMla, 512>(a, ht, nbuf, T, st);
 }
 
 hipError_t launch_mla_combine(const MlaArgs& a, int T, hipStream_t st) {
