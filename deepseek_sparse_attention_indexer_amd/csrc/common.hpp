@@ -178,6 +178,14 @@ __device__ __forceinline__ void fnuz4_to_f32(uint32_t w, float* o) {
 // 2^(e-127) for a UE8M0 byte 1..254 (exact, built from the exponent field).
 __device__ __forceinline__ float ue8m0_scale(uint32_t e) { return __uint_as_float(e << 23); }
 
+// Two OCP e4m3 bytes (bytes 0-1 of w, or 2-3 with HI) -> two bf16 (low half = the lower byte)
+// times 2^(exponent field of s): gfx950's scaled conversion applies only the exponent of its
+// fp32 scale, so for a power-of-two scale the result is the exact product.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2_pow2(uint32_t w, float s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, s, HI));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_bcast_first(T v) {
   return __builtin_amdgcn_readfirstlane(v);

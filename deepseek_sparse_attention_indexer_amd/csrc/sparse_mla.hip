@@ -96,6 +96,19 @@ __device__ __forceinline__ void store_unit(const RawUnit& r, int u, uint16_t* lr
     *reinterpret_cast<u32x4_t*>(lrow + 448 + 8 * (u - 28)) = r.v;
     return;
   }
+  if constexpr (FMT == kFmtDsMla) {   // UE8M0 scale, a power of two: one scaled conversion per pair
+    u32x4_t lo, hi;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      lo[2 * k] = fp8x2_to_bf16x2_pow2<false>(r.v[k], r.sc);
+      lo[2 * k + 1] = fp8x2_to_bf16x2_pow2<true>(r.v[k], r.sc);
+      hi[2 * k] = fp8x2_to_bf16x2_pow2<false>(r.v[2 + k], r.sc);
+      hi[2 * k + 1] = fp8x2_to_bf16x2_pow2<true>(r.v[2 + k], r.sc);
+    }
+    *reinterpret_cast<u32x4_t*>(lrow + 16 * u) = lo;
+    *reinterpret_cast<u32x4_t*>(lrow + 16 * u + 8) = hi;
+    return;
+  }
   float f[16];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {

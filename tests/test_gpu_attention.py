@@ -37,6 +37,11 @@ CASES = [
                                  n_pad=100, sink=True)),
     ("bf16_all_padded_sink", dict(fmt="bf16", B=2, H=16, n_ctx=300, n_idx=64, pad="all", sink=True,
                                   lse_log2=True)),
+    # 16 rows x 64 heads in decode: 64-head workgroups with splits and a ring of four blocks
+    # (ragged last block, padding spread over the lists)
+    ("bf16_h64_b16_ring", dict(fmt="bf16", B=16, H=64, n_ctx=5000, n_idx=2000, pad="shuffled", n_pad=77)),
+    ("ds_mla_h64_b16_ring_two_lists", dict(fmt="fp8_ds_mla", B=16, H=64, n_ctx=5000, n_idx=1000,
+                                           page_size=64, n_extra=230, pad="tail", n_pad=7)),
     ("ds_mla_two_lists_sink_log2", dict(fmt="fp8_ds_mla", B=3, H=16, n_ctx=2000, n_idx=128,
                                         page_size=256, n_extra=300, pad="tail", n_pad=5, sink=True,
                                         lse_log2=True)),
