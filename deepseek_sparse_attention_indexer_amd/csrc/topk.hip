@@ -190,18 +190,22 @@ __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
 // list is deterministic.
 //  * chunk workgroups: offset = sum of the earlier chunks' counts above the bin, then a
 //    thread-major scan of the chunk's own scores;
-//  * the resolver: gathers the bin's candidates (kept in LDS when there are at most
-//    kTopkCandLds, else re-read from the workspace), takes the second digit and the
+//  * the resolver: gathers the bin's candidates (up to 4096 held in registers, up to CAND
+//    more in LDS, else re-read from the workspace), takes the second digit and the
 //    threshold sub-bin's last 8 bits by histogram, breaks ties at the threshold key toward
 //    the smaller position, then writes the selected candidates. It also returns the
 //    first-digit histogram to zero, writes lens and pads short rows with -1.
+// CAND: candidate capacity in LDS. The LDS of a kernel is reserved for every workgroup, so a
+// large grid (many rows) takes CAND = 0: its chunk workgroups then fit four to a CU, and a
+// row with more than 4096 candidates re-reads them from the workspace.
+template <int CAND>
 __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_w[kNT / 64];
   __shared__ uint32_t s_res[8];
   __shared__ uint32_t s_off[kMaxChunks + 1];   // the bin's candidates per chunk -> prefixes
-  __shared__ uint32_t s_ck[kTopkCandLds];      // candidate keys
-  __shared__ int32_t s_cp[kTopkCandLds];       // and positions
+  __shared__ uint32_t s_ck[CAND > 0 ? CAND : 1];   // candidate keys
+  __shared__ int32_t s_cp[CAND > 0 ? CAND : 1];    // and positions
 
   constexpr int D1 = 32 - kHistBits;
   constexpr int D2 = D1 - kHistBits;
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
     lds_barrier();
   }
   const uint32_t n_cand = s_off[nch];
-  const bool in_lds = n_cand <= (uint32_t)kTopkCandLds;
+  const bool in_lds = CAND > 0 && n_cand <= (uint32_t)CAND;
   // Chunk of candidate i (candidates are numbered chunk by chunk): the largest c < nch with
   // prefix[c] <= i, by binary lifting with a uniform number of steps, so that several lookups
   // interleave their LDS reads. prefix[nch] = n_cand > i stops every probe past the end.
@@ -440,7 +444,9 @@ hipError_t launch_topk_filter(const TopkArgs& a, int T, hipStream_t st) {
 
 hipError_t launch_topk_finalize(const TopkArgs& a, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  launch_kernel(k_topk_finalize, dim3(a.n_chunks + 1, T), dim3(kNT), st, a);
+  const dim3 grid(a.n_chunks + 1, T);
+  if ((int64_t)grid.x * T <= 256) launch_kernel(k_topk_finalize<kTopkCandLds>, grid, dim3(kNT), st, a);
+  else launch_kernel(k_topk_finalize<0>, grid, dim3(kNT), st, a);
   return hipGetLastError();
 }
 

@@ -85,3 +85,21 @@ def test_topk_workspace_reuse_is_clean():
         x = _logits(rng, 2, 40000, 16)
         idx, lens = run_topk(torch.from_numpy(x).cuda(), [40000, 39000], 2, 512, ws=ws)
         _check(x, [40000, 39000], 512, idx, lens)
+
+
+@pytest.mark.parametrize("T,n,ties", [(2, 131072, 6000), (2, 40000, 9000), (70, 17000, 6000)],
+                         ids=["few_rows_6000_ties", "few_rows_9000_ties", "70_rows_6000_ties"])
+def test_topk_threshold_bin_capacity(T, n, ties):
+    """The resolver holds up to 4096 threshold-bin candidates in registers, up to 8192 more in
+    LDS when the grid is small, and re-reads the workspace otherwise (always, for a large
+    grid). Exact ties at the k-th value fill the threshold bin past each capacity; the k
+    smallest tied positions must win."""
+    rng = np.random.default_rng(T * 7 + ties)
+    x = (rng.standard_normal((T, n)) * 0.01).astype(np.float32)
+    for t in range(T):
+        pos = rng.choice(n, ties, replace=False)
+        x[t, pos] = 5.0
+    row_len = [n] * T
+    say("topk ties", T, n, ties)
+    idx, lens = run_topk(torch.from_numpy(x).cuda(), row_len, T, 2048)
+    _check(x, row_len, 2048, idx, lens)
