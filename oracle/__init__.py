@@ -8,4 +8,5 @@ from . import compare  # noqa: F401
 from .dsa_oracle import (  # noqa: F401
     bf16_to_f64, FP8_E4M3FN, ue8m0_to_f64, slots_of, key_rows, kv_rows,
     index_scores_row, topk_row, attention_row, layer_row, order_key,
+    attention_math, attention_backward_math, attention_backward_row,
 )

@@ -32,6 +32,16 @@ What it computes, per query row t of request b that sees candidates s in [0, n_t
        out[t, h, :] = sum_i exp(l_i) c_i[:d_v] / (exp(sink_h) + sum_i exp(l_i)),
        lse[t, h] = log(exp(sink_h) + sum_i exp(l_i))
    (an empty list: out = 0, lse = sink_h). The base-2 lse is lse / ln 2.
+5. Backward of step 3 with the step-4 sink (radixark/miles PR 3608, section "What": dq, and
+   dKV atomic-added through the clamped indices; the pages give no formula, so this is the
+   exact gradient of the forward above, for one list). For an upstream gradient dout[h, :]:
+       p_i = exp(l_i - lse_h),  p_sink = exp(sink_h - lse_h),  D_h = dout[h, :] . out[h, :],
+       dl_i = p_i * (dout[h, :] . c_i[:d_v] - D_h),
+       dq[h, :] = softmax_scale * sum_i dl_i * c_i[:d_qk],
+       dc_i[:d_qk] += softmax_scale * dl_i * q[h, :],   dc_i[:d_v] += p_i * dout[h, :],
+       dsink_h = -p_sink * D_h
+   summed over heads for dc_i; an entry listed twice contributes twice (each listed entry is
+   its own term of the softmax).
 """
 from __future__ import annotations
 
@@ -227,13 +237,62 @@ def attention_row(prob, t: int, idx_main: np.ndarray, idx_extra: np.ndarray | No
         return np.zeros((H, d_v)), sink / base
     rows = np.concatenate(parts, axis=0)                        # [n, D]
     q = bf16_to_f64(prob.q[t])                                  # [H, d_qk]
-    logits = float(prob.softmax_scale) * (q @ rows[:, :prob.d_qk].T)   # [H, n]
+    out, lse = attention_math(q, rows, sink, float(prob.softmax_scale), prob.d_qk, d_v)
+    return out, lse / base
+
+
+def attention_math(q: np.ndarray, rows: np.ndarray, sink: np.ndarray, scale: float, d_qk: int,
+                   d_v: int):
+    """Step 3/4 on float64 arrays: q [H, d_qk], rows [n >= 1, D], sink [H] (-inf: none).
+    Returns (out [H, d_v], natural-log lse [H])."""
+    logits = scale * (q @ rows[:, :d_qk].T)                     # [H, n]
     m = np.maximum(logits.max(axis=1), sink)[:, None]           # finite: there is a row
     e = np.exp(logits - m)
     z = e.sum(axis=1, keepdims=True) + np.exp(sink[:, None] - m)
     out = (e @ rows[:, :d_v]) / z
     lse = (m + np.log(z))[:, 0]
-    return out, lse / base
+    return out, lse
+
+
+def attention_backward_math(q: np.ndarray, rows: np.ndarray, sink: np.ndarray, scale: float,
+                            d_qk: int, d_v: int, dout: np.ndarray):
+    """Step 5 on float64 arrays (q [H, d_qk], rows [n >= 1, D], sink [H], dout [H, d_v]).
+    Returns (dq [H, d_qk], drows [n, max(d_qk, d_v)] per listed entry, dsink [H])."""
+    logits = scale * (q @ rows[:, :d_qk].T)                     # [H, n]
+    m = np.maximum(logits.max(axis=1), sink)[:, None]
+    lse = m + np.log(np.exp(logits - m).sum(axis=1, keepdims=True) + np.exp(sink[:, None] - m))
+    p = np.exp(logits - lse)                                    # [H, n]
+    p_sink = np.exp(sink[:, None] - lse)[:, 0]                  # [H]
+    out = p @ rows[:, :d_v]                                     # [H, d_v]
+    D = (dout * out).sum(axis=1)                                # [H]
+    dp = dout @ rows[:, :d_v].T                                 # [H, n]
+    dl = p * (dp - D[:, None])                                  # [H, n]
+    dq = scale * (dl @ rows[:, :d_qk])                          # [H, d_qk]
+    drows = np.zeros((rows.shape[0], max(d_qk, d_v)))
+    drows[:, :d_qk] += scale * (dl.T @ q)
+    drows[:, :d_v] += p.T @ dout
+    dsink = -p_sink * D
+    return dq, drows, dsink
+
+
+def attention_backward_row(prob, t: int, idx: np.ndarray, dout: np.ndarray):
+    """Step 5 for row t over one list (main cache): dout float64 [H, d_v]. Returns
+    (dq [H, d_qk], slots [n] of the valid listed entries in list order, drows [n, D],
+    dsink [H]); an empty list gives zeros."""
+    b = int(prob.row_req[t])
+    lst = np.asarray(idx, dtype=np.int64)
+    keep = lst[lst != -1]
+    H = prob.H
+    sink = getattr(prob, "sink", None)
+    sink = np.full(H, -np.inf) if sink is None else np.asarray(sink, dtype=np.float64)
+    D = max(prob.d_qk, prob.d_v)
+    if keep.size == 0:
+        return np.zeros((H, prob.d_qk)), np.zeros(0, np.int64), np.zeros((0, D)), np.zeros(H)
+    rows = kv_rows(prob.kv, b, keep)
+    q = bf16_to_f64(prob.q[t])
+    dq, drows, dsink = attention_backward_math(q, rows, sink, float(prob.softmax_scale), prob.d_qk,
+                                               prob.d_v, np.asarray(dout, dtype=np.float64))
+    return dq, slots_of(prob.kv, b, keep), drows, dsink
 
 
 def layer_row(prob, t: int) -> dict:
