@@ -473,7 +473,7 @@ dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
 // ==================================================================== exported entry points
 extern "C" {
 
-int32_t dsa_abi_version(void) { return 3; }
+int32_t dsa_abi_version(void) { return 4; }
 dsa_status dsa_kv_cache_write(const void* src, int64_t ld_src, int32_t n_tok, const int32_t* slots,
                               const dsa_kv_cache* kv, void* stream) {
   if (n_tok < 0 || !kv) return DSA_ERR_ARG;
@@ -647,6 +647,61 @@ dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cach
   st = check_mla(m);
   if (st != DSA_OK) return st;
   return run_mla(m, false, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cache* kv,
+                                   const int32_t* idx, int64_t ld_idx, int32_t n_idx,
+                                   const dsa_rows* rows, int32_t H, int32_t d_qk, int32_t d_v,
+                                   float softmax_scale, const void* out, int64_t ld_out,
+                                   const float* lse, const void* dout, int64_t ld_dout,
+                                   const dsa_attn_opts* opts, float* dq, int64_t ld_dq,
+                                   float* dkv, float* dsink, void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if (H <= 0 || n_idx < 0) return DSA_ERR_ARG;
+  if (H % 16 || d_v != 512 || (d_qk != 512 && d_qk != 576)) return DSA_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return DSA_ERR_ARG;
+  st = check_opts(opts);
+  if (st != DSA_OK) return st;
+  st = check_kv(kv, d_qk);
+  if (st != DSA_OK) return st;
+  if (kv->format != DSA_KV_BF16) return DSA_ERR_UNSUPPORTED;
+  if (dsink && (!opts || !opts->sink || !al4(dsink))) return DSA_ERR_ARG;
+  const int T = rows->T;
+  if (T == 0) return DSA_OK;
+  if (!q || !al16(q) || ld_q < (int64_t)H * d_qk || ld_q % 8) return DSA_ERR_ARG;
+  if (!out || !al16(out) || ld_out < (int64_t)H * d_v || ld_out % 8) return DSA_ERR_ARG;
+  if (!dout || !al16(dout) || ld_dout < (int64_t)H * d_v || ld_dout % 8) return DSA_ERR_ARG;
+  if (!lse || !al4(lse)) return DSA_ERR_ARG;
+  if (n_idx > 0 && (!idx || !al4(idx) || ld_idx < n_idx)) return DSA_ERR_ARG;
+  if (!dq || !al16(dq) || ld_dq < (int64_t)H * d_qk || ld_dq % 4) return DSA_ERR_ARG;
+  if (!dkv || !al4(dkv)) return DSA_ERR_ARG;
+  MlaBwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.ld_q = ld_q;
+  a.kv = make_kv(kv);
+  a.idx = idx;
+  a.ld_idx = ld_idx;
+  a.n_idx = n_idx;
+  a.row_req = rows->row_req;
+  a.n_req = rows->n_req;
+  a.H = H;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.out = static_cast<const uint16_t*>(out);
+  a.ld_out = ld_out;
+  a.lse = lse;
+  a.lse_log2 = opts ? opts->lse_log2 : 0;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.ld_dout = ld_dout;
+  a.sink = opts ? opts->sink : nullptr;
+  a.dq = dq;
+  a.ld_dq = ld_dq;
+  a.dkv = dkv;
+  a.dsink = dsink;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  return hip_status(timed("sparse_mla_bwd", hs, [&] { return launch_sparse_mla_bwd(a, d_qk, T, hs); }));
 }
 
 dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld_q_idx,

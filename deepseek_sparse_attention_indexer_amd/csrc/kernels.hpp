@@ -125,6 +125,34 @@ struct MlaArgs {
 hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int nbuf, int T, hipStream_t st);
 hipError_t launch_mla_combine(const MlaArgs& a, int T, hipStream_t st);
 
+// backward of the sparse MLA attention: one list, bf16 rows
+struct MlaBwdArgs {
+  const uint16_t* q;       // bf16 [T, H, d_qk]
+  int64_t ld_q;
+  KvDev kv;
+  const int32_t* idx;      // [T, n_idx]
+  int64_t ld_idx;
+  int32_t n_idx;
+  const int32_t* row_req;  // nullptr: row t is request t
+  int32_t n_req;
+  int32_t H;
+  float scale;             // softmax_scale
+  float scale_log2;        // softmax_scale * log2(e)
+  const uint16_t* out;     // bf16 [T, H, 512] (the forward's output)
+  int64_t ld_out;
+  const float* lse;        // [T, H] the forward's lse
+  int32_t lse_log2;        // lse in base 2
+  const uint16_t* dout;    // bf16 [T, H, 512]
+  int64_t ld_dout;
+  const float* sink;       // [H] or nullptr
+  float* dq;               // fp32 [T, H, d_qk]
+  int64_t ld_dq;
+  float* dkv;              // fp32 [n_slots, d_qk], added to
+  float* dsink;            // fp32 [H], added to, or nullptr
+};
+
+hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st);
+
 // cache writes: bf16 rows -> a cache format, one row per token at slots[token]
 enum { kCwBf16 = 0, kCwScaled = 1, kCwDsMla = 2, kCwScaledFnuz = 3 };
 struct CacheWriteArgs {

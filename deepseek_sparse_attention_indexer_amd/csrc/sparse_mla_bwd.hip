@@ -1,0 +1,361 @@
+// Backward of the sparse absorbed-MLA attention (one list, bf16 latent rows), gfx950 MFMA.
+//
+// For the forward out[t,h] = sum_i p_i c_i[0:d_v], p_i = exp(l_i - lse[t,h]),
+// l_i = softmax_scale * q[t,h] . c_i[0:d_qk] over the listed rows c_i (entries -1 contribute
+// nothing), an upstream gradient dout gives, with D = dout[t,h] . out[t,h]:
+//   dl_i = p_i (dout[t,h] . c_i[0:d_v] - D)
+//   dq[t,h] = softmax_scale * sum_i dl_i c_i[0:d_qk]
+//   dkv[slot_i] += softmax_scale * dl_i q[t,h]  (columns 0:d_qk)  +  p_i dout[t,h]  (0:d_v)
+//   dsink[h] += -exp(sink[h] - lse[t,h]) D
+// (radixark/miles PR 3608, section "What": the backward takes the forward's lse with the sink
+// folded in, and adds dKV through the listed indices atomically; the lse here may be in base 2).
+//
+// A workgroup takes one query row and 16 heads (4 waves) and walks the row's list in blocks of
+// 32 rows gathered into LDS (direct global->LDS loads). Per block, with S^T = K Q^T and
+// dP^T = V dO^T split over the waves as in the forward (two row tiles x two halves of the
+// contraction, the partials meeting in LDS):
+//   * P and dZ from the forward's lse (no second pass over the list);
+//   * dq^T += K^T dZ^T, with dZ^T taken straight from the S^T accumulator layout as the B
+//     operand and K^T from an 8x8 transpose of LDS rows in registers (the forward's value
+//     product); each wave owns 128 columns, the 64 RoPE columns are shared out in pairs of
+//     column phases;
+//   * dKV^T = Q^T (scale dZ) + dO^T P over the 16 heads (16x16x16 MFMAs, k = heads): dZ and P
+//     cross lanes once through LDS into the B layout, Q^T and dO^T are A operands built once
+//     per workgroup; each wave owns a quarter of the columns, and the 32 x d_qk block goes
+//     to memory by fp32 atomic adds (rows of padding entries are skipped).
+// One block in flight per workgroup.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kBwdNB = 32;         // rows per block
+constexpr int kBwdResolve = 1024;  // list entries resolved to slots per pass
+constexpr int kBwdDV = 512;
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+
+// 16x16x16 bf16 MFMA: lane l supplies A[l%16][4(l/16)+j] and B[4(l/16)+j][l%16] (j = 0..3)
+// and receives C[4(l/16)+r][l%16] (r = 0..3).
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x16(u32x2_t a, u32x2_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_u16(const uint16_t* p) { return *p; }
+
+}  // namespace
+
+template <int DQK>
+__global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int NT = 256;
+  constexpr int RE = DQK + 8;                 // padded bf16 row in LDS
+  constexpr int KS = DQK / 32;                // k-steps of the score product
+  constexpr int KQ = KS / 2;                  // per wave (split over the two halves)
+  constexpr int D4 = DQK / 4;                 // columns of dKV per wave
+  constexpr int MT = D4 / 16;                 // 16-column tiles of dKV per wave
+  constexpr bool kRope = DQK > kBwdDV;        // columns 512..575 (4 x 16) beyond the value
+  static_assert(KS % 2 == 0 && D4 % 16 == 0, "shapes");
+  __shared__ __align__(16) uint16_t s_rows[kBwdNB][RE];
+  __shared__ __align__(16) int32_t s_slot[kBwdResolve];
+  __shared__ const uint8_t* s_ra[kBwdNB];
+  __shared__ f32x4_t s_ss[NW][64];
+  __shared__ f32x4_t s_sd[NW][64];
+  __shared__ __align__(16) uint16_t s_tz[kBwdNB][16];   // bf16 scale * dZ[row][head]
+  __shared__ __align__(16) uint16_t s_tp[kBwdNB][16];   // bf16 P[row][head]
+  __shared__ float s_D[16];
+  __shared__ float s_l2[16];
+
+  const int t = blockIdx.y;
+  const int hg = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int head0 = hg * 16;
+  const int b = min(max(a.row_req ? a.row_req[t] : t, 0), a.n_req - 1);
+  const KvDev kv = a.kv;
+  // the paging rebuilt field by field: a table/base select on the argument copy itself would
+  // be lowered to an indexed load from a scratch copy of the struct
+  const Paging pg = pick_paging(false, a.kv.pg, a.kv.pg);
+  const int32_t* const idx = a.idx + (int64_t)t * a.ld_idx;
+  const int ntot = a.n_idx;
+
+  // ---- prologue: q and dout of the 16 heads staged in the row buffer, the register operands
+  // built from them; D = dout . out and the lse in base 2 per head
+  static_assert(16 * RE + 16 * (kBwdDV + 8) <= kBwdNB * RE, "staging");
+  uint16_t* const s_q = &s_rows[0][0];                  // [16][RE]
+  uint16_t* const s_do = &s_rows[0][0] + 16 * RE;       // [16][kBwdDV + 8]
+  constexpr int DOS = kBwdDV + 8;
+  {
+    const uint16_t* qg = a.q + (int64_t)t * a.ld_q + (int64_t)head0 * DQK;
+    for (int o = threadIdx.x * 8; o < 16 * DQK; o += NT * 8)
+      *reinterpret_cast<u32x4_t*>(s_q + (o / DQK) * RE + o % DQK) = *reinterpret_cast<const u32x4_t*>(qg + o);
+    const uint16_t* dg = a.dout + (int64_t)t * a.ld_dout + (int64_t)head0 * kBwdDV;
+    for (int o = threadIdx.x * 8; o < 16 * kBwdDV; o += NT * 8)
+      *reinterpret_cast<u32x4_t*>(s_do + (o / kBwdDV) * DOS + o % kBwdDV) = *reinterpret_cast<const u32x4_t*>(dg + o);
+    // D: 16 threads per head, 32 columns each
+    const int h = threadIdx.x >> 4;
+    const int c0 = (threadIdx.x & 15) * 32;
+    const uint16_t* og = a.out + (int64_t)t * a.ld_out + (int64_t)(head0 + h) * kBwdDV + c0;
+    const uint16_t* dh = dg + h * kBwdDV + c0;
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(og + i);
+      const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(dh + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d = fmaf(__uint_as_float(ov[j] << 16), __uint_as_float(dv[j] << 16), d);
+        d = fmaf(__uint_as_float(ov[j] & 0xffff0000u), __uint_as_float(dv[j] & 0xffff0000u), d);
+      }
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) d += __shfl_xor(d, m);
+    if ((threadIdx.x & 15) == 0) {
+      s_D[h] = d;
+      const float l = a.lse[(int64_t)t * a.H + head0 + h];
+      s_l2[h] = a.lse_log2 ? l : l * kLog2e;
+    }
+  }
+  __syncthreads();
+  // B operand of S^T = K Q^T for this wave's half of the contraction, and of dP^T = V dO^T
+  const int kq0 = (wave & 1) * KQ;
+  u32x4_t qb[KQ];
+#pragma unroll
+  for (int kb = 0; kb < KQ; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(s_q + c * RE + 32 * (kq0 + kb) + 8 * g);
+  u32x4_t dob[8];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+    dob[kb] = *reinterpret_cast<const u32x4_t*>(s_do + c * DOS + 256 * (wave & 1) + 32 * kb + 8 * g);
+  // A operands of dKV^T (m = this wave's columns, k = the 16 heads): Q^T and dO^T
+  u32x2_t qta[MT], dota[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int col = wave * D4 + 16 * mt + c;
+    uint32_t h4[4], d4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h4[j] = lds_u16(s_q + (4 * g + j) * RE + col);
+      d4[j] = col < kBwdDV ? lds_u16(s_do + (4 * g + j) * DOS + col) : 0u;
+    }
+    qta[mt] = u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
+    dota[mt] = u32x2_t{d4[0] | (d4[1] << 16), d4[2] | (d4[3] << 16)};
+  }
+  const float Dc = s_D[c];
+  const float l2c = s_l2[c];
+  if (a.sink && a.dsink && threadIdx.x < 16) {
+    const float sk = a.sink[head0 + threadIdx.x];
+    if (sk > -INFINITY) unsafeAtomicAdd(a.dsink + head0 + threadIdx.x, -exp2f(sk * kLog2e - s_l2[threadIdx.x]) * s_D[threadIdx.x]);
+  }
+  __syncthreads();   // the staging area becomes the row buffer
+
+  // dq^T accumulators: 128 columns of group `wave` (8 column phases), and for d_qk = 576 two
+  // phases of the RoPE group (columns 512 + 8 m + e, e = 2 wave + i, m < 8)
+  f32x4_t oq[8];
+  f32x4_t o4[2];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) oq[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  o4[0] = o4[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  int pass_n = 0;
+  for (int p0 = 0; p0 < ntot; p0 += kBwdResolve) {
+    const int p1 = min(ntot, p0 + kBwdResolve);
+    const int nb = (p1 - p0 + kBwdNB - 1) / kBwdNB;
+    pass_n = p1 - p0;
+    {   // the pass's entries to slots: every index read, then every table read
+      constexpr int RPT = kBwdResolve / NT;
+      int e[RPT];
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) e[k] = idx[min(p0 + (int)threadIdx.x + k * NT, p1 - 1)];
+      SlotRead sr[RPT];
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) sr[k] = slot_read(pg, b, max(e[k], 0));
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int j = threadIdx.x + k * NT;
+        const int64_t sl = slot_done(pg, sr[k]);
+        if (j < pass_n) s_slot[j] = e[k] >= 0 ? (int32_t)sl : -1;
+      }
+    }
+    __syncthreads();
+    for (int it = 0; it < nb; ++it) {
+      const int jb = it * kBwdNB;
+      // row addresses (one lane per row; padding reads row 0), then the block's loads
+      if (threadIdx.x < kBwdNB) {
+        const int j = jb + threadIdx.x;
+        const int32_t v = j < pass_n ? s_slot[j] : -1;
+        s_ra[threadIdx.x] = kv.data + (int64_t)max(v, 0) * (DQK * 2);
+      }
+      lds_barrier();
+      {
+        constexpr int RW = DQK / 8 + 1;
+        constexpr int SLOTS = kBwdNB * RW;
+        constexpr int NINS = (SLOTS + 63) / 64;
+        constexpr int PER = (NINS + NW - 1) / NW;
+        auto* lbase = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(
+            reinterpret_cast<uintptr_t>(&s_rows[0][0]) & 0xffffffffu);
+        const uint8_t* src[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          const int j = min((wave + k * NW) * 64 + lane, SLOTS - 1);
+          const int r = j / RW;
+          int cc = j - r * RW;
+          cc = cc == RW - 1 ? 0 : cc;
+          src[k] = s_ra[r] + 16 * cc;
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          const int ins = wave + k * NW;
+          if (ins < NINS && ins * 64 + lane < SLOTS) {
+            const uint8_t* sp = src[k];
+            __builtin_amdgcn_global_load_lds(sp, lbase + ins * 1024, 16, 0, 0);
+          }
+        }
+      }
+      wait_vmcnt<0>();
+      lds_barrier();
+
+      // ---- S^T and dP^T, split over the waves
+      const int jm = jb + 4 * g;
+      const u32x4_t sl0 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm]);
+      const u32x4_t sl1 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm + 16]);
+      {
+        const uint16_t* rp = &s_rows[16 * (wave >> 1) + c][8 * g];
+        f32x4_t sp = f32x4_t{0.f, 0.f, 0.f, 0.f}, dp = sp;
+#pragma unroll
+        for (int kb = 0; kb < KQ; ++kb)
+          sp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 32 * (kq0 + kb)), qb[kb], sp);
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+          dp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 256 * (wave & 1) + 32 * kb), dob[kb], dp);
+        s_ss[wave][lane] = sp;
+        s_sd[wave][lane] = dp;
+      }
+      lds_barrier();
+      const f32x4_t s0 = s_ss[0][lane] + s_ss[1][lane], s1 = s_ss[2][lane] + s_ss[3][lane];
+      const f32x4_t d0 = s_sd[0][lane] + s_sd[1][lane], d1 = s_sd[2][lane] + s_sd[3][lane];
+      // ---- P and dZ of rows 4g + r and 16 + 4g + r, head c
+      float p[8], dz[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok0 = jm + r < pass_n && (int32_t)sl0[r] >= 0;
+        const bool ok1 = jm + 16 + r < pass_n && (int32_t)sl1[r] >= 0;
+        p[r] = ok0 ? exp2f(s0[r] * a.scale_log2 - l2c) : 0.f;
+        p[4 + r] = ok1 ? exp2f(s1[r] * a.scale_log2 - l2c) : 0.f;
+        dz[r] = p[r] * (d0[r] - Dc);
+        dz[4 + r] = p[4 + r] * (d1[r] - Dc);
+      }
+      // dZ and P into LDS, row-major by head, for the dKV product's B layout
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s_tz[4 * g + r][c] = (uint16_t)bf16_rne_bits(dz[r] * a.scale);
+        s_tz[16 + 4 * g + r][c] = (uint16_t)bf16_rne_bits(dz[4 + r] * a.scale);
+        s_tp[4 * g + r][c] = (uint16_t)bf16_rne_bits(p[r]);
+        s_tp[16 + 4 * g + r][c] = (uint16_t)bf16_rne_bits(p[4 + r]);
+      }
+      // ---- dq^T += K^T dZ^T: dZ^T from the accumulator layout (k-slot 8g + i of the B
+      // operand is row 4g + i, then 16 + 4g + i - 4), K^T by 8x8 transposes of LDS rows
+      u32x4_t zb;
+      zb[0] = pack_bf16_rne(dz[0], dz[1]);
+      zb[1] = pack_bf16_rne(dz[2], dz[3]);
+      zb[2] = pack_bf16_rne(dz[4], dz[5]);
+      zb[3] = pack_bf16_rne(dz[6], dz[7]);
+      {
+        u32x4_t vr[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[4 * g + j][128 * wave + 8 * c]);
+          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[16 + 4 * g + j][128 * wave + 8 * c]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          u32x4_t av;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) av[pp] = __builtin_amdgcn_perm(vr[2 * pp + 1][w], vr[2 * pp][w], sel);
+          oq[e] = mfma_bf16_16x16x32(av, zb, oq[e]);
+        }
+      }
+      if constexpr (kRope) {   // columns 512 + 8 m + e for m = c < 8; phases e = 2 wave + i
+        // (the two phases of a wave are the two halves of dword `wave` of the 8 columns)
+        uint32_t vw[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vw[j] = *reinterpret_cast<const uint32_t*>(&s_rows[4 * g + j][kBwdDV + 8 * (c & 7) + 2 * wave]);
+          vw[4 + j] = *reinterpret_cast<const uint32_t*>(&s_rows[16 + 4 * g + j][kBwdDV + 8 * (c & 7) + 2 * wave]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t sel = i ? 0x07060302u : 0x05040100u;
+          u32x4_t av;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) av[pp] = c < 8 ? __builtin_amdgcn_perm(vw[2 * pp + 1], vw[2 * pp], sel) : 0u;
+          o4[i] = mfma_bf16_16x16x32(av, zb, o4[i]);
+        }
+      }
+      lds_barrier();
+      // ---- dKV^T = Q^T (scale dZ) + dO^T P over the 16 heads; row 16 nt + c of this lane
+      int32_t rs[2];
+      u32x2_t bz[2], bp[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int j = jb + 16 * nt + c;
+        rs[nt] = j < pass_n ? s_slot[j] : -1;
+        bz[nt] = *reinterpret_cast<const u32x2_t*>(&s_tz[16 * nt + c][4 * g]);
+        bp[nt] = *reinterpret_cast<const u32x2_t*>(&s_tp[16 * nt + c][4 * g]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m0 = wave * D4 + 16 * mt;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          f32x4_t acc = mfma_bf16_16x16x16(qta[mt], bz[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
+          if (m0 < kBwdDV) acc = mfma_bf16_16x16x16(dota[mt], bp[nt], acc);
+          if (rs[nt] >= 0) {
+            float* dst = a.dkv + (int64_t)rs[nt] * DQK + m0 + 4 * g;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dst + r, acc[r]);
+          }
+        }
+      }
+    }
+    __syncthreads();   // every wave is done with this pass's slots
+  }
+
+  // ---- dq: lane (c = head, g) holds columns 128 wave + 8 (4g + r) + e (and the RoPE phases)
+  float* dqh = a.dq + (int64_t)t * a.ld_dq + (int64_t)(head0 + c) * DQK;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    f32x4_t v0, v1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v0[e] = oq[e][r] * a.scale; v1[e] = oq[4 + e][r] * a.scale; }
+    float* d = dqh + 128 * wave + 8 * (4 * g + r);
+    *reinterpret_cast<f32x4_t*>(d) = v0;
+    *reinterpret_cast<f32x4_t*>(d + 4) = v1;
+  }
+  if constexpr (kRope) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      if (m < 8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dqh[kBwdDV + 8 * m + 2 * wave + i] = o4[i][r] * a.scale;
+      }
+    }
+  }
+}
+
+hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  const dim3 grid(a.H / 16, T);
+  if (d_qk == 576) launch_kernel(k_sparse_mla_bwd<576>, grid, dim3(256), st, a);
+  else launch_kernel(k_sparse_mla_bwd<512>, grid, dim3(256), st, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -183,6 +183,36 @@ dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cach
                                   const dsa_attn_opts* opts, void* workspace, size_t ws_bytes,
                                   void* stream);
 
+/* ---------------------------------------------------------------- backward of step 3
+ * The gradient of step 3 for training (radixark/miles PR 3608, section "What": dq, and dKV
+ * added atomically through the listed indices; the backward takes the forward's lse with the
+ * sink folded in). One list into one bf16 cache. With l_i = softmax_scale * q[t,h] . c_i,
+ * p_i = e^(l_i - lse[t,h]) and D = dout[t,h] . out[t,h]:
+ *   dq[t,h]      = softmax_scale * sum_i p_i (dout[t,h] . c_i[0:d_v] - D) c_i[0:d_qk]
+ *   dkv[slot_i] += softmax_scale * p_i (dout[t,h] . c_i[0:d_v] - D) q[t,h]   (columns 0:d_qk)
+ *                + p_i dout[t,h]                                             (columns 0:d_v)
+ *   dsink[h]    += -e^(sink[h] - lse[t,h]) D
+ * summed over heads and rows; -1 entries contribute nothing, an entry listed twice twice.
+ * q, kv, idx, rows: as in dsa_sparse_mla_prefill (rows names each row's request; row_len is
+ *      not read). out, lse: the forward's outputs for the same inputs and opts (lse base per
+ *      opts->lse_log2; its values are taken as given, so P is recomputed from them).
+ * dout: bf16 [T, H, d_v], row stride ld_dout (>= H*d_v, multiple of 8).
+ * dq:  fp32 [T, H, d_qk], row stride ld_dq (>= H*d_qk, multiple of 4), 16-byte aligned;
+ *      written.
+ * dkv: fp32 [kv->n_slots, d_qk] indexed by cache slot; ADDED TO by fp32 atomics in no fixed
+ *      order (the caller zeroes it first; the last bits vary between runs).
+ * dsink: fp32 [H] added to by atomics, or NULL; needs opts->sink.
+ * No workspace. Envelope: DSA_KV_BF16 cache; H multiple of 16; d_qk in {512, 576}; d_v = 512.
+ * Errors: DSA_ERR_ARG for null pointers, bad strides or alignment, dsink without a sink;
+ * DSA_ERR_UNSUPPORTED outside the envelope. */
+dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cache* kv,
+                                   const int32_t* idx, int64_t ld_idx, int32_t n_idx,
+                                   const dsa_rows* rows, int32_t H, int32_t d_qk, int32_t d_v,
+                                   float softmax_scale, const void* out, int64_t ld_out,
+                                   const float* lse, const void* dout, int64_t ld_dout,
+                                   const dsa_attn_opts* opts, float* dq, int64_t ld_dq,
+                                   float* dkv, float* dsink, void* stream);
+
 /* ---------------------------------------------------------------- fused layer
  * Steps 1-3 on one stream with no host sync: scores into the workspace, top-k, attention
  * over the selected positions. idx_out / lens_out (nullable) receive the selection as

@@ -96,3 +96,26 @@ def run_decode(prob, d=None):
                  sink=d.sink, lse_log2=d.lse_log2)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), lens.cpu().numpy()
+
+
+def run_backward(prob, dout, d=None, idx=None, with_dsink=False):
+    """Forward (one workgroup per row) for out and lse, then the backward. dout: float32 numpy
+    [T, H, d_v], rounded to bf16 here (the tests hand the same bf16 values to the oracle).
+    Returns (dq [T, H, d_qk], dkv [n_slots, d_qk], dsink [H] or None, dout as float64)."""
+    m = dsa()
+    d = d or upload(prob)
+    idx_main = d.idx_main if idx is None else idx
+    T, H = prob.T, prob.H
+    out = torch.full((T, H, prob.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, H), float("nan"), device="cuda")
+    m.dsa_sparse_mla_prefill(d.q, d.kv, idx_main, None, None, d.rows, H, prob.d_qk, prob.d_v,
+                             prob.softmax_scale, out, lse, sink=d.sink, lse_log2=d.lse_log2)
+    do = torch.from_numpy(np.ascontiguousarray(dout, dtype=np.float32)).to(torch.bfloat16).cuda()
+    dq = torch.full((T, H, prob.d_qk), float("nan"), device="cuda")
+    dkv = torch.zeros((int(d.kv.c.n_slots), prob.d_qk), device="cuda")
+    dsink = torch.zeros((H,), device="cuda") if with_dsink else None
+    m.dsa_sparse_mla_backward(d.q, d.kv, idx_main, d.rows, H, prob.d_qk, prob.d_v, prob.softmax_scale,
+                              out, lse, do, dq, dkv, dsink, sink=d.sink, lse_log2=d.lse_log2)
+    torch.cuda.synchronize()
+    return (dq.cpu().numpy(), dkv.cpu().numpy(), dsink.cpu().numpy() if with_dsink else None,
+            do.float().cpu().numpy().astype(np.float64))

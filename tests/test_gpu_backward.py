@@ -1,0 +1,96 @@
+"""Backward of the sparse attention on the GPU (dsa_sparse_mla_backward) against the fp64
+oracle's exact gradient (step 5 of the oracle's description).
+
+The kernel's inputs are bf16 and exact; what it rounds: P and scale * dZ to bf16 as MFMA
+operands (2^-9 relative per term), D from the forward's bf16 out, fp32 accumulation (and fp32
+atomics in any order for dkv). dq and dkv are held to 2% of the largest reference value of the
+(row, head) and of the whole dkv respectively (measured worst: 0.3% and 0.4%); the sink
+gradient to a bound derived from D's rounding (below)."""
+import numpy as np
+import pytest
+
+import oracle
+from dev import need_gpu, run_backward, say, upload, workload
+
+pytestmark = [pytest.mark.gpu, need_gpu]
+
+CASES = [
+    ("bf16_576_tail", dict(fmt="bf16", B=3, H=16, n_ctx=700, n_idx=96, pad="tail", n_pad=10)),
+    ("bf16_576_h64_two_passes", dict(fmt="bf16", B=2, H=64, n_ctx=3000, n_idx=2048, pad="shuffled", n_pad=100)),
+    ("bf16_512", dict(fmt="bf16", B=2, H=32, n_ctx=500, n_idx=70, d_nope=448, d_v=512, n_pad=0)),
+    ("bf16_sink_log2", dict(fmt="bf16", B=3, H=16, n_ctx=700, n_idx=96, pad="tail", n_pad=10,
+                            sink=True, lse_log2=True)),
+    ("bf16_all_padded", dict(fmt="bf16", B=2, H=16, n_ctx=300, n_idx=64, pad="all")),
+]
+
+
+def _reference(prob, idx, dout):
+    T, H = prob.T, prob.H
+    dq = np.zeros((T, H, prob.d_qk))
+    dkv = {}
+    dsink = np.zeros(H)
+    for t in range(T):
+        q_t, slots, drows, ds = oracle.attention_backward_row(prob, t, idx[t], dout[t])
+        dq[t] = q_t
+        for s, r in zip(slots.tolist(), drows[:, :prob.d_qk]):
+            dkv[s] = dkv.get(s, 0.0) + r
+        dsink += ds
+    return dq, dkv, dsink
+
+
+def _check(prob, idx, dout, dq, dkv, dsink=None):
+    dq_ref, dkv_ref, dsink_ref = _reference(prob, idx, dout)
+    err = np.abs(dq - dq_ref)
+    scale = np.abs(dq_ref).max(axis=2, keepdims=True)
+    worst = float((err / (scale + 1e-30)).max()) if dq_ref.size else 0.0
+    say("  dq: max err", float(err.max()), "worst relative to the (row, head) max", worst)
+    assert np.all(err <= 2e-2 * scale + 1e-5), "dq"
+    touched = np.zeros(dkv.shape[0], bool)
+    if dkv_ref:
+        slots = np.array(sorted(dkv_ref))
+        ref = np.stack([dkv_ref[s] for s in slots])
+        got = dkv[slots]
+        touched[slots] = True
+        e = np.abs(got - ref)
+        say("  dkv: max err", float(e.max()), "max |ref|", float(np.abs(ref).max()),
+            "frobenius rel", float(np.linalg.norm(got - ref) / np.linalg.norm(ref)))
+        assert np.all(e <= 2e-2 * np.abs(ref).max() + 1e-5), "dkv"
+    assert np.all(dkv[~touched] == 0.0), "dkv rows outside the lists changed"
+    if dsink is not None:
+        # dsink_h = -sum_t p_sink D with D = dout . out, and the kernel takes D from the forward's
+        # bf16 out (rounding error <= 2^-9 per element): |error| <= sum_t p_sink 2^-8 sum_d
+        # |dout| |out| (a factor 2 for the fp32 sum), which stays the same when D cancels
+        bound = np.zeros(prob.H)
+        sink = np.asarray(prob.sink, dtype=np.float64)
+        base = np.log(2.0) if getattr(prob, "lse_log2", False) else 1.0
+        for t in range(prob.T):
+            out_ref, lse_ref = oracle.attention_row(prob, t, idx[t])
+            p_sink = np.exp(sink - lse_ref * base)
+            bound += p_sink * 2.0 ** -8 * (np.abs(dout[t]) * np.abs(out_ref)).sum(axis=1)
+        say("  dsink: max err", float(np.abs(dsink - dsink_ref).max()), "bound", float(bound.max()))
+        assert np.all(np.abs(dsink - dsink_ref) <= bound + 2.0 ** -8 * np.abs(dsink_ref) + 1e-5), "dsink"
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_backward(name, kw):
+    prob = workload("attention_case", **kw)
+    say("backward", name)
+    rng = np.random.default_rng(len(name))
+    dout = rng.standard_normal((prob.T, prob.H, prob.d_v)).astype(np.float32)
+    with_dsink = getattr(prob, "sink", None) is not None
+    dq, dkv, dsink, do = run_backward(prob, dout, with_dsink=with_dsink)
+    _check(prob, prob.idx_main, do, dq, dkv, dsink)
+
+
+def test_backward_repeated_entry():
+    """An entry listed twice contributes twice (to the softmax and to dKV)."""
+    import torch
+    prob = workload("attention_case", fmt="bf16", B=2, H=16, n_ctx=400, n_idx=40, n_pad=0)
+    idx = prob.idx_main.copy()
+    idx[:, 5] = idx[:, 3]
+    say("backward repeated entry")
+    d = upload(prob)
+    rng = np.random.default_rng(3)
+    dout = rng.standard_normal((prob.T, prob.H, prob.d_v)).astype(np.float32)
+    dq, dkv, _, do = run_backward(prob, dout, d=d, idx=torch.from_numpy(idx).cuda())
+    _check(prob, idx, do, dq, dkv)
