@@ -19,10 +19,11 @@
 //     operand and K^T from an 8x8 transpose of LDS rows in registers (the forward's value
 //     product); each wave owns 128 columns, the 64 RoPE columns are shared out in pairs of
 //     column phases;
-//   * dKV^T = Q^T (scale dZ) + dO^T P over the 16 heads (16x16x16 MFMAs, k = heads): dZ and P
-//     cross lanes once through LDS into the B layout, Q^T and dO^T are A operands built once
-//     per workgroup; each wave owns a quarter of the columns, and the 32 x d_qk block goes
-//     to memory by fp32 atomic adds (rows of padding entries are skipped).
+//   * dKV = (scale dZ)^T Q + P^T dO over the 16 heads (16x16x16 MFMAs, k = heads): dZ and P
+//     cross lanes once through LDS into the A layout, Q and dO are B operands built once per
+//     workgroup; each wave owns a quarter of the columns, and the 32 x d_qk block goes to
+//     memory by fp32 atomic adds, 16 consecutive columns of 4 rows per instruction (rows of
+//     padding entries are skipped).
 // One block in flight per workgroup.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
     dob[kb] = *reinterpret_cast<const u32x4_t*>(s_do + c * DOS + 256 * (wave & 1) + 32 * kb + 8 * g);
-  // A operands of dKV^T (m = this wave's columns, k = the 16 heads): Q^T and dO^T
+  // B operands of dKV (k = the 16 heads, n = this wave's columns): Q and dO
   u32x2_t qta[MT], dota[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -299,28 +300,29 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
         }
       }
       lds_barrier();
-      // ---- dKV^T = Q^T (scale dZ) + dO^T P over the 16 heads; row 16 nt + c of this lane
-      int32_t rs[2];
+      // ---- dKV = (scale dZ)^T Q + P^T dO over the 16 heads (m = rows, n = this wave's
+      // columns): lane (c, g) ends with rows 16 nt + 4g + r of column m0 + c, so one atomic
+      // instruction covers 4 rows x 16 consecutive columns
+      int32_t rs[2][4];
       u32x2_t bz[2], bp[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int j = jb + 16 * nt + c;
-        rs[nt] = j < pass_n ? s_slot[j] : -1;
         bz[nt] = *reinterpret_cast<const u32x2_t*>(&s_tz[16 * nt + c][4 * g]);
         bp[nt] = *reinterpret_cast<const u32x2_t*>(&s_tp[16 * nt + c][4 * g]);
+        const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + 16 * nt + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rs[nt][r] = jb + 16 * nt + 4 * g + r < pass_n ? (int32_t)sv[r] : -1;
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m0 = wave * D4 + 16 * mt;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          f32x4_t acc = mfma_bf16_16x16x16(qta[mt], bz[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
-          if (m0 < kBwdDV) acc = mfma_bf16_16x16x16(dota[mt], bp[nt], acc);
-          if (rs[nt] >= 0) {
-            float* dst = a.dkv + (int64_t)rs[nt] * DQK + m0 + 4 * g;
+          f32x4_t acc = mfma_bf16_16x16x16(bz[nt], qta[mt], f32x4_t{0.f, 0.f, 0.f, 0.f});
+          if (m0 < kBwdDV) acc = mfma_bf16_16x16x16(bp[nt], dota[mt], acc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dst + r, acc[r]);
-          }
+          for (int r = 0; r < 4; ++r)
+            if (rs[nt][r] >= 0) unsafeAtomicAdd(a.dkv + (int64_t)rs[nt][r] * DQK + m0 + c, acc[r]);
         }
       }
     }
