@@ -19,11 +19,11 @@
 //     operand and K^T from an 8x8 transpose of LDS rows in registers (the forward's value
 //     product); each wave owns 128 columns, the 64 RoPE columns are shared out in pairs of
 //     column phases;
-//   * dKV = (scale dZ)^T Q + P^T dO over the 16 heads (16x16x16 MFMAs, k = heads): dZ and P
+//   * dKV = (scale dZ)^T Q + P^T dO over the 16 heads (32x32x8 MFMAs, k = heads): dZ and P
 //     cross lanes once through LDS into the A layout, Q and dO are B operands built once per
-//     workgroup; each wave owns a quarter of the columns, and the 32 x d_qk block goes to
-//     memory by fp32 atomic adds, 16 consecutive columns of 4 rows per instruction (rows of
-//     padding entries are skipped).
+//     workgroup; the 32-column tiles are shared out over the waves, and the 32 x d_qk block
+//     goes to memory by fp32 atomic adds, 32 consecutive columns of 2 rows per instruction
+//     (rows of padding entries are skipped). The atomics bound the kernel.
 // One block in flight per workgroup.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -45,6 +45,14 @@ __device__ __forceinline__ f32x4_t mfma_bf16_16x16x16(u32x2_t a, u32x2_t b, f32x
                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
 }
 
+// 32x32x8 bf16 MFMA: lane l supplies A[l%32][4(l/32)+j] and B[4(l/32)+j][l%32] (j = 0..3) and
+// receives C[8(r/4) + 4(l/32) + r%4][l%32] in accumulator r = 0..15.
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+__device__ __forceinline__ f32x16_t mfma_bf16_32x32x8(u32x2_t a, u32x2_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                  __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t lds_u16(const uint16_t* p) { return *p; }
 
 }  // namespace
@@ -56,10 +64,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   constexpr int RE = DQK + 8;                 // padded bf16 row in LDS
   constexpr int KS = DQK / 32;                // k-steps of the score product
   constexpr int KQ = KS / 2;                  // per wave (split over the two halves)
-  constexpr int D4 = DQK / 4;                 // columns of dKV per wave
-  constexpr int MT = D4 / 16;                 // 16-column tiles of dKV per wave
+  constexpr int CT = DQK / 32;                // 32-column tiles of dKV
+  constexpr int CTW = (CT + NW - 1) / NW;     // per wave, at most
   constexpr bool kRope = DQK > kBwdDV;        // columns 512..575 (4 x 16) beyond the value
-  static_assert(KS % 2 == 0 && D4 % 16 == 0, "shapes");
+  static_assert(KS % 2 == 0 && DQK % 32 == 0, "shapes");
   __shared__ __align__(16) uint16_t s_rows[kBwdNB][RE];
   __shared__ __align__(16) int32_t s_slot[kBwdResolve];
   __shared__ const uint8_t* s_ra[kBwdNB];
@@ -132,19 +140,28 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
     dob[kb] = *reinterpret_cast<const u32x4_t*>(s_do + c * DOS + 256 * (wave & 1) + 32 * kb + 8 * g);
-  // B operands of dKV (k = the 16 heads, n = this wave's columns): Q and dO
-  u32x2_t qta[MT], dota[MT];
+  // B operands of dKV (k = the 16 heads in two steps of 8, n = 32 columns): Q and dO for the
+  // wave's column tiles ct0 .. ct0 + nct - 1 (tile counts (CT + 3 - w) / 4: 5, 5, 4, 4 of 18)
+  const int nct = (CT + NW - 1 - wave) / NW;
+  const int ct0 = wave * (CT / NW) + min(wave, CT % NW);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  u32x2_t qkb[CTW][2], dkb[CTW][2];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int col = wave * D4 + 16 * mt + c;
-    uint32_t h4[4], d4[4];
+  for (int k = 0; k < CTW; ++k) {
+    const int col = min(ct0 + k, CT - 1) * 32 + l32;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      h4[j] = lds_u16(s_q + (4 * g + j) * RE + col);
-      d4[j] = col < kBwdDV ? lds_u16(s_do + (4 * g + j) * DOS + col) : 0u;
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t h4[4], d4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int head = 8 * ks + 4 * hh + j;
+        h4[j] = lds_u16(s_q + head * RE + col);
+        d4[j] = col < kBwdDV ? lds_u16(s_do + head * DOS + col) : 0u;
+      }
+      qkb[k][ks] = u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
+      dkb[k][ks] = u32x2_t{d4[0] | (d4[1] << 16), d4[2] | (d4[3] << 16)};
     }
-    qta[mt] = u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
-    dota[mt] = u32x2_t{d4[0] | (d4[1] << 16), d4[2] | (d4[3] << 16)};
   }
   const float Dc = s_D[c];
   const float l2c = s_l2[c];
@@ -300,29 +317,36 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
         }
       }
       lds_barrier();
-      // ---- dKV = (scale dZ)^T Q + P^T dO over the 16 heads (m = rows, n = this wave's
-      // columns): lane (c, g) ends with rows 16 nt + 4g + r of column m0 + c, so one atomic
-      // instruction covers 4 rows x 16 consecutive columns
-      int32_t rs[2][4];
-      u32x2_t bz[2], bp[2];
+      // ---- dKV = (scale dZ)^T Q + P^T dO over the 16 heads (m = the 32 rows, n = 32 columns):
+      // accumulator r of lane l is row 8 (r / 4) + 4 hh + r % 4 and column tile * 32 + l32
+      u32x2_t az[2], ap[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        bz[nt] = *reinterpret_cast<const u32x2_t*>(&s_tz[16 * nt + c][4 * g]);
-        bp[nt] = *reinterpret_cast<const u32x2_t*>(&s_tp[16 * nt + c][4 * g]);
-        const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + 16 * nt + 4 * g]);
+      for (int ks = 0; ks < 2; ++ks) {
+        az[ks] = *reinterpret_cast<const u32x2_t*>(&s_tz[l32][8 * ks + 4 * hh]);
+        ap[ks] = *reinterpret_cast<const u32x2_t*>(&s_tp[l32][8 * ks + 4 * hh]);
+      }
+      int32_t rs[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) rs[nt][r] = jb + 16 * nt + 4 * g + r < pass_n ? (int32_t)sv[r] : -1;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = 8 * q4 + 4 * hh;
+        const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + r0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rs[4 * q4 + i] = jb + r0 + i < pass_n ? (int32_t)sv[i] : -1;
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m0 = wave * D4 + 16 * mt;
+      for (int k = 0; k < CTW; ++k) {
+        if (k < nct) {
+          const int col = (ct0 + k) * 32 + l32;
+          f32x16_t acc = {};
+          acc = mfma_bf16_32x32x8(az[0], qkb[k][0], acc);
+          acc = mfma_bf16_32x32x8(az[1], qkb[k][1], acc);
+          if ((ct0 + k) * 32 < kBwdDV) {
+            acc = mfma_bf16_32x32x8(ap[0], dkb[k][0], acc);
+            acc = mfma_bf16_32x32x8(ap[1], dkb[k][1], acc);
+          }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          f32x4_t acc = mfma_bf16_16x16x16(bz[nt], qta[mt], f32x4_t{0.f, 0.f, 0.f, 0.f});
-          if (m0 < kBwdDV) acc = mfma_bf16_16x16x16(bp[nt], dota[mt], acc);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (rs[nt][r] >= 0) unsafeAtomicAdd(a.dkv + (int64_t)rs[nt][r] * DQK + m0 + c, acc[r]);
+          for (int r = 0; r < 16; ++r)
+            if (rs[r] >= 0) unsafeAtomicAdd(a.dkv + (int64_t)rs[r] * DQK + col, acc[r]);
         }
       }
     }
