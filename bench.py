@@ -189,6 +189,49 @@ def other_configs(dsa, to_device, workloads, torch, dev, flush, names, reps=15):
     return res
 
 
+def attention_backward(dsa, workloads, torch, dev, reps=5):
+    """The attention backward (dq, dKV by fp32 atomics, one list) on 64 rows x 64 heads x 2048
+    listed rows (of 4096-token contexts, bf16 576 rows), after its forward: time, atomics and
+    MFMA-equivalent rate. Its cost depends on the listed rows, not on the context length."""
+    import numpy as np
+    from deepseek_sparse_attention_indexer_amd.upload import to_device
+    prob = workloads.attention_case(fmt="bf16", B=64, H=64, n_ctx=4096, n_idx=2048, pad="tail", n_pad=0)
+    d = to_device(prob, dev)
+    T, H = prob.T, prob.H
+    out = torch.empty(T, H, prob.d_v, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(T, H, device=dev)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    dout = torch.randn(T, H, prob.d_v, generator=g).to(torch.bfloat16).to(dev)
+    dq = torch.empty(T, H, prob.d_qk, device=dev)
+    dkv = torch.zeros(int(d.kv.c.n_slots), prob.d_qk, device=dev)
+    dsa.dsa_sparse_mla_prefill(d.q, d.kv, d.idx_main, None, None, d.rows, H, prob.d_qk, prob.d_v,
+                               prob.softmax_scale, out, lse)
+
+    def run():
+        dsa.dsa_sparse_mla_backward(d.q, d.kv, d.idx_main, d.rows, H, prob.d_qk, prob.d_v,
+                                    prob.softmax_scale, out, lse, dout, dq, dkv)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    dsa.dsa_profile_enable(True)
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    prof = dsa.dsa_profile_collect()
+    dsa.dsa_profile_enable(False)
+    us = prof["sparse_mla_bwd"]["total_ms"] / prof["sparse_mla_bwd"]["count"] * 1e3
+    pairs = int((np.asarray(prob.idx_main) >= 0).sum())
+    flops = pairs * H * 2 * (2 * prob.d_qk + prob.d_v + prob.d_qk + prob.d_v)
+    atomics = pairs * (H // 16) * prob.d_qk
+    return {"workload": "attention backward, 64 rows x 64 heads x 2048 of 4096 rows (bf16 576)",
+            "kernel": "sparse_mla_bwd", "avg_us": round(us, 1), "gflop": round(flops / 1e9, 2),
+            "achieved_tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "fp32_atomics": atomics, "atomics_per_s": round(atomics / (us * 1e-6) / 1e9, 1),
+            "bound": "fp32 atomics (one per row, column and 16-head group)",
+            "timing": "HIP events from each dispatch, inputs resident"}
+
+
 def cpu_baseline(prob, seconds):
     import numpy as np  # noqa: F401
     import oracle
@@ -220,6 +263,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the attention backward measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (32k, 1M fp8-key decode, DSv4 fp8 attention, multi-token)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -339,6 +383,9 @@ def main():
     if not args.no_prefill:
         log("prefill indexer ...")
         res["prefill_indexer"] = prefill_indexer(dsa, to_device, workloads, torch, dev)
+    if not args.no_backward:
+        log("attention backward ...")
+        res["attention_backward"] = attention_backward(dsa, workloads, torch, dev)
     if not args.no_configs:
         log("other workloads ...")
         res["other_configs"] = other_configs(dsa, to_device, workloads, torch, dev, flush,
