@@ -23,7 +23,7 @@ if not os.path.exists(lib_path()):
 _lib = C.CDLL(lib_path())
 
 DSA_OK, DSA_ERR_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
-ENTRY_TOPK, ENTRY_MLA_DECODE, ENTRY_MLA_PREFILL, ENTRY_DECODE = 1, 2, 3, 4
+ENTRY_TOPK, ENTRY_MLA_DECODE, ENTRY_MLA_PREFILL, ENTRY_DECODE, ENTRY_MLA_BACKWARD = 1, 2, 3, 4, 5
 KEY_BF16, KEY_FP8 = 0, 1
 KV_BF16, KV_FP8_UNIFORM, KV_FP8_DS_MLA, KV_FP8_UNIFORM_FNUZ = 0, 1, 2, 3
 
@@ -76,7 +76,7 @@ _sigs = {
                                C.POINTER(_AttnOpts), _P, _SZ, _P],
     "dsa_sparse_mla_backward": [_P, _I64, C.POINTER(_KVCache), _P, _I64, _I32, C.POINTER(_Rows), _I32,
                                 _I32, _I32, _F, _P, _I64, _P, _P, _I64, C.POINTER(_AttnOpts), _P,
-                                _I64, _P, _P, _P],
+                                _I64, _P, _P, _P, _SZ, _P],
     "dsa_decode": [_P, _I64, _P, _I64, _P, _I64, C.POINTER(_KeyCache), C.POINTER(_KVCache),
                    C.POINTER(_Rows), _I32, _I32, _I32, _I32, _I32, _I32, _F, _F, _P, _I64, _P,
                    C.POINTER(_AttnOpts), _P, _I64, _P, _P, _SZ, _P],
@@ -94,7 +94,7 @@ _lib.dsa_status_string.argtypes = [_I32]
 _lib.dsa_status_string.restype = C.c_char_p
 _lib.dsa_abi_version.argtypes = []
 _lib.dsa_abi_version.restype = _I32
-ABI_VERSION = 4   # the signatures above
+ABI_VERSION = 5   # the signatures above
 if _lib.dsa_abi_version() != ABI_VERSION:
     raise ImportError(f"{lib_path()} has ABI version {_lib.dsa_abi_version()}, this binding needs "
                       f"{ABI_VERSION}: rebuild the library")
@@ -327,14 +327,15 @@ def dsa_sparse_mla_prefill(q, kv: KVCache, idx, extra_kv: Optional[KVCache], ext
 
 
 def dsa_sparse_mla_backward(q, kv: KVCache, idx, rows: Rows, H: int, d_qk: int, d_v: int,
-                            softmax_scale: float, out, lse, dout, dq, dkv, dsink=None, stream=None,
-                            sink=None, lse_log2: bool = False):
+                            softmax_scale: float, out, lse, dout, dq, dkv, ws: "Workspace", dsink=None,
+                            stream=None, sink=None, lse_log2: bool = False):
     n_idx = int(idx.shape[1]) if idx is not None else 0
     _check(_lib.dsa_sparse_mla_backward(
         _ptr(q), _ld(q), C.byref(kv.c), _ptr(idx), _ld(idx) if idx is not None else 0, n_idx,
         C.byref(rows.c), int(H), int(d_qk), int(d_v), float(softmax_scale), _ptr(out), _ld(out),
         _ptr(lse), _ptr(dout), _ld(dout), _opts(sink, lse_log2), _ptr(dq), _ld(dq), _ptr(dkv),
-        _ptr(dsink), _stream(stream)), "dsa_sparse_mla_backward")
+        _ptr(dsink), ws.ptr if ws else None, ws.nbytes if ws else 0, _stream(stream)),
+        "dsa_sparse_mla_backward")
 
 
 def dsa_decode(q, q_idx, w, keys: KeyCache, kv: KVCache, rows: Rows, H: int, d_qk: int, d_v: int,

@@ -162,6 +162,12 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   return p;
 }
 
+// backward: bf16 scale * dZ and P per (row, listed entry, head), and the entries' slots
+int64_t mla_bwd_ws_bytes(int T, int H, int n_idx) {
+  const int64_t e = (int64_t)T * n_idx;
+  return align256(e * H * 2) * 2 + align256(e * 4);
+}
+
 int64_t mla_ws_bytes(int T, int H, int ntot, bool decode) {
   const MlaPlan p = plan_mla(T, H, ntot, decode);
   if (p.n_split <= 1) return 0;
@@ -473,7 +479,7 @@ dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
 // ==================================================================== exported entry points
 extern "C" {
 
-int32_t dsa_abi_version(void) { return 4; }
+int32_t dsa_abi_version(void) { return 5; }
 dsa_status dsa_kv_cache_write(const void* src, int64_t ld_src, int32_t n_tok, const int32_t* slots,
                               const dsa_kv_cache* kv, void* stream) {
   if (n_tok < 0 || !kv) return DSA_ERR_ARG;
@@ -576,6 +582,9 @@ size_t dsa_workspace_size(int32_t entry, const dsa_problem* p) {
       return (size_t)(kHeaderBytes + mla_ws_bytes(p->T, p->H, p->n_idx, true));
     case DSA_ENTRY_MLA_PREFILL:
       return 0;
+    case DSA_ENTRY_MLA_BACKWARD:
+      if (p->H % 16 || p->H > 128) return SIZE_MAX;
+      return (size_t)(kHeaderBytes + mla_bwd_ws_bytes(p->T, p->H, p->n_idx));
     case DSA_ENTRY_DECODE: {
       if (p->H % 16) return SIZE_MAX;
       const int64_t ld = logits_ld(p->n_max);
@@ -655,11 +664,12 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
                                    float softmax_scale, const void* out, int64_t ld_out,
                                    const float* lse, const void* dout, int64_t ld_dout,
                                    const dsa_attn_opts* opts, float* dq, int64_t ld_dq,
-                                   float* dkv, float* dsink, void* stream) {
+                                   float* dkv, float* dsink, void* workspace, size_t ws_bytes,
+                                   void* stream) {
   dsa_status st = check_rows(rows);
   if (st != DSA_OK) return st;
   if (H <= 0 || n_idx < 0) return DSA_ERR_ARG;
-  if (H % 16 || d_v != 512 || (d_qk != 512 && d_qk != 576)) return DSA_ERR_UNSUPPORTED;
+  if (H % 16 || H > 128 || d_v != 512 || (d_qk != 512 && d_qk != 576)) return DSA_ERR_UNSUPPORTED;
   if (!std::isfinite(softmax_scale)) return DSA_ERR_ARG;
   st = check_opts(opts);
   if (st != DSA_OK) return st;
@@ -676,6 +686,8 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
   if (n_idx > 0 && (!idx || !al4(idx) || ld_idx < n_idx)) return DSA_ERR_ARG;
   if (!dq || !al16(dq) || ld_dq < (int64_t)H * d_qk || ld_dq % 4) return DSA_ERR_ARG;
   if (!dkv || !al4(dkv)) return DSA_ERR_ARG;
+  const int64_t need = kHeaderBytes + mla_bwd_ws_bytes(T, H, n_idx);
+  if (!workspace || (int64_t)ws_bytes < need || !al16(workspace)) return DSA_ERR_WORKSPACE;
   MlaBwdArgs a;
   memset(&a, 0, sizeof(a));
   a.q = static_cast<const uint16_t*>(q);
@@ -700,8 +712,19 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
   a.ld_dq = ld_dq;
   a.dkv = dkv;
   a.dsink = dsink;
+  {
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    Carve cv;
+    const int64_t e = (int64_t)T * n_idx;
+    a.ws_dz = reinterpret_cast<uint16_t*>(w + cv.take(e * H * 2));
+    a.ws_p = reinterpret_cast<uint16_t*>(w + cv.take(e * H * 2));
+    a.ws_slot = reinterpret_cast<int32_t*>(w + cv.take(e * 4));
+  }
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  return hip_status(timed("sparse_mla_bwd", hs, [&] { return launch_sparse_mla_bwd(a, d_qk, T, hs); }));
+  dsa_status s = hip_status(timed("sparse_mla_bwd", hs, [&] { return launch_sparse_mla_bwd(a, d_qk, T, hs); }));
+  if (s == DSA_OK)
+    s = hip_status(timed("sparse_mla_bwd_dkv", hs, [&] { return launch_sparse_mla_bwd_dkv(a, d_qk, T, hs); }));
+  return s;
 }
 
 dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld_q_idx,

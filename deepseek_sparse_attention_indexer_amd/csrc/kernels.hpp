@@ -149,9 +149,13 @@ struct MlaBwdArgs {
   int64_t ld_dq;
   float* dkv;              // fp32 [n_slots, d_qk], added to
   float* dsink;            // fp32 [H], added to, or nullptr
+  uint16_t* ws_dz;         // workspace: bf16 [T, n_idx, H] softmax_scale * dZ
+  uint16_t* ws_p;          // workspace: bf16 [T, n_idx, H] P
+  int32_t* ws_slot;        // workspace: [T, n_idx] slots (-1: padding)
 };
 
 hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st);
+hipError_t launch_sparse_mla_bwd_dkv(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st);
 
 // cache writes: bf16 rows -> a cache format, one row per token at slots[token]
 enum { kCwBf16 = 0, kCwScaled = 1, kCwDsMla = 2, kCwScaledFnuz = 3 };

@@ -19,11 +19,15 @@
 //     operand and K^T from an 8x8 transpose of LDS rows in registers (the forward's value
 //     product); each wave owns 128 columns, the 64 RoPE columns are shared out in pairs of
 //     column phases;
-//   * dKV = (scale dZ)^T Q + P^T dO over the 16 heads (32x32x8 MFMAs, k = heads): dZ and P
-//     cross lanes once through LDS into the A layout, Q and dO are B operands built once per
-//     workgroup; the 32-column tiles are shared out over the waves, and the 32 x d_qk block
-//     goes to memory by fp32 atomic adds, 32 consecutive columns of 2 rows per instruction
-//     (rows of padding entries are skipped). The atomics bound the kernel.
+//   * scale dZ and P cross lanes once through LDS and go to a workspace as bf16 [row][head],
+//     with the rows' resolved slots.
+// A second kernel (k_sparse_mla_bwd_dkv) then forms dKV = (scale dZ)^T Q + P^T dO over ALL
+// heads of a query row at once (32x32x8 MFMAs, k = heads; q and dout are its B operands, held
+// in registers for the workgroup's column tiles), so that a listed row costs one fp32 atomic
+// add per column whatever the head count: the atomics bound the backward, and summing the
+// heads first divides them by H / 16. An atomic instruction covers 32 consecutive columns of
+// 2 rows; rows of padding entries are skipped. With 16 heads there is nothing to sum first, and
+// the first kernel adds dKV itself (same products, no workspace round trip).
 // One block in flight per workgroup.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -57,17 +61,19 @@ __device__ __forceinline__ uint32_t lds_u16(const uint16_t* p) { return *p; }
 
 }  // namespace
 
-template <int DQK>
+// FUSED: dKV of the workgroup's 16 heads added straight from this kernel (a single 16-head group
+// per row: nothing to sum first); else dZ and P go to the workspace for k_sparse_mla_bwd_dkv.
+template <int DQK, bool FUSED>
 __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   constexpr int NW = 4;
   constexpr int NT = 256;
   constexpr int RE = DQK + 8;                 // padded bf16 row in LDS
   constexpr int KS = DQK / 32;                // k-steps of the score product
   constexpr int KQ = KS / 2;                  // per wave (split over the two halves)
-  constexpr int CT = DQK / 32;                // 32-column tiles of dKV
-  constexpr int CTW = (CT + NW - 1) / NW;     // per wave, at most
   constexpr bool kRope = DQK > kBwdDV;        // columns 512..575 (4 x 16) beyond the value
-  static_assert(KS % 2 == 0 && DQK % 32 == 0, "shapes");
+  constexpr int CT = DQK / 32;                // 32-column tiles of dKV
+  constexpr int CTW = FUSED ? (CT + NW - 1) / NW : 1;   // per wave, at most
+  static_assert(KS % 2 == 0, "shapes");
   __shared__ __align__(16) uint16_t s_rows[kBwdNB][RE];
   __shared__ __align__(16) int32_t s_slot[kBwdResolve];
   __shared__ const uint8_t* s_ra[kBwdNB];
@@ -149,6 +155,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   u32x2_t qkb[CTW][2], dkb[CTW][2];
 #pragma unroll
   for (int k = 0; k < CTW; ++k) {
+    if constexpr (!FUSED) break;
     const int col = min(ct0 + k, CT - 1) * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -317,37 +324,55 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
         }
       }
       lds_barrier();
-      // ---- dKV = (scale dZ)^T Q + P^T dO over the 16 heads (m = the 32 rows, n = 32 columns):
-      // accumulator r of lane l is row 8 (r / 4) + 4 hh + r % 4 and column tile * 32 + l32
-      u32x2_t az[2], ap[2];
+      if constexpr (FUSED) {
+        // ---- dKV = (scale dZ)^T Q + P^T dO over the 16 heads (m = the 32 rows, n = 32 columns):
+        // accumulator r of lane l is row 8 (r / 4) + 4 hh + r % 4 and column tile * 32 + l32
+        u32x2_t az[2], ap[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        az[ks] = *reinterpret_cast<const u32x2_t*>(&s_tz[l32][8 * ks + 4 * hh]);
-        ap[ks] = *reinterpret_cast<const u32x2_t*>(&s_tp[l32][8 * ks + 4 * hh]);
-      }
-      int32_t rs[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int r0 = 8 * q4 + 4 * hh;
-        const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + r0]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rs[4 * q4 + i] = jb + r0 + i < pass_n ? (int32_t)sv[i] : -1;
-      }
-#pragma unroll
-      for (int k = 0; k < CTW; ++k) {
-        if (k < nct) {
-          const int col = (ct0 + k) * 32 + l32;
-          f32x16_t acc = {};
-          acc = mfma_bf16_32x32x8(az[0], qkb[k][0], acc);
-          acc = mfma_bf16_32x32x8(az[1], qkb[k][1], acc);
-          if ((ct0 + k) * 32 < kBwdDV) {
-            acc = mfma_bf16_32x32x8(ap[0], dkb[k][0], acc);
-            acc = mfma_bf16_32x32x8(ap[1], dkb[k][1], acc);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (rs[r] >= 0) unsafeAtomicAdd(a.dkv + (int64_t)rs[r] * DQK + col, acc[r]);
+        for (int ks = 0; ks < 2; ++ks) {
+          az[ks] = *reinterpret_cast<const u32x2_t*>(&s_tz[l32][8 * ks + 4 * hh]);
+          ap[ks] = *reinterpret_cast<const u32x2_t*>(&s_tp[l32][8 * ks + 4 * hh]);
         }
+        int32_t rs[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int r0 = 8 * q4 + 4 * hh;
+          const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + r0]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rs[4 * q4 + i] = jb + r0 + i < pass_n ? (int32_t)sv[i] : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < CTW; ++k) {
+          if (k < nct) {
+            const int col = (ct0 + k) * 32 + l32;
+            f32x16_t acc = {};
+            acc = mfma_bf16_32x32x8(az[0], qkb[k][0], acc);
+            acc = mfma_bf16_32x32x8(az[1], qkb[k][1], acc);
+            if ((ct0 + k) * 32 < kBwdDV) {
+              acc = mfma_bf16_32x32x8(ap[0], dkb[k][0], acc);
+              acc = mfma_bf16_32x32x8(ap[1], dkb[k][1], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (rs[r] >= 0) unsafeAtomicAdd(a.dkv + (int64_t)rs[r] * DQK + col, acc[r]);
+          }
+        }
+      } else {
+      // ---- scale dZ, P (bf16, [row][head] with the row's heads contiguous) and the slots to
+      // the workspace for the dKV kernel: 16 bytes (8 heads) per thread
+      if (threadIdx.x < 2 * 2 * kBwdNB) {
+        const int arr = threadIdx.x >> 6;              // 0: dZ, 1: P
+        const int row = (threadIdx.x >> 1) & (kBwdNB - 1);
+        const int half = threadIdx.x & 1;
+        const int j = jb + row;
+        if (j < pass_n) {
+          const uint16_t* src = arr ? &s_tp[row][8 * half] : &s_tz[row][8 * half];
+          uint16_t* dst = (arr ? a.ws_p : a.ws_dz) + ((int64_t)t * ntot + p0 + j) * a.H + head0 + 8 * half;
+          *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+        }
+      }
+      if (hg == 0 && threadIdx.x < kBwdNB && jb + (int)threadIdx.x < pass_n)
+        a.ws_slot[(int64_t)t * ntot + p0 + jb + threadIdx.x] = s_slot[jb + threadIdx.x];
       }
     }
     __syncthreads();   // every wave is done with this pass's slots
@@ -376,11 +401,111 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   }
 }
 
+// dKV of one query row over all its heads, for CG 32-column tiles: workgroup (tile group, row),
+// its 4 waves take every 4th 32-row block of the row's list. B operands (k = heads in steps of
+// 8, n = 32 columns): q and dout of the row, built once; A operands: scale dZ and P of the
+// block's 32 rows from the workspace (lane l: row l % 32, heads 8 ks + 4 (l / 32) .. + 3).
+template <int DQK, int HK>   // HK = H / 8 head steps
+__global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd_dkv(MlaBwdArgs a, int cg) {
+  constexpr int CT = DQK / 32;
+  constexpr int CGM = HK >= 16 ? 2 : 3;       // tiles per workgroup, at most (registers)
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int ct0 = blockIdx.x * cg;
+  const int nct = min(cg, CT - ct0);
+  const int ntot = a.n_idx;
+  u32x2_t qkb[CGM][HK], dkb[CGM][HK];
+  {
+    const uint16_t* qr = a.q + (int64_t)t * a.ld_q;
+    const uint16_t* dr = a.dout + (int64_t)t * a.ld_dout;
+#pragma unroll
+    for (int k = 0; k < CGM; ++k) {
+      const int col = min(ct0 + k, CT - 1) * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < HK; ++ks) {
+        uint32_t h4[4], d4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int head = 8 * ks + 4 * hh + j;
+          h4[j] = qr[(int64_t)head * DQK + col];
+          d4[j] = col < kBwdDV ? dr[(int64_t)head * kBwdDV + col] : 0u;
+        }
+        qkb[k][ks] = u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
+        dkb[k][ks] = u32x2_t{d4[0] | (d4[1] << 16), d4[2] | (d4[3] << 16)};
+      }
+    }
+  }
+  const int nb = (ntot + 31) / 32;
+  for (int blk = wave; blk < nb; blk += 4) {
+    const int r0 = blk * 32;
+    // this lane's A rows and the slots of the 16 rows its accumulators hold
+    const int ra = min(r0 + l32, ntot - 1);
+    const uint16_t* zr = a.ws_dz + ((int64_t)t * ntot + ra) * a.H + 4 * hh;
+    const uint16_t* pr = a.ws_p + ((int64_t)t * ntot + ra) * a.H + 4 * hh;
+    u32x2_t az[HK], ap[HK];
+#pragma unroll
+    for (int ks = 0; ks < HK; ++ks) {
+      az[ks] = *reinterpret_cast<const u32x2_t*>(zr + 8 * ks);
+      ap[ks] = *reinterpret_cast<const u32x2_t*>(pr + 8 * ks);
+    }
+    int32_t rs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      rs[r] = row < ntot ? a.ws_slot[(int64_t)t * ntot + row] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < CGM; ++k) {
+      if (k < nct) {
+        const int col = (ct0 + k) * 32 + l32;
+        f32x16_t acc = {};
+#pragma unroll
+        for (int ks = 0; ks < HK; ++ks) acc = mfma_bf16_32x32x8(az[ks], qkb[k][ks], acc);
+        if ((ct0 + k) * 32 < kBwdDV) {
+#pragma unroll
+          for (int ks = 0; ks < HK; ++ks) acc = mfma_bf16_32x32x8(ap[ks], dkb[k][ks], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (rs[r] >= 0) unsafeAtomicAdd(a.dkv + (int64_t)rs[r] * DQK + col, acc[r]);
+      }
+    }
+  }
+}
+
+template <int DQK>
+static void launch_dkv(const MlaBwdArgs& a, int T, hipStream_t st) {
+  constexpr int CT = DQK / 32;
+  const int hk = a.H / 8;
+  const int cg = hk >= 16 ? 2 : 3;
+  const dim3 grid((CT + cg - 1) / cg, T);
+  if (hk == 2) launch_kernel(k_sparse_mla_bwd_dkv<DQK, 2>, grid, dim3(256), st, a, cg);
+  else if (hk == 4) launch_kernel(k_sparse_mla_bwd_dkv<DQK, 4>, grid, dim3(256), st, a, cg);
+  else if (hk == 8) launch_kernel(k_sparse_mla_bwd_dkv<DQK, 8>, grid, dim3(256), st, a, cg);
+  else launch_kernel(k_sparse_mla_bwd_dkv<DQK, 16>, grid, dim3(256), st, a, cg);
+}
+
 hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const dim3 grid(a.H / 16, T);
-  if (d_qk == 576) launch_kernel(k_sparse_mla_bwd<576>, grid, dim3(256), st, a);
-  else launch_kernel(k_sparse_mla_bwd<512>, grid, dim3(256), st, a);
+  const bool fused = a.H == 16;
+  if (d_qk == 576) {
+    if (fused) launch_kernel(k_sparse_mla_bwd<576, true>, grid, dim3(256), st, a);
+    else launch_kernel(k_sparse_mla_bwd<576, false>, grid, dim3(256), st, a);
+  } else {
+    if (fused) launch_kernel(k_sparse_mla_bwd<512, true>, grid, dim3(256), st, a);
+    else launch_kernel(k_sparse_mla_bwd<512, false>, grid, dim3(256), st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_mla_bwd_dkv(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st) {
+  if (T <= 0 || a.n_idx <= 0 || a.H == 16) return hipSuccess;   // 16 heads: fused above
+  if (d_qk == 576) launch_dkv<576>(a, T, st);
+  else launch_dkv<512>(a, T, st);
   return hipGetLastError();
 }
 

@@ -202,16 +202,21 @@ dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cach
  * dkv: fp32 [kv->n_slots, d_qk] indexed by cache slot; ADDED TO by fp32 atomics in no fixed
  *      order (the caller zeroes it first; the last bits vary between runs).
  * dsink: fp32 [H] added to by atomics, or NULL; needs opts->sink.
- * No workspace. Envelope: DSA_KV_BF16 cache; H multiple of 16; d_qk in {512, 576}; d_v = 512.
+ * Two kernels: per (row, 16 heads) dq, and P and dZ into the workspace (bf16, 4 bytes per
+ * (row, entry, head), plus the entries' slots); then per row dKV over all heads, so that an
+ * entry costs one atomic per column whatever H is (H = 16: one kernel, the workspace unused).
+ * Workspace: dsa_workspace_size(DSA_ENTRY_MLA_BACKWARD, {T, H, n_idx}).
+ * Envelope: DSA_KV_BF16 cache; H a multiple of 16 up to 128; d_qk in {512, 576}; d_v = 512.
  * Errors: DSA_ERR_ARG for null pointers, bad strides or alignment, dsink without a sink;
- * DSA_ERR_UNSUPPORTED outside the envelope. */
+ * DSA_ERR_WORKSPACE for a missing or small workspace; DSA_ERR_UNSUPPORTED outside the envelope. */
 dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cache* kv,
                                    const int32_t* idx, int64_t ld_idx, int32_t n_idx,
                                    const dsa_rows* rows, int32_t H, int32_t d_qk, int32_t d_v,
                                    float softmax_scale, const void* out, int64_t ld_out,
                                    const float* lse, const void* dout, int64_t ld_dout,
                                    const dsa_attn_opts* opts, float* dq, int64_t ld_dq,
-                                   float* dkv, float* dsink, void* stream);
+                                   float* dkv, float* dsink, void* workspace, size_t ws_bytes,
+                                   void* stream);
 
 /* ---------------------------------------------------------------- fused layer
  * Steps 1-3 on one stream with no host sync: scores into the workspace, top-k, attention
@@ -230,7 +235,8 @@ typedef enum dsa_entry {
   DSA_ENTRY_TOPK = 1,
   DSA_ENTRY_MLA_DECODE = 2,
   DSA_ENTRY_MLA_PREFILL = 3,
-  DSA_ENTRY_DECODE = 4
+  DSA_ENTRY_DECODE = 4,
+  DSA_ENTRY_MLA_BACKWARD = 5
 } dsa_entry;
 
 /* Problem sizes the workspace depends on (unused fields may be 0). */

@@ -114,8 +114,9 @@ def run_backward(prob, dout, d=None, idx=None, with_dsink=False):
     dq = torch.full((T, H, prob.d_qk), float("nan"), device="cuda")
     dkv = torch.zeros((int(d.kv.c.n_slots), prob.d_qk), device="cuda")
     dsink = torch.zeros((H,), device="cuda") if with_dsink else None
+    ws = m.Workspace(m.dsa_workspace_size(m.ENTRY_MLA_BACKWARD, T=T, H=H, n_idx=int(idx_main.shape[1])))
     m.dsa_sparse_mla_backward(d.q, d.kv, idx_main, d.rows, H, prob.d_qk, prob.d_v, prob.softmax_scale,
-                              out, lse, do, dq, dkv, dsink, sink=d.sink, lse_log2=d.lse_log2)
+                              out, lse, do, dq, dkv, ws, dsink, sink=d.sink, lse_log2=d.lse_log2)
     torch.cuda.synchronize()
     return (dq.cpu().numpy(), dkv.cpu().numpy(), dsink.cpu().numpy() if with_dsink else None,
             do.float().cpu().numpy().astype(np.float64))
