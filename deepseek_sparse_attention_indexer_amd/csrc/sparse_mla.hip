@@ -167,11 +167,16 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   // bf16 rows: NBUF gathered blocks in LDS. fp8 rows: one bf16 block, plus NBUF raw blocks
   // (bytes as stored, data then scales) that the direct loads fill ahead of use
   constexpr bool kRaw = FMT != kFmtBf16;
+  // fp8_ds_mla with one head tile and four waves: no bf16 block; the score and value products
+  // convert their operands straight from the raw bytes (the scaled conversion is exact for
+  // the power-of-two scales), which saves the LDS-to-LDS pass and its barrier
+  constexpr bool kDirect = FMT == kFmtDsMla && HT == 1 && WD == 4;
   constexpr int BB = kNB * RE * 2;                            // bytes of one bf16 block
   constexpr int RDB = RawGeom<FMT, DQK>::kData;
   constexpr int RSB = RawGeom<FMT, DQK>::kScale;
   constexpr int RAWB = kNB * (RDB + RSB);                     // bytes of one raw block
-  constexpr int LDSB = kRaw ? BB + NBUF * RAWB : NBUF * BB;
+  constexpr int RAW0 = kDirect ? 0 : BB;                      // offset of the raw ring
+  constexpr int LDSB = kDirect ? NBUF * RAWB : (kRaw ? BB + NBUF * RAWB : NBUF * BB);
   static_assert(RDB % 16 == 0 && RSB % 4 == 0 && (kNB * RDB) % 1024 == 0, "raw staging");
   __shared__ __align__(16) uint8_t s_lds[LDSB];
   uint16_t (*const s_rows)[kNB][RE] = reinterpret_cast<uint16_t (*)[kNB][RE]>(s_lds);
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   // i.e. 16-byte chunk q = 64 ins + l = row q / (RDB / 16), chunk q % (RDB / 16); the scales
   // follow as dwords), one block ahead of its use
   auto gather_raw = [&](int buf) {   // the block in ring slot buf (addresses in s_ra[buf])
-    uint8_t* rb = s_lds + BB + buf * RAWB;
+    uint8_t* rb = s_lds + RAW0 + buf * RAWB;
     auto* lds_d = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(reinterpret_cast<uintptr_t>(rb) & 0xffffffffu);
     auto* lds_s = lds_d + kNB * RDB;
     constexpr int CPR = RDB / 16;                    // 16-byte chunks per row
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   // (the LDS reads of a batch of units go out before its first conversion; batches of three
   // keep the kernel at two waves per SIMD)
   auto dequant = [&](int buf, int jb) {
-    const uint8_t* rb = s_lds + BB + buf * RAWB;
+    const uint8_t* rb = s_lds + RAW0 + buf * RAWB;
     constexpr int QN = (kNB * UN + NT - 1) / NT;     // units per thread
     constexpr int QB = 3;                            // units per batch
 #pragma unroll
@@ -456,10 +461,26 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
     // the addresses of the block after it, into the slot this block's loads used (read by
     // the next iteration's loads, after its barrier)
     if (it + NBUF < nb && threadIdx.x < kNB) row_addrs(it % NBUF, jb + NBUF * kNB, threadIdx.x);
-    if constexpr (kRaw) {
+    if constexpr (kRaw && !kDirect) {
       dequant(it % NBUF, jb);
       lds_barrier();                     // bf16 rows complete; the loads just issued stay in flight
     }
+    // raw rows of this block (direct conversion): row r's data at rdb + r * RDB (448 fp8 NoPE
+    // bytes then 64 bf16 RoPE values), its UE8M0 scale bytes at rsb + r * RSB
+    const uint8_t* const rdb = s_lds + RAW0 + (it % NBUF) * RAWB;
+    const uint8_t* const rsb = rdb + kNB * RDB;
+    // 8 consecutive columns c0.. of raw row r as 8 bf16 (NoPE: 8 fp8 bytes times their group's
+    // scale; RoPE: read as stored)
+    auto raw8 = [&](int r, int c0) -> u32x4_t {
+      const uint8_t* rd = rdb + r * RDB;
+      if (c0 < 448) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(rd + c0);
+        const float sc = ue8m0_scale(rsb[r * RSB + (c0 >> 6)]);
+        return u32x4_t{fp8x2_to_bf16x2_pow2<false>(w[0], sc), fp8x2_to_bf16x2_pow2<true>(w[0], sc),
+                       fp8x2_to_bf16x2_pow2<false>(w[1], sc), fp8x2_to_bf16x2_pow2<true>(w[1], sc)};
+      }
+      return *reinterpret_cast<const u32x4_t*>(rd + 448 + 2 * (c0 - 448));
+    };
 
     // the block's row validity for the softmax (rows 4g..4g+3 and 16+4g..16+4g+3 of this lane),
     // read before the score product so the reads overlap it
@@ -473,7 +494,12 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
       const uint16_t* rp = &s_rows[cur][16 * (wave >> 1) + c][8 * g + 32 * kq0];
       f32x4_t sp = s0;
 #pragma unroll
-      for (int kb = 0; kb < KQ; ++kb) sp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 32 * kb), qb[kb], sp);
+      for (int kb = 0; kb < KQ; ++kb) {
+        if constexpr (kDirect)
+          sp = mfma_bf16_16x16x32(raw8(16 * (wave >> 1) + c, 8 * g + 32 * (kq0 + kb)), qb[kb], sp);
+        else
+          sp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 32 * kb), qb[kb], sp);
+      }
       s_sp[wave][lane] = sp;
       lds_barrier();
       s0 = s_sp[0][lane] + s_sp[1][lane];
@@ -532,10 +558,25 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
     for (int i = 0; i < GD; ++i) {
       const int gd = gd0 + i;
       u32x4_t vr[8];
+      if constexpr (kDirect) {
+        // rows of list padding give zero values (their weights are zero, and their bytes, read
+        // from slot 0, are not trusted to be finite)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * gd + 8 * c]);
-        vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * gd + 8 * c]);
+        for (int j = 0; j < 4; ++j) {
+          const bool ok0 = jm + j < pass_n && (int32_t)sl0[j] >= 0;
+          const bool ok1 = jm + 16 + j < pass_n && (int32_t)sl1[j] >= 0;
+          const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
+          const u32x4_t v0 = raw8(4 * g + j, 128 * gd + 8 * c);
+          const u32x4_t v1 = raw8(16 + 4 * g + j, 128 * gd + 8 * c);
+          vr[j] = ok0 ? v0 : z;
+          vr[4 + j] = ok1 ? v1 : z;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * gd + 8 * c]);
+          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * gd + 8 * c]);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
