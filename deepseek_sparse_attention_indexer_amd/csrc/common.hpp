@@ -21,6 +21,15 @@ __device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(u32x4_t a, u32x4_t b, f32x
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// 32x32x16 bf16 MFMA. Lane l supplies A[l%32][8(l/32)+j] and B[8(l/32)+j][l%32] (j = 0..7)
+// and receives C[8(r/4) + 4(l/32) + r%4][l%32] in accumulator r = 0..15; verified on gfx950 by
+// an in-bounds probe against a host product.
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+__device__ __forceinline__ f32x16_t mfma_bf16_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // Paging of a token cache, resolved on the host into device-friendly fields.
 struct Paging {
   const int32_t* bt;      // block table or nullptr

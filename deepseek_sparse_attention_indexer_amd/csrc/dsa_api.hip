@@ -137,8 +137,7 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   // rows (16 or more) there is enough parallelism to share each gathered block among 64
   // heads instead (a quarter of the gathers), one workgroup per CU, splits only to reach
   // one workgroup per CU. Prefill rows have no split; all heads of a row share each block.
-  // A workgroup that walks more than two blocks keeps three in flight (ring of four) when it
-  // holds all of a CU anyway (64 heads: the registers allow one workgroup per CU).
+  // Blocks stream through a ring of two.
   MlaPlan p;
   const int tiles = H / 16;
   const int nblk = std::max(1, (ntot + 31) / 32);
@@ -158,7 +157,7 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   const int bps = (nblk + s - 1) / s;           // blocks per split
   p.rows_per_split = bps * 32;
   p.n_split = (nblk + bps - 1) / bps;
-  p.nbuf = (p.ht == 4 && bps > 2) ? 4 : 2;
+  p.nbuf = 2;
   return p;
 }
 

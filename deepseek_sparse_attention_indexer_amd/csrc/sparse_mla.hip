@@ -12,7 +12,11 @@
 //
 // Workgroup = HT x WD waves sharing each gathered 32-row block: a wave owns 16 heads (one of
 // HT head tiles) and 512 / WD value columns (decode runs one head tile with WD = 4, so four
-// waves issue the gather and the PV product and the score product is repeated per wave).
+// waves issue the gather and the PV product and the score product is split over the waves).
+// 64 heads (HT = 4) take 32x32x16 MFMAs instead: wave w owns 32 heads (half w & 1) and 256
+// value columns (half w >> 1); the two waves of a head half split the score product's
+// contraction and swap partials through LDS. Each block is then read from LDS half as often
+// as with 16 heads per wave.
 // Blocks stream through a ring of NBUF buffers in LDS: while a block is computed, the next
 // NBUF - 1 blocks' rows are in flight (direct global->LDS loads; bf16 rows land in place, fp8
 // rows land as raw bytes and are dequantised to one bf16 block just before use). Each wave
@@ -400,19 +404,36 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   constexpr int KQ = kSplitK ? KS / 2 : KS;          // k-steps of the score product per wave
   const int kq0 = kSplitK ? (wave & 1) * KQ : 0;     // this wave's first k-step
   __shared__ f32x4_t s_sp[kSplitK ? 4 : 1][64];      // the partials
-  u32x4_t qb[KQ];
-  {
+  // 64 heads, 32x32x16 MFMAs (see the top): lane l of wave w is head 32 hh + l32 of the
+  // workgroup's 64 and reads k-slots 8 hl .. 8 hl + 7; the wave's half of the contraction is
+  // k-steps kq32 .. kq32 + KQ32 - 1 (16 columns each)
+  constexpr bool kW32 = HT == 4 && WD == 1;
+  constexpr int KQ32 = DQK / 32;                      // k-steps of 16 per wave (half of DQK / 16)
+  const int hh = wave & 1, vh = wave >> 1;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int kq32 = vh * KQ32;
+  __shared__ f32x4_t s_sp32[kW32 ? 4 : 1][4][64];    // the score partials, 16 floats per lane
+  u32x4_t qb[kW32 ? 1 : KQ];
+  u32x4_t qb32[kW32 ? KQ32 : 1];
+  if constexpr (kW32) {
+    const uint16_t* qp = &s_rows[0][0][0] + (32 * hh + l32) * RE + 8 * hl;
+#pragma unroll
+    for (int kb = 0; kb < KQ32; ++kb) qb32[kb] = *reinterpret_cast<const u32x4_t*>(qp + 16 * (kq32 + kb));
+  } else {
     const uint16_t* qp = &s_rows[0][0][0] + (ht * 16 + c) * RE + 8 * g;
 #pragma unroll
     for (int kb = 0; kb < KQ; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(qp + 32 * (kq0 + kb));
   }
-  float m_run = -INFINITY;   // running max (base-2 units) of head c; rescaled lazily
+  float m_run = -INFINITY;   // running max (base-2 units) of this lane's head; rescaled lazily
   float l_run = 0.f;         // lane-partial sum of exp2(s - m_run)
-  f32x4_t o[GD][8];
+  f32x4_t o[kW32 ? 1 : GD][8];
+  f32x16_t o32[kW32 ? 8 : 1];
 #pragma unroll
-  for (int i = 0; i < GD; ++i)
+  for (int i = 0; i < (kW32 ? 1 : GD); ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[i][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < (kW32 ? 8 : 1); ++e) o32[e] = f32x16_t{};
 
   __syncthreads();   // q is in registers before the first rows land in the buffers
   // loads this wave issues per block (instructions of a block are dealt round-robin to the
@@ -488,109 +509,216 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
     const u32x4_t sl0 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm]);
     const u32x4_t sl1 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm + 16]);
 
-    // ---- S^T = K Q^T
-    f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-    if constexpr (kSplitK) {
-      const uint16_t* rp = &s_rows[cur][16 * (wave >> 1) + c][8 * g + 32 * kq0];
-      f32x4_t sp = s0;
+    if constexpr (kW32) {
+      // ---- S^T partial over this wave's half of the contraction: 32 rows x 32 heads
+      f32x16_t sp = {};
+      {
+        const uint16_t* rp = &s_rows[cur][l32][8 * hl + 16 * kq32];
 #pragma unroll
-      for (int kb = 0; kb < KQ; ++kb) {
-        if constexpr (kDirect)
-          sp = mfma_bf16_16x16x32(raw8(16 * (wave >> 1) + c, 8 * g + 32 * (kq0 + kb)), qb[kb], sp);
-        else
-          sp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 32 * kb), qb[kb], sp);
+        for (int kb = 0; kb < KQ32; ++kb) sp = mfma_bf16_32x32x16(*reinterpret_cast<const u32x4_t*>(rp + 16 * kb), qb32[kb], sp);
       }
-      s_sp[wave][lane] = sp;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s_sp32[wave][q][lane] = f32x4_t{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]};
+      // rows of accumulator r: 8 (r / 4) + 4 hl + r % 4; their validity
+      u32x4_t slq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) slq[q] = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + 8 * q + 4 * hl]);
       lds_barrier();
-      s0 = s_sp[0][lane] + s_sp[1][lane];
-      s1 = s_sp[2][lane] + s_sp[3][lane];
+      float p[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t o4 = s_sp32[wave ^ 2][q][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = jb + 8 * q + 4 * hl + i;
+          const bool ok = row < pass_n && (int32_t)slq[q][i] >= 0;
+          const float x = ok ? (sp[4 * q + i] + o4[i]) * a.scale_log2 : -INFINITY;
+          p[4 * q + i] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__any(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        if (m_run != -INFINITY || __any(l_run != 0.f)) {
+          l_run *= alpha;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o32[e] *= alpha;
+        }
+        m_run = m_new;
+      }
+      const bool none = m_run == -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = none ? 0.f : exp2f(p[i] - m_run);
+        l_run += p[i];
+      }
+      // ---- O^T += V^T P^T over this wave's 256 value columns, two k-steps of 16 rows. k-slot
+      // 8 hl + j of k-step ks is row 16 ks + 4 hl + j (j < 4) or 16 ks + 8 + 4 hl + j - 4: the
+      // accumulator rows of S^T, so P^T needs no lane exchange; V^T by 8x8 transposes of LDS
+      // rows (m-tile e = columns 256 vh + 8 m + e)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4_t pb;
+        pb[0] = pack_bf16_rne(p[8 * ks], p[8 * ks + 1]);
+        pb[1] = pack_bf16_rne(p[8 * ks + 2], p[8 * ks + 3]);
+        pb[2] = pack_bf16_rne(p[8 * ks + 4], p[8 * ks + 5]);
+        pb[3] = pack_bf16_rne(p[8 * ks + 6], p[8 * ks + 7]);
+        u32x4_t vr[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = 16 * ks + (j < 4 ? 4 * hl + j : 8 + 4 * hl + j - 4);
+          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][row][256 * vh + 8 * l32]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          u32x4_t av;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) av[pp] = __builtin_amdgcn_perm(vr[2 * pp + 1][w], vr[2 * pp][w], sel);
+          o32[e] = mfma_bf16_32x32x16(av, pb, o32[e]);
+        }
+      }
     } else {
-      const uint16_t* r0 = &s_rows[cur][c][8 * g];
-      const uint16_t* r1 = &s_rows[cur][16 + c][8 * g];
-#pragma unroll
-      for (int kb = 0; kb < KS; ++kb) {
-        s0 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r0 + 32 * kb), qb[kb], s0);
-        s1 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r1 + 32 * kb), qb[kb], s1);
-      }
-    }
-    // ---- online softmax (base 2); the accumulators are rescaled only when some head's max
-    // grows by more than 2^8, so exp2(s - m_run) stays <= 256
-    float p[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok0 = jm + r < pass_n && (int32_t)sl0[r] >= 0;
-      const bool ok1 = jm + 16 + r < pass_n && (int32_t)sl1[r] >= 0;
-      const float x0 = ok0 ? s0[r] * a.scale_log2 : -INFINITY;
-      const float x1 = ok1 ? s1[r] * a.scale_log2 : -INFINITY;
-      p[r] = x0;
-      p[4 + r] = x1;
-      mx = fmaxf(mx, fmaxf(x0, x1));
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (__any(mx > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-      if (m_run != -INFINITY || __any(l_run != 0.f)) {   // nothing to rescale before the first rows
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < GD; ++i)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[i][e] *= alpha;
-      }
-      m_run = m_new;
-    }
-    const bool none = m_run == -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = none ? 0.f : exp2f(p[i] - m_run);
-      l_run += p[i];
-    }
-    u32x4_t pb;
-    pb[0] = pack_bf16_rne(p[0], p[1]);
-    pb[1] = pack_bf16_rne(p[2], p[3]);
-    pb[2] = pack_bf16_rne(p[4], p[5]);
-    pb[3] = pack_bf16_rne(p[6], p[7]);
-    // ---- O^T += V^T P^T over this wave's value columns; V^T tiles come from 8 rows x 8
-    // consecutive columns, transposed in registers
-#pragma unroll
-    for (int i = 0; i < GD; ++i) {
-      const int gd = gd0 + i;
-      u32x4_t vr[8];
-      if constexpr (kDirect) {
-        // rows of list padding give zero values (their weights are zero, and their bytes, read
-        // from slot 0, are not trusted to be finite)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool ok0 = jm + j < pass_n && (int32_t)sl0[j] >= 0;
-          const bool ok1 = jm + 16 + j < pass_n && (int32_t)sl1[j] >= 0;
-          const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
-          const u32x4_t v0 = raw8(4 * g + j, 128 * gd + 8 * c);
-          const u32x4_t v1 = raw8(16 + 4 * g + j, 128 * gd + 8 * c);
-          vr[j] = ok0 ? v0 : z;
-          vr[4 + j] = ok1 ? v1 : z;
+    // ---- S^T = K Q^T
+      f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      if constexpr (kSplitK) {
+        const uint16_t* rp = &s_rows[cur][16 * (wave >> 1) + c][8 * g + 32 * kq0];
+        f32x4_t sp = s0;
+  #pragma unroll
+        for (int kb = 0; kb < KQ; ++kb) {
+          if constexpr (kDirect)
+            sp = mfma_bf16_16x16x32(raw8(16 * (wave >> 1) + c, 8 * g + 32 * (kq0 + kb)), qb[kb], sp);
+          else
+            sp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 32 * kb), qb[kb], sp);
         }
+        s_sp[wave][lane] = sp;
+        lds_barrier();
+        s0 = s_sp[0][lane] + s_sp[1][lane];
+        s1 = s_sp[2][lane] + s_sp[3][lane];
       } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * gd + 8 * c]);
-          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * gd + 8 * c]);
+        const uint16_t* r0 = &s_rows[cur][c][8 * g];
+        const uint16_t* r1 = &s_rows[cur][16 + c][8 * g];
+  #pragma unroll
+        for (int kb = 0; kb < KS; ++kb) {
+          s0 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r0 + 32 * kb), qb[kb], s0);
+          s1 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r1 + 32 * kb), qb[kb], s1);
         }
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t av;
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) av[pp] = __builtin_amdgcn_perm(vr[2 * pp + 1][w], vr[2 * pp][w], sel);
-        o[i][e] = mfma_bf16_16x16x32(av, pb, o[i][e]);
+      // ---- online softmax (base 2); the accumulators are rescaled only when some head's max
+      // grows by more than 2^8, so exp2(s - m_run) stays <= 256
+      float p[8];
+      float mx = -INFINITY;
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok0 = jm + r < pass_n && (int32_t)sl0[r] >= 0;
+        const bool ok1 = jm + 16 + r < pass_n && (int32_t)sl1[r] >= 0;
+        const float x0 = ok0 ? s0[r] * a.scale_log2 : -INFINITY;
+        const float x1 = ok1 ? s1[r] * a.scale_log2 : -INFINITY;
+        p[r] = x0;
+        p[4 + r] = x1;
+        mx = fmaxf(mx, fmaxf(x0, x1));
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__any(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        if (m_run != -INFINITY || __any(l_run != 0.f)) {   // nothing to rescale before the first rows
+          l_run *= alpha;
+  #pragma unroll
+          for (int i = 0; i < GD; ++i)
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) o[i][e] *= alpha;
+        }
+        m_run = m_new;
+      }
+      const bool none = m_run == -INFINITY;
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = none ? 0.f : exp2f(p[i] - m_run);
+        l_run += p[i];
+      }
+      u32x4_t pb;
+      pb[0] = pack_bf16_rne(p[0], p[1]);
+      pb[1] = pack_bf16_rne(p[2], p[3]);
+      pb[2] = pack_bf16_rne(p[4], p[5]);
+      pb[3] = pack_bf16_rne(p[6], p[7]);
+      // ---- O^T += V^T P^T over this wave's value columns; V^T tiles come from 8 rows x 8
+      // consecutive columns, transposed in registers
+  #pragma unroll
+      for (int i = 0; i < GD; ++i) {
+        const int gd = gd0 + i;
+        u32x4_t vr[8];
+        if constexpr (kDirect) {
+          // rows of list padding give zero values (their weights are zero, and their bytes, read
+          // from slot 0, are not trusted to be finite)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool ok0 = jm + j < pass_n && (int32_t)sl0[j] >= 0;
+            const bool ok1 = jm + 16 + j < pass_n && (int32_t)sl1[j] >= 0;
+            const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
+            const u32x4_t v0 = raw8(4 * g + j, 128 * gd + 8 * c);
+            const u32x4_t v1 = raw8(16 + 4 * g + j, 128 * gd + 8 * c);
+            vr[j] = ok0 ? v0 : z;
+            vr[4 + j] = ok1 ? v1 : z;
+          }
+        } else {
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * gd + 8 * c]);
+            vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * gd + 8 * c]);
+          }
+        }
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          u32x4_t av;
+  #pragma unroll
+          for (int pp = 0; pp < 4; ++pp) av[pp] = __builtin_amdgcn_perm(vr[2 * pp + 1][w], vr[2 * pp][w], sel);
+          o[i][e] = mfma_bf16_16x16x32(av, pb, o[i][e]);
+        }
       }
     }
   }
   }
 
+  if constexpr (kW32) {
+    // lane l holds head 32 hh + l32 (of the workgroup's 64), columns 256 vh + 8 m + e for
+    // m = 8 (r / 4) + 4 hl + r % 4 of accumulator r, e = 0..7
+    l_run += __shfl_xor(l_run, 32);
+    const int headw = hg * 64 + 32 * hh + l32;
+    if constexpr (!SPLIT) {
+      const Finish fin = finish_softmax(m_run, l_run, a.sink ? a.sink[headw] : -INFINITY, a.lse_log2);
+      uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)headw * kDV + 256 * vh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
+        u32x4_t v;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) v[e2] = pack_bf16_rne(o32[2 * e2][r] * fin.inv, o32[2 * e2 + 1][r] * fin.inv);
+        *reinterpret_cast<u32x4_t*>(op + 8 * m) = v;
+      }
+      if (a.lse && hl == 0 && vh == 0) a.lse[(int64_t)t * a.H + headw] = fin.lse;
+    } else {
+      float* po = a.part_o + (((int64_t)t * a.H + headw) * a.n_split + split) * kDV + 256 * vh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
+        *reinterpret_cast<f32x4_t*>(po + 8 * m) = f32x4_t{o32[0][r], o32[1][r], o32[2][r], o32[3][r]};
+        *reinterpret_cast<f32x4_t*>(po + 8 * m + 4) = f32x4_t{o32[4][r], o32[5][r], o32[6][r], o32[7][r]};
+      }
+      if (hl == 0 && vh == 0) {
+        float* pml = a.part_ml + (((int64_t)t * a.H + headw) * a.n_split + split) * 2;
+        pml[0] = m_run;
+        pml[1] = l_run;
+      }
+    }
+  } else {
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
@@ -657,6 +785,7 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
       pml[0] = m_run;
       pml[1] = l_run;
     }
+  }
   }
 }
 
@@ -754,15 +883,12 @@ static hipError_t launch_h(const MlaArgs& a, int T, hipStream_t st) {
   return hipGetLastError();
 }
 
-// ht head tiles per workgroup (ht == 1 splits the value columns over 4 waves instead); a ring
-// of 2 or 4 blocks
+// ht head tiles per workgroup (ht == 1 splits the value columns over 4 waves instead). Every
+// plan takes a ring of two blocks (nbuf): deeper rings measured slower once a second
+// workgroup per CU, or the 32-head layout, hides the gathers (the kernel keeps the parameter).
 template <int FMT, int DQK>
 static hipError_t launch_d(const MlaArgs& a, int ht, int nbuf, int T, hipStream_t st) {
-  if (nbuf > 2) {
-    if (ht == 4) return launch_h<FMT, DQK, 4, 1, 4>(a, T, st);
-    if (ht == 2) return launch_h<FMT, DQK, 2, 2, 4>(a, T, st);
-    return launch_h<FMT, DQK, 1, 4, 4>(a, T, st);
-  }
+  (void)nbuf;
   if (ht == 4) return launch_h<FMT, DQK, 4, 1, 2>(a, T, st);
   if (ht == 2) return launch_h<FMT, DQK, 2, 2, 2>(a, T, st);
   return launch_h<FMT, DQK, 1, 4, 2>(a, T, st);

@@ -51,7 +51,6 @@ __device__ __forceinline__ f32x4_t mfma_bf16_16x16x16(u32x2_t a, u32x2_t b, f32x
 
 // 32x32x8 bf16 MFMA: lane l supplies A[l%32][4(l/32)+j] and B[4(l/32)+j][l%32] (j = 0..3) and
 // receives C[8(r/4) + 4(l/32) + r%4][l%32] in accumulator r = 0..15.
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 __device__ __forceinline__ f32x16_t mfma_bf16_32x32x8(u32x2_t a, u32x2_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4_t, a),
                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
