@@ -138,6 +138,39 @@ def prefill_indexer(dsa, to_device, workloads, torch, dev, reps=5):
             "timing": "HIP events from each dispatch, inputs resident (8193 rows x 64 x 128 bf16)"}
 
 
+def calibration(torch, dev, reps=5):
+    """Measured ceilings beside the published ones: a plain device copy (HBM read + write) and a
+    dense bf16 GEMM from the vendor library (torch.mm on contiguous 8192^3 operands)."""
+    src = torch.ones(128 << 20, dtype=torch.float32, device=dev)       # 512 MiB
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = None
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best * 1e-3
+
+    t_copy = timed(lambda: dst.copy_(src))
+    t_mm = timed(lambda: torch.mm(a, b))
+    copy_gbs = 2 * src.numel() * 4 / t_copy / 1e9
+    gemm_tflops = 2 * 8192 ** 3 / t_mm / 1e12
+    del src, dst, a, b
+    return {"copy_GBps": round(copy_gbs, 1),
+            "copy": "device copy of 512 MiB (bytes read + written per second), best of 5",
+            "bf16_gemm_TFLOPs": round(gemm_tflops, 1),
+            "gemm": "torch.mm bf16 8192 x 8192 x 8192, contiguous, best of 5"}
+
+
 def other_configs(dsa, to_device, workloads, torch, dev, flush, names, reps=15):
     """Cold per-call latency of the other single-GPU workloads (context beside the headline):
     the fused layer for decode shapes, the attention stage alone for the DSv4 fp8 case."""
@@ -383,9 +416,16 @@ def main():
         "vs_baseline_note": "value / 411 us: the pages' Gluon 128k decode total (tokenspeed PR 627, "
                             "GFX9-class GPU, heads and precision unstated); context, not the target",
     }
+    log("measured ceilings ...")
+    cal = calibration(torch, dev)
+    cal["layer_frac_of_copy"] = round((ab["total"] / (cal["copy_GBps"] * 1e9)) / (cold * 1e-6), 4)
+    if achieved:
+        cal["roofline_kernel_frac_of_copy"] = round(achieved / cal["copy_GBps"], 4)
+    res["measured_ceilings"] = cal
     if not args.no_prefill:
         log("prefill indexer ...")
-        res["prefill_indexer"] = prefill_indexer(dsa, to_device, workloads, torch, dev)
+        res["prefill_indexer"] = pf = prefill_indexer(dsa, to_device, workloads, torch, dev)
+        pf["frac_of_measured_gemm"] = round(pf["achieved"] / cal["bf16_gemm_TFLOPs"], 4)
     if not args.no_backward:
         log("attention backward ...")
         res["attention_backward"] = attention_backward(dsa, workloads, torch, dev)

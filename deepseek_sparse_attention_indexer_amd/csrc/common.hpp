@@ -30,6 +30,21 @@ __device__ __forceinline__ f32x16_t mfma_bf16_32x32x16(u32x4_t a, u32x4_t b, f32
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Reduce-scatter of four per-lane partials over the four 16-lane rows of a wave: p_j at lane
+// 16 g + c holds row g's share of item 16 j + c, and lane l receives the sum over g of p_{l/16}
+// at lane 16 g + l % 16. gfx950's lane swaps do the exchange in the vector ALU (permlane32_swap:
+// lanes 32..63 of the first operand trade places with lanes 0..31 of the second; permlane16_swap:
+// the odd 16-lane rows of the first with the even rows of the second); each add then sums the
+// same two values an xor-32 / xor-16 lane exchange would.
+__device__ __forceinline__ float reduce_scatter_rows4(float p0, float p1, float p2, float p3) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+  const float k0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const float k1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+  const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
 // Paging of a token cache, resolved on the host into device-friendly fields.
 struct Paging {
   const int32_t* bt;      // block table or nullptr

@@ -16,8 +16,8 @@
 // and a tile is one contiguous 16 KiB (bf16, page 64) or 8 KiB (fp8) burst. The query heads
 // are requested first (every MFMA waits on them), the first tile's keys right after, and
 // every later tile is prefetched one step ahead. The epilogue applies ReLU and the
-// head weights in fp32 on the accumulators, reduces the four lane groups with a 3-shuffle
-// reduce-scatter so lane l ends up with candidate s0 + l, and stores one coalesced 256-byte
+// head weights in fp32 on the accumulators, reduce-scatters over the four lane groups with
+// three lane swaps so lane l ends up with candidate s0 + l, and stores one coalesced 256-byte
 // row segment. Optionally the same pass counts a 4096-bin histogram of the top 12 bits of
 // the order-preserving key of each score (first radix digit of the top-k select).
 #include "common.hpp"
@@ -219,13 +219,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_index_scores(ScoreArgs a) {
       part[st] = p;
     }
     // reduce-scatter over the 4 lane groups: group g keeps the full sum of sub-tile st = g
-    const bool hi2 = lane & 32;
-    float k0 = hi2 ? part[2] : part[0];
-    float k1 = hi2 ? part[3] : part[1];
-    k0 += __shfl_xor(hi2 ? part[0] : part[2], 32);
-    k1 += __shfl_xor(hi2 ? part[1] : part[3], 32);
-    const bool hi1 = lane & 16;
-    const float total = (hi1 ? k1 : k0) + __shfl_xor(hi1 ? k0 : k1, 16);
+    const float total = reduce_scatter_rows4(part[0], part[1], part[2], part[3]);
 
     const int s = s0 + lane;
     if (s < n) {

@@ -14,8 +14,8 @@
 // double-buffered LDS tile and used by all 8 rows. The tile is stored XOR-swizzled (16-byte
 // chunk p of key row r at p ^ (r mod chunks-per-row)) so that the 16 lanes that read one
 // column of 16 key rows hit distinct banks. The epilogue is the decode kernel's: ReLU and the
-// head weights in fp32 on the accumulators, a 3-shuffle reduce-scatter, one coalesced store
-// of 64 scores per row and tile.
+// head weights in fp32 on the accumulators, a reduce-scatter by three lane swaps, one
+// coalesced store of 64 scores per row and tile.
 //
 // Rows of a block that belong to different requests are processed one request after the
 // other (each with its own keys); rows of the same request share the tiles. A row writes
@@ -155,91 +155,115 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArg
     // position q = 64 ins + l = (key row r = q / CPR, position p = q % CPR); the lane fetches
     // global chunk p ^ (r % CPR) of that row, which stores the tile swizzled. Rows past the
     // request's last key re-read its last key (masked at the store). The loads complete on the
-    // vector-memory counter, so the waits for them are explicit.
+    // vector-memory counter, so the waits for them are explicit. The cache slots a tile's
+    // loads need are read from LDS one tile ahead, so a tile's loads issue without waiting.
     constexpr int NINS = TB / 1024;
-    auto dma_tile = [&](int j, int buf) {
+    constexpr int NPW = NINS / kPfRows;         // load instructions per wave and tile
+    static_assert(NINS % kPfRows == 0, "whole instructions per wave");
+    int slot_nx[NPW];
+    auto read_slots = [&](int j) {
+#pragma unroll
+      for (int k = 0; k < NPW; ++k) {
+        const int r = ((wave + k * kPfRows) * 64 + lane) / CPR;
+        slot_nx[k] = s_slot[min(c0 + j * kPfTile + r, kend - 1) - c0];
+      }
+    };
+    auto dma_tile = [&](int buf) {
       auto* lbase = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(
           reinterpret_cast<uintptr_t>(&s_k[buf][0]) & 0xffffffffu);
-      static_assert(NINS % kPfRows == 0, "whole instructions per wave");
 #pragma unroll
-      for (int k = 0; k < NINS / kPfRows; ++k) {
+      for (int k = 0; k < NPW; ++k) {
         const int ins = wave + k * kPfRows;
         const int q = ins * 64 + lane;
         const int r = q / CPR;
         const int p = q - r * CPR;
-        const int sp = min(c0 + j * kPfTile + r, kend - 1);
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)s_slot[sp - c0] * RB +
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)slot_nx[k] * RB +
                              ((p ^ (r % CPR)) * 16);
         __builtin_amdgcn_global_load_lds(src, lbase + ins * 1024, 16, 0, 0);
       }
     };
-    dma_tile(0, 0);
+    read_slots(0);
+    dma_tile(0);
+    if (ntile > 1) read_slots(1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    for (int j = 0; j < ntile; ++j) {
-      const int cur = j & 1;
-      if (j + 1 < ntile) dma_tile(j + 1, cur ^ 1);   // buffer cur ^ 1 was last read a tile ago
-      const int s0 = c0 + j * kPfTile;
-      const bool have = mine && s0 < my_n;
-      bool stored = false;
-      if (have) {
-        // every B operand of the tile is read from LDS up front, so the MFMAs run back to back
-        u32x4_t bv[4][KB];
+
+    auto mma = [&](const u32x4_t (&bv)[4][KB], int st, f32x4_t* acc) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int r = 16 * st + c;
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const int cc = 4 * kb + g;
-            bv[st][kb] = *reinterpret_cast<const u32x4_t*>(&s_k[cur][r * RB + ((cc ^ (r % CPR)) * 16)]);
-          }
-        }
-        // the MFMAs of sub-tile st + 1 are issued before the epilogue of sub-tile st, so the
-        // matrix cores run while the vector ALU applies ReLU and the head weights
-        auto mma = [&](int st, f32x4_t* acc) {
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16_16x16x32(qa[mt][kb], bv[st][kb], acc[mt]);
+    };
+    auto epi = [&](const f32x4_t* acc) {
+      float pp = 0.f;
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16_16x16x32(qa[mt][kb], bv[st][kb], acc[mt]);
-        };
-        auto epi = [&](const f32x4_t* acc) {
-          float pp = 0.f;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) pp = fmaf(wv[mt][rr], relu_f32(acc[mt][rr]), pp);
-          return pp;
-        };
-        float part[4];
-        f32x4_t acc0[MT], acc1[MT];
-        mma(0, acc0);
-        mma(1, acc1);
-        part[0] = epi(acc0);
-        mma(2, acc0);
-        part[1] = epi(acc1);
-        mma(3, acc1);
-        part[2] = epi(acc0);
-        part[3] = epi(acc1);
-        // reduce-scatter over the 4 lane groups: lane l ends with the score of key s0 + l
-        const bool hi2 = lane & 32;
-        float k0 = hi2 ? part[2] : part[0];
-        float k1 = hi2 ? part[3] : part[1];
-        k0 += __shfl_xor(hi2 ? part[0] : part[2], 32);
-        k1 += __shfl_xor(hi2 ? part[1] : part[3], 32);
-        const bool hi1 = lane & 16;
-        const float total = (hi1 ? k1 : k0) + __shfl_xor(hi1 ? k0 : k1, 16);
-        const int s = s0 + lane;
-        if (s < my_n && s < kend) a.logits[(int64_t)t * a.ld_logits + s] = total;
-        stored = true;
+        for (int rr = 0; rr < 4; ++rr) pp = fmaf(wv[mt][rr], relu_f32(acc[mt][rr]), pp);
+      return pp;
+    };
+    // A tile's last sub-tile (accumulators acc1) is finished during the next tile's first
+    // MFMAs: its epilogue, the reduce-scatter over the lane groups (lane l ends with the score
+    // of key s0 + l) and the store.
+    f32x4_t acc0[MT], acc1[MT];
+    float part[4];
+    auto finish = [&](int s0) {
+      part[3] = epi(acc1);
+      const float total = reduce_scatter_rows4(part[0], part[1], part[2], part[3]);
+      const int s = s0 + lane;
+      if (s < my_n && s < kend) a.logits[(int64_t)t * a.ld_logits + s] = total;
+    };
+    auto advance = [&](int j) {                 // loads of tile j + 1, slots of tile j + 2
+      if (j + 1 < ntile) {
+        dma_tile((j & 1) ^ 1);                  // that buffer was last read a tile ago
+        if (j + 2 < ntile) read_slots(j + 2);
       }
-      // the next tile's loads are complete for this wave; the one store issued after them
-      // (counted in issue order) may still be in flight
-      if (stored) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    };
+    // the wave scores tiles [0, jh) (its row sees them), then only loads and waits with the
+    // others; the next tile's loads are complete before each barrier, while a store issued
+    // after them (vector memory operations complete in issue order) may still be in flight
+    const int jh = mine ? min(ntile, max(0, (my_n - c0 + kPfTile - 1) / kPfTile)) : 0;
+    for (int j = 0; j < jh; ++j) {
+      advance(j);
+      const int cur = j & 1;
+      // every B operand of the tile is read from LDS up front, so the MFMAs run back to back
+      u32x4_t bv[4][KB];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int r = 16 * st + c;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int cc = 4 * kb + g;
+          bv[st][kb] = *reinterpret_cast<const u32x4_t*>(&s_k[cur][r * RB + ((cc ^ (r % CPR)) * 16)]);
+        }
+      }
+      // the MFMAs of sub-tile st + 1 are issued before the epilogue of sub-tile st, so the
+      // matrix cores run while the vector ALU applies ReLU and the head weights
+      mma(bv, 0, acc0);
+      if (j > 0) finish(c0 + (j - 1) * kPfTile);
+      mma(bv, 1, acc1);
+      part[0] = epi(acc0);
+      mma(bv, 2, acc0);
+      part[1] = epi(acc1);
+      mma(bv, 3, acc1);
+      part[2] = epi(acc0);
+      if (j > 0) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       lds_barrier();
     }
+    for (int j = jh; j < ntile; ++j) {
+      advance(j);
+      if (j == jh && jh > 0) {
+        finish(c0 + (jh - 1) * kPfTile);
+        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      lds_barrier();
+    }
+    if (jh == ntile && jh > 0) finish(c0 + (jh - 1) * kPfTile);
   }
 }
 
