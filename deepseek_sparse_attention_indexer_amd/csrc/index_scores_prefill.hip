@@ -9,9 +9,11 @@
 // Per query row this is a [heads x di] x [di x keys] contraction followed by a ReLU-weighted
 // head reduction. One query row per workgroup (the decode kernel) re-reads every key tile
 // for every row, which makes a long causal prefill L2-bandwidth bound. Here a workgroup
-// takes 8 consecutive rows (one per wave, all heads held in registers as MFMA A operands) and
+// takes 4 consecutive rows (one per wave, all heads held in registers as MFMA A operands) and
 // a chunk of up to 8192 key positions; each 64-key tile is read from memory once into a
-// double-buffered LDS tile and used by all 8 rows. The tile is stored XOR-swizzled (16-byte
+// double-buffered LDS tile and used by all 4 rows. Two such workgroups share a CU (registers
+// allow two waves per SIMD); their barriers are independent, so one workgroup's MFMAs run
+// while the other waits on LDS or a barrier. The tile is stored XOR-swizzled (16-byte
 // chunk p of key row r at p ^ (r mod chunks-per-row)) so that the 16 lanes that read one
 // column of 16 key rows hit distinct banks. The epilogue is the decode kernel's: ReLU and the
 // head weights in fp32 on the accumulators, a reduce-scatter by three lane swaps, one
@@ -25,7 +27,7 @@
 
 namespace dsa {
 
-constexpr int kPfRows = 8;                      // query rows per workgroup, one per wave
+constexpr int kPfRows = 4;                      // query rows per workgroup, one per wave
 constexpr int kPfThreads = 64 * kPfRows;
 constexpr int kPfTile = 64;                     // keys per LDS tile
 constexpr int kPfChunkMax = 8192;               // key positions per workgroup (grid x), at most
