@@ -742,7 +742,9 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
     // un-normalised partial (o, m, l) of this split; k_mla_combine merges them. A lane holds
     // 128 contiguous bytes of one head's row, so direct stores would spread every instruction
     // over 64 cache lines; the block is staged in LDS (free once every wave is past its last
-    // block) and written back one head row at a time, 1 KiB per instruction.
+    // block) and written back one head row at a time, 1 KiB per instruction, with streaming
+    // (non-temporal) stores: whole lines that the next kernel reads (a streaming store of a
+    // partial line, as the direct stores below would make, measured far slower).
     constexpr int PS = kDV + 4;                       // padded fp32 row of one head in LDS
     if constexpr (HT * 16 * PS * 4 <= LDSB) {
       float* s_po = reinterpret_cast<float*>(s_lds);
@@ -763,8 +765,8 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
       for (int q = threadIdx.x * 4; q < HT * 16 * kDV; q += NT * 4) {
         const int hl = q / kDV;
         const int col = q - hl * kDV;
-        *reinterpret_cast<f32x4_t*>(po + (int64_t)hl * a.n_split * kDV + col) =
-            *reinterpret_cast<const f32x4_t*>(s_po + hl * PS + col);
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(s_po + hl * PS + col),
+                                    reinterpret_cast<f32x4_t*>(po + (int64_t)hl * a.n_split * kDV + col));
       }
     } else {                                          // too many heads to stage: direct stores
       float* po = a.part_o + (((int64_t)t * a.H + head) * a.n_split + split) * kDV;
