@@ -302,6 +302,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the attention backward measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (32k, 1M fp8-key decode, DSv4 fp8 attention, multi-token)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured copy / GEMM ceilings (e.g. under counter passes)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -416,16 +418,19 @@ def main():
         "vs_baseline_note": "value / 411 us: the pages' Gluon 128k decode total (tokenspeed PR 627, "
                             "GFX9-class GPU, heads and precision unstated); context, not the target",
     }
-    log("measured ceilings ...")
-    cal = calibration(torch, dev)
-    cal["layer_frac_of_copy"] = round((ab["total"] / (cal["copy_GBps"] * 1e9)) / (cold * 1e-6), 4)
-    if achieved:
-        cal["roofline_kernel_frac_of_copy"] = round(achieved / cal["copy_GBps"], 4)
-    res["measured_ceilings"] = cal
+    cal = None
+    if not args.no_ceilings:
+        log("measured ceilings ...")
+        cal = calibration(torch, dev)
+        cal["layer_frac_of_copy"] = round((ab["total"] / (cal["copy_GBps"] * 1e9)) / (cold * 1e-6), 4)
+        if achieved:
+            cal["roofline_kernel_frac_of_copy"] = round(achieved / cal["copy_GBps"], 4)
+        res["measured_ceilings"] = cal
     if not args.no_prefill:
         log("prefill indexer ...")
         res["prefill_indexer"] = pf = prefill_indexer(dsa, to_device, workloads, torch, dev)
-        pf["frac_of_measured_gemm"] = round(pf["achieved"] / cal["bf16_gemm_TFLOPs"], 4)
+        if cal:
+            pf["frac_of_measured_gemm"] = round(pf["achieved"] / cal["bf16_gemm_TFLOPs"], 4)
     if not args.no_backward:
         log("attention backward ...")
         res["attention_backward"] = attention_backward(dsa, workloads, torch, dev)
