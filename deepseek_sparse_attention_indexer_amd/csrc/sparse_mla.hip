@@ -19,10 +19,11 @@
 // as with 16 heads per wave.
 // Blocks stream through a ring of NBUF buffers in LDS: while a block is computed, the next
 // NBUF - 1 blocks' rows are in flight (direct global->LDS loads; bf16 rows land in place, fp8
-// rows land as raw bytes and are dequantised to one bf16 block just before use). Each wave
-// waits only for its own loads of the block it needs (vmcnt = the loads of the later blocks),
-// so the barriers never drain the ring. A workgroup with one or two blocks to cover takes
-// NBUF = 2; many blocks per workgroup take a deeper ring. Each wave computes
+// rows land as raw bytes; fp8_ds_mla rows under one 16-head tile are converted straight into
+// the MFMA operands, other fp8 rows are dequantised to one bf16 block just before use). Each
+// wave waits only for its own loads of the block it needs (vmcnt = the loads of the later
+// blocks), so the barriers never drain the ring. Every launch plan takes NBUF = 2 (deeper
+// rings measured slower: they cost the second resident workgroup). Each wave computes
 //   S^T[32 rows x 16 heads] = K Q^T   (A = rows from LDS, B = q held in registers),
 // an online softmax in base 2, and
 //   O^T[512 x 16 heads] += V^T P^T   (A = V^T read from LDS and transposed 8x8 in registers,
