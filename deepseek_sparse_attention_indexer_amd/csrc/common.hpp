@@ -157,14 +157,20 @@ __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
-// fp32 -> bf16 round-to-nearest-even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round-to-nearest-even: one gfx950
+// v_cvt_pk_bf16_f32 (checked on the GPU bit for bit against the integer rounding
+// (u + 0x7fff + ((u >> 16) & 1)) >> 16 over 2^25 finite patterns, denormals and ties included).
 __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
-  return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return pack_bf16_rne(f, 0.f) & 0xFFFFu; }
+
+// 2^x by the hardware exponential (v_exp_f32). exp2f adds a rescaling around it only so that
+// results below 2^-126 come out as exact denormals; softmax weights that small vanish against
+// a sum whose largest term is at least 2^-8, so the hot loops take the bare instruction.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 4 OCP e4m3 bytes -> 4 floats (gfx950's conversion is the OCP e4m3fn decode).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {

@@ -13,10 +13,11 @@
 // Workgroup = HT x WD waves sharing each gathered 32-row block: a wave owns 16 heads (one of
 // HT head tiles) and 512 / WD value columns (decode runs one head tile with WD = 4, so four
 // waves issue the gather and the PV product and the score product is split over the waves).
-// 64 heads (HT = 4) take 32x32x16 MFMAs instead: wave w owns 32 heads (half w & 1) and 256
-// value columns (half w >> 1); the two waves of a head half split the score product's
-// contraction and swap partials through LDS. Each block is then read from LDS half as often
-// as with 16 heads per wave.
+// 64 heads (HT = 4, WD = 2: 8 waves) take 32x32x16 MFMAs instead: wave w owns 32 heads (half
+// w & 1) and 128 value columns (quarter w >> 1); the four waves of a head half split the score
+// product's contraction four ways and sum the partials through LDS in a fixed order. Each
+// block is then read from LDS half as often as with 16 heads per wave, and a wave needs about
+// 200 registers, so two waves share each SIMD.
 // Blocks stream through a ring of NBUF buffers in LDS: while a block is computed, the next
 // NBUF - 1 blocks' rows are in flight (direct global->LDS loads; bf16 rows land in place, fp8
 // rows land as raw bytes; fp8_ds_mla rows under one 16-head tile are converted straight into
@@ -161,7 +162,7 @@ __device__ __forceinline__ Finish finish_softmax(float m, float l, float sink, b
 }
 
 template <int FMT, int DQK, int HT, int WD, bool SPLIT, int NBUF>
-__global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(MlaArgs a) {
+__global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2 : 1) void k_sparse_mla(MlaArgs a) {
   static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
   constexpr int NW = HT * WD;                 // waves: HT head tiles x WD value-column slices
   constexpr int NT = 64 * NW;
@@ -406,14 +407,19 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   const int kq0 = kSplitK ? (wave & 1) * KQ : 0;     // this wave's first k-step
   __shared__ f32x4_t s_sp[kSplitK ? 4 : 1][64];      // the partials
   // 64 heads, 32x32x16 MFMAs (see the top): lane l of wave w is head 32 hh + l32 of the
-  // workgroup's 64 and reads k-slots 8 hl .. 8 hl + 7; the wave's half of the contraction is
+  // workgroup's 64 and reads k-slots 8 hl .. 8 hl + 7. The NVS = 2 WD waves of a head half
+  // take value slice vh (VC columns each) and the vh-th of NVS parts of the contraction,
   // k-steps kq32 .. kq32 + KQ32 - 1 (16 columns each)
-  constexpr bool kW32 = HT == 4 && WD == 1;
-  constexpr int KQ32 = DQK / 32;                      // k-steps of 16 per wave (half of DQK / 16)
+  constexpr bool kW32 = HT == 4 && (WD == 1 || WD == 2);
+  constexpr int NVS = 2 * WD;                         // waves per head half
+  constexpr int VC = kDV / NVS;                       // value columns per wave
+  constexpr int CPL = VC / 32;                        // columns per lane and row (m-tiles)
+  constexpr int KQ32 = DQK / (16 * NVS);              // k-steps of 16 per wave
+  static_assert(!kW32 || (DQK % (16 * NVS) == 0 && (CPL == 8 || CPL == 4)), "32-head split");
   const int hh = wave & 1, vh = wave >> 1;
   const int l32 = lane & 31, hl = lane >> 5;
   const int kq32 = vh * KQ32;
-  __shared__ f32x4_t s_sp32[kW32 ? 4 : 1][4][64];    // the score partials, 16 floats per lane
+  __shared__ f32x4_t s_sp32[kW32 ? NW : 1][4][64];   // the score partials, 16 floats per lane
   u32x4_t qb[kW32 ? 1 : KQ];
   u32x4_t qb32[kW32 ? KQ32 : 1];
   if constexpr (kW32) {
@@ -428,13 +434,13 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   float m_run = -INFINITY;   // running max (base-2 units) of this lane's head; rescaled lazily
   float l_run = 0.f;         // lane-partial sum of exp2(s - m_run)
   f32x4_t o[kW32 ? 1 : GD][8];
-  f32x16_t o32[kW32 ? 8 : 1];
+  f32x16_t o32[kW32 ? CPL : 1];
 #pragma unroll
   for (int i = 0; i < (kW32 ? 1 : GD); ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[i][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < (kW32 ? 8 : 1); ++e) o32[e] = f32x16_t{};
+  for (int e = 0; e < (kW32 ? CPL : 1); ++e) o32[e] = f32x16_t{};
 
   __syncthreads();   // q is in registers before the first rows land in the buffers
   // loads this wave issues per block (instructions of a block are dealt round-robin to the
@@ -518,8 +524,9 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
 #pragma unroll
         for (int kb = 0; kb < KQ32; ++kb) sp = mfma_bf16_32x32x16(*reinterpret_cast<const u32x4_t*>(rp + 16 * kb), qb32[kb], sp);
       }
+      auto sp4 = [&](int q) { return f32x4_t{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]}; };
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s_sp32[wave][q][lane] = f32x4_t{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]};
+      for (int q = 0; q < 4; ++q) s_sp32[wave][q][lane] = sp4(q);
       // rows of accumulator r: 8 (r / 4) + 4 hl + r % 4; their validity
       u32x4_t slq[4];
 #pragma unroll
@@ -529,12 +536,16 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
       float mx = -INFINITY;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4_t o4 = s_sp32[wave ^ 2][q][lane];
+        // the head half's partials in a fixed order (slice 0 first), so that all its waves
+        // hold the same scores
+        f32x4_t st = NVS == 2 ? sp4(q) : s_sp32[hh][q][lane];
+#pragma unroll
+        for (int v = 1; v < NVS; ++v) st += NVS == 2 ? s_sp32[wave ^ 2][q][lane] : s_sp32[hh + 2 * v][q][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = jb + 8 * q + 4 * hl + i;
           const bool ok = row < pass_n && (int32_t)slq[q][i] >= 0;
-          const float x = ok ? (sp[4 * q + i] + o4[i]) * a.scale_log2 : -INFINITY;
+          const float x = ok ? st[i] * a.scale_log2 : -INFINITY;
           p[4 * q + i] = x;
           mx = fmaxf(mx, x);
         }
@@ -542,24 +553,24 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        const float alpha = m_run == -INFINITY ? 0.f : exp2_hw(m_run - m_new);
         if (m_run != -INFINITY || __any(l_run != 0.f)) {
           l_run *= alpha;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o32[e] *= alpha;
+          for (int e = 0; e < CPL; ++e) o32[e] *= alpha;
         }
         m_run = m_new;
       }
       const bool none = m_run == -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = none ? 0.f : exp2f(p[i] - m_run);
+        p[i] = none ? 0.f : exp2_hw(p[i] - m_run);
         l_run += p[i];
       }
-      // ---- O^T += V^T P^T over this wave's 256 value columns, two k-steps of 16 rows. k-slot
+      // ---- O^T += V^T P^T over this wave's VC value columns, two k-steps of 16 rows. k-slot
       // 8 hl + j of k-step ks is row 16 ks + 4 hl + j (j < 4) or 16 ks + 8 + 4 hl + j - 4: the
-      // accumulator rows of S^T, so P^T needs no lane exchange; V^T by 8x8 transposes of LDS
-      // rows (m-tile e = columns 256 vh + 8 m + e)
+      // accumulator rows of S^T, so P^T needs no lane exchange; V^T by 8 x CPL transposes of
+      // LDS rows (m-tile e = columns VC vh + CPL m + e)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32x4_t pb;
@@ -571,10 +582,16 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int row = 16 * ks + (j < 4 ? 4 * hl + j : 8 + 4 * hl + j - 4);
-          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][row][256 * vh + 8 * l32]);
+          const uint16_t* vp = &s_rows[cur][row][VC * vh + CPL * l32];
+          if constexpr (CPL == 8) {
+            vr[j] = *reinterpret_cast<const u32x4_t*>(vp);
+          } else {
+            const u32x2_t v2 = *reinterpret_cast<const u32x2_t*>(vp);
+            vr[j] = u32x4_t{v2[0], v2[1], 0u, 0u};
+          }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < CPL; ++e) {
           const int w = e >> 1;
           const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
           u32x4_t av;
@@ -627,7 +644,7 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        const float alpha = m_run == -INFINITY ? 0.f : exp2_hw(m_run - m_new);
         if (m_run != -INFINITY || __any(l_run != 0.f)) {   // nothing to rescale before the first rows
           l_run *= alpha;
   #pragma unroll
@@ -640,7 +657,7 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
       const bool none = m_run == -INFINITY;
   #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = none ? 0.f : exp2f(p[i] - m_run);
+        p[i] = none ? 0.f : exp2_hw(p[i] - m_run);
         l_run += p[i];
       }
       u32x4_t pb;
@@ -689,29 +706,37 @@ __global__ __launch_bounds__(64 * HT * WD, HT == 1 ? 2 : 1) void k_sparse_mla(Ml
   }
 
   if constexpr (kW32) {
-    // lane l holds head 32 hh + l32 (of the workgroup's 64), columns 256 vh + 8 m + e for
-    // m = 8 (r / 4) + 4 hl + r % 4 of accumulator r, e = 0..7
+    // lane l holds head 32 hh + l32 (of the workgroup's 64), columns VC vh + CPL m + e for
+    // m = 8 (r / 4) + 4 hl + r % 4 of accumulator r, e = 0..CPL-1
     l_run += __shfl_xor(l_run, 32);
     const int headw = hg * 64 + 32 * hh + l32;
     if constexpr (!SPLIT) {
       const Finish fin = finish_softmax(m_run, l_run, a.sink ? a.sink[headw] : -INFINITY, a.lse_log2);
-      uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)headw * kDV + 256 * vh;
+      uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)headw * kDV + VC * vh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
-        u32x4_t v;
+        if constexpr (CPL == 8) {
+          u32x4_t v;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) v[e2] = pack_bf16_rne(o32[2 * e2][r] * fin.inv, o32[2 * e2 + 1][r] * fin.inv);
-        *reinterpret_cast<u32x4_t*>(op + 8 * m) = v;
+          for (int e2 = 0; e2 < 4; ++e2) v[e2] = pack_bf16_rne(o32[2 * e2][r] * fin.inv, o32[2 * e2 + 1][r] * fin.inv);
+          *reinterpret_cast<u32x4_t*>(op + 8 * m) = v;
+        } else {
+          u32x2_t v;
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) v[e2] = pack_bf16_rne(o32[2 * e2][r] * fin.inv, o32[2 * e2 + 1][r] * fin.inv);
+          *reinterpret_cast<u32x2_t*>(op + 4 * m) = v;
+        }
       }
       if (a.lse && hl == 0 && vh == 0) a.lse[(int64_t)t * a.H + headw] = fin.lse;
     } else {
-      float* po = a.part_o + (((int64_t)t * a.H + headw) * a.n_split + split) * kDV + 256 * vh;
+      float* po = a.part_o + (((int64_t)t * a.H + headw) * a.n_split + split) * kDV + VC * vh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
-        *reinterpret_cast<f32x4_t*>(po + 8 * m) = f32x4_t{o32[0][r], o32[1][r], o32[2][r], o32[3][r]};
-        *reinterpret_cast<f32x4_t*>(po + 8 * m + 4) = f32x4_t{o32[4][r], o32[5][r], o32[6][r], o32[7][r]};
+        *reinterpret_cast<f32x4_t*>(po + CPL * m) = f32x4_t{o32[0][r], o32[1][r], o32[2][r], o32[3][r]};
+        if constexpr (CPL == 8)
+          *reinterpret_cast<f32x4_t*>(po + 8 * m + 4) = f32x4_t{o32[4][r], o32[5][r], o32[6][r], o32[7][r]};
       }
       if (hl == 0 && vh == 0) {
         float* pml = a.part_ml + (((int64_t)t * a.H + headw) * a.n_split + split) * 2;
@@ -892,7 +917,7 @@ static hipError_t launch_h(const MlaArgs& a, int T, hipStream_t st) {
 template <int FMT, int DQK>
 static hipError_t launch_d(const MlaArgs& a, int ht, int nbuf, int T, hipStream_t st) {
   (void)nbuf;
-  if (ht == 4) return launch_h<FMT, DQK, 4, 1, 2>(a, T, st);
+  if (ht == 4) return launch_h<FMT, DQK, 4, 2, 2>(a, T, st);
   if (ht == 2) return launch_h<FMT, DQK, 2, 2, 2>(a, T, st);
   return launch_h<FMT, DQK, 1, 4, 2>(a, T, st);
 }

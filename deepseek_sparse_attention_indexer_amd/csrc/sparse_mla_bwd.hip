@@ -268,8 +268,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const bool ok0 = jm + r < pass_n && (int32_t)sl0[r] >= 0;
         const bool ok1 = jm + 16 + r < pass_n && (int32_t)sl1[r] >= 0;
-        p[r] = ok0 ? exp2f(s0[r] * a.scale_log2 - l2c) : 0.f;
-        p[4 + r] = ok1 ? exp2f(s1[r] * a.scale_log2 - l2c) : 0.f;
+        p[r] = ok0 ? exp2_hw(s0[r] * a.scale_log2 - l2c) : 0.f;
+        p[4 + r] = ok1 ? exp2_hw(s1[r] * a.scale_log2 - l2c) : 0.f;
         dz[r] = p[r] * (d0[r] - Dc);
         dz[4 + r] = p[4 + r] * (d1[r] - Dc);
       }
