@@ -45,6 +45,16 @@ __device__ __forceinline__ float reduce_scatter_rows4(float p0, float p1, float 
   return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
+// max of x and its lane-xor-32 / lane-xor-16 partner, by the lane swaps (no LDS round trip)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Paging of a token cache, resolved on the host into device-friendly fields.
 struct Paging {
   const int32_t* bt;      // block table or nullptr

@@ -234,7 +234,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     for (int k = 0; k < RPT; ++k) {
       const int j = threadIdx.x + k * NT;
       const int64_t slot = slot_done(pick_paging(li[k], kv1.pg, kv0.pg), sr[k]);
-      if (j < p1 - p0) s_slot[j] = e[k] >= 0 ? (int32_t)slot | ((int32_t)li[k] << 30) : -1;
+      // entries past the pass read as padding, so a block's row validity is its slot's sign
+      s_slot[j] = j < p1 - p0 && e[k] >= 0 ? (int32_t)slot | ((int32_t)li[k] << 30) : -1;
     }
   };
   // cache row of pass entry j (a padding entry reads row 0 of the main cache: finite data,
@@ -543,14 +544,12 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         for (int v = 1; v < NVS; ++v) st += NVS == 2 ? s_sp32[wave ^ 2][q][lane] : s_sp32[hh + 2 * v][q][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = jb + 8 * q + 4 * hl + i;
-          const bool ok = row < pass_n && (int32_t)slq[q][i] >= 0;
-          const float x = ok ? st[i] * a.scale_log2 : -INFINITY;
+          const float x = (int32_t)slq[q][i] >= 0 ? st[i] * a.scale_log2 : -INFINITY;
           p[4 * q + i] = x;
           mx = fmaxf(mx, x);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(mx);
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = m_run == -INFINITY ? 0.f : exp2_hw(m_run - m_new);
@@ -561,10 +560,11 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         }
         m_run = m_new;
       }
-      const bool none = m_run == -INFINITY;
+      // no valid row yet (m_run = -inf): every x is -inf, and exp2(-inf - 0) = 0
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = none ? 0.f : exp2_hw(p[i] - m_run);
+        p[i] = exp2_hw(p[i] - m_use);
         l_run += p[i];
       }
       // ---- O^T += V^T P^T over this wave's VC value columns, two k-steps of 16 rows. k-slot
@@ -632,16 +632,13 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       float mx = -INFINITY;
   #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok0 = jm + r < pass_n && (int32_t)sl0[r] >= 0;
-        const bool ok1 = jm + 16 + r < pass_n && (int32_t)sl1[r] >= 0;
-        const float x0 = ok0 ? s0[r] * a.scale_log2 : -INFINITY;
-        const float x1 = ok1 ? s1[r] * a.scale_log2 : -INFINITY;
+        const float x0 = (int32_t)sl0[r] >= 0 ? s0[r] * a.scale_log2 : -INFINITY;
+        const float x1 = (int32_t)sl1[r] >= 0 ? s1[r] * a.scale_log2 : -INFINITY;
         p[r] = x0;
         p[4 + r] = x1;
         mx = fmaxf(mx, fmaxf(x0, x1));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = m_run == -INFINITY ? 0.f : exp2_hw(m_run - m_new);
@@ -654,10 +651,10 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         }
         m_run = m_new;
       }
-      const bool none = m_run == -INFINITY;
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;   // as in the 32-head path
   #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = none ? 0.f : exp2_hw(p[i] - m_run);
+        p[i] = exp2_hw(p[i] - m_use);
         l_run += p[i];
       }
       u32x4_t pb;
