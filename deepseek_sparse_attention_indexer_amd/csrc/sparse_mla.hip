@@ -15,9 +15,11 @@
 // waves issue the gather and the PV product and the score product is split over the waves).
 // 64 heads (HT = 4, WD = 2: 8 waves) take 32x32x16 MFMAs instead: wave w owns 32 heads (half
 // w & 1) and 128 value columns (quarter w >> 1); the four waves of a head half split the score
-// product's contraction four ways and sum the partials through LDS in a fixed order. Each
-// block is then read from LDS half as often as with 16 heads per wave, and a wave needs about
-// 200 registers, so two waves share each SIMD.
+// product's contraction four ways and meet in LDS: each wave sums the four partials (in a
+// fixed order) for its own 8 rows only, runs their softmax and publishes their packed weights,
+// which every wave of the head half then reads as its P^T operand. Each block is read from
+// LDS half as often as with 16 heads per wave, and a wave needs about 200 registers, so two
+// waves share each SIMD.
 // Blocks stream through a ring of NBUF buffers in LDS: while a block is computed, the next
 // NBUF - 1 blocks' rows are in flight (direct global->LDS loads; bf16 rows land in place, fp8
 // rows land as raw bytes; fp8_ds_mla rows under one 16-head tile are converted straight into
@@ -411,16 +413,20 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   // workgroup's 64 and reads k-slots 8 hl .. 8 hl + 7. The NVS = 2 WD waves of a head half
   // take value slice vh (VC columns each) and the vh-th of NVS parts of the contraction,
   // k-steps kq32 .. kq32 + KQ32 - 1 (16 columns each)
-  constexpr bool kW32 = HT == 4 && (WD == 1 || WD == 2);
+  constexpr bool kW32 = HT == 4 && WD == 2;
   constexpr int NVS = 2 * WD;                         // waves per head half
   constexpr int VC = kDV / NVS;                       // value columns per wave
   constexpr int CPL = VC / 32;                        // columns per lane and row (m-tiles)
   constexpr int KQ32 = DQK / (16 * NVS);              // k-steps of 16 per wave
-  static_assert(!kW32 || (DQK % (16 * NVS) == 0 && (CPL == 8 || CPL == 4)), "32-head split");
+  static_assert(!kW32 || (DQK % (16 * NVS) == 0 && NVS == 4 && CPL == 4), "32-head split");
   const int hh = wave & 1, vh = wave >> 1;
   const int l32 = lane & 31, hl = lane >> 5;
   const int kq32 = vh * KQ32;
   __shared__ f32x4_t s_sp32[kW32 ? NW : 1][4][64];   // the score partials, 16 floats per lane
+  __shared__ u32x2_t s_pw[kW32 ? NW : 1][64];         // each wave's rows' weights, packed bf16
+  __shared__ float s_mx[kW32 ? NW : 1][32];           // each wave's max per head
+  __shared__ float s_lw[kW32 ? NW : 1][32];           // each wave's weight sum per head (end)
+  __shared__ int s_grow[kW32 ? NW : 1];
   u32x4_t qb[kW32 ? 1 : KQ];
   u32x4_t qb32[kW32 ? KQ32 : 1];
   if constexpr (kW32) {
@@ -518,40 +524,54 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     const u32x4_t sl1 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm + 16]);
 
     if constexpr (kW32) {
-      // ---- S^T partial over this wave's half of the contraction: 32 rows x 32 heads
+      // ---- S^T partial over this wave's quarter of the contraction: 32 rows x 32 heads
       f32x16_t sp = {};
       {
         const uint16_t* rp = &s_rows[cur][l32][8 * hl + 16 * kq32];
 #pragma unroll
         for (int kb = 0; kb < KQ32; ++kb) sp = mfma_bf16_32x32x16(*reinterpret_cast<const u32x4_t*>(rp + 16 * kb), qb32[kb], sp);
       }
-      auto sp4 = [&](int q) { return f32x4_t{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]}; };
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s_sp32[wave][q][lane] = sp4(q);
-      // rows of accumulator r: 8 (r / 4) + 4 hl + r % 4; their validity
-      u32x4_t slq[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) slq[q] = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + 8 * q + 4 * hl]);
+      for (int q = 0; q < 4; ++q) s_sp32[wave][q][lane] = f32x4_t{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]};
+      // Each wave finishes the softmax of its own 8 rows only: accumulator group vh of the
+      // head half's partials, i.e. rows 8 vh + 4 hl + i (i = 0..3) of head 32 hh + l32.
+      const u32x4_t slv = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + 8 * vh + 4 * hl]);
       lds_barrier();
-      float p[16];
+      // the four partials in a fixed order, so that a score does not depend on who sums it
+      f32x4_t st = s_sp32[hh][vh][lane];
+#pragma unroll
+      for (int v = 1; v < NVS; ++v) st += s_sp32[hh + 2 * v][vh][lane];
+      float x[4];
       float mx = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // the head half's partials in a fixed order (slice 0 first), so that all its waves
-        // hold the same scores
-        f32x4_t st = NVS == 2 ? sp4(q) : s_sp32[hh][q][lane];
-#pragma unroll
-        for (int v = 1; v < NVS; ++v) st += NVS == 2 ? s_sp32[wave ^ 2][q][lane] : s_sp32[hh + 2 * v][q][lane];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = (int32_t)slq[q][i] >= 0 ? st[i] * a.scale_log2 : -INFINITY;
-          p[4 * q + i] = x;
-          mx = fmaxf(mx, x);
-        }
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (int32_t)slv[i] >= 0 ? st[i] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[i]);
       }
-      mx = max_xor32(mx);
-      if (__any(mx > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, mx);
+      mx = max_xor32(mx);                          // over the wave's 8 rows, per head
+      // Weights against the running max, published as packed bf16 for the value product of
+      // every wave of the head half. They stand unless some wave's rows raise a head's max
+      // by more than 2^8; then every wave of the workgroup rescales and publishes again.
+      float p[4];
+      auto weights = [&]() {
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;   // no valid row yet: x = -inf
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = exp2_hw(x[i] - m_use);
+        s_pw[wave][lane] = u32x2_t{pack_bf16_rne(p[0], p[1]), pack_bf16_rne(p[2], p[3])};
+      };
+      weights();
+      const bool grow = __any(mx > m_run + 8.f);
+      if (lane == 0) s_grow[wave] = grow ? 1 : 0;
+      if (hl == 0) s_mx[wave][l32] = mx;
+      lds_barrier();
+      bool any_grow = false;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) any_grow |= s_grow[w] != 0;
+      if (any_grow) {                              // the same branch in every wave
+        float bm = s_mx[hh][l32];
+#pragma unroll
+        for (int v = 1; v < NVS; ++v) bm = fmaxf(bm, s_mx[hh + 2 * v][l32]);
+        const float m_new = fmaxf(m_run, bm);
         const float alpha = m_run == -INFINITY ? 0.f : exp2_hw(m_run - m_new);
         if (m_run != -INFINITY || __any(l_run != 0.f)) {
           l_run *= alpha;
@@ -559,36 +579,26 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
           for (int e = 0; e < CPL; ++e) o32[e] *= alpha;
         }
         m_run = m_new;
+        weights();
+        lds_barrier();
       }
-      // no valid row yet (m_run = -inf): every x is -inf, and exp2(-inf - 0) = 0
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = exp2_hw(p[i] - m_use);
-        l_run += p[i];
-      }
+      for (int i = 0; i < 4; ++i) l_run += p[i];   // this wave's rows; the waves meet at the end
       // ---- O^T += V^T P^T over this wave's VC value columns, two k-steps of 16 rows. k-slot
-      // 8 hl + j of k-step ks is row 16 ks + 4 hl + j (j < 4) or 16 ks + 8 + 4 hl + j - 4: the
-      // accumulator rows of S^T, so P^T needs no lane exchange; V^T by 8 x CPL transposes of
-      // LDS rows (m-tile e = columns VC vh + CPL m + e)
+      // 8 hl + j of k-step ks is row 16 ks + 4 hl + j (j < 4) or 16 ks + 8 + 4 hl + j - 4, i.e.
+      // the weights that the same lane of slices 2 ks and 2 ks + 1 published; V^T by 8 x CPL
+      // transposes of LDS rows (m-tile e = columns VC vh + CPL m + e)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        u32x4_t pb;
-        pb[0] = pack_bf16_rne(p[8 * ks], p[8 * ks + 1]);
-        pb[1] = pack_bf16_rne(p[8 * ks + 2], p[8 * ks + 3]);
-        pb[2] = pack_bf16_rne(p[8 * ks + 4], p[8 * ks + 5]);
-        pb[3] = pack_bf16_rne(p[8 * ks + 6], p[8 * ks + 7]);
+        const u32x2_t pa = s_pw[hh + 2 * (2 * ks)][lane];
+        const u32x2_t pc = s_pw[hh + 2 * (2 * ks + 1)][lane];
+        const u32x4_t pb = u32x4_t{pa[0], pa[1], pc[0], pc[1]};
         u32x4_t vr[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int row = 16 * ks + (j < 4 ? 4 * hl + j : 8 + 4 * hl + j - 4);
-          const uint16_t* vp = &s_rows[cur][row][VC * vh + CPL * l32];
-          if constexpr (CPL == 8) {
-            vr[j] = *reinterpret_cast<const u32x4_t*>(vp);
-          } else {
-            const u32x2_t v2 = *reinterpret_cast<const u32x2_t*>(vp);
-            vr[j] = u32x4_t{v2[0], v2[1], 0u, 0u};
-          }
+          const u32x2_t v2 = *reinterpret_cast<const u32x2_t*>(&s_rows[cur][row][VC * vh + CPL * l32]);
+          vr[j] = u32x4_t{v2[0], v2[1], 0u, 0u};
         }
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
@@ -704,8 +714,14 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
 
   if constexpr (kW32) {
     // lane l holds head 32 hh + l32 (of the workgroup's 64), columns VC vh + CPL m + e for
-    // m = 8 (r / 4) + 4 hl + r % 4 of accumulator r, e = 0..CPL-1
+    // m = 8 (r / 4) + 4 hl + r % 4 of accumulator r, e = 0..CPL-1. The weight sum: over the
+    // lane halves, then over the head half's four waves (each summed its own rows)
     l_run += __shfl_xor(l_run, 32);
+    if (hl == 0) s_lw[wave][l32] = l_run;
+    __syncthreads();
+    l_run = s_lw[hh][l32];
+#pragma unroll
+    for (int v = 1; v < NVS; ++v) l_run += s_lw[hh + 2 * v][l32];
     const int headw = hg * 64 + 32 * hh + l32;
     if constexpr (!SPLIT) {
       const Finish fin = finish_softmax(m_run, l_run, a.sink ? a.sink[headw] : -INFINITY, a.lse_log2);
@@ -713,17 +729,9 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
-        if constexpr (CPL == 8) {
-          u32x4_t v;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) v[e2] = pack_bf16_rne(o32[2 * e2][r] * fin.inv, o32[2 * e2 + 1][r] * fin.inv);
-          *reinterpret_cast<u32x4_t*>(op + 8 * m) = v;
-        } else {
-          u32x2_t v;
-#pragma unroll
-          for (int e2 = 0; e2 < 2; ++e2) v[e2] = pack_bf16_rne(o32[2 * e2][r] * fin.inv, o32[2 * e2 + 1][r] * fin.inv);
-          *reinterpret_cast<u32x2_t*>(op + 4 * m) = v;
-        }
+        const u32x2_t v = u32x2_t{pack_bf16_rne(o32[0][r] * fin.inv, o32[1][r] * fin.inv),
+                                  pack_bf16_rne(o32[2][r] * fin.inv, o32[3][r] * fin.inv)};
+        *reinterpret_cast<u32x2_t*>(op + 4 * m) = v;
       }
       if (a.lse && hl == 0 && vh == 0) a.lse[(int64_t)t * a.H + headw] = fin.lse;
     } else {
@@ -731,9 +739,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
-        *reinterpret_cast<f32x4_t*>(po + CPL * m) = f32x4_t{o32[0][r], o32[1][r], o32[2][r], o32[3][r]};
-        if constexpr (CPL == 8)
-          *reinterpret_cast<f32x4_t*>(po + 8 * m + 4) = f32x4_t{o32[4][r], o32[5][r], o32[6][r], o32[7][r]};
+        *reinterpret_cast<f32x4_t*>(po + 4 * m) = f32x4_t{o32[0][r], o32[1][r], o32[2][r], o32[3][r]};
       }
       if (hl == 0 && vh == 0) {
         float* pml = a.part_ml + (((int64_t)t * a.H + headw) * a.n_split + split) * 2;
