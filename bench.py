@@ -222,6 +222,57 @@ def other_configs(dsa, to_device, workloads, torch, dev, flush, names, reps=15):
     return res
 
 
+def prefill_chain(dsa, to_device, workloads, torch, dev, reps=3):
+    """The causal prefill chain (segments 8192 + 1): scores -> top-k -> sparse attention over
+    64 heads, each stage timed by its own HIP events; the attention against the bf16 MFMA
+    peak (2 * 64 * (576 + 512) FLOP per (row, listed entry)) and the top-k against one read
+    of the logits."""
+    import numpy as np
+    prob = workloads.causal_prefill((8192, 1), name="causal_prefill_8k")
+    d = to_device(prob, dev)
+    T = prob.T
+    ld = ((prob.n_max + 63) // 64) * 64
+    logits = torch.empty(T, ld, dtype=torch.float32, device=dev)
+    idx = torch.empty(T, prob.topk, dtype=torch.int32, device=dev)
+    lens = torch.empty(T, dtype=torch.int32, device=dev)
+    out = torch.empty(T, prob.H, prob.d_v, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(T, prob.H, dtype=torch.float32, device=dev)
+    ws = dsa.Workspace(dsa.dsa_workspace_size(dsa.ENTRY_TOPK, T=T, n_max=prob.n_max, topk=prob.topk), dev)
+
+    def run():
+        dsa.dsa_index_scores(d.q_idx, d.w, d.keys, d.rows, prob.Hi, prob.di, prob.index_scale, logits)
+        dsa.dsa_topk(logits, d.rows, prob.topk, idx, lens, ws)
+        dsa.dsa_sparse_mla_prefill(d.q, d.kv, idx, None, None, d.rows, prob.H, prob.d_qk, prob.d_v,
+                                   prob.softmax_scale, out, lse)
+
+    run()
+    torch.cuda.synchronize()
+    dsa.dsa_profile_enable(True)
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    prof = dsa.dsa_profile_collect()
+    dsa.dsa_profile_enable(False)
+    us = {k: round(v["total_ms"] / v["count"] * 1e3, 1) for k, v in prof.items()}
+    n = prob.row_len.astype(np.int64)
+    visits = int(np.minimum(n, prob.topk).sum())
+    att_flop = visits * 2 * prob.H * (prob.d_qk + prob.d_v)
+    att_us = us.get("sparse_mla")
+    topk_us = sum(v for k, v in us.items() if k.startswith("topk"))
+    logit_bytes = int(n.sum()) * 4
+    res = {"workload": "causal_prefill_8k (8193 rows, 64 heads x 576/512, indexer 64 x 128, topk 2048)",
+           "stages_us": us, "total_us": round(sum(us.values()), 1),
+           "attention": {"row_visits": visits, "tflop": round(att_flop / 1e12, 3),
+                         "achieved_TFLOPs": round(att_flop / (att_us * 1e-6) / 1e12, 1) if att_us else None,
+                         "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "frac": round(att_flop / (att_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4) if att_us else None},
+           "topk": {"logits_MB": round(logit_bytes / 1e6, 1), "us": round(topk_us, 1),
+                    "GBps": round(logit_bytes / (topk_us * 1e-6) / 1e9, 1) if topk_us else None},
+           "timing": "HIP events from each dispatch, inputs resident"}
+    del d, logits, idx, out, lse, ws
+    return res
+
+
 def attention_backward(dsa, workloads, torch, dev, reps=5):
     """The attention backward (dq, dKV by fp32 atomics, one list) on 64 rows x 64 heads x 2048
     listed rows (of 4096-token contexts, bf16 576 rows), after its forward: time, atomics and
@@ -431,6 +482,12 @@ def main():
         res["prefill_indexer"] = pf = prefill_indexer(dsa, to_device, workloads, torch, dev)
         if cal:
             pf["frac_of_measured_gemm"] = round(pf["achieved"] / cal["bf16_gemm_TFLOPs"], 4)
+    if not args.no_prefill:
+        log("prefill chain ...")
+        res["prefill_chain"] = prefill_chain(dsa, to_device, workloads, torch, dev)
+        if cal and res["prefill_chain"]["attention"]["achieved_TFLOPs"]:
+            res["prefill_chain"]["attention"]["frac_of_measured_gemm"] = round(
+                res["prefill_chain"]["attention"]["achieved_TFLOPs"] / cal["bf16_gemm_TFLOPs"], 4)
     if not args.no_backward:
         log("attention backward ...")
         res["attention_backward"] = attention_backward(dsa, workloads, torch, dev)

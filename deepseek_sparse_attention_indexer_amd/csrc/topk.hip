@@ -28,8 +28,12 @@ namespace dsa {
 constexpr int kNT = 512;   // threads of the select workgroups
 
 // ------------------------------------------------------------------ rows that fit in LDS
+// CAP: key capacity. CAP = kTopkLdsMax takes 80 KiB + 48 B of LDS (one workgroup per CU);
+// rows of at most 8192 candidates (a causal prefill of 8K tokens) take CAP = 8192, 48 KiB,
+// three workgroups per CU.
+template <int CAP>
 __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
-  __shared__ uint32_t s_key[kTopkLdsMax];
+  __shared__ uint32_t s_key[CAP];
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_w[kNT / 64];
   __shared__ uint32_t s_res[4];
@@ -424,7 +428,8 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
 
 hipError_t launch_topk_lds(const TopkArgs& a, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  launch_kernel(k_topk_lds, dim3(T), dim3(kNT), st, a);
+  if (a.n_max <= 8192) launch_kernel(k_topk_lds<8192>, dim3(T), dim3(kNT), st, a);
+  else launch_kernel(k_topk_lds<kTopkLdsMax>, dim3(T), dim3(kNT), st, a);
   return hipGetLastError();
 }
 
