@@ -37,11 +37,18 @@ CASES = [
                                  n_pad=100, sink=True)),
     ("bf16_all_padded_sink", dict(fmt="bf16", B=2, H=16, n_ctx=300, n_idx=64, pad="all", sink=True,
                                   lse_log2=True)),
-    # 16 rows x 64 heads in decode: 64-head workgroups with splits and a ring of four blocks
-    # (ragged last block, padding spread over the lists)
+    # 16 rows x 64 heads in decode: 8-wave 64-head workgroups (each wave finishes 8 rows of
+    # the softmax) with splits (ragged last block, padding spread over the lists), for every
+    # row format and width, with sinks and a base-2 lse
     ("bf16_h64_b16_ring", dict(fmt="bf16", B=16, H=64, n_ctx=5000, n_idx=2000, pad="shuffled", n_pad=77)),
     ("ds_mla_h64_b16_ring_two_lists", dict(fmt="fp8_ds_mla", B=16, H=64, n_ctx=5000, n_idx=1000,
                                            page_size=64, n_extra=230, pad="tail", n_pad=7)),
+    ("uniform_h64_b16", dict(fmt="fp8_uniform", B=16, H=64, n_ctx=3000, n_idx=700, pad="shuffled",
+                             n_pad=11)),
+    ("fnuz_576_h64_b16_two_lists", dict(fmt="fp8_uniform_fnuz", B=16, H=64, n_ctx=1500, n_idx=256,
+                                        n_extra=100, d_nope=512, d_v=512, n_pad=3)),
+    ("bf16_d512_h64_b16_sink_log2", dict(fmt="bf16", B=16, H=64, n_ctx=2000, n_idx=600, d_nope=448,
+                                         d_v=512, pad="shuffled", n_pad=5, sink=True, lse_log2=True)),
     ("ds_mla_two_lists_sink_log2", dict(fmt="fp8_ds_mla", B=3, H=16, n_ctx=2000, n_idx=128,
                                         page_size=256, n_extra=300, pad="tail", n_pad=5, sink=True,
                                         lse_log2=True)),
