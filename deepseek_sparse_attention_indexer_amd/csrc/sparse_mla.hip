@@ -735,11 +735,33 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       }
       if (a.lse && hl == 0 && vh == 0) a.lse[(int64_t)t * a.H + headw] = fin.lse;
     } else {
-      float* po = a.part_o + (((int64_t)t * a.H + headw) * a.n_split + split) * kDV + VC * vh;
+      // The partial (o, m, l). A lane's pieces are 16 bytes scattered over 32 head rows, so
+      // the block is staged in LDS (the ring is free: every wave is past the barrier above)
+      // one head half at a time and written back one 2 KiB head row per 512 threads (whole
+      // lines; as streaming stores they slowed the combine that reads them, 10.7 -> 12.6 us).
+      constexpr int PS = kDV + 4;                       // padded fp32 row of one head in LDS
+      static_assert(32 * PS * 4 <= LDSB, "partial staging");
+      float* s_po = reinterpret_cast<float*>(s_lds);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
-        *reinterpret_cast<f32x4_t*>(po + 4 * m) = f32x4_t{o32[0][r], o32[1][r], o32[2][r], o32[3][r]};
+      for (int half = 0; half < 2; ++half) {
+        if (half) __syncthreads();                      // the first half is written out
+        if (hh == half) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
+            *reinterpret_cast<f32x4_t*>(s_po + l32 * PS + VC * vh + 4 * m) =
+                f32x4_t{o32[0][r], o32[1][r], o32[2][r], o32[3][r]};
+          }
+        }
+        __syncthreads();
+        float* po = a.part_o + ((int64_t)t * a.H + hg * 64 + 32 * half) * a.n_split * kDV +
+                    (int64_t)split * kDV;
+        for (int q = threadIdx.x * 4; q < 32 * kDV; q += NT * 4) {
+          const int hr = q / kDV;
+          const int col = q - hr * kDV;
+          *reinterpret_cast<f32x4_t*>(po + (int64_t)hr * a.n_split * kDV + col) =
+              *reinterpret_cast<const f32x4_t*>(s_po + hr * PS + col);
+        }
       }
       if (hl == 0 && vh == 0) {
         float* pml = a.part_ml + (((int64_t)t * a.H + headw) * a.n_split + split) * 2;
