@@ -276,6 +276,25 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   const int c0 = 2 * threadIdx.x;
   const uint32_t r0 = c0 < a.n_chunks ? cnt[2 * c0 + 1] : 0u;
   const uint32_t r1 = c0 + 1 < a.n_chunks ? cnt[2 * c0 + 3] : 0u;
+  // Up to RU * kNT candidates stay in registers (kk, pp) for every later step. With at most
+  // 64 chunks, the first SJ = 2^sj_log candidates of every chunk fill those slots exactly
+  // (slot q = u * kNT + thread: chunk q >> sj_log, entry q & (SJ - 1)); they are requested
+  // together with the counts, a round trip earlier than counts-then-candidates, and masked
+  // once the counts are known. A chunk holding more than SJ (rare) takes the general path.
+  constexpr int RU = 8;
+  uint32_t kk[RU];
+  int32_t pp[RU];
+  const int sj_log = 31 - __clz((RU * kNT) / max(a.n_chunks, 1));   // uniform
+  if (sj_log >= 6) {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int q = u * kNT + threadIdx.x;
+      const int cc = min(q >> sj_log, a.n_chunks - 1);
+      const int64_t at = ((int64_t)t * a.n_chunks + cc) * kTopkChunk + (q & ((1 << sj_log) - 1));
+      kk[u] = a.cand_key[at];
+      pp[u] = a.cand_pos[at];
+    }
+  }
   int n = a.row_len[t];
   n = min(max(n, 0), a.n_max);
   const int nch = (n + kTopkChunk - 1) / kTopkChunk;
@@ -294,13 +313,16 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
     const uint32_t v0 = c0 < nch ? r0 : 0u;
     const uint32_t v1 = c0 + 1 < nch ? r1 : 0u;
     for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
+    if (threadIdx.x == 0) s_res[4] = 0;           // set below if a chunk overflows SJ
     uint32_t total;
     const uint32_t incl = block_incl_scan<kNT>(v0 + v1, s_w, &total);
     if (c0 < nch) s_off[c0] = incl - v0 - v1;
     if (c0 + 1 < nch) s_off[c0 + 1] = incl - v1;
     if (threadIdx.x == 0) s_off[nch] = total;
+    if (sj_log >= 6 && (v0 > (1u << sj_log) || v1 > (1u << sj_log))) s_res[4] = 1;
     lds_barrier();
   }
+  const bool spec = sj_log >= 6 && s_res[4] == 0;    // uniform
   const uint32_t n_cand = s_off[nch];
   const bool in_lds = CAND > 0 && n_cand <= (uint32_t)CAND;
   // Chunk of candidate i (candidates are numbered chunk by chunk): the largest c < nch with
@@ -317,13 +339,27 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   };
   auto key_of = [&](uint32_t i) { return in_lds ? s_ck[i] : a.cand_key[cand_at(i)]; };
   auto pos_of = [&](uint32_t i) { return in_lds ? s_cp[i] : a.cand_pos[cand_at(i)]; };
-  // 1. gather the candidates; histogram of their second digit. Up to RU * kNT candidates stay
-  // in registers (candidate u * kNT + thread) for every later step.
-  constexpr int RU = 8;
+  // 1. gather the candidates; histogram of their second digit. In registers: slot u of this
+  // thread holds a candidate when bit u of vmask is set (the speculative layout above, or
+  // candidate u * kNT + thread of the general path).
   const bool in_regs = n_cand <= (uint32_t)(RU * kNT);
-  uint32_t kk[RU];
-  int32_t pp[RU];
-  for (uint32_t i0 = 0; i0 < n_cand; i0 += RU * kNT) {
+  uint32_t vmask = 0;
+  if (spec) {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int q = u * kNT + threadIdx.x;
+      const int c = q >> sj_log;
+      const uint32_t j = (uint32_t)(q & ((1 << sj_log) - 1));
+      if (c < nch && j < s_off[c + 1] - s_off[c]) {
+        vmask |= 1u << u;
+        atomicAdd(&s_hist[(kk[u] >> D2) & (kHistBins - 1)], 1u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) vmask |= (uint32_t)(u * kNT + threadIdx.x < (int)n_cand) << u;
+  }
+  for (uint32_t i0 = 0; !spec && i0 < n_cand; i0 += RU * kNT) {
     // lanes past the end re-read the last candidate (n_cand >= 1: the bin holds the k-th key)
     uint32_t ic[RU];
     int lo[RU];
@@ -365,14 +401,14 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   if (in_regs) {
     auto get_key = [&](int u, uint32_t& key) {
       key = kk[u];
-      return u * kNT + threadIdx.x < n_cand;
+      return (vmask >> u & 1u) != 0;
     };
     thr = radix_select_regs<kNT, RU>(get_key, pre << D2, ~0u << D2, D2, need, &eq, s_hist, s_w, s_res);
     if (eq > need) {
       uint32_t need2 = need, eq2 = 0;
       auto get_tie = [&](int u, uint32_t& key) {
         key = ~(uint32_t)pp[u];
-        return u * kNT + threadIdx.x < n_cand && kk[u] == thr;
+        return (vmask >> u & 1u) != 0 && kk[u] == thr;
       };
       pos_thr = radix_select_regs<kNT, RU>(get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
     }
@@ -400,7 +436,7 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
     uint32_t sel = 0, m = 0;
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
-      const bool x = u * kNT + threadIdx.x < n_cand && selected(kk[u], pp[u]);
+      const bool x = (vmask >> u & 1u) != 0 && selected(kk[u], pp[u]);
       sel |= (uint32_t)x << u;
       m += x;
     }
