@@ -165,10 +165,13 @@ __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
       n_eq += dg == d1;
     }
   }
-  uint32_t tot_gt, tot_eq;
-  block_incl_scan<kNT>(n_gt, s_w, &tot_gt);
-  const uint32_t inc_eq = block_incl_scan<kNT>(n_eq, s_w, &tot_eq);
-  uint32_t o_eq = inc_eq - n_eq;
+  // one scan for both counts: above the bin in the high 16 bits, in it in the low 16 (a chunk
+  // holds kTopkChunk <= 65535 candidates, so the low half never carries into the high one)
+  static_assert(kTopkChunk < 65536, "packed counts");
+  uint32_t tot;
+  const uint32_t inc = block_incl_scan<kNT>((n_gt << 16) | n_eq, s_w, &tot);
+  const uint32_t tot_gt = tot >> 16, tot_eq = tot & 0xFFFFu;
+  uint32_t o_eq = (inc & 0xFFFFu) - n_eq;
   const int64_t region = ((int64_t)t * a.n_chunks + blockIdx.x) * kTopkChunk;
   uint32_t* ck = a.cand_key + region;
   int32_t* cp = a.cand_pos + region;
