@@ -135,8 +135,9 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   // workgroup (the waves split the value columns) and about two workgroups per CU, so two
   // gathered blocks are in flight per CU (splits never go below one 32-row block). With many
   // rows (16 or more) there is enough parallelism to share each gathered block among 64
-  // heads instead (a quarter of the gathers), one workgroup per CU, splits only to reach
-  // one workgroup per CU. Prefill rows have no split; all heads of a row share each block.
+  // heads instead (a quarter of the gathers; 8-wave workgroups, one per CU), splits only to
+  // reach one workgroup per CU. Prefill rows have no split; all heads of a row share each
+  // block.
   // Blocks stream through a ring of two.
   MlaPlan p;
   const int tiles = H / 16;

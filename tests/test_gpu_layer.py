@@ -25,8 +25,8 @@ DECODE = [
     ("spec_b3_q4", "glm_decode", dict(n_ctx=20000, B=3, q_len=4, ctx_lens=(20000, 17001, 900), H=16)),
     ("extend_64_20k", "glm_decode", dict(n_ctx=20000, q_len=64, H=16)),
     ("spec_b24_q4", "glm_decode", dict(n_ctx=9000, B=24, q_len=4, H=16, topk=512)),
-    # 16 rows x 64 heads: the attention shares each gathered block among all 64 heads, with
-    # splits and a ring of four blocks
+    # 16 rows x 64 heads: the attention shares each gathered block among all 64 heads (8-wave
+    # workgroups), with splits
     ("spec_b4_q4_h64", "glm_decode", dict(n_ctx=6000, B=4, q_len=4, ctx_lens=(6000, 5001, 2100, 4444))),
 ]
 
