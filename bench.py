@@ -373,8 +373,8 @@ def main():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the single-GPU hot path only; multi-GPU runs are not part of this "
-              "build (see DESIGN.md for how the layer shards)", file=sys.stderr)
+        print("bench.py measures the single-GPU hot path only: the library runs the layer on one "
+              "GPU's share (heads or a slice of the candidates), with no collectives", file=sys.stderr)
         sys.exit(2)
 
     import torch
