@@ -317,8 +317,15 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
     const uint32_t v1 = c0 + 1 < nch ? r1 : 0u;
     for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
     if (threadIdx.x == 0) s_res[4] = 0;           // set below if a chunk overflows SJ
-    uint32_t total;
-    const uint32_t incl = block_incl_scan<kNT>(v0 + v1, s_w, &total);
+    // up to 128 chunks every count sits in wave 0 (the other waves hold zeros): a wave scan,
+    // no workgroup barriers
+    uint32_t total, incl;
+    if (nch <= 128) {
+      incl = wave_incl_scan(v0 + v1);
+      total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    } else {
+      incl = block_incl_scan<kNT>(v0 + v1, s_w, &total);
+    }
     if (c0 < nch) s_off[c0] = incl - v0 - v1;
     if (c0 + 1 < nch) s_off[c0 + 1] = incl - v1;
     if (threadIdx.x == 0) s_off[nch] = total;
