@@ -25,6 +25,8 @@ LSE_TOL = 1e-3
 def scores_ok(gpu: np.ndarray, ref: np.ndarray) -> tuple[bool, str]:
     ref = np.asarray(ref, dtype=np.float64)
     gpu = np.asarray(gpu, dtype=np.float64)
+    if gpu.shape != ref.shape:
+        return False, f"shape {gpu.shape} != {ref.shape}"
     if ref.size == 0:
         return gpu.size == 0, "empty"
     floor = 1e-3 * np.abs(ref).max()
@@ -41,10 +43,12 @@ def topk_ok(ref_scores: np.ndarray, k: int, gpu_idx: np.ndarray, gpu_len: int) -
     n = int(ref_scores.shape[0])
     m = min(k, n)
     gpu_idx = np.asarray(gpu_idx, dtype=np.int64)
+    if gpu_idx.ndim != 1 or gpu_idx.shape[0] < k:
+        return False, f"index row of shape {gpu_idx.shape} for topk {k}"
     if int(gpu_len) != m:
         return False, f"lens {gpu_len} != {m}"
     sel = gpu_idx[:m]
-    if np.any(gpu_idx[m:] != -1):
+    if np.any(gpu_idx[m:k] != -1):
         return False, "entries after lens are not -1"
     if np.any(sel < 0) or np.any(sel >= n):
         return False, "selected position out of range"
@@ -65,6 +69,9 @@ def topk_ok(ref_scores: np.ndarray, k: int, gpu_idx: np.ndarray, gpu_len: int) -
 
 def attention_ok(out_gpu, lse_gpu, out_ref, lse_ref, fmt: str) -> tuple[bool, str]:
     out_gpu = np.asarray(out_gpu, dtype=np.float64)
+    out_ref = np.asarray(out_ref, dtype=np.float64)
+    if out_gpu.shape != out_ref.shape:
+        return False, f"out shape {out_gpu.shape} != {out_ref.shape}"
     err = float(np.abs(out_gpu - out_ref).max()) if out_ref.size else 0.0
     if not np.isfinite(out_gpu).all():
         return False, "non-finite output"
@@ -73,6 +80,11 @@ def attention_ok(out_gpu, lse_gpu, out_ref, lse_ref, fmt: str) -> tuple[bool, st
         return False, msg
     if lse_gpu is not None:
         lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
+        lse_ref = np.asarray(lse_ref, dtype=np.float64)
+        if lse_gpu.shape != lse_ref.shape:
+            return False, msg + f"; lse shape {lse_gpu.shape} != {lse_ref.shape}"
+        if np.isnan(lse_gpu).any():
+            return False, msg + "; NaN lse"
         inf_ref = np.isneginf(lse_ref)
         if not np.array_equal(np.isneginf(lse_gpu), inf_ref):
             return False, msg + "; -inf lse mismatch"
