@@ -7,19 +7,6 @@
 
 namespace dsa {
 
-// Reserve one output slot per lane with `pred` set: one LDS atomic per wave (ballot +
-// popcount) instead of one per element, which serialises on a single address.
-__device__ __forceinline__ uint32_t wave_reserve(bool pred, uint32_t* counter) {
-  const uint64_t m = __ballot(pred);
-  if (m == 0) return 0u;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)m) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-  base = __shfl(base, leader);
-  return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-}
-
 // Inclusive scan over the 64 lanes with DPP moves (a few cycles each) instead of LDS
 // permutes: shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the row totals carried
 // forward with the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (rows 2, 3).

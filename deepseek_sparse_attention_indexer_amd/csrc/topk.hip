@@ -6,12 +6,14 @@
 // Ties are broken toward the smaller position, so the selected SET is deterministic.
 //
 // Method: radix select on the order-preserving uint32 image of the fp32 scores, most
-// significant digit first, counting with histograms and reserving output slots with atomic
-// adds (the threshold / greater / equal counting of the PR 627 selector). Digits are 12, 12
-// and 8 bits. When more candidates share the threshold key than slots remain, the ties are
-// resolved by a second radix select on the complemented position.
+// significant digit first, counting with histograms (the threshold / greater / equal counting
+// of the PR 627 selector). Digits are 12, 12 and 8 bits. When more candidates share the
+// threshold key than slots remain, the ties are resolved by a second radix select on the
+// complemented position. Output slots come from prefix sums of the selection counts, never
+// from racing atomics, so the list's order is the same on every run.
 //
-//  * k_topk_lds: one 512-thread workgroup per row, the row's keys held in LDS (<= 16K).
+//  * k_topk_lds: one 512-thread workgroup per row, the row's keys held in LDS (<= 16K); the
+//    list is in position order.
 //  * long rows: the first-digit histogram is built per chunk (k_topk_hist, or fused into
 //    the score kernel). k_topk_filter's workgroups (one per chunk) find the threshold bin and
 //    write their chunk's threshold-bin candidates and counts. In k_topk_finalize one
@@ -50,7 +52,6 @@ __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
   }
   const float* row = a.logits + (int64_t)t * a.ld_logits;
   for (int i = threadIdx.x; i < n; i += kNT) s_key[i] = float_key(row[i]);
-  if (threadIdx.x == 0) s_res[2] = 0;
   lds_barrier();
 
   uint32_t need = (uint32_t)k, eq = 0;
@@ -64,11 +65,38 @@ __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
     pos_thr = radix_select_desc<kNT>(n, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
   }
   const bool all_ties = eq <= need;
-  for (int i0 = 0; i0 < n; i0 += kNT) {       // uniform trip count: wave_reserve needs all lanes
-    const int i = i0 + threadIdx.x;
+  // Compaction in position order, so the list (and everything computed from it in list order)
+  // is the same on every run: the selected count of every (pass, wave) pair, one scan over
+  // those counts (pass-major), then each lane writes at its pair's offset plus the selected
+  // lanes below it. The histogram is free for the counts.
+  constexpr int NW = kNT / 64;
+  static_assert((CAP / kNT) * NW <= kNT && (CAP / kNT) * NW <= kHistBins, "pair counts");
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int n_pass = (n + kNT - 1) / kNT;
+  auto selected = [&](int i) {
     const uint32_t key = i < n ? s_key[i] : 0u;
-    const bool sel = i < n && (key > thr || (key == thr && (all_ties || ~(uint32_t)i >= pos_thr)));
-    const uint32_t o = wave_reserve(sel, &s_res[2]);
+    return i < n && (key > thr || (key == thr && (all_ties || ~(uint32_t)i >= pos_thr)));
+  };
+  for (int ps = 0; ps < n_pass; ++ps) {
+    const uint64_t m = __ballot(selected(ps * kNT + (int)threadIdx.x));
+    if (lane == 0) s_hist[ps * NW + wv] = (uint32_t)__popcll(m);
+  }
+  lds_barrier();
+  {
+    const int j = threadIdx.x;
+    const uint32_t c = j < n_pass * NW ? s_hist[j] : 0u;
+    const uint32_t incl = block_incl_scan<kNT>(c, s_w, nullptr);
+    lds_barrier();                             // every count read before the offsets replace them
+    if (j < n_pass * NW) s_hist[j] = incl - c;
+  }
+  lds_barrier();
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int ps = 0; ps < n_pass; ++ps) {
+    const int i = ps * kNT + threadIdx.x;
+    const bool sel = selected(i);
+    const uint64_t m = __ballot(sel);
+    const uint32_t o = s_hist[ps * NW + wv] + (uint32_t)__popcll(m & below);
     if (sel && o < (uint32_t)k) out[o] = i;
   }
   if (threadIdx.x == 0) a.lens[t] = k;

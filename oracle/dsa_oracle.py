@@ -41,7 +41,10 @@ What it computes, per query row t of request b that sees candidates s in [0, n_t
        dc_i[:d_qk] += softmax_scale * dl_i * q[h, :],   dc_i[:d_v] += p_i * dout[h, :],
        dsink_h = -p_sink * D_h
    summed over heads for dc_i; an entry listed twice contributes twice (each listed entry is
-   its own term of the softmax).
+   its own term of the softmax). The backward is handed the forward's outputs (the same PR's
+   forward bullet: the backward takes the forward's lse); when they are given, lse_h and
+   out[h, :] are taken as given (p_i and p_sink from that lse, D_h from that out), which is
+   exactly the gradient above when they equal the forward's exact values.
 """
 from __future__ import annotations
 
@@ -255,16 +258,23 @@ def attention_math(q: np.ndarray, rows: np.ndarray, sink: np.ndarray, scale: flo
 
 
 def attention_backward_math(q: np.ndarray, rows: np.ndarray, sink: np.ndarray, scale: float,
-                            d_qk: int, d_v: int, dout: np.ndarray):
+                            d_qk: int, d_v: int, dout: np.ndarray, out: np.ndarray | None = None,
+                            lse: np.ndarray | None = None):
     """Step 5 on float64 arrays (q [H, d_qk], rows [n >= 1, D], sink [H], dout [H, d_v]).
+    out [H, d_v] and lse [H] (natural log), when given, are the forward's outputs as handed to
+    the backward; otherwise the exact forward values are used.
     Returns (dq [H, d_qk], drows [n, max(d_qk, d_v)] per listed entry, dsink [H])."""
     logits = scale * (q @ rows[:, :d_qk].T)                     # [H, n]
-    m = np.maximum(logits.max(axis=1), sink)[:, None]
-    lse = m + np.log(np.exp(logits - m).sum(axis=1, keepdims=True) + np.exp(sink[:, None] - m))
+    if lse is None:
+        m = np.maximum(logits.max(axis=1), sink)[:, None]
+        lse = m + np.log(np.exp(logits - m).sum(axis=1, keepdims=True) + np.exp(sink[:, None] - m))
+    else:
+        lse = np.asarray(lse, dtype=np.float64)[:, None]
     p = np.exp(logits - lse)                                    # [H, n]
     p_sink = np.exp(sink[:, None] - lse)[:, 0]                  # [H]
-    out = p @ rows[:, :d_v]                                     # [H, d_v]
-    D = (dout * out).sum(axis=1)                                # [H]
+    if out is None:
+        out = p @ rows[:, :d_v]                                 # [H, d_v]
+    D = (dout * np.asarray(out, dtype=np.float64)).sum(axis=1)  # [H]
     dp = dout @ rows[:, :d_v].T                                 # [H, n]
     dl = p * (dp - D[:, None])                                  # [H, n]
     dq = scale * (dl @ rows[:, :d_qk])                          # [H, d_qk]
@@ -275,10 +285,12 @@ def attention_backward_math(q: np.ndarray, rows: np.ndarray, sink: np.ndarray, s
     return dq, drows, dsink
 
 
-def attention_backward_row(prob, t: int, idx: np.ndarray, dout: np.ndarray):
-    """Step 5 for row t over one list (main cache): dout float64 [H, d_v]. Returns
-    (dq [H, d_qk], slots [n] of the valid listed entries in list order, drows [n, D],
-    dsink [H]); an empty list gives zeros."""
+def attention_backward_row(prob, t: int, idx: np.ndarray, dout: np.ndarray,
+                           out: np.ndarray | None = None, lse: np.ndarray | None = None):
+    """Step 5 for row t over one list (main cache): dout float64 [H, d_v]. out [H, d_v] and
+    lse [H] (in the base prob.lse_log2 names), when given, are the forward's outputs handed to
+    the backward. Returns (dq [H, d_qk], slots [n] of the valid listed entries in list order,
+    drows [n, D], dsink [H]); an empty list gives zeros."""
     b = int(prob.row_req[t])
     lst = np.asarray(idx, dtype=np.int64)
     keep = lst[lst != -1]
@@ -290,8 +302,12 @@ def attention_backward_row(prob, t: int, idx: np.ndarray, dout: np.ndarray):
         return np.zeros((H, prob.d_qk)), np.zeros(0, np.int64), np.zeros((0, D)), np.zeros(H)
     rows = kv_rows(prob.kv, b, keep)
     q = bf16_to_f64(prob.q[t])
+    if lse is not None:
+        base = math.log(2.0) if getattr(prob, "lse_log2", False) else 1.0
+        lse = np.asarray(lse, dtype=np.float64) * base
     dq, drows, dsink = attention_backward_math(q, rows, sink, float(prob.softmax_scale), prob.d_qk,
-                                               prob.d_v, np.asarray(dout, dtype=np.float64))
+                                               prob.d_v, np.asarray(dout, dtype=np.float64),
+                                               out=out, lse=lse)
     return dq, slots_of(prob.kv, b, keep), drows, dsink
 
 

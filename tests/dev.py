@@ -98,18 +98,30 @@ def run_decode(prob, d=None):
     return out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), lens.cpu().numpy()
 
 
-def run_backward(prob, dout, d=None, idx=None, with_dsink=False):
-    """Forward (one workgroup per row) for out and lse, then the backward. dout: float32 numpy
-    [T, H, d_v], rounded to bf16 here (the tests hand the same bf16 values to the oracle).
+def bf16_round(x):
+    """float array -> the float64 values of its bf16 rounding (RNE, torch cast)."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy() \
+        .astype(np.float64)
+
+
+def run_backward(prob, dout, d=None, idx=None, with_dsink=False, fwd=None):
+    """The backward. Its forward outputs: fwd = (out [T, H, d_v], lse [T, H]) given as numpy
+    (out is rounded to bf16, lse to fp32 on the way in), or None for the GPU's own forward
+    (one workgroup per row). dout: float32 numpy [T, H, d_v], rounded to bf16 here (the tests
+    hand the same bf16 values to the oracle).
     Returns (dq [T, H, d_qk], dkv [n_slots, d_qk], dsink [H] or None, dout as float64)."""
     m = dsa()
     d = d or upload(prob)
     idx_main = d.idx_main if idx is None else idx
     T, H = prob.T, prob.H
-    out = torch.full((T, H, prob.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
-    lse = torch.full((T, H), float("nan"), device="cuda")
-    m.dsa_sparse_mla_prefill(d.q, d.kv, idx_main, None, None, d.rows, H, prob.d_qk, prob.d_v,
-                             prob.softmax_scale, out, lse, sink=d.sink, lse_log2=d.lse_log2)
+    if fwd is None:
+        out = torch.full((T, H, prob.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((T, H), float("nan"), device="cuda")
+        m.dsa_sparse_mla_prefill(d.q, d.kv, idx_main, None, None, d.rows, H, prob.d_qk, prob.d_v,
+                                 prob.softmax_scale, out, lse, sink=d.sink, lse_log2=d.lse_log2)
+    else:
+        out = torch.from_numpy(np.ascontiguousarray(fwd[0], dtype=np.float32)).to(torch.bfloat16).cuda()
+        lse = torch.from_numpy(np.ascontiguousarray(fwd[1], dtype=np.float32)).cuda()
     do = torch.from_numpy(np.ascontiguousarray(dout, dtype=np.float32)).to(torch.bfloat16).cuda()
     dq = torch.full((T, H, prob.d_qk), float("nan"), device="cuda")
     dkv = torch.zeros((int(d.kv.c.n_slots), prob.d_qk), device="cuda")

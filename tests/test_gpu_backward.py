@@ -2,15 +2,23 @@
 oracle's exact gradient (step 5 of the oracle's description).
 
 The kernel's inputs are bf16 and exact; what it rounds: P and scale * dZ to bf16 as MFMA
-operands (2^-9 relative per term), D from the forward's bf16 out, fp32 accumulation (and fp32
-atomics in any order for dkv). dq and dkv are held to 2% of the largest reference value of the
-(row, head) and of the whole dkv respectively (measured worst: 0.3% and 0.4%); the sink
-gradient to a bound derived from D's rounding (below)."""
+operands (2^-9 relative per term), fp32 accumulation (and fp32 atomics in any order for dkv).
+dq and dkv are held to 2% of the largest reference value of the (row, head) and of the whole
+dkv respectively (measured worst: 0.3% and 0.4%).
+
+Two ways to feed the backward its forward outputs (out, lse):
+* the oracle's forward, out rounded to bf16 and lse to fp32 (test_backward): the reference is
+  the oracle's gradient taken at those same given outputs (D from the given out, P from the
+  given lse), so no forward error is charged to the backward, and the sink gradient, which
+  needs no bf16 operand, is held to 2e-2 relative;
+* the GPU's own forward (test_backward_chained, the end-to-end case): the reference is the
+  exact gradient, and the sink gradient is held to a bound derived from the rounding of D
+  that the bf16 out brings (below)."""
 import numpy as np
 import pytest
 
 import oracle
-from dev import need_gpu, run_backward, say, upload, workload
+from dev import bf16_round, need_gpu, run_backward, say, upload, workload
 
 pytestmark = [pytest.mark.gpu, need_gpu]
 
@@ -24,13 +32,14 @@ CASES = [
 ]
 
 
-def _reference(prob, idx, dout):
+def _reference(prob, idx, dout, fwd=None):
     T, H = prob.T, prob.H
     dq = np.zeros((T, H, prob.d_qk))
     dkv = {}
     dsink = np.zeros(H)
     for t in range(T):
-        q_t, slots, drows, ds = oracle.attention_backward_row(prob, t, idx[t], dout[t])
+        given = {} if fwd is None else {"out": fwd[0][t], "lse": fwd[1][t]}
+        q_t, slots, drows, ds = oracle.attention_backward_row(prob, t, idx[t], dout[t], **given)
         dq[t] = q_t
         for s, r in zip(slots.tolist(), drows[:, :prob.d_qk]):
             dkv[s] = dkv.get(s, 0.0) + r
@@ -38,8 +47,10 @@ def _reference(prob, idx, dout):
     return dq, dkv, dsink
 
 
-def _check(prob, idx, dout, dq, dkv, dsink=None):
-    dq_ref, dkv_ref, dsink_ref = _reference(prob, idx, dout)
+def _check(prob, idx, dout, dq, dkv, dsink=None, fwd=None):
+    """fwd: the (out, lse) the kernel was handed, as the float64 values it received, or None
+    (the GPU's own forward; the reference is then the exact gradient)."""
+    dq_ref, dkv_ref, dsink_ref = _reference(prob, idx, dout, fwd)
     err = np.abs(dq - dq_ref)
     scale = np.abs(dq_ref).max(axis=2, keepdims=True)
     worst = float((err / (scale + 1e-30)).max()) if dq_ref.size else 0.0
@@ -56,7 +67,19 @@ def _check(prob, idx, dout, dq, dkv, dsink=None):
             "frobenius rel", float(np.linalg.norm(got - ref) / np.linalg.norm(ref)))
         assert np.all(e <= 2e-2 * np.abs(ref).max() + 1e-5), "dkv"
     assert np.all(dkv[~touched] == 0.0), "dkv rows outside the lists changed"
-    if dsink is not None:
+    if dsink is not None and fwd is not None:
+        # the reference takes D from the same bf16 out and p_sink from the same lse: what is
+        # left is fp32 arithmetic (and atomic order), far inside 2e-2 relative; the floor covers
+        # a head whose rows' terms cancel
+        terms = np.zeros(prob.H)
+        sink = np.asarray(prob.sink, dtype=np.float64)
+        base = np.log(2.0) if getattr(prob, "lse_log2", False) else 1.0
+        for t in range(prob.T):
+            terms += np.exp(sink - fwd[1][t] * base) * np.abs((dout[t] * fwd[0][t]).sum(axis=1))
+        err = np.abs(dsink - dsink_ref)
+        say("  dsink: max err", float(err.max()), "max rel", float((err / (np.abs(dsink_ref) + 1e-30)).max()))
+        assert np.all(err <= 2e-2 * np.abs(dsink_ref) + 1e-6 * terms + 1e-7), "dsink"
+    elif dsink is not None:
         # dsink_h = -sum_t p_sink D with D = dout . out, and the kernel takes D from the forward's
         # bf16 out (rounding error <= 2^-9 per element): |error| <= sum_t p_sink 2^-8 sum_d
         # |dout| |out| (a factor 2 for the fp32 sum), which stays the same when D cancels
@@ -71,10 +94,37 @@ def _check(prob, idx, dout, dq, dkv, dsink=None):
         assert np.all(np.abs(dsink - dsink_ref) <= bound + 2.0 ** -8 * np.abs(dsink_ref) + 1e-5), "dsink"
 
 
+def _oracle_forward(prob, idx):
+    """The oracle's forward outputs as the backward receives them: out rounded to bf16 (RNE),
+    lse to fp32, both returned as the float64 values handed over."""
+    outs, lses = [], []
+    for t in range(prob.T):
+        o, l = oracle.attention_row(prob, t, idx[t])
+        outs.append(o)
+        lses.append(l)
+    out = bf16_round(np.stack(outs))
+    lse = np.stack(lses).astype(np.float32).astype(np.float64)
+    return out, lse
+
+
 @pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
 def test_backward(name, kw):
+    """The backward on the oracle's forward outputs."""
     prob = workload("attention_case", **kw)
-    say("backward", name)
+    say("backward (oracle forward)", name)
+    rng = np.random.default_rng(len(name))
+    dout = rng.standard_normal((prob.T, prob.H, prob.d_v)).astype(np.float32)
+    with_dsink = getattr(prob, "sink", None) is not None
+    fwd = _oracle_forward(prob, prob.idx_main)
+    dq, dkv, dsink, do = run_backward(prob, dout, with_dsink=with_dsink, fwd=fwd)
+    _check(prob, prob.idx_main, do, dq, dkv, dsink, fwd=fwd)
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_backward_chained(name, kw):
+    """End to end: the GPU's forward, then the backward, against the exact gradient."""
+    prob = workload("attention_case", **kw)
+    say("backward (GPU forward)", name)
     rng = np.random.default_rng(len(name))
     dout = rng.standard_normal((prob.T, prob.H, prob.d_v)).astype(np.float32)
     with_dsink = getattr(prob, "sink", None) is not None

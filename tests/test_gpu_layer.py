@@ -98,20 +98,45 @@ def test_prefill_chain_small_all_rows():
     _check_prefill_rows(prob, _prefill_chain(prob), range(prob.T))
 
 
-def test_prefill_chain_full_size_sampled_rows():
+def _prefill_sample(prob, n=256, seed=7):
+    """A seeded stratified sample of the causal prefill's rows: one row from each of n - 24
+    equal strata of the 8192-token segment, plus fixed rows: the first, every row 2040..2055
+    (where the -1 padding ends at topk 2048), the last of the segment and the 1-token segment."""
+    fixed = [0, 1, 2, 63, 64] + list(range(2040, 2056)) + [4096, 8191, prob.T - 1]
+    seg = int(prob.row_len[prob.T - 2])                        # the long segment's length
+    rng = np.random.default_rng(seed)
+    edges = np.linspace(0, seg, n - len(fixed) + 1).astype(int)
+    strat = [int(rng.integers(lo, hi)) for lo, hi in zip(edges[:-1], edges[1:]) if hi > lo]
+    rows = sorted(set(fixed) | set(strat))
+    assert len(rows) >= n - 8
+    return rows
+
+
+def test_prefill_chain_full_size():
     """One 8192-token segment plus a 1-token segment, topk 2048 with -1 padding for the first
-    2047 rows; sampled rows are compared whole, every row's top-k shape is checked."""
+    2047 rows. Every row: the top-k set equals the oracle's stable top-k of the GPU's own fp32
+    logits exactly (the selection is integer work on the same scores), lens and the -1 tail.
+    A stratified sample of 256 rows: scores against the fp64 oracle, rule T against the
+    oracle's fp64 scores, attention against the oracle on the GPU's selection."""
     prob = workload("causal_prefill", seg_lens=(8192, 1))
     say("prefill chain 8193 rows")
     res = _prefill_chain(prob)
-    _, idx, lens, out, _ = res
+    logits, idx, lens, out, _ = res
     exp_lens = np.minimum(prob.row_len, prob.topk)
     assert np.array_equal(lens, exp_lens)
-    for t in range(prob.T):
-        m = int(exp_lens[t])
-        assert np.all(idx[t, m:] == -1) and np.all(idx[t, :m] >= 0) and np.all(idx[t, :m] < prob.row_len[t])
     assert np.isfinite(out).all()
-    _check_prefill_rows(prob, res, [0, 1, 2, 2046, 2047, 2048, 5000, 8191, 8192])
+    for t in range(prob.T):
+        n = int(prob.row_len[t])
+        m = int(exp_lens[t])
+        ref_idx, m_ref = oracle.topk_row(logits[t, :n].astype(np.float64), prob.topk)
+        assert m_ref == m
+        assert np.all(idx[t, m:] == -1), f"row {t}: padding"
+        got = idx[t, :m]
+        assert np.unique(got).size == m, f"row {t}: duplicates"
+        assert set(got.tolist()) == set(ref_idx[:m].tolist()), f"row {t}: set differs from the exact top-k of its logits"
+    rows = _prefill_sample(prob)
+    say(f"  all {prob.T} top-k sets exact; {len(rows)} sampled rows against the oracle")
+    _check_prefill_rows(prob, res, rows)
     # the 1-token segment attends to its own row only
     row = oracle.kv_rows(prob.kv, 1, np.array([0]))[0]
     assert np.abs(out[8192] - row[None, :512]).max() < 2e-2

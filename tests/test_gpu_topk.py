@@ -43,6 +43,9 @@ CASES = [
     ("long_short_row", 3, [17000, 1500, 16385], 2048, None),
     ("long_batches", 70, [17000] * 70, 256, 32),
     ("long_1m", 1, [1 << 20], 2048, None),
+    # 65..128 chunks of 4096 candidates: the chunk counts are scanned by one wave whose upper
+    # lanes carry counts, and the resolver gathers its candidates in the general way
+    ("long_400k", 2, [400000, 300000], 2048, 256),
 ]
 
 
@@ -87,8 +90,10 @@ def test_topk_workspace_reuse_is_clean():
         _check(x, [40000, 39000], 512, idx, lens)
 
 
-@pytest.mark.parametrize("T,n,ties", [(2, 131072, 6000), (2, 40000, 9000), (70, 17000, 6000)],
-                         ids=["few_rows_6000_ties", "few_rows_9000_ties", "70_rows_6000_ties"])
+@pytest.mark.parametrize("T,n,ties", [(2, 131072, 6000), (2, 40000, 9000), (70, 17000, 6000),
+                                      (2, 400000, 5000)],
+                         ids=["few_rows_6000_ties", "few_rows_9000_ties", "70_rows_6000_ties",
+                              "400k_5000_ties"])
 def test_topk_threshold_bin_capacity(T, n, ties):
     """The resolver holds up to 4096 threshold-bin candidates in registers, up to 8192 more in
     LDS when the grid is small, and re-reads the workspace otherwise (always, for a large

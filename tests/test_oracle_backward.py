@@ -75,3 +75,52 @@ def test_backward_rope_gradient_sums_to_zero_without_sink():
     _, drows, _ = oracle.attention_backward_math(q, rows, np.full(H, -np.inf), 0.3, d_qk, d_v, dout)
     assert np.abs(drows[:, d_v:].sum(axis=0)).max() < 1e-12
     assert np.abs(drows[:, :d_v].sum(axis=0)).max() > 1e-3      # the value part does not cancel
+
+
+def _given_case(seed=21):
+    rng = np.random.default_rng(seed)
+    H, n, d_qk, d_v = 3, 6, 20, 16
+    q = rng.standard_normal((H, d_qk))
+    rows = rng.standard_normal((n, d_qk))
+    sink = np.array([0.4, -np.inf, -0.9])
+    dout = rng.standard_normal((H, d_v))
+    out, lse = oracle.attention_math(q, rows, sink, 0.45, d_qk, d_v)
+    return q, rows, sink, dout, out, lse, 0.45, d_qk, d_v
+
+
+def test_backward_given_forward_outputs_equal_the_exact_ones():
+    q, rows, sink, dout, out, lse, scale, d_qk, d_v = _given_case()
+    ref = oracle.attention_backward_math(q, rows, sink, scale, d_qk, d_v, dout)
+    got = oracle.attention_backward_math(q, rows, sink, scale, d_qk, d_v, dout, out=out, lse=lse)
+    for a, b in zip(ref, got):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def test_backward_given_out_enters_through_D_only():
+    """A perturbed given out (out + delta) changes only D_h by dout_h . delta_h: in closed form
+    dsink_h moves by -p_sink_h (dout_h . delta_h), dq_h by -scale (dout_h . delta_h)
+    sum_i p_i c_i[:d_qk], and the key part of drows by -scale (dout_h . delta_h) p_i q_h summed
+    over h; the value part (p_i dout_h) does not move."""
+    q, rows, sink, dout, out, lse, scale, d_qk, d_v = _given_case()
+    delta = np.random.default_rng(3).standard_normal(out.shape) * 1e-2
+    dq0, dr0, ds0 = oracle.attention_backward_math(q, rows, sink, scale, d_qk, d_v, dout, out=out, lse=lse)
+    dq1, dr1, ds1 = oracle.attention_backward_math(q, rows, sink, scale, d_qk, d_v, dout,
+                                                   out=out + delta, lse=lse)
+    dD = (dout * delta).sum(axis=1)                                     # [H]
+    p = np.exp(scale * (q @ rows[:, :d_qk].T) - lse[:, None])           # [H, n]
+    p_sink = np.exp(sink - lse)
+    assert np.allclose(ds1 - ds0, -p_sink * dD, atol=1e-14)
+    assert np.allclose(dq1 - dq0, -scale * dD[:, None] * (p @ rows[:, :d_qk]), atol=1e-13)
+    assert np.allclose(dr1[:, :d_qk] - dr0[:, :d_qk], -scale * (p * dD[:, None]).T @ q, atol=1e-13)
+    assert np.allclose(dr1[:, d_qk:], dr0[:, d_qk:], atol=0)
+
+
+def test_backward_given_lse_scales_the_weights():
+    """A given lse shifted by eps multiplies every weight p_i and p_sink by e^-eps; with out held,
+    dq, the key and value parts of drows and dsink all scale by e^-eps exactly."""
+    q, rows, sink, dout, out, lse, scale, d_qk, d_v = _given_case()
+    eps = 0.3
+    a = oracle.attention_backward_math(q, rows, sink, scale, d_qk, d_v, dout, out=out, lse=lse)
+    b = oracle.attention_backward_math(q, rows, sink, scale, d_qk, d_v, dout, out=out, lse=lse + eps)
+    for x, y in zip(a, b):
+        assert np.allclose(y, np.exp(-eps) * x, rtol=1e-12, atol=1e-15)
