@@ -9,6 +9,7 @@ without the built library raises.
 from ._binding import (  # noqa: F401
     DSAError, KeyCache, KVCache, Rows, lib_path,
     dsa_index_scores, dsa_topk, dsa_sparse_mla_decode, dsa_sparse_mla_prefill, dsa_decode,
+    dsa_decode_static, STATIC_SCRATCH_BYTES, DSA_ERR_SCRATCH_LIMIT,
     dsa_sparse_mla_backward,
     dsa_workspace_size, dsa_workspace_init, dsa_status_string, dsa_abi_version,
     dsa_profile_enable, dsa_profile_collect, dsa_kv_cache_write, dsa_key_cache_write,

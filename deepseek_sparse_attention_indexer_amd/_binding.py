@@ -23,6 +23,8 @@ if not os.path.exists(lib_path()):
 _lib = C.CDLL(lib_path())
 
 DSA_OK, DSA_ERR_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
+DSA_ERR_SCRATCH_LIMIT = -5
+STATIC_SCRATCH_BYTES = 64 << 20   # DSA_STATIC_SCRATCH_BYTES of include/dsa.h
 ENTRY_TOPK, ENTRY_MLA_DECODE, ENTRY_MLA_PREFILL, ENTRY_DECODE, ENTRY_MLA_BACKWARD = 1, 2, 3, 4, 5
 KEY_BF16, KEY_FP8 = 0, 1
 KV_BF16, KV_FP8_UNIFORM, KV_FP8_DS_MLA, KV_FP8_UNIFORM_FNUZ = 0, 1, 2, 3
@@ -80,6 +82,9 @@ _sigs = {
     "dsa_decode": [_P, _I64, _P, _I64, _P, _I64, C.POINTER(_KeyCache), C.POINTER(_KVCache),
                    C.POINTER(_Rows), _I32, _I32, _I32, _I32, _I32, _I32, _F, _F, _P, _I64, _P,
                    C.POINTER(_AttnOpts), _P, _I64, _P, _P, _SZ, _P],
+    "dsa_decode_static": [_P, _I64, _P, _I64, _P, _I64, C.POINTER(_KeyCache), C.POINTER(_KVCache),
+                          C.POINTER(_Rows), _I32, _I32, _I32, _I32, _I32, _I32, _F, _F, _P, _I64, _P,
+                          C.POINTER(_AttnOpts), _P, _I64, _P, _P],
     "dsa_workspace_init": [_P, _SZ, _P],
     "dsa_kv_cache_write": [_P, _I64, _I32, _P, C.POINTER(_KVCache), _P],
     "dsa_key_cache_write": [_P, _I64, _I32, _P, C.POINTER(_KeyCache), _I32, _P],
@@ -94,7 +99,7 @@ _lib.dsa_status_string.argtypes = [_I32]
 _lib.dsa_status_string.restype = C.c_char_p
 _lib.dsa_abi_version.argtypes = []
 _lib.dsa_abi_version.restype = _I32
-ABI_VERSION = 5   # the signatures above
+ABI_VERSION = 6   # the signatures above
 if _lib.dsa_abi_version() != ABI_VERSION:
     raise ImportError(f"{lib_path()} has ABI version {_lib.dsa_abi_version()}, this binding needs "
                       f"{ABI_VERSION}: rebuild the library")
@@ -347,3 +352,15 @@ def dsa_decode(q, q_idx, w, keys: KeyCache, kv: KVCache, rows: Rows, H: int, d_q
         int(topk), float(index_scale), float(softmax_scale), _ptr(out), _ld(out), _ptr(lse),
         _opts(sink, lse_log2), _ptr(idx_out), _ld(idx_out) if idx_out is not None else 0, _ptr(lens_out),
         ws.ptr, ws.nbytes, _stream(stream)), "dsa_decode")
+
+
+def dsa_decode_static(q, q_idx, w, keys: KeyCache, kv: KVCache, rows: Rows, H: int, d_qk: int, d_v: int,
+                      Hi: int, di: int, topk: int, index_scale: float, softmax_scale: float, out, lse,
+                      idx_out, lens_out, stream=None, sink=None, lse_log2: bool = False):
+    """dsa_decode on the library's static device scratch (no workspace argument)."""
+    _check(_lib.dsa_decode_static(
+        _ptr(q), _ld(q), _ptr(q_idx), _ld(q_idx), _ptr(w), _ld(w),
+        C.byref(keys.c), C.byref(kv.c), C.byref(rows.c), int(H), int(d_qk), int(d_v), int(Hi), int(di),
+        int(topk), float(index_scale), float(softmax_scale), _ptr(out), _ld(out), _ptr(lse),
+        _opts(sink, lse_log2), _ptr(idx_out), _ld(idx_out) if idx_out is not None else 0, _ptr(lens_out),
+        _stream(stream)), "dsa_decode_static")

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <stdint.h>
 #include <string.h>
+#include <mutex>
 #include <vector>
 
 #include "dsa.h"
@@ -474,12 +475,177 @@ dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
   }));
 }
 
+
+// ---------------------------------------------------------------- the fused layer
+struct DecodeIn {
+  const void* q;
+  int64_t ld_q;
+  const void* q_idx;
+  int64_t ld_q_idx;
+  const float* w;
+  int64_t ld_w;
+  const dsa_key_cache* keys;
+  const dsa_kv_cache* kv;
+  const dsa_rows* rows;
+  int32_t H, d_qk, d_v, Hi, di, topk;
+  float index_scale, softmax_scale;
+  void* out;
+  int64_t ld_out;
+  float* lse;
+  const dsa_attn_opts* opts;
+  int32_t* idx_out;
+  int64_t ld_idx_out;
+  int32_t* lens_out;
+};
+
+// Every argument check of the three steps, on the host (no HIP call); *need = workspace bytes.
+dsa_status decode_check(const DecodeIn& d, size_t* need) {
+  const dsa_rows* rows = d.rows;
+  dsa_status s = check_rows(rows);
+  if (s != DSA_OK) return s;
+  if (d.topk < 1) return DSA_ERR_ARG;
+  if (d.topk > 65536 || rows->n_max > kMaxChunks * kTopkChunk) return DSA_ERR_UNSUPPORTED;
+  if (d.idx_out && (!al4(d.idx_out) || d.ld_idx_out < d.topk)) return DSA_ERR_ARG;
+  if (d.lens_out && !al4(d.lens_out)) return DSA_ERR_ARG;
+  const int T = rows->T;
+  const int64_t ld = logits_ld(rows->n_max);
+  // logits and indices are workspace-backed: stand-in pointers for the checks
+  float* const dummy_f = reinterpret_cast<float*>(uintptr_t(256));
+  const ScoreIn sc{d.q_idx, d.ld_q_idx, d.w, d.ld_w, d.keys, rows, d.Hi, d.di, d.index_scale, dummy_f, ld};
+  s = check_scores(sc);
+  if (s != DSA_OK) return s;
+  const MlaIn m{d.q, d.ld_q, d.kv, reinterpret_cast<const int32_t*>(uintptr_t(256)), d.topk, d.topk,
+                nullptr, nullptr, 0, 0, T, rows->row_req, rows->n_req, d.H, d.d_qk, d.d_v,
+                d.softmax_scale, d.out, d.ld_out, d.lse, d.opts};
+  s = check_mla(m);
+  if (s != DSA_OK) return s;
+  const dsa_problem pr{T, rows->n_max, d.topk, d.H, d.topk, 0};
+  *need = dsa_workspace_size(DSA_ENTRY_DECODE, &pr);
+  return *need == SIZE_MAX ? DSA_ERR_ARG : DSA_OK;
+}
+
+// The three steps on one stream over a checked problem (T > 0) and a workspace of at least
+// the size decode_check gave, whose header is zero.
+dsa_status decode_run(const DecodeIn& d, uint8_t* wsb, size_t ws_bytes, hipStream_t st) {
+  const dsa_rows* rows = d.rows;
+  const int T = rows->T;
+  const int64_t ld = logits_ld(rows->n_max);
+  Carve cv;
+  float* logits = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * ld * 4));
+  int32_t* idx_ws = reinterpret_cast<int32_t*>(wsb + cv.take((int64_t)T * d.topk * 4));
+  int32_t* lens_ws = reinterpret_cast<int32_t*>(wsb + cv.take((int64_t)T * 4));
+  int32_t* idx = d.idx_out ? d.idx_out : idx_ws;
+  const int64_t ld_idx = d.idx_out ? d.ld_idx_out : d.topk;
+  int32_t* lens = d.lens_out ? d.lens_out : lens_ws;
+
+  // step 1 (+ the first top-k digit when the long-row path will run and fits one batch)
+  const bool long_rows = rows->n_max > kTopkLdsMax;
+  // (rows that share their keys are scored by the shared-key kernel, which has no histogram)
+  const bool fuse_hist = long_rows && T <= kMaxLongRows && !shared_key_rows(*rows, *d.keys);
+  const ScoreIn sc{d.q_idx, d.ld_q_idx, d.w, d.ld_w, d.keys, rows, d.Hi, d.di, d.index_scale, logits, ld};
+  dsa_status s = run_scores(sc, fuse_hist ? reinterpret_cast<uint32_t*>(wsb + kOffHist) : nullptr, st);
+  if (s != DSA_OK) return s;
+  // step 2: top-k; its candidate lists are carved after the regions above
+  {
+    if (!long_rows) {
+      const TopkIn tk{logits, ld, rows, d.topk, idx, ld_idx, lens};
+      s = run_topk(tk, false, nullptr, 0, st);
+    } else {
+      TopkArgs a;
+      memset(&a, 0, sizeof(a));
+      a.logits = logits;
+      a.ld_logits = ld;
+      a.row_len = rows->row_len;
+      a.n_max = rows->n_max;
+      a.topk = d.topk;
+      a.indices = idx;
+      a.ld_idx = ld_idx;
+      a.lens = lens;
+      carve_topk(a, cv, wsb, T, rows->n_max);
+      s = run_topk_long(a, *rows, fuse_hist, st);
+    }
+    if (s != DSA_OK) return s;
+  }
+  // step 3: attention over the selection; split partials after our regions
+  const bool decode = T <= 1024;
+  const MlaPlan p = plan_mla(T, d.H, d.topk, decode);
+  MlaArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(d.q);
+  a.ld_q = d.ld_q;
+  a.kv[0] = make_kv(d.kv);
+  a.kv[1] = a.kv[0];
+  a.idx[0] = idx;
+  a.idx[1] = idx;
+  a.ld_idx[0] = ld_idx;
+  a.ld_idx[1] = ld_idx;
+  a.n_idx[0] = d.topk;
+  a.n_idx[1] = 0;
+  a.row_req = rows->row_req;
+  a.n_req = rows->n_req;
+  a.H = d.H;
+  a.n_split = p.n_split;
+  a.rows_per_split = p.rows_per_split;
+  a.scale_log2 = d.softmax_scale * kLog2e;
+  a.out = static_cast<uint16_t*>(d.out);
+  a.ld_out = d.ld_out;
+  a.lse = d.lse;
+  apply_opts(a, d.opts);
+  if (p.n_split > 1) {
+    a.part_o = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * d.H * p.n_split * 512 * 4));
+    a.part_ml = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * d.H * p.n_split * 8));
+    if ((size_t)cv.off > ws_bytes) return DSA_ERR_WORKSPACE;
+  }
+  const int fmt = kv_fmt(d.kv);
+  s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, d.d_qk, p.ht, p.nbuf, T, st); }));
+  if (s == DSA_OK && p.n_split > 1)
+    s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, T, st); }));
+  return s;
+}
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of dsa_decode_static: one file-scope device array, which every GPU the library
+// runs on holds until the process ends. In host code `scratch` names a host-side stand-in; the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is ever handed to a kernel.
+__device__ __align__(256) uint8_t scratch[DSA_STATIC_SCRATCH_BYTES];
+
+struct StaticScratch {
+  void* ptr = nullptr;     // this device's copy of `scratch`
+  bool dirty = true;       // its header must be zeroed before the next use
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+StaticScratch g_scratch[kMaxDevices];
+
+// The scratch of the device that `st` runs on (the current device for the null stream).
+dsa_status static_scratch(hipStream_t st, StaticScratch** out) {
+  int dev = -1;
+  if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) return DSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  StaticScratch& sc = g_scratch[dev];
+  if (!sc.ptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return DSA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return DSA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return DSA_ERR_HIP;
+    if (e != hipSuccess || !p || ((uintptr_t)p & 255u)) return DSA_ERR_HIP;
+    sc.ptr = p;
+    sc.dirty = true;
+  }
+  *out = &sc;
+  return DSA_OK;
+}
+
 }  // namespace
 
 // ==================================================================== exported entry points
 extern "C" {
 
-int32_t dsa_abi_version(void) { return 5; }
+int32_t dsa_abi_version(void) { return 6; }
 dsa_status dsa_kv_cache_write(const void* src, int64_t ld_src, int32_t n_tok, const int32_t* slots,
                               const dsa_kv_cache* kv, void* stream) {
   if (n_tok < 0 || !kv) return DSA_ERR_ARG;
@@ -568,6 +734,8 @@ const char* dsa_status_string(int32_t status) {
     case DSA_ERR_UNSUPPORTED: return "unsupported shape or format (outside the compiled envelope)";
     case DSA_ERR_WORKSPACE: return "workspace missing or too small (see dsa_workspace_size)";
     case DSA_ERR_HIP: return "HIP launch failed";
+    case DSA_ERR_SCRATCH_LIMIT:
+      return "problem needs more than the static scratch of dsa_decode_static (DSA_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -735,100 +903,39 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
                       const dsa_attn_opts* opts, int32_t* idx_out, int64_t ld_idx_out,
                       int32_t* lens_out,
                       void* workspace, size_t ws_bytes, void* stream) {
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  dsa_status s = check_rows(rows);
-  if (s != DSA_OK) return s;
-  if (topk < 1) return DSA_ERR_ARG;
-  if (topk > 65536 || rows->n_max > kMaxChunks * kTopkChunk) return DSA_ERR_UNSUPPORTED;
-  if (idx_out && (!al4(idx_out) || ld_idx_out < topk)) return DSA_ERR_ARG;
-  if (lens_out && !al4(lens_out)) return DSA_ERR_ARG;
-  const int T = rows->T;
-  const int64_t ld = logits_ld(rows->n_max);
-  // validate all three steps before enqueueing anything (logits/indices are workspace-backed)
-  float* const dummy_f = reinterpret_cast<float*>(uintptr_t(256));
-  ScoreIn sc{q_idx, ld_q_idx, w, ld_w, keys, rows, Hi, di, index_scale, dummy_f, ld};
-  s = check_scores(sc);
-  if (s != DSA_OK) return s;
-  MlaIn m{q, ld_q, kv, reinterpret_cast<const int32_t*>(uintptr_t(256)), topk, topk, nullptr, nullptr,
-          0, 0, T, rows->row_req, rows->n_req, H, d_qk, d_v, softmax_scale, out, ld_out, lse, opts};
-  s = check_mla(m);
-  if (s != DSA_OK) return s;
-  if (T == 0) return DSA_OK;
-  dsa_problem pr{T, rows->n_max, topk, H, topk, 0};
-  const size_t need = dsa_workspace_size(DSA_ENTRY_DECODE, &pr);
+  const DecodeIn d{q, ld_q, q_idx, ld_q_idx, w, ld_w, keys, kv, rows, H, d_qk, d_v, Hi, di, topk,
+                   index_scale, softmax_scale, out, ld_out, lse, opts, idx_out, ld_idx_out, lens_out};
+  size_t need = 0;
+  dsa_status s = decode_check(d, &need);
+  if (s != DSA_OK || rows->T == 0) return s;
   if (!workspace || !al16(workspace) || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  return decode_run(d, static_cast<uint8_t*>(workspace), ws_bytes, static_cast<hipStream_t>(stream));
+}
 
-  uint8_t* wsb = static_cast<uint8_t*>(workspace);
-  Carve cv;
-  float* logits = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * ld * 4));
-  int32_t* idx_ws = reinterpret_cast<int32_t*>(wsb + cv.take((int64_t)T * topk * 4));
-  int32_t* lens_ws = reinterpret_cast<int32_t*>(wsb + cv.take((int64_t)T * 4));
-  int32_t* idx = idx_out ? idx_out : idx_ws;
-  const int64_t ld_idx = idx_out ? ld_idx_out : topk;
-  int32_t* lens = lens_out ? lens_out : lens_ws;
-
-  // step 1 (+ the first top-k digit when the long-row path will run and fits one batch)
-  const bool long_rows = rows->n_max > kTopkLdsMax;
-  // (rows that share their keys are scored by the shared-key kernel, which has no histogram)
-  const bool fuse_hist = long_rows && T <= kMaxLongRows && !shared_key_rows(*rows, *keys);
-  sc.logits = logits;
-  s = run_scores(sc, fuse_hist ? reinterpret_cast<uint32_t*>(wsb + kOffHist) : nullptr, st);
+dsa_status dsa_decode_static(const void* q, int64_t ld_q, const void* q_idx, int64_t ld_q_idx,
+                             const float* w, int64_t ld_w, const dsa_key_cache* keys,
+                             const dsa_kv_cache* kv, const dsa_rows* rows, int32_t H,
+                             int32_t d_qk, int32_t d_v, int32_t Hi, int32_t di, int32_t topk,
+                             float index_scale, float softmax_scale, void* out, int64_t ld_out,
+                             float* lse, const dsa_attn_opts* opts, int32_t* idx_out,
+                             int64_t ld_idx_out, int32_t* lens_out, void* stream) {
+  const DecodeIn d{q, ld_q, q_idx, ld_q_idx, w, ld_w, keys, kv, rows, H, d_qk, d_v, Hi, di, topk,
+                   index_scale, softmax_scale, out, ld_out, lse, opts, idx_out, ld_idx_out, lens_out};
+  size_t need = 0;
+  dsa_status s = decode_check(d, &need);
+  if (s != DSA_OK || rows->T == 0) return s;
+  if (need > (size_t)DSA_STATIC_SCRATCH_BYTES) return DSA_ERR_SCRATCH_LIMIT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  StaticScratch* sc = nullptr;
+  s = static_scratch(st, &sc);
   if (s != DSA_OK) return s;
-  // step 2: top-k; its candidate lists are carved after the regions above
-  TopkIn tk{logits, ld, rows, topk, idx, ld_idx, lens};
-  {
-    TopkArgs a;
-    memset(&a, 0, sizeof(a));
-    if (!long_rows) {
-      s = run_topk(tk, false, nullptr, 0, st);
-    } else {
-      a.logits = logits;
-      a.ld_logits = ld;
-      a.row_len = rows->row_len;
-      a.n_max = rows->n_max;
-      a.topk = topk;
-      a.indices = idx;
-      a.ld_idx = ld_idx;
-      a.lens = lens;
-      carve_topk(a, cv, wsb, T, rows->n_max);
-      s = run_topk_long(a, *rows, fuse_hist, st);
-    }
+  if (sc->dirty) {                                   // first call on this device, or after a failure
+    s = hip_status(launch_fill_zero(sc->ptr, (size_t)kHeaderBytes, st));
     if (s != DSA_OK) return s;
+    sc->dirty = false;
   }
-  // step 3: attention over the selection; split partials after our regions
-  const bool decode = T <= 1024;
-  const MlaPlan p = plan_mla(T, H, topk, decode);
-  MlaArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = static_cast<const uint16_t*>(q);
-  a.ld_q = ld_q;
-  a.kv[0] = make_kv(kv);
-  a.kv[1] = a.kv[0];
-  a.idx[0] = idx;
-  a.idx[1] = idx;
-  a.ld_idx[0] = ld_idx;
-  a.ld_idx[1] = ld_idx;
-  a.n_idx[0] = topk;
-  a.n_idx[1] = 0;
-  a.row_req = rows->row_req;
-  a.n_req = rows->n_req;
-  a.H = H;
-  a.n_split = p.n_split;
-  a.rows_per_split = p.rows_per_split;
-  a.scale_log2 = softmax_scale * kLog2e;
-  a.out = static_cast<uint16_t*>(out);
-  a.ld_out = ld_out;
-  a.lse = lse;
-  apply_opts(a, opts);
-  if (p.n_split > 1) {
-    a.part_o = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * H * p.n_split * 512 * 4));
-    a.part_ml = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * H * p.n_split * 8));
-    if ((size_t)cv.off > ws_bytes) return DSA_ERR_WORKSPACE;
-  }
-  const int fmt = kv_fmt(kv);
-  s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, d_qk, p.ht, p.nbuf, T, st); }));
-  if (s == DSA_OK && p.n_split > 1)
-    s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, T, st); }));
+  s = decode_run(d, static_cast<uint8_t*>(sc->ptr), (size_t)DSA_STATIC_SCRATCH_BYTES, st);
+  if (s == DSA_ERR_HIP) sc->dirty = true;            // the control words may not be back at zero
   return s;
 }
 

@@ -49,7 +49,8 @@ typedef enum dsa_status {
   DSA_ERR_ARG = -1,          /* null pointer, bad shape, bad stride or alignment */
   DSA_ERR_UNSUPPORTED = -2,  /* valid, but outside the compiled envelope; never a fallback */
   DSA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than dsa_workspace_size() */
-  DSA_ERR_HIP = -4           /* a HIP launch failed */
+  DSA_ERR_HIP = -4,          /* a HIP launch failed */
+  DSA_ERR_SCRATCH_LIMIT = -5 /* dsa_decode_static: the problem needs more than its static scratch */
 } dsa_status;
 
 typedef enum dsa_key_dtype {
@@ -229,6 +230,31 @@ dsa_status dsa_decode(const void* q, int64_t ld_q, const void* q_idx, int64_t ld
                       float softmax_scale, void* out, int64_t ld_out, float* lse,
                       const dsa_attn_opts* opts, int32_t* idx_out, int64_t ld_idx_out,
                       int32_t* lens_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- fused layer, no allocation
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): dsa_decode with the same arguments and results,
+ * minus the workspace. Its scratch is one static device array of DSA_STATIC_SCRATCH_BYTES
+ * that every GPU the library runs on holds until the process ends; the entry never calls
+ * hipMalloc, hipFree or any allocating routine. The first call on a device looks up that
+ * device's copy of the array and zeroes its control words with a kernel (no memset node);
+ * every call leaves them zero, so later calls need no clearing (after DSA_ERR_HIP the next
+ * call clears them again).
+ * Limits: a problem whose dsa_workspace_size(DSA_ENTRY_DECODE, ...) exceeds
+ * DSA_STATIC_SCRATCH_BYTES is rejected with DSA_ERR_SCRATCH_LIMIT before anything is enqueued
+ * (64 MiB holds, e.g., one row of 1M candidates, or 64 rows of 32K at topk 2048 and 64 heads).
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller. The device is the
+ * stream's (hipStreamGetDevice; the current device for the null stream). */
+#define DSA_STATIC_SCRATCH_BYTES (64u << 20)
+
+dsa_status dsa_decode_static(const void* q, int64_t ld_q, const void* q_idx, int64_t ld_q_idx,
+                             const float* w, int64_t ld_w, const dsa_key_cache* keys,
+                             const dsa_kv_cache* kv, const dsa_rows* rows, int32_t H,
+                             int32_t d_qk, int32_t d_v, int32_t Hi, int32_t di, int32_t topk,
+                             float index_scale, float softmax_scale, void* out, int64_t ld_out,
+                             float* lse, const dsa_attn_opts* opts, int32_t* idx_out,
+                             int64_t ld_idx_out, int32_t* lens_out, void* stream);
 
 /* ---------------------------------------------------------------- workspace and errors */
 typedef enum dsa_entry {

@@ -174,3 +174,39 @@ def test_workspace_sizes():
 def test_workspace_init_rejects():
     assert B._lib.dsa_workspace_init(None, 1 << 24, None) == B.DSA_ERR_ARG
     assert B._lib.dsa_workspace_init(FAKE, 16, None) == B.DSA_ERR_WORKSPACE
+
+
+def decode_static(**kw):
+    a = dict(q=FAKE, ld_q=64 * 576, q_idx=FAKE, ld_q_idx=64 * 128, w=FAKE, ld_w=64, keys=_keys(n_slots=1 << 22),
+             kv=_kv(n_slots=1 << 22), rows=_rows(n_max=131072), H=64, d_qk=576, d_v=512, Hi=64, di=128,
+             topk=2048, index_scale=1.0, scale=0.04, out=FAKE, ld_out=64 * 512, lse=None, opts=None,
+             idx_out=None, ld_idx_out=0, lens_out=None)
+    a.update(kw)
+    return B._lib.dsa_decode_static(
+        a["q"], a["ld_q"], a["q_idx"], a["ld_q_idx"], a["w"], a["ld_w"], C.byref(a["keys"]), C.byref(a["kv"]),
+        C.byref(a["rows"]), a["H"], a["d_qk"], a["d_v"], a["Hi"], a["di"], a["topk"], a["index_scale"],
+        a["scale"], a["out"], a["ld_out"], a["lse"], C.byref(a["opts"]) if a["opts"] is not None else None,
+        a["idx_out"], a["ld_idx_out"], a["lens_out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.DSA_ERR_ARG),
+    (dict(topk=0), B.DSA_ERR_ARG),
+    (dict(H=20), B.DSA_ERR_UNSUPPORTED),
+    (dict(Hi=65), B.DSA_ERR_UNSUPPORTED),
+    (dict(idx_out=FAKE, ld_idx_out=2047), B.DSA_ERR_ARG),        # idx_out row shorter than topk
+    # more scratch than the static array holds: 64 rows of 1M candidates
+    (dict(rows=_rows(T=64, n_req=64, n_max=1 << 20)), B.DSA_ERR_SCRATCH_LIMIT),
+])
+def test_decode_static_rejects_before_any_hip_call(kw, status):
+    """Argument and size checks come before the scratch lookup (no GPU here: a HIP call would
+    fail with DSA_ERR_HIP instead)."""
+    assert decode_static(**kw) == status
+
+
+def test_decode_static_limit_matches_the_workspace_size():
+    need_1m = dsa.dsa_workspace_size(dsa.ENTRY_DECODE, T=1, n_max=1 << 20, topk=2048, H=64)
+    assert need_1m <= dsa.STATIC_SCRATCH_BYTES       # one 1M-candidate row fits
+    need_big = dsa.dsa_workspace_size(dsa.ENTRY_DECODE, T=64, n_max=1 << 20, topk=2048, H=64)
+    assert need_big > dsa.STATIC_SCRATCH_BYTES
+    assert dsa.dsa_status_string(dsa.DSA_ERR_SCRATCH_LIMIT) != "unknown status"
