@@ -123,6 +123,11 @@ hipError_t timed(const char* name, hipStream_t st, F&& launch) {
 }
 
 // ---------------------------------------------------------------- attention policy
+// Heads padded to whole 16-head tiles (the forward's workgroups and split partials), and the
+// backward's padded count (its dKV kernel sums heads in groups of 16, 32, 64 or 128).
+int heads_padded(int H) { return (H + 15) / 16 * 16; }
+int heads_padded_bwd(int H) { return H <= 16 ? 16 : H <= 32 ? 32 : H <= 64 ? 64 : 128; }
+
 struct MlaPlan {
   int ht;          // head tiles per workgroup
   int nbuf;        // depth of the block ring in LDS
@@ -141,7 +146,7 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   // block.
   // Blocks stream through a ring of two.
   MlaPlan p;
-  const int tiles = H / 16;
+  const int tiles = heads_padded(H) / 16;
   const int nblk = std::max(1, (ntot + 31) / 32);
   int s = 1;
   if (decode && !(T >= 16 && tiles % 4 == 0)) {
@@ -163,16 +168,17 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   return p;
 }
 
-// backward: bf16 scale * dZ and P per (row, listed entry, head), and the entries' slots
+// backward: bf16 scale * dZ and P per (row, listed entry, padded head), and the entries' slots
 int64_t mla_bwd_ws_bytes(int T, int H, int n_idx) {
   const int64_t e = (int64_t)T * n_idx;
-  return align256(e * H * 2) * 2 + align256(e * 4);
+  return align256(e * heads_padded_bwd(H) * 2) * 2 + align256(e * 4);
 }
 
 int64_t mla_ws_bytes(int T, int H, int ntot, bool decode) {
   const MlaPlan p = plan_mla(T, H, ntot, decode);
   if (p.n_split <= 1) return 0;
-  return align256((int64_t)T * H * p.n_split * 512 * 4) + align256((int64_t)T * H * p.n_split * 8);
+  const int64_t hp = heads_padded(H);
+  return align256((int64_t)T * hp * p.n_split * 512 * 4) + align256((int64_t)T * hp * p.n_split * 8);
 }
 
 int topk_chunks_of(int n_max) { return std::max(1, (n_max + kTopkChunk - 1) / kTopkChunk); }
@@ -278,7 +284,6 @@ struct MlaIn {
 dsa_status check_mla(const MlaIn& m) {
   if (m.T < 0 || m.H <= 0 || m.n_idx < 0 || m.n_extra < 0) return DSA_ERR_ARG;
   if (m.T > 65535) return DSA_ERR_UNSUPPORTED;
-  if (m.H % 16) return DSA_ERR_UNSUPPORTED;
   if (m.d_v != 512) return DSA_ERR_UNSUPPORTED;
   if (m.d_qk != 512 && m.d_qk != 576) return DSA_ERR_UNSUPPORTED;
   if (!std::isfinite(m.softmax_scale)) return DSA_ERR_ARG;
@@ -319,6 +324,7 @@ dsa_status run_mla(const MlaIn& m, bool decode, void* ws, size_t ws_bytes, hipSt
   a.row_req = m.row_req;
   a.n_req = m.n_req;
   a.H = m.H;
+  a.Hp = heads_padded(m.H);
   a.n_split = p.n_split;
   a.rows_per_split = p.rows_per_split;
   a.scale_log2 = m.softmax_scale * kLog2e;
@@ -331,8 +337,8 @@ dsa_status run_mla(const MlaIn& m, bool decode, void* ws, size_t ws_bytes, hipSt
     if (!ws || (int64_t)ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
     uint8_t* w = static_cast<uint8_t*>(ws);
     Carve cv;
-    a.part_o = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * m.H * p.n_split * 512 * 4));
-    a.part_ml = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * m.H * p.n_split * 8));
+    a.part_o = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * a.Hp * p.n_split * 512 * 4));
+    a.part_ml = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * a.Hp * p.n_split * 8));
   }
   const int fmt = kv_fmt(m.kv);
   dsa_status s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, m.d_qk, p.ht, p.nbuf, m.T, st); }));
@@ -584,6 +590,7 @@ dsa_status decode_run(const DecodeIn& d, uint8_t* wsb, size_t ws_bytes, hipStrea
   a.row_req = rows->row_req;
   a.n_req = rows->n_req;
   a.H = d.H;
+  a.Hp = heads_padded(d.H);
   a.n_split = p.n_split;
   a.rows_per_split = p.rows_per_split;
   a.scale_log2 = d.softmax_scale * kLog2e;
@@ -592,8 +599,8 @@ dsa_status decode_run(const DecodeIn& d, uint8_t* wsb, size_t ws_bytes, hipStrea
   a.lse = d.lse;
   apply_opts(a, d.opts);
   if (p.n_split > 1) {
-    a.part_o = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * d.H * p.n_split * 512 * 4));
-    a.part_ml = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * d.H * p.n_split * 8));
+    a.part_o = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * a.Hp * p.n_split * 512 * 4));
+    a.part_ml = reinterpret_cast<float*>(wsb + cv.take((int64_t)T * a.Hp * p.n_split * 8));
     if ((size_t)cv.off > ws_bytes) return DSA_ERR_WORKSPACE;
   }
   const int fmt = kv_fmt(d.kv);
@@ -746,15 +753,13 @@ size_t dsa_workspace_size(int32_t entry, const dsa_problem* p) {
     case DSA_ENTRY_TOPK:
       return (size_t)(kHeaderBytes + topk_ws_bytes(p->T, p->n_max));
     case DSA_ENTRY_MLA_DECODE:
-      if (p->H % 16) return SIZE_MAX;
       return (size_t)(kHeaderBytes + mla_ws_bytes(p->T, p->H, p->n_idx, true));
     case DSA_ENTRY_MLA_PREFILL:
       return 0;
     case DSA_ENTRY_MLA_BACKWARD:
-      if (p->H % 16 || p->H > 128) return SIZE_MAX;
+      if (p->H > 128) return SIZE_MAX;
       return (size_t)(kHeaderBytes + mla_bwd_ws_bytes(p->T, p->H, p->n_idx));
     case DSA_ENTRY_DECODE: {
-      if (p->H % 16) return SIZE_MAX;
       const int64_t ld = logits_ld(p->n_max);
       int64_t b = kHeaderBytes;
       b = align256(b + (int64_t)p->T * ld * 4);                 // logits
@@ -837,7 +842,7 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
   dsa_status st = check_rows(rows);
   if (st != DSA_OK) return st;
   if (H <= 0 || n_idx < 0) return DSA_ERR_ARG;
-  if (H % 16 || H > 128 || d_v != 512 || (d_qk != 512 && d_qk != 576)) return DSA_ERR_UNSUPPORTED;
+  if (H > 128 || d_v != 512 || (d_qk != 512 && d_qk != 576)) return DSA_ERR_UNSUPPORTED;
   if (!std::isfinite(softmax_scale)) return DSA_ERR_ARG;
   st = check_opts(opts);
   if (st != DSA_OK) return st;
@@ -867,6 +872,7 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
   a.row_req = rows->row_req;
   a.n_req = rows->n_req;
   a.H = H;
+  a.Hp = heads_padded_bwd(H);
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * kLog2e;
   a.out = static_cast<const uint16_t*>(out);
@@ -884,8 +890,8 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
     uint8_t* w = static_cast<uint8_t*>(workspace);
     Carve cv;
     const int64_t e = (int64_t)T * n_idx;
-    a.ws_dz = reinterpret_cast<uint16_t*>(w + cv.take(e * H * 2));
-    a.ws_p = reinterpret_cast<uint16_t*>(w + cv.take(e * H * 2));
+    a.ws_dz = reinterpret_cast<uint16_t*>(w + cv.take(e * a.Hp * 2));
+    a.ws_p = reinterpret_cast<uint16_t*>(w + cv.take(e * a.Hp * 2));
     a.ws_slot = reinterpret_cast<int32_t*>(w + cv.take(e * 4));
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -109,7 +109,8 @@ struct MlaArgs {
   int32_t n_idx[2];
   const int32_t* row_req;  // nullptr: row t is request t
   int32_t n_req;
-  int32_t H;
+  int32_t H;               // heads of q, out, lse and sink
+  int32_t Hp;              // H rounded up to whole 16-head tiles: the head grid and the partials
   int32_t n_split;         // workgroups per (row, head group)
   int32_t rows_per_split;  // multiple of 32
   float scale_log2;        // softmax_scale * log2(e)
@@ -118,8 +119,8 @@ struct MlaArgs {
   float* lse;              // [T, H] or nullptr
   const float* sink;       // [H] per-head sink logit (natural-log units) or nullptr
   int32_t lse_log2;        // lse in base 2 instead of natural log
-  float* part_o;           // [T, H, n_split, 512]
-  float* part_ml;          // [T, H, n_split, 2]
+  float* part_o;           // [T, Hp, n_split, 512]
+  float* part_ml;          // [T, Hp, n_split, 2]
 };
 
 hipError_t launch_sparse_mla(const MlaArgs& a, int fmt, int d_qk, int ht, int nbuf, int T, hipStream_t st);
@@ -135,7 +136,8 @@ struct MlaBwdArgs {
   int32_t n_idx;
   const int32_t* row_req;  // nullptr: row t is request t
   int32_t n_req;
-  int32_t H;
+  int32_t H;               // heads of q, out, lse, dout, dq and sink
+  int32_t Hp;              // 16, 32, 64 or 128 >= H: the head grid and the workspace rows
   float scale;             // softmax_scale
   float scale_log2;        // softmax_scale * log2(e)
   const uint16_t* out;     // bf16 [T, H, 512] (the forward's output)
@@ -149,8 +151,8 @@ struct MlaBwdArgs {
   int64_t ld_dq;
   float* dkv;              // fp32 [n_slots, d_qk], added to
   float* dsink;            // fp32 [H], added to, or nullptr
-  uint16_t* ws_dz;         // workspace: bf16 [T, n_idx, H] softmax_scale * dZ
-  uint16_t* ws_p;          // workspace: bf16 [T, n_idx, H] P
+  uint16_t* ws_dz;         // workspace: bf16 [T, n_idx, Hp] softmax_scale * dZ
+  uint16_t* ws_p;          // workspace: bf16 [T, n_idx, Hp] P
   int32_t* ws_slot;        // workspace: [T, n_idx] slots (-1: padding)
 };
 

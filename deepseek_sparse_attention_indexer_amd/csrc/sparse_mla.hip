@@ -385,11 +385,14 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   static_assert(HT * 16 * RE * 2 <= LDSB, "q staging");
   u32x4_t qreg[QIT];
   {
+    // heads past H (a head count that is not a whole number of tiles) read as zero rows: their
+    // scores are 0 and nothing of them is ever written
+    const int qbytes = min(QBYTES, (a.H - hg * HT * 16) * DQK * 2);
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)t * a.ld_q + (int64_t)(hg * HT * 16) * DQK);
 #pragma unroll
     for (int i = 0; i < QIT; ++i) {
       const int o = (threadIdx.x + i * NT) * 16;
-      qreg[i] = o < QBYTES ? *reinterpret_cast<const u32x4_t*>(qsrc + o) : u32x4_t{0u, 0u, 0u, 0u};
+      qreg[i] = o < qbytes ? *reinterpret_cast<const u32x4_t*>(qsrc + o) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
   if (u_end > u_begin) resolve_pass(u_begin, min(u_end, u_begin + kResolve));
@@ -723,17 +726,18 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
 #pragma unroll
     for (int v = 1; v < NVS; ++v) l_run += s_lw[hh + 2 * v][l32];
     const int headw = hg * 64 + 32 * hh + l32;
+    const bool hv = headw < a.H;                        // not a padding head
     if constexpr (!SPLIT) {
-      const Finish fin = finish_softmax(m_run, l_run, a.sink ? a.sink[headw] : -INFINITY, a.lse_log2);
+      const Finish fin = finish_softmax(m_run, l_run, a.sink && hv ? a.sink[headw] : -INFINITY, a.lse_log2);
       uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)headw * kDV + VC * vh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
         const u32x2_t v = u32x2_t{pack_bf16_rne(o32[0][r] * fin.inv, o32[1][r] * fin.inv),
                                   pack_bf16_rne(o32[2][r] * fin.inv, o32[3][r] * fin.inv)};
-        *reinterpret_cast<u32x2_t*>(op + 4 * m) = v;
+        if (hv) *reinterpret_cast<u32x2_t*>(op + 4 * m) = v;
       }
-      if (a.lse && hl == 0 && vh == 0) a.lse[(int64_t)t * a.H + headw] = fin.lse;
+      if (a.lse && hv && hl == 0 && vh == 0) a.lse[(int64_t)t * a.H + headw] = fin.lse;
     } else {
       // The partial (o, m, l). A lane's pieces are 16 bytes scattered over 32 head rows, so
       // the block is staged in LDS (the ring is free: every wave is past the barrier above)
@@ -754,7 +758,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
           }
         }
         __syncthreads();
-        float* po = a.part_o + ((int64_t)t * a.H + hg * 64 + 32 * half) * a.n_split * kDV +
+        float* po = a.part_o + ((int64_t)t * a.Hp + hg * 64 + 32 * half) * a.n_split * kDV +
                     (int64_t)split * kDV;
         for (int q = threadIdx.x * 4; q < 32 * kDV; q += NT * 4) {
           const int hr = q / kDV;
@@ -764,7 +768,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         }
       }
       if (hl == 0 && vh == 0) {
-        float* pml = a.part_ml + (((int64_t)t * a.H + headw) * a.n_split + split) * 2;
+        float* pml = a.part_ml + (((int64_t)t * a.Hp + headw) * a.n_split + split) * 2;
         pml[0] = m_run;
         pml[1] = l_run;
       }
@@ -774,8 +778,9 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   l_run += __shfl_xor(l_run, 32);
 
   const int head = head0 + c;
+  const bool hv = head < a.H;                         // not a padding head
   if constexpr (!SPLIT) {
-    const Finish fin = finish_softmax(m_run, l_run, a.sink ? a.sink[head] : -INFINITY, a.lse_log2);
+    const Finish fin = finish_softmax(m_run, l_run, a.sink && hv ? a.sink[head] : -INFINITY, a.lse_log2);
     const float inv = fin.inv;
     uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)head * kDV;
 #pragma unroll
@@ -786,9 +791,9 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2)
           v[e2] = pack_bf16_rne(o[i][2 * e2][r] * inv, o[i][2 * e2 + 1][r] * inv);
-        *reinterpret_cast<u32x4_t*>(op + 128 * (gd0 + i) + 32 * g + 8 * r) = v;
+        if (hv) *reinterpret_cast<u32x4_t*>(op + 128 * (gd0 + i) + 32 * g + 8 * r) = v;
       }
-    if (a.lse && g == 0 && gd0 == 0) a.lse[(int64_t)t * a.H + head] = fin.lse;
+    if (a.lse && hv && g == 0 && gd0 == 0) a.lse[(int64_t)t * a.H + head] = fin.lse;
   } else {
     // un-normalised partial (o, m, l) of this split; k_mla_combine merges them. A lane holds
     // 128 contiguous bytes of one head's row, so direct stores would spread every instruction
@@ -812,7 +817,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
           *reinterpret_cast<f32x4_t*>(d + 4) = v1;
         }
       lds_barrier();
-      float* po = a.part_o + ((int64_t)t * a.H + hg * HT * 16) * a.n_split * kDV + (int64_t)split * kDV;
+      float* po = a.part_o + ((int64_t)t * a.Hp + hg * HT * 16) * a.n_split * kDV + (int64_t)split * kDV;
       for (int q = threadIdx.x * 4; q < HT * 16 * kDV; q += NT * 4) {
         const int hl = q / kDV;
         const int col = q - hl * kDV;
@@ -820,7 +825,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
                                     reinterpret_cast<f32x4_t*>(po + (int64_t)hl * a.n_split * kDV + col));
       }
     } else {                                          // too many heads to stage: direct stores
-      float* po = a.part_o + (((int64_t)t * a.H + head) * a.n_split + split) * kDV;
+      float* po = a.part_o + (((int64_t)t * a.Hp + head) * a.n_split + split) * kDV;
 #pragma unroll
       for (int i = 0; i < GD; ++i)
 #pragma unroll
@@ -834,7 +839,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         }
     }
     if (g == 0 && gd0 == 0) {
-      float* pml = a.part_ml + (((int64_t)t * a.H + head) * a.n_split + split) * 2;
+      float* pml = a.part_ml + (((int64_t)t * a.Hp + head) * a.n_split + split) * 2;
       pml[0] = m_run;
       pml[1] = l_run;
     }
@@ -861,8 +866,8 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
   const int ci = threadIdx.x % TPG;
   const int d0 = blockIdx.x * 128 * QW + ci * 4;
   const int S = a.n_split;
-  const float* pml = a.part_ml + ((int64_t)t * a.H + head) * S * 2;
-  const float* po = a.part_o + ((int64_t)t * a.H + head) * S * kDV + d0;
+  const float* pml = a.part_ml + ((int64_t)t * a.Hp + head) * S * 2;
+  const float* po = a.part_o + ((int64_t)t * a.Hp + head) * S * kDV + d0;
   // one pass: every partial (o, m, l) of this group's splits is requested at once and merged
   // online in registers (base-2 maxima); no separate pass for the global maximum
   float mg = -INFINITY, lg = 0.f;
@@ -928,7 +933,7 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
 
 template <int FMT, int DQK, int HT, int WD, int NBUF>
 static hipError_t launch_h(const MlaArgs& a, int T, hipStream_t st) {
-  dim3 grid(a.n_split, a.H / (16 * HT), T);
+  dim3 grid(a.n_split, a.Hp / (16 * HT), T);
   if (a.n_split > 1)
     launch_kernel(k_sparse_mla<FMT, DQK, HT, WD, true, NBUF>, grid, dim3(64 * HT * WD), st, a);
   else

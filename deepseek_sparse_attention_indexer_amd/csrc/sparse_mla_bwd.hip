@@ -104,18 +104,25 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   uint16_t* const s_q = &s_rows[0][0];                  // [16][RE]
   uint16_t* const s_do = &s_rows[0][0] + 16 * RE;       // [16][kBwdDV + 8]
   constexpr int DOS = kBwdDV + 8;
+  // Heads past H (a head count that is not a whole number of 16-head groups) read q, dout and
+  // out as zero and lse as 0: their P is finite and their dZ and P dout are zero, so they add
+  // nothing to dKV, and nothing of them is written.
+  const int hval = a.H - head0;                         // valid heads of this group (>= 1)
   {
     const uint16_t* qg = a.q + (int64_t)t * a.ld_q + (int64_t)head0 * DQK;
     for (int o = threadIdx.x * 8; o < 16 * DQK; o += NT * 8)
-      *reinterpret_cast<u32x4_t*>(s_q + (o / DQK) * RE + o % DQK) = *reinterpret_cast<const u32x4_t*>(qg + o);
+      *reinterpret_cast<u32x4_t*>(s_q + (o / DQK) * RE + o % DQK) =
+          o / DQK < hval ? *reinterpret_cast<const u32x4_t*>(qg + o) : u32x4_t{0u, 0u, 0u, 0u};
     const uint16_t* dg = a.dout + (int64_t)t * a.ld_dout + (int64_t)head0 * kBwdDV;
     for (int o = threadIdx.x * 8; o < 16 * kBwdDV; o += NT * 8)
-      *reinterpret_cast<u32x4_t*>(s_do + (o / kBwdDV) * DOS + o % kBwdDV) = *reinterpret_cast<const u32x4_t*>(dg + o);
+      *reinterpret_cast<u32x4_t*>(s_do + (o / kBwdDV) * DOS + o % kBwdDV) =
+          o / kBwdDV < hval ? *reinterpret_cast<const u32x4_t*>(dg + o) : u32x4_t{0u, 0u, 0u, 0u};
     // D: 16 threads per head, 32 columns each
     const int h = threadIdx.x >> 4;
     const int c0 = (threadIdx.x & 15) * 32;
-    const uint16_t* og = a.out + (int64_t)t * a.ld_out + (int64_t)(head0 + h) * kBwdDV + c0;
-    const uint16_t* dh = dg + h * kBwdDV + c0;
+    const int hr = min(h, hval - 1);                    // padding heads read a valid row, then drop it
+    const uint16_t* og = a.out + (int64_t)t * a.ld_out + (int64_t)(head0 + hr) * kBwdDV + c0;
+    const uint16_t* dh = dg + hr * kBwdDV + c0;
     float d = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {
@@ -130,8 +137,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) d += __shfl_xor(d, m);
     if ((threadIdx.x & 15) == 0) {
-      s_D[h] = d;
-      const float l = a.lse[(int64_t)t * a.H + head0 + h];
+      s_D[h] = h < hval ? d : 0.f;
+      const float l = h < hval ? a.lse[(int64_t)t * a.H + head0 + h] : 0.f;
       s_l2[h] = a.lse_log2 ? l : l * kLog2e;
     }
   }
@@ -171,7 +178,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   }
   const float Dc = s_D[c];
   const float l2c = s_l2[c];
-  if (a.sink && a.dsink && threadIdx.x < 16) {
+  if (a.sink && a.dsink && (int)threadIdx.x < min(16, hval)) {
     const float sk = a.sink[head0 + threadIdx.x];
     if (sk > -INFINITY) unsafeAtomicAdd(a.dsink + head0 + threadIdx.x, -exp2f(sk * kLog2e - s_l2[threadIdx.x]) * s_D[threadIdx.x]);
   }
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
         const int j = jb + row;
         if (j < pass_n) {
           const uint16_t* src = arr ? &s_tp[row][8 * half] : &s_tz[row][8 * half];
-          uint16_t* dst = (arr ? a.ws_p : a.ws_dz) + ((int64_t)t * ntot + p0 + j) * a.H + head0 + 8 * half;
+          uint16_t* dst = (arr ? a.ws_p : a.ws_dz) + ((int64_t)t * ntot + p0 + j) * a.Hp + head0 + 8 * half;
           *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
         }
       }
@@ -378,6 +385,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   }
 
   // ---- dq: lane (c = head, g) holds columns 128 wave + 8 (4g + r) + e (and the RoPE phases)
+  if (c >= hval) return;                                // a padding head: no dq
   float* dqh = a.dq + (int64_t)t * a.ld_dq + (int64_t)(head0 + c) * DQK;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -429,8 +437,9 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd_dkv(MlaBwdArgs a, int
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int head = 8 * ks + 4 * hh + j;
-          h4[j] = qr[(int64_t)head * DQK + col];
-          d4[j] = col < kBwdDV ? dr[(int64_t)head * kBwdDV + col] : 0u;
+          const bool hv = head < a.H;                   // padding heads: zero operands
+          h4[j] = hv ? qr[(int64_t)head * DQK + col] : 0u;
+          d4[j] = hv && col < kBwdDV ? dr[(int64_t)head * kBwdDV + col] : 0u;
         }
         qkb[k][ks] = u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
         dkb[k][ks] = u32x2_t{d4[0] | (d4[1] << 16), d4[2] | (d4[3] << 16)};
@@ -442,8 +451,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd_dkv(MlaBwdArgs a, int
     const int r0 = blk * 32;
     // this lane's A rows and the slots of the 16 rows its accumulators hold
     const int ra = min(r0 + l32, ntot - 1);
-    const uint16_t* zr = a.ws_dz + ((int64_t)t * ntot + ra) * a.H + 4 * hh;
-    const uint16_t* pr = a.ws_p + ((int64_t)t * ntot + ra) * a.H + 4 * hh;
+    const uint16_t* zr = a.ws_dz + ((int64_t)t * ntot + ra) * a.Hp + 4 * hh;
+    const uint16_t* pr = a.ws_p + ((int64_t)t * ntot + ra) * a.Hp + 4 * hh;
     u32x2_t az[HK], ap[HK];
 #pragma unroll
     for (int ks = 0; ks < HK; ++ks) {
@@ -478,7 +487,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd_dkv(MlaBwdArgs a, int
 template <int DQK>
 static void launch_dkv(const MlaBwdArgs& a, int T, hipStream_t st) {
   constexpr int CT = DQK / 32;
-  const int hk = a.H / 8;
+  const int hk = a.Hp / 8;
   const int cg = hk >= 16 ? 2 : 3;
   const dim3 grid((CT + cg - 1) / cg, T);
   if (hk == 2) launch_kernel(k_sparse_mla_bwd_dkv<DQK, 2>, grid, dim3(256), st, a, cg);
@@ -489,8 +498,8 @@ static void launch_dkv(const MlaBwdArgs& a, int T, hipStream_t st) {
 
 hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid(a.H / 16, T);
-  const bool fused = a.H == 16;
+  const dim3 grid(a.Hp / 16, T);
+  const bool fused = a.Hp == 16;
   if (d_qk == 576) {
     if (fused) launch_kernel(k_sparse_mla_bwd<576, true>, grid, dim3(256), st, a);
     else launch_kernel(k_sparse_mla_bwd<576, false>, grid, dim3(256), st, a);
@@ -502,7 +511,7 @@ hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream
 }
 
 hipError_t launch_sparse_mla_bwd_dkv(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st) {
-  if (T <= 0 || a.n_idx <= 0 || a.H == 16) return hipSuccess;   // 16 heads: fused above
+  if (T <= 0 || a.n_idx <= 0 || a.Hp == 16) return hipSuccess;   // 16 heads: fused above
   if (d_qk == 576) launch_dkv<576>(a, T, st);
   else launch_dkv<512>(a, T, st);
   return hipGetLastError();

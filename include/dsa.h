@@ -164,8 +164,9 @@ typedef struct dsa_attn_opts {
  *      listed entry give out = 0.
  * lse: fp32 [T, H] natural-log logsumexp of the scaled logits (-inf for empty rows); may be NULL.
  * opts: sink and lse base (see dsa_attn_opts); may be NULL.
- * Envelope: H multiple of 16; d_qk = d_nope + d_rope in {512, 576}; d_v = 512; both caches
- * of the same format. The decode entry splits each row's list over workgroups and merges the
+ * Envelope: H >= 1 (heads run in tiles of 16; in a partial tile the missing heads are read
+ * as zero and nothing is written for them, so H = 8, a TP=8 share of 64 heads, costs one tile);
+ * d_qk = d_nope + d_rope in {512, 576}; d_v = 512; both caches of the same format. The decode entry splits each row's list over workgroups and merges the
  * partials (PR 664 split-KV + LSE merge); the prefill entry gives each row one workgroup. */
 dsa_status dsa_sparse_mla_decode(const void* q, int64_t ld_q, const dsa_kv_cache* kv,
                                  const int32_t* idx, int64_t ld_idx, int32_t n_idx,
@@ -207,7 +208,8 @@ dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cach
  * (row, entry, head), plus the entries' slots); then per row dKV over all heads, so that an
  * entry costs one atomic per column whatever H is (H = 16: one kernel, the workspace unused).
  * Workspace: dsa_workspace_size(DSA_ENTRY_MLA_BACKWARD, {T, H, n_idx}).
- * Envelope: DSA_KV_BF16 cache; H a multiple of 16 up to 128; d_qk in {512, 576}; d_v = 512.
+ * Envelope: DSA_KV_BF16 cache; 1 <= H <= 128 (heads padded to 16, 32, 64 or 128 inside, the
+ * padding heads reading as zero); d_qk in {512, 576}; d_v = 512.
  * Errors: DSA_ERR_ARG for null pointers, bad strides or alignment, dsink without a sink;
  * DSA_ERR_WORKSPACE for a missing or small workspace; DSA_ERR_UNSUPPORTED outside the envelope. */
 dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cache* kv,

@@ -128,8 +128,8 @@ def mla(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(H=20), B.DSA_ERR_UNSUPPORTED),
     (dict(H=0), B.DSA_ERR_ARG),
+    (dict(H=8, ld_q=8 * 576 - 8, ld_out=8 * 512), B.DSA_ERR_ARG),    # q row shorter than 8 heads
     (dict(d_v=256, ld_out=16 * 256), B.DSA_ERR_UNSUPPORTED),
     (dict(d_qk=640, ld_q=16 * 640), B.DSA_ERR_UNSUPPORTED),
     (dict(q=None), B.DSA_ERR_ARG),
@@ -167,8 +167,13 @@ def test_workspace_sizes():
     assert dec >= hdr + 131072 * 4
     with pytest.raises(dsa.DSAError):
         dsa.dsa_workspace_size(9, T=1)
+    # a head count that is not whole 16-head tiles is padded inside: 8 heads split like 16
+    assert dsa.dsa_workspace_size(dsa.ENTRY_MLA_DECODE, T=1, H=8, n_idx=2048) == \
+        dsa.dsa_workspace_size(dsa.ENTRY_MLA_DECODE, T=1, H=16, n_idx=2048)
+    assert dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=2, H=40, n_idx=256) == \
+        dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=2, H=64, n_idx=256)
     with pytest.raises(dsa.DSAError):
-        dsa.dsa_workspace_size(dsa.ENTRY_DECODE, T=1, n_max=10, topk=4, H=20)
+        dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=1, H=129, n_idx=64)
 
 
 def test_workspace_init_rejects():
@@ -192,7 +197,7 @@ def decode_static(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), B.DSA_ERR_ARG),
     (dict(topk=0), B.DSA_ERR_ARG),
-    (dict(H=20), B.DSA_ERR_UNSUPPORTED),
+    (dict(H=0), B.DSA_ERR_ARG),
     (dict(Hi=65), B.DSA_ERR_UNSUPPORTED),
     (dict(idx_out=FAKE, ld_idx_out=2047), B.DSA_ERR_ARG),        # idx_out row shorter than topk
     # more scratch than the static array holds: 64 rows of 1M candidates

@@ -52,6 +52,14 @@ CASES = [
     ("ds_mla_two_lists_sink_log2", dict(fmt="fp8_ds_mla", B=3, H=16, n_ctx=2000, n_idx=128,
                                         page_size=256, n_extra=300, pad="tail", n_pad=5, sink=True,
                                         lse_log2=True)),
+    # head counts that are not whole 16-head tiles (the missing heads of the last tile are
+    # padding): 8 heads (the TP=8 share of 64), 40, and 56 on the 64-head workgroups
+    ("bf16_h8_split", dict(fmt="bf16", B=2, H=8, n_ctx=3000, n_idx=2048, pad="shuffled", n_pad=100)),
+    ("ds_mla_h8_two_lists_sink", dict(fmt="fp8_ds_mla", B=3, H=8, n_ctx=2000, n_idx=128, page_size=256,
+                                      n_extra=300, pad="tail", n_pad=5, sink=True)),
+    ("bf16_h40", dict(fmt="bf16", B=3, H=40, n_ctx=900, n_idx=333, pad="shuffled", n_pad=7, sink=True)),
+    ("bf16_h56_b16", dict(fmt="bf16", B=16, H=56, n_ctx=2000, n_idx=600, pad="shuffled", n_pad=5,
+                          sink=True, lse_log2=True)),
 ]
 
 

@@ -29,6 +29,9 @@ CASES = [
     ("bf16_sink_log2", dict(fmt="bf16", B=3, H=16, n_ctx=700, n_idx=96, pad="tail", n_pad=10,
                             sink=True, lse_log2=True)),
     ("bf16_all_padded", dict(fmt="bf16", B=2, H=16, n_ctx=300, n_idx=64, pad="all")),
+    # head counts padded inside: 8 (one 16-head group) and 40 (64 in the dKV head sum)
+    ("bf16_576_h8_sink", dict(fmt="bf16", B=3, H=8, n_ctx=700, n_idx=96, pad="tail", n_pad=10, sink=True)),
+    ("bf16_576_h40", dict(fmt="bf16", B=2, H=40, n_ctx=900, n_idx=300, pad="shuffled", n_pad=20)),
 ]
 
 

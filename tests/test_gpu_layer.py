@@ -28,6 +28,8 @@ DECODE = [
     # 16 rows x 64 heads: the attention shares each gathered block among all 64 heads (8-wave
     # workgroups), with splits
     ("spec_b4_q4_h64", "glm_decode", dict(n_ctx=6000, B=4, q_len=4, ctx_lens=(6000, 5001, 2100, 4444))),
+    # the TP=8 share of a 64-head model: 8 attention heads
+    ("glm_128k_h8", "glm_decode", dict(n_ctx=131072, H=8)),
 ]
 
 

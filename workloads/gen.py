@@ -476,3 +476,53 @@ WORKLOADS = {
 
 def make_workload(name: str, seed: int = 0) -> DSAProblem:
     return WORKLOADS[name](seed=seed)
+
+
+# The row layouts of the prefill correctness grid (radixark/miles PR 3608, section
+# "Correctness": packed, 1-token segments, causal, batch 2).
+GRID_LAYOUTS = {
+    "causal": dict(seg_lens=(200,)),                         # one causal sequence
+    "packed": dict(seg_lens=(90, 57, 33)),                   # sequences back to back
+    "one_token": dict(seg_lens=(1,) * 6 + (40,) + (1,) * 6),  # packed, with 1-token segments
+    "batch2": dict(seg_lens=(120, 100), paged=True),         # two requests in a paged cache
+}
+
+
+def grid_base(layout: str, H: int, seed: int = 0, d_nope: int = 512, d_rope: int = 64) -> DSAProblem:
+    """Rows and caches of one layout of the grid (no lists yet): causal rows (the row at
+    position p of its sequence sees [0, p]); packed layouts share one contiguous cache through
+    req_base, "batch2" puts each request in its own pages of a shuffled 64-token page table."""
+    spec = GRID_LAYOUTS[layout]
+    seg = np.asarray(spec["seg_lens"], dtype=np.int64)
+    T = int(seg.sum())
+    D = d_nope + d_rope
+    row_req = np.repeat(np.arange(len(seg), dtype=np.int32), seg)
+    row_len = np.concatenate([np.arange(1, s + 1) for s in seg]).astype(np.int32)
+    if spec.get("paged"):
+        page = 64
+        ppr = (seg + page - 1) // page
+        bt, n_pages = shuffled_pages(seed, _T_BT, len(seg), ppr)
+        kv = _make_kv(seed, _T_KV, "bf16", n_pages * page, d_nope, d_rope, page, bt, None)
+    else:
+        base = np.concatenate([[0], np.cumsum(seg)[:-1]]).astype(np.int32)
+        kv = _make_kv(seed, _T_KV, "bf16", T, d_nope, d_rope, 1, None, base)
+    q = _bf16_normal(seed, _T_Q, (T, H, D))
+    return DSAProblem(name=f"grid_{layout}_h{H}", T=T, H=H, d_qk=D, d_v=d_nope, topk=0, q=q, kv=kv,
+                      row_req=row_req, row_len=row_len, n_req=len(seg),
+                      softmax_scale=1.0 / math.sqrt(D))
+
+
+def grid_lists(base: DSAProblem, topk: int, pad: str, seed: int = 0) -> np.ndarray:
+    """Index lists int32 [T, topk] for the grid: row t lists m distinct positions of [0, n_t)
+    drawn at random, m = min(topk, n_t) when n_t < topk and topk - topk // 8 otherwise (so every
+    row has some -1 padding); pad "tail" puts the m positions first, "shuffled" scatters them
+    over the row's topk slots."""
+    rng = _rng(seed, _T_LIST)
+    idx = np.full((base.T, topk), -1, dtype=np.int32)
+    for t in range(base.T):
+        n = int(base.row_len[t])
+        m = n if n < topk else topk - topk // 8
+        pos = rng.choice(n, size=m, replace=False).astype(np.int32)
+        where = np.arange(m) if pad == "tail" else np.sort(rng.choice(topk, size=m, replace=False))
+        idx[t, where] = pos
+    return idx
