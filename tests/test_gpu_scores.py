@@ -65,3 +65,20 @@ def test_scores_full_size_causal_prefill_sampled_rows():
         n = int(prob.row_len[t])
         ok, msg = scores_ok(logits[t, :n], oracle.index_scores_row(prob, t))
         assert ok, f"row {t}: {msg}"
+
+
+def test_scores_fp8_keys_with_negative_scales():
+    """fp8 keys whose per-token scale is negative for some tokens (the cache writer never makes
+    one, but the formula takes any scale): every score still matches the oracle."""
+    import dataclasses
+    base = workload("glm_decode", n_ctx=3000, B=2, ctx_lens=(3000, 1999), key_dtype="fp8", make_kv=False)
+    scale = base.kpool.scale.copy()
+    scale[::3] *= -1.0
+    scale[5::7] = 0.0
+    prob = dataclasses.replace(base, kpool=dataclasses.replace(base.kpool, scale=scale))
+    say("scores fp8 negative scales")
+    logits = run_scores(prob).cpu().numpy()
+    for t in range(prob.T):
+        n = int(prob.row_len[t])
+        ok, msg = scores_ok(logits[t, :n], oracle.index_scores_row(prob, t))
+        assert ok, f"row {t}: {msg}"
