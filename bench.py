@@ -185,12 +185,40 @@ def calibration(torch, dev, reps=5):
             "gemm": "torch.mm bf16 8192 x 8192 x 8192, contiguous, best of 5"}
 
 
-def other_configs(dsa, to_device, workloads, torch, dev, flush, names, reps=15):
+def touched_line_bytes(prob, line=128):
+    """Bytes of the distinct `line`-byte cache lines the attention's gathers touch (fp8_ds_mla:
+    a token's 576 data bytes and its 8 scale bytes lie in different lines of its page)."""
+    import numpy as np
+    total = 0
+    for pool, lists in ((prob.kv, prob.idx_main), (prob.extra_kv, prob.idx_extra)):
+        if pool is None or lists is None:
+            continue
+        P = pool.page_size
+        ids = []
+        for b in range(prob.T):
+            pos = np.asarray(lists[b], dtype=np.int64)
+            pos = pos[pos >= 0]
+            slots = np.asarray(pool.block_table[b], dtype=np.int64)[pos // P] * P + pos % P
+            base = (slots // P) * (P * 584)
+            inpg = slots % P
+            for lo, n in ((base + inpg * 576, 576), (base + P * 576 + inpg * 8, 8)):
+                first, last = lo // line, (lo + n - 1) // line
+                span = int((last - first).max()) + 1
+                cand = first[:, None] + np.arange(span)[None, :]
+                ids.append(cand[cand <= last[:, None]])
+        total += np.unique(np.concatenate(ids)).size * line
+    return total
+
+
+def other_configs(dsa, to_device, workloads, torch, dev, flush, names, reps=15, keep=None):
     """Cold per-call latency of the other single-GPU workloads (context beside the headline):
-    the fused layer for decode shapes, the attention stage alone for the DSv4 fp8 case."""
+    the fused layer for decode shapes, the attention stage alone for the DSv4 fp8 case.
+    keep: a dict that receives the generated problems (for the oracle's timing)."""
     res = {}
     for name in names:
         prob = workloads.make_workload(name)
+        if keep is not None:
+            keep[name] = prob
         d = to_device(prob, dev)
         T, H = prob.T, prob.H
         out = torch.empty(T, H, prob.d_v, dtype=torch.bfloat16, device=dev)
@@ -230,19 +258,27 @@ def other_configs(dsa, to_device, workloads, torch, dev, flush, names, reps=15):
         us = statistics.median([a.elapsed_time(b) * 1e3 for a, b in evs])
         res[name] = {"stage": stage, "rows": int(T), "context_max": int(prob.n_max), "cold_us": round(us, 2),
                      "algorithmic_bytes": int(ab), "hbm_roofline_frac": round(ab / (HBM_PEAK_GBS * 1e9) / (us * 1e-6), 4)}
+        if prob.kv.fmt == "fp8_ds_mla":
+            tb = touched_line_bytes(prob) + T * H * (prob.d_qk * 2 + prob.d_v * 2 + 4)
+            res[name]["touched_line_bytes"] = int(tb)
+            res[name]["touched_line_frac"] = round(tb / (HBM_PEAK_GBS * 1e9) / (us * 1e-6), 4)
+            res[name]["touched_note"] = ("distinct 128-byte lines of the gathered rows (576 data bytes and the "
+                                         "8 scale bytes of a token sit in different lines) plus q, out and lse")
         del d, out, lse, ws
         torch.cuda.empty_cache()
         log(f"  {name}: {us:.2f} us cold")
     return res
 
 
-def prefill_chain(dsa, to_device, workloads, torch, dev, reps=3):
+def prefill_chain(dsa, to_device, workloads, torch, dev, reps=3, keep=None):
     """The causal prefill chain (segments 8192 + 1): scores -> top-k -> sparse attention over
     64 heads, each stage timed by its own HIP events; the attention against the bf16 MFMA
     peak (2 * 64 * (576 + 512) FLOP per (row, listed entry)) and the top-k against one read
     of the logits."""
     import numpy as np
     prob = workloads.causal_prefill((8192, 1), name="causal_prefill_8k")
+    if keep is not None:
+        keep["causal_prefill_8k"] = prob
     d = to_device(prob, dev)
     T = prob.T
     ld = ((prob.n_max + 63) // 64) * 64
@@ -333,26 +369,75 @@ def attention_backward(dsa, workloads, torch, dev, reps=5):
             "timing": "HIP events from each dispatch, inputs resident"}
 
 
+def host_cores():
+    """The host cores this process may run on (BLAS threads are set to the same count)."""
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(prob, seconds):
-    import numpy as np  # noqa: F401
+    """The oracle's whole layer for the headline workload, repeated for about `seconds`."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oracle.layer_row(prob, 0)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    from threadpoolctl import threadpool_limits
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.layer_row(prob, 0)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
     us = el / reps * 1e6
     return {"value": round(us, 1), "unit": "us", "cores": int(cores), "kind": "oracle",
             "sample": f"the whole layer of the same workload (fp64 scores of all {int(prob.row_len[0])} "
                       f"candidates, stable top-{prob.topk}, attention), repeated {reps}x in {el:.1f} s"}
+
+
+def cpu_oracle_configs(probs, sample_rows=512):
+    """The oracle (numpy fp64, all host cores) on the other workloads: the tiny, 32k and 1M
+    decode layers and the DSv4 attention stage whole; the causal prefill on a seeded stratified
+    sample of rows (rows 0, 2046, 2047, 8191 and the 1-token segment among them), its time per
+    row scaled to all rows and labelled extrapolated."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    cores = host_cores()
+    res = {}
+    with threadpool_limits(limits=cores):
+        for name in ("tiny_decode", "glm_decode_32k", "long_decode_1m"):
+            if name not in probs:
+                continue
+            prob = probs[name]
+            t0 = time.perf_counter()
+            for t in range(prob.T):
+                oracle.layer_row(prob, t)
+            el = time.perf_counter() - t0
+            res[name] = {"us": round(el * 1e6, 1), "rows": int(prob.T), "what": "whole layer (scores, top-k, attention)"}
+        if "dsv4_fp8_decode" in probs:
+            prob = probs["dsv4_fp8_decode"]
+            t0 = time.perf_counter()
+            for t in range(prob.T):
+                oracle.attention_row(prob, t, prob.idx_main[t], prob.idx_extra[t])
+            el = time.perf_counter() - t0
+            res["dsv4_fp8_decode"] = {"us": round(el * 1e6, 1), "rows": int(prob.T),
+                                      "what": "whole attention stage (main + extra lists)"}
+        if "causal_prefill_8k" in probs:
+            prob = probs["causal_prefill_8k"]
+            seg = int(prob.row_len[prob.T - 2])
+            rng = np.random.default_rng(11)
+            fixed = [0, 2046, 2047, seg - 1, prob.T - 1]
+            edges = np.linspace(0, seg, sample_rows - len(fixed) + 1).astype(int)
+            rows = sorted(set(fixed) | {int(rng.integers(lo, hi)) for lo, hi in zip(edges[:-1], edges[1:]) if hi > lo})
+            t0 = time.perf_counter()
+            for t in rows:
+                oracle.layer_row(prob, t)
+            el = time.perf_counter() - t0
+            res["causal_prefill_8k"] = {"us": round(el / len(rows) * prob.T * 1e6, 1), "rows": int(prob.T),
+                                        "sampled_rows": len(rows), "sample_s": round(el, 2),
+                                        "what": "whole layer per row on a stratified sample, scaled to all rows: "
+                                                "extrapolated"}
+    return {"cores": cores, "configs": res}
 
 
 def main():
@@ -479,7 +564,11 @@ def main():
         "layer": {"algorithmic_bytes": ab, "hbm_roofline_frac": round(layer_frac, 4),
                   "warm_us": round(warm, 2), "cold_us_p10_p90": [round(sorted(cold_us)[K // 10], 2),
                                                                   round(sorted(cold_us)[(9 * K) // 10], 2)],
-                  "per_kernel_us": per_kernel, "timed_wall_s": round(wall, 4)},
+                  "per_kernel_us": per_kernel, "kernel_sum_us": round(sum(per_kernel.values()), 2),
+                  "gap_us": round(cold - sum(per_kernel.values()), 2),
+                  "gap_note": "layer time minus the sum of its kernels' own durations: launch and "
+                              "inter-kernel idle time of the dependent kernels on one stream",
+                  "timed_wall_s": round(wall, 4)},
         "vs_baseline_note": "value / 411 us: the pages' Gluon 128k decode total (tokenspeed PR 627, "
                             "GFX9-class GPU, heads and precision unstated); context, not the target",
     }
@@ -496,9 +585,10 @@ def main():
         res["prefill_indexer"] = pf = prefill_indexer(dsa, to_device, workloads, torch, dev)
         if cal:
             pf["frac_of_measured_gemm"] = round(pf["achieved"] / cal["bf16_gemm_TFLOPs"], 4)
+    kept = {}
     if not args.no_prefill:
         log("prefill chain ...")
-        res["prefill_chain"] = prefill_chain(dsa, to_device, workloads, torch, dev)
+        res["prefill_chain"] = prefill_chain(dsa, to_device, workloads, torch, dev, keep=kept)
         if cal and res["prefill_chain"]["attention"]["achieved_TFLOPs"]:
             res["prefill_chain"]["attention"]["frac_of_measured_gemm"] = round(
                 res["prefill_chain"]["attention"]["achieved_TFLOPs"] / cal["bf16_gemm_TFLOPs"], 4)
@@ -508,11 +598,13 @@ def main():
     if not args.no_configs:
         log("other workloads ...")
         res["other_configs"] = other_configs(dsa, to_device, workloads, torch, dev, flush,
-                                             ["glm_decode_32k", "long_decode_1m", "dsv4_fp8_decode",
-                                              "spec_decode_b16_q4_32k", "extend_64_128k"])
+                                             ["tiny_decode", "glm_decode_32k", "long_decode_1m", "dsv4_fp8_decode",
+                                              "spec_decode_b16_q4_32k", "extend_64_128k"], keep=kept)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
+        if kept:
+            res["cpu_oracle_configs"] = cpu_oracle_configs(kept)
     log(f"cold {cold:.2f} us  warm {warm:.2f} us  per-kernel {per_kernel}  wall {wall:.3f} s")
     print(json.dumps(res), flush=True)
 
