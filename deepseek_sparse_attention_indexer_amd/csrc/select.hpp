@@ -74,7 +74,10 @@ __device__ void find_digit_desc(const uint32_t* h, int nb, uint32_t need, uint32
 // Radix select (descending) over items i < cnt for which get(i, key) is true and whose key
 // matches `prefix` under `pmask`. Resolves the low `low_bits` bits in 12-bit digits; on
 // return `need` is the number still to take among keys equal to the returned threshold and
-// *eq_count the number of such keys.
+// *eq_count the number of such keys. It stops early once the threshold digit's bin holds
+// exactly the keys still needed: every key with that prefix is taken, so the remaining low
+// bits of the returned threshold are zero and *eq_count == need (a caller that takes the keys
+// above the threshold and, when *eq_count <= need, all keys equal to it selects exactly them).
 template <int NT, class Get>
 __device__ uint32_t radix_select_desc(int cnt, Get get, uint32_t prefix, uint32_t pmask,
                                       int low_bits, uint32_t& need, uint32_t* eq_count,
@@ -100,6 +103,7 @@ __device__ uint32_t radix_select_desc(int cnt, Get get, uint32_t prefix, uint32_
     prefix |= d << shift;
     pmask |= dm << shift;
     lds_barrier();
+    if (last_eq == need) break;   // uniform: the bin is taken whole
   }
   *eq_count = last_eq;
   return prefix;
@@ -133,6 +137,7 @@ __device__ uint32_t radix_select_regs(Get get, uint32_t prefix, uint32_t pmask, 
     prefix |= d << shift;
     pmask |= dm << shift;
     lds_barrier();
+    if (last_eq == need) break;   // uniform: the bin is taken whole
   }
   *eq_count = last_eq;
   return prefix;

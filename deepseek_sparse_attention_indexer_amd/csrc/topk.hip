@@ -433,10 +433,16 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
   find_digit_desc<kNT>(s_hist, kHistBins, need1, s_w, s_res);
   const uint32_t pre = (d1 << kHistBits) | s_res[0];     // top 24 bits of the threshold key
   uint32_t need = need1 - s_res[1], eq = 0, pos_thr = 0;
+  const uint32_t sub = s_hist[s_res[0]];                  // candidates in the threshold sub-bin
   lds_barrier();
-  // 2. the threshold sub-bin: its last 8 bits, then ties toward the smaller position
+  // 2. the threshold sub-bin: its last 8 bits, then ties toward the smaller position; a
+  // sub-bin that holds exactly the candidates still needed (the usual case: a 24-bit prefix
+  // rarely holds more than one) is taken whole
   uint32_t thr;
-  if (in_regs) {
+  if (sub == need) {
+    thr = pre << D2;
+    eq = need;
+  } else if (in_regs) {
     auto get_key = [&](int u, uint32_t& key) {
       key = kk[u];
       return (vmask >> u & 1u) != 0;
