@@ -6,8 +6,9 @@
 // prefill kernels"), or fp8 rows of aiter PR 4382 "Paged Sparse Attention Gluon Kernel"
 // (uniform pool: fp8 * fp32 scale per 64 columns, the bytes OCP or fnuz e4m3 (section "fp8
 // flavors"; fnuz has no native conversion and is decoded by bit placement); fp8_ds_mla: 448 NoPE fp8 * 2^(e-127) per 64
-// columns + 64 RoPE bf16, page-planar 584 bytes/token). -1 entries are masked from the
-// original list while their rows are never read (radixark/miles PR 3608, "What", padding).
+// columns + 64 RoPE bf16, page-planar 584 bytes/token). -1 entries contribute nothing
+// (radixark/miles PR 3608, "What", padding): they are dropped when a pass of the list is
+// resolved to cache slots, so their rows are never read and they cost no blocks.
 // A second list (extra) into a second cache shares the softmax (PR 4382, two-loop layout).
 //
 // Workgroup = HT x WD waves sharing each gathered 32-row block: a wave owns 16 heads (one of
@@ -213,13 +214,17 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   const int u_begin = split * a.rows_per_split;
   const int u_end = min(ntot, u_begin + a.rows_per_split);
   static_assert(kResolve % NT == 0 && kResolve % kNB == 0, "resolve pass");
-  int pass_n = 0;   // entries of the current pass (slot table rows at or past it are padding)
+  int pass_n = 0;   // listed rows of the current pass (slot table rows at or past it are padding)
+  constexpr int RPT = kResolve / NT;
+  __shared__ uint32_t s_cnt[RPT * NW];   // listed rows per (entry group, wave) of a pass
 
   // Entries [p0, p1) of the split (at most kResolve) to slots, all at once: every index read
   // of the thread, then every table read, then the slots (two round trips per pass instead
-  // of two per block).
-  auto resolve_pass = [&](int p0, int p1) {
-    constexpr int RPT = kResolve / NT;
+  // of two per block). Padding entries (-1) are dropped: the listed rows are packed to the
+  // front of the slot table in list order (a ballot per wave and entry group, their counts
+  // through LDS), so that blocks hold listed rows only and a list padded with -1 costs no
+  // blocks for its padding. Returns the number of listed rows; the table reads -1 past it.
+  auto resolve_pass = [&](int p0, int p1) -> int {
     int e[RPT];
     bool li[RPT];
 #pragma unroll
@@ -232,13 +237,38 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     SlotRead sr[RPT];
 #pragma unroll
     for (int k = 0; k < RPT; ++k) sr[k] = slot_read(pick_paging(li[k], kv1.pg, kv0.pg), b, max(e[k], 0));
+    int32_t sv[RPT];
+    uint64_t vm[RPT];
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int j = threadIdx.x + k * NT;
       const int64_t slot = slot_done(pick_paging(li[k], kv1.pg, kv0.pg), sr[k]);
-      // entries past the pass read as padding, so a block's row validity is its slot's sign
-      s_slot[j] = j < p1 - p0 && e[k] >= 0 ? (int32_t)slot | ((int32_t)li[k] << 30) : -1;
+      const bool v = j < p1 - p0 && e[k] >= 0;
+      sv[k] = v ? (int32_t)slot | ((int32_t)li[k] << 30) : -1;
+      vm[k] = __ballot(v);
+      if (lane == 0) s_cnt[k * NW + wave] = (uint32_t)__popcll(vm[k]);
     }
+    __syncthreads();
+    uint32_t total = 0, before[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) before[k] = 0;
+#pragma unroll
+    for (int q = 0; q < RPT * NW; ++q) {
+      const uint32_t cq = s_cnt[q];
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) before[k] += q < k * NW + wave ? cq : 0u;
+      total += cq;
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int j = threadIdx.x + k * NT;
+      if (sv[k] >= 0) s_slot[before[k] + (uint32_t)__popcll(vm[k] & below)] = sv[k];
+      // rows past the listed ones read as padding, so a block's row validity is its slot's sign
+      if (j >= (int)total) s_slot[j] = -1;
+    }
+    // the same in every lane: said so, so that the block loop's bounds and waits stay scalar
+    return __builtin_amdgcn_readfirstlane((int)total);
   };
   // cache row of pass entry j (a padding entry reads row 0 of the main cache: finite data,
   // masked by the softmax)
@@ -395,7 +425,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       qreg[i] = o < qbytes ? *reinterpret_cast<const u32x4_t*>(qsrc + o) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  if (u_end > u_begin) resolve_pass(u_begin, min(u_end, u_begin + kResolve));
+  const int first_n = u_end > u_begin ? resolve_pass(u_begin, min(u_end, u_begin + kResolve)) : 0;
   {
     uint8_t* qdst = reinterpret_cast<uint8_t*>(&s_rows[0][0][0]);
 #pragma unroll
@@ -465,15 +495,14 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
                              : (NINS - w_u + NW - 1) / NW;
   for (int p0 = u_begin; p0 < u_end; p0 += kResolve) {
     const int p1 = min(u_end, p0 + kResolve);
-    const int nb = (p1 - p0 + kNB - 1) / kNB;
     if (p0 != u_begin) {
       __syncthreads();                   // every wave is done with the previous pass's slots
-      pass_n = p1 - p0;
-      resolve_pass(p0, p1);
+      pass_n = resolve_pass(p0, p1);
       __syncthreads();
     } else {
-      pass_n = p1 - p0;
+      pass_n = first_n;
     }
+    const int nb = (pass_n + kNB - 1) / kNB;   // blocks of listed rows
     // the addresses of the first NBUF blocks (one thread per row), then the first NBUF - 1
     // blocks' loads
     for (int t = threadIdx.x; t < NBUF * kNB && t < nb * kNB; t += NT) row_addrs(t / kNB, (t / kNB) * kNB, t % kNB);
