@@ -2,6 +2,11 @@
 
 Every source compiles to its own object in parallel (a few hipcc processes at once), then one
 link step makes the shared library.
+
+build(asan=True) makes a copy whose host code (argument checks, workspace carving, launch
+policies) is built with AddressSanitizer, for the CPU tests of the C ABI: the GPU code is
+compiled as usual, and the sanitizer's runtime is not linked in (the process that loads the
+library preloads it; asan_runtime() names it).
 """
 from __future__ import annotations
 
@@ -27,10 +32,24 @@ def sources(src_dir: str | None = None) -> list[str]:
     return sorted(glob.glob(os.path.join(src_dir or os.path.join(HERE, "csrc"), "*.hip")))
 
 
+# host code only: each sanitizer flag is bound to the host compilation
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The AddressSanitizer runtime of the compiler that builds the library (to preload)."""
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise FileNotFoundError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm/lib/clang")
+    return found[-1]
+
+
 def build(verbose: bool = False, src_dir: str | None = None, out: str | None = None,
-          extra_flags: tuple[str, ...] = ()) -> str:
+          extra_flags: tuple[str, ...] = (), asan: bool = False) -> str:
     out = out or os.path.join(HERE, "libdsa.so")
-    obj_dir = os.path.join(os.path.dirname(out), "_build")
+    if asan:
+        extra_flags = tuple(extra_flags) + tuple(ASAN_HOST_FLAGS)
+    obj_dir = os.path.join(os.path.dirname(out), "_build_asan" if asan else "_build")
     os.makedirs(obj_dir, exist_ok=True)
     inc = "-I" + os.path.join(ROOT, "include")
 
@@ -51,8 +70,10 @@ def build(verbose: bool = False, src_dir: str | None = None, out: str | None = N
         objs = list(ex.map(compile_one, srcs))
     tmp = out + ".tmp"
     # -z defs: a symbol left undefined (e.g. a kernel whose host stub was not emitted) fails
-    # the link here instead of the first load of the library
-    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
+    # the link here instead of the first load of the library (not for the sanitized copy, whose
+    # sanitizer symbols come from the preloaded runtime)
+    defs = [] if asan else ["-Wl,-z,defs"]
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *defs, *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

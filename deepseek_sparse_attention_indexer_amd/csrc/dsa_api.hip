@@ -2,7 +2,10 @@
 // See include/dsa.h for the contract of every entry point.
 #include <math.h>
 #include <algorithm>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 #include <mutex>
 #include <vector>
@@ -101,11 +104,31 @@ hipEvent_t pool_event() {
   return e;
 }
 
+// ---------------------------------------------------------------- launch log
+// With DSA_LOG set (to anything but "" or "0"; read once per process) every kernel launch
+// prints one line on stderr: the kernel and the launch row that chose it (the problem's shape
+// and the plan taken for it), set by each driver before its launches.
+bool log_on() {
+  static const bool on = [] {
+    const char* e = getenv("DSA_LOG");
+    return e != nullptr && e[0] != 0 && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+thread_local char t_row[320] = "";
+void set_row(const char* fmt, ...) {
+  if (!log_on()) return;
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(t_row, sizeof(t_row), fmt, ap);
+  va_end(ap);
+}
+
 // Run one kernel launch; in timing mode the launch records a pair of events at its kernel's
 // start and end (launch_kernel), on the stream it runs on.
 template <class F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
-  (void)st;
+  if (log_on()) fprintf(stderr, "[dsa] %-22s stream %p  %s\n", name, (void*)st, t_row);
   if (!g_prof) return launch();
   ProfRec r{name, pool_event(), pool_event()};
   if (!r.a || !r.b) return launch();
@@ -166,6 +189,13 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   p.n_split = (nblk + bps - 1) / bps;
   p.nbuf = 2;
   return p;
+}
+
+void set_mla_row(int T, int H, int n_main, int n_extra, int fmt, int d_qk, bool decode, const MlaPlan& p) {
+  set_row("T=%d H=%d (padded %d) list %d+%d fmt=%d d_qk=%d %s: %d head tile(s) of 16 per workgroup, "
+          "%d split(s) of %d rows, ring of %d",
+          T, H, heads_padded(H), n_main, n_extra, fmt, d_qk, decode ? "decode" : "prefill", p.ht, p.n_split,
+          p.rows_per_split, p.nbuf);
 }
 
 // backward: bf16 scale * dZ and P per (row, listed entry, padded head), and the entries' slots
@@ -341,6 +371,7 @@ dsa_status run_mla(const MlaIn& m, bool decode, void* ws, size_t ws_bytes, hipSt
     a.part_ml = reinterpret_cast<float*>(w + cv.take((int64_t)m.T * a.Hp * p.n_split * 8));
   }
   const int fmt = kv_fmt(m.kv);
+  set_mla_row(m.T, m.H, m.n_idx, m.n_extra, fmt, m.d_qk, decode, p);
   dsa_status s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, m.d_qk, p.ht, p.nbuf, m.T, st); }));
   if (s == DSA_OK && p.n_split > 1)
     s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, m.T, st); }));
@@ -372,6 +403,9 @@ dsa_status check_topk(const TopkIn& k) {
 
 // Long rows, in batches of kMaxLongRows rows: [first-digit histogram] -> filter -> finalize.
 dsa_status run_topk_long(const TopkArgs& a, const dsa_rows& r, bool hist_ready, hipStream_t st) {
+  set_row("T=%d n_max=%d topk=%d: long rows, batches of %d rows, %d chunks of %d, first digit %s", r.T,
+          r.n_max, a.topk, kMaxLongRows, (r.n_max + kTopkChunk - 1) / kTopkChunk, kTopkChunk,
+          hist_ready ? "from the score kernel" : "by its own kernel");
   for (int r0 = 0; r0 < r.T; r0 += kMaxLongRows) {
     const int nb = std::min(kMaxLongRows, r.T - r0);
     TopkArgs b = a;
@@ -403,8 +437,11 @@ dsa_status run_topk(const TopkIn& k, bool hist_ready, void* ws, size_t ws_bytes,
   a.indices = k.indices;
   a.ld_idx = k.ld_idx;
   a.lens = k.lens;
-  if (r.n_max <= kTopkLdsMax)
+  if (r.n_max <= kTopkLdsMax) {
+    set_row("T=%d n_max=%d topk=%d: one workgroup per row, keys in LDS (capacity %d)", r.T, r.n_max, k.topk,
+            r.n_max <= 8192 ? 8192 : kTopkLdsMax);
     return hip_status(timed("topk_lds", st, [&] { return launch_topk_lds(a, r.T, st); }));
+  }
   const int64_t need = kHeaderBytes + topk_ws_bytes(r.T, r.n_max);
   if (!ws || (int64_t)ws_bytes < need || !al16(ws)) return DSA_ERR_WORKSPACE;
   Carve cv;
@@ -447,7 +484,7 @@ dsa_status check_scores(const ScoreIn& s) {
 
 // Many rows that share requests (more rows than requests: a prefill, an extend chunk,
 // speculative verification): scored by the kernel whose workgroups share each key tile among
-// 8 rows. Otherwise one row per workgroup.
+// 4 rows. Otherwise one row per workgroup.
 bool shared_key_rows(const dsa_rows& r, const dsa_key_cache& k) {
   return r.row_req != nullptr && r.T >= kPrefillMinRows && r.T > r.n_req && k.dtype == DSA_KEY_BF16 &&
          k.n_slots <= INT32_MAX;
@@ -474,7 +511,13 @@ dsa_status run_scores(const ScoreIn& s, uint32_t* hist, hipStream_t st) {
   a.logits = s.logits;
   a.ld_logits = s.ld_logits;
   a.hist = hist;
-  if (hist == nullptr && shared_key_rows(r, *s.keys))
+  const bool shared = hist == nullptr && shared_key_rows(r, *s.keys);
+  set_row("T=%d n_max=%d Hi=%d di=%d keys %s, page %d%s: %s", r.T, r.n_max, s.Hi, s.di,
+          s.keys->dtype == DSA_KEY_FP8 ? "fp8" : "bf16", (int)s.keys->paging.page_size,
+          s.keys->paging.block_table ? " (table)" : " (packed)",
+          shared ? "rows sharing keys, 4 rows per workgroup" :
+          hist ? "one row per workgroup, first top-k digit counted" : "one row per workgroup");
+  if (shared)
     return hip_status(timed("index_scores_prefill", st, [&] { return launch_index_scores_prefill(a, s.di, r.T, st); }));
   return hip_status(timed(hist ? "index_scores_hist" : "index_scores", st, [&] {
     return launch_index_scores(a, s.di, s.keys->dtype == DSA_KEY_FP8, hist != nullptr, r.T, st);
@@ -604,6 +647,7 @@ dsa_status decode_run(const DecodeIn& d, uint8_t* wsb, size_t ws_bytes, hipStrea
     if ((size_t)cv.off > ws_bytes) return DSA_ERR_WORKSPACE;
   }
   const int fmt = kv_fmt(d.kv);
+  set_mla_row(T, d.H, d.topk, 0, fmt, d.d_qk, decode, p);
   s = hip_status(timed("sparse_mla", st, [&] { return launch_sparse_mla(a, fmt, d.d_qk, p.ht, p.nbuf, T, st); }));
   if (s == DSA_OK && p.n_split > 1)
     s = hip_status(timed("mla_combine", st, [&] { return launch_mla_combine(a, T, st); }));
@@ -699,6 +743,8 @@ dsa_status dsa_kv_cache_write(const void* src, int64_t ld_src, int32_t n_tok, co
       return DSA_ERR_ARG;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  set_row("%d token(s) of %d + %d columns into a %s cache", n_tok, kv->d_nope, kv->d_rope,
+          kind == kCwBf16 ? "bf16" : kind == kCwDsMla ? "fp8_ds_mla" : kind == kCwScaledFnuz ? "fnuz fp8" : "fp8");
   return hip_status(timed("cache_write_kv", st, [&] { return launch_cache_write(a, kind, st); }));
 }
 
@@ -730,6 +776,7 @@ dsa_status dsa_key_cache_write(const void* src, int64_t ld_src, int32_t n_tok, c
     return DSA_ERR_ARG;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  set_row("%d key(s) of %d into a %s key cache", n_tok, di, kind == kCwBf16 ? "bf16" : "fp8");
   return hip_status(timed("cache_write_keys", st, [&] { return launch_cache_write(a, kind, st); }));
 }
 
@@ -895,6 +942,8 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
     a.ws_slot = reinterpret_cast<int32_t*>(w + cv.take(e * 4));
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  set_row("T=%d H=%d (padded %d) list %d d_qk=%d: one workgroup per (row, 16 heads), dKV over all heads", T,
+          H, (int)a.Hp, n_idx, d_qk);
   dsa_status s = hip_status(timed("sparse_mla_bwd", hs, [&] { return launch_sparse_mla_bwd(a, d_qk, T, hs); }));
   if (s == DSA_OK)
     s = hip_status(timed("sparse_mla_bwd_dkv", hs, [&] { return launch_sparse_mla_bwd_dkv(a, d_qk, T, hs); }));

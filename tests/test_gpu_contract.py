@@ -4,8 +4,14 @@
   offsets (and straddling them) are read correctly (64-bit addressing of every gather);
 * the fused decode captured once in a HIP graph and replayed with new inputs in place gives
   exactly the eager results (the workspace's control words stay zero at rest; no memset node);
-* every forward entry gives bit-identical results when run twice on the same inputs.
+* every forward entry gives bit-identical results when run twice on the same inputs;
+* DSA_LOG=1 prints one line per kernel launch with the launch row that chose it, and nothing
+  without it.
 """
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -293,3 +299,40 @@ def test_attention_two_lists_fp8_deterministic():
                                 prob.d_v, prob.softmax_scale, out, lse, ws)
         return [out, lse]
     _twice(run)
+
+
+# --------------------------------------------------------------------------- launch log
+
+_LOG_CHILD = """
+import sys
+sys.path.insert(0, {tests!r})
+sys.path.insert(0, {root!r})
+import torch
+from dev import run_decode, workload
+run_decode(workload("tiny_decode"))
+torch.cuda.synchronize()
+print("child done", flush=True)
+"""
+
+
+@pytest.mark.parametrize("log", ["1", None])
+def test_dsa_log_prints_the_launch_rows(log):
+    """DSA_LOG is read once per process, so each setting runs the tiny decode in a child."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = _LOG_CHILD.format(tests=here, root=os.path.dirname(here))
+    env = {k: v for k, v in os.environ.items() if k != "DSA_LOG"}
+    if log:
+        env["DSA_LOG"] = log
+    say(f"DSA_LOG={log}: tiny decode in a child process")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0 and "child done" in r.stdout, r.stderr[-2000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[dsa] ")]
+    if not log:
+        assert lines == []
+        return
+    kernels = [ln.split()[1] for ln in lines]
+    assert kernels == ["index_scores", "topk_lds", "sparse_mla", "mla_combine"], lines
+    assert "T=1 n_max=512 Hi=4 di=64" in lines[0], lines[0]
+    assert "topk=128" in lines[1] and "in LDS" in lines[1], lines[1]
+    assert "H=16 (padded 16) list 128+0" in lines[2] and "decode" in lines[2], lines[2]
+    assert "split(s)" in lines[3], lines[3]
