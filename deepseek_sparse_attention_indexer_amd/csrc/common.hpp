@@ -170,6 +170,16 @@ __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
 // Two fp32 -> packed bf16 pair (lo in bits 0..15), round-to-nearest-even: one gfx950
 // v_cvt_pk_bf16_f32 (checked on the GPU bit for bit against the integer rounding
 // (u + 0x7fff + ((u >> 16) & 1)) >> 16 over 2^25 finite patterns, denormals and ties included).
+// Transposing LDS read of 16-bit data (gfx950 ds_read_b64_tr_b16). Each lane addresses a piece
+// of four consecutive elements (8-byte aligned); in each group of 16 lanes, lane 4 a + b
+// receives element b of the pieces of lanes a, a + 4, a + 8 and a + 12 of its group, in that
+// order (lane layout measured on the hardware).
+__device__ __forceinline__ u32x2_t ds_read_tr16(const uint16_t* p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  auto* lp = reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(reinterpret_cast<uintptr_t>(p) & 0xffffffffu);
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));

@@ -618,28 +618,28 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       for (int i = 0; i < 4; ++i) l_run += p[i];   // this wave's rows; the waves meet at the end
       // ---- O^T += V^T P^T over this wave's VC value columns, two k-steps of 16 rows. k-slot
       // 8 hl + j of k-step ks is row 16 ks + 4 hl + j (j < 4) or 16 ks + 8 + 4 hl + j - 4, i.e.
-      // the weights that the same lane of slices 2 ks and 2 ks + 1 published; V^T by 8 x CPL
-      // transposes of LDS rows (m-tile e = columns VC vh + CPL m + e)
+      // the weights that the same lane of slices 2 ks and 2 ks + 1 published. m-tile e is
+      // columns VC vh + 32 e .. + 31, and its V^T operand comes from two transposing LDS reads
+      // (ds_read_b64_tr_b16): in each 16-lane group, lane 4 a + b receives element b of the
+      // 4-column pieces that lanes a, a + 4, a + 8, a + 12 address, so lane 16 G + 4 j + a
+      // addresses row 16 ks + 4 (G / 2) + j (+ 8 for k-slots 4..7) at column 16 (G % 2) + 4 a
+      // of the tile, and every lane ends with its column (lane % 32) of its 8 rows.
+      {
+        const int tg = lane >> 4, tj = (lane >> 2) & 3, ta = lane & 3;
+        const int tr_row = 4 * (tg >> 1) + tj;
+        const int tr_col = VC * vh + 16 * (tg & 1) + 4 * ta;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x2_t pa = s_pw[hh + 2 * (2 * ks)][lane];
-        const u32x2_t pc = s_pw[hh + 2 * (2 * ks + 1)][lane];
-        const u32x4_t pb = u32x4_t{pa[0], pa[1], pc[0], pc[1]};
-        u32x4_t vr[8];
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x2_t pa = s_pw[hh + 2 * (2 * ks)][lane];
+          const u32x2_t pc = s_pw[hh + 2 * (2 * ks + 1)][lane];
+          const u32x4_t pb = u32x4_t{pa[0], pa[1], pc[0], pc[1]};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = 16 * ks + (j < 4 ? 4 * hl + j : 8 + 4 * hl + j - 4);
-          const u32x2_t v2 = *reinterpret_cast<const u32x2_t*>(&s_rows[cur][row][VC * vh + CPL * l32]);
-          vr[j] = u32x4_t{v2[0], v2[1], 0u, 0u};
-        }
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          const int w = e >> 1;
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          u32x4_t av;
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) av[pp] = __builtin_amdgcn_perm(vr[2 * pp + 1][w], vr[2 * pp][w], sel);
-          o32[e] = mfma_bf16_32x32x16(av, pb, o32[e]);
+          for (int e = 0; e < CPL; ++e) {
+            const uint16_t* rp = &s_rows[cur][16 * ks + tr_row][tr_col + 32 * e];
+            const u32x2_t lo = ds_read_tr16(rp);
+            const u32x2_t hi = ds_read_tr16(rp + 8 * RE);
+            o32[e] = mfma_bf16_32x32x16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb, o32[e]);
+          }
         }
       }
     } else {
@@ -745,9 +745,10 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   }
 
   if constexpr (kW32) {
-    // lane l holds head 32 hh + l32 (of the workgroup's 64), columns VC vh + CPL m + e for
-    // m = 8 (r / 4) + 4 hl + r % 4 of accumulator r, e = 0..CPL-1. The weight sum: over the
-    // lane halves, then over the head half's four waves (each summed its own rows)
+    // lane l holds head 32 hh + l32 (of the workgroup's 64), columns VC vh + 32 e + m for
+    // m = 8 (r / 4) + 4 hl + r % 4 of accumulator r of m-tile e: four consecutive columns per
+    // group of four accumulators. The weight sum: over the lane halves, then over the head
+    // half's four waves (each summed its own rows)
     l_run += __shfl_xor(l_run, 32);
     if (hl == 0) s_lw[wave][l32] = l_run;
     __syncthreads();
@@ -758,14 +759,15 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     const bool hv = headw < a.H;                        // not a padding head
     if constexpr (!SPLIT) {
       const Finish fin = finish_softmax(m_run, l_run, a.sink && hv ? a.sink[headw] : -INFINITY, a.lse_log2);
-      uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)headw * kDV + VC * vh;
+      uint16_t* op = a.out + (int64_t)t * a.ld_out + (int64_t)headw * kDV + VC * vh + 4 * hl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
-        const u32x2_t v = u32x2_t{pack_bf16_rne(o32[0][r] * fin.inv, o32[1][r] * fin.inv),
-                                  pack_bf16_rne(o32[2][r] * fin.inv, o32[3][r] * fin.inv)};
-        if (hv) *reinterpret_cast<u32x2_t*>(op + 4 * m) = v;
-      }
+      for (int e = 0; e < CPL; ++e)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2_t v = u32x2_t{pack_bf16_rne(o32[e][4 * q] * fin.inv, o32[e][4 * q + 1] * fin.inv),
+                                    pack_bf16_rne(o32[e][4 * q + 2] * fin.inv, o32[e][4 * q + 3] * fin.inv)};
+          if (hv) *reinterpret_cast<u32x2_t*>(op + 32 * e + 8 * q) = v;
+        }
       if (a.lse && hv && hl == 0 && vh == 0) a.lse[(int64_t)t * a.H + headw] = fin.lse;
     } else {
       // The partial (o, m, l). A lane's pieces are 16 bytes scattered over 32 head rows, so
@@ -780,11 +782,11 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         if (half) __syncthreads();                      // the first half is written out
         if (hh == half) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
-            *reinterpret_cast<f32x4_t*>(s_po + l32 * PS + VC * vh + 4 * m) =
-                f32x4_t{o32[0][r], o32[1][r], o32[2][r], o32[3][r]};
-          }
+          for (int e = 0; e < CPL; ++e)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<f32x4_t*>(s_po + l32 * PS + VC * vh + 32 * e + 8 * q + 4 * hl) =
+                  f32x4_t{o32[e][4 * q], o32[e][4 * q + 1], o32[e][4 * q + 2], o32[e][4 * q + 3]};
         }
         __syncthreads();
         float* po = a.part_o + ((int64_t)t * a.Hp + hg * 64 + 32 * half) * a.n_split * kDV +
