@@ -442,30 +442,30 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   constexpr int KQ = kSplitK ? KS / 2 : KS;          // k-steps of the score product per wave
   const int kq0 = kSplitK ? (wave & 1) * KQ : 0;     // this wave's first k-step
   __shared__ f32x4_t s_sp[kSplitK ? 4 : 1][64];      // the partials
-  // 64 heads, 32x32x16 MFMAs (see the top): lane l of wave w is head 32 hh + l32 of the
-  // workgroup's 64 and reads k-slots 8 hl .. 8 hl + 7. The NVS = 2 WD waves of a head half
-  // take value slice vh (VC columns each) and the vh-th of NVS parts of the contraction,
-  // k-steps kq32 .. kq32 + KQ32 - 1 (16 columns each)
+  // 64 heads (see the top): wave w belongs to head half hh = w & 1 and takes value slice
+  // vh = w >> 1 (VC columns) of the half's 32 heads on 32x32x16 MFMAs (lane l: head 32 hh + l32,
+  // k-slots 8 hl .. 8 hl + 7). Its score tile is 16 rows x 16 heads over the whole
+  // contraction on 16x16x32 MFMAs: rows 16 rx .. + 15 and heads 16 hx .. + 15 of the half
+  // (rx = vh & 1, hx = vh >> 1), so scores never cross waves; only the weights do.
   constexpr bool kW32 = HT == 4 && WD == 2;
   constexpr int NVS = 2 * WD;                         // waves per head half
   constexpr int VC = kDV / NVS;                       // value columns per wave
   constexpr int CPL = VC / 32;                        // columns per lane and row (m-tiles)
-  constexpr int KQ32 = DQK / (16 * NVS);              // k-steps of 16 per wave
-  static_assert(!kW32 || (DQK % (16 * NVS) == 0 && NVS == 4 && CPL == 4), "32-head split");
+  static_assert(!kW32 || (NVS == 4 && CPL == 4), "32-head split");
   const int hh = wave & 1, vh = wave >> 1;
   const int l32 = lane & 31, hl = lane >> 5;
-  const int kq32 = vh * KQ32;
-  __shared__ f32x4_t s_sp32[kW32 ? NW : 1][4][64];   // the score partials, 16 floats per lane
-  __shared__ u32x2_t s_pw[kW32 ? NW : 1][64];         // each wave's rows' weights, packed bf16
-  __shared__ float s_mx[kW32 ? NW : 1][32];           // each wave's max per head
-  __shared__ float s_lw[kW32 ? NW : 1][32];           // each wave's weight sum per head (end)
+  const int rx = vh & 1, hx = vh >> 1;
+  auto wv = [&](int r, int h) { return hh + 2 * (r + 2 * h); };   // the half's wave of tile (r, h)
+  constexpr int PTS = 32 + 4;                         // padded row count of a head's weights
+  __shared__ __align__(8) uint16_t s_pt[kW32 ? 2 : 1][32][PTS];   // P^T per half: [head][row], bf16
+  __shared__ float s_mx[kW32 ? NW : 1][16];           // each wave's block max per score head
+  __shared__ float s_lw[kW32 ? NW : 1][16];           // each wave's weight sum per score head (end)
   __shared__ int s_grow[kW32 ? NW : 1];
-  u32x4_t qb[kW32 ? 1 : KQ];
-  u32x4_t qb32[kW32 ? KQ32 : 1];
+  u32x4_t qb[KQ];
   if constexpr (kW32) {
-    const uint16_t* qp = &s_rows[0][0][0] + (32 * hh + l32) * RE + 8 * hl;
+    const uint16_t* qp = &s_rows[0][0][0] + (32 * hh + 16 * hx + c) * RE + 8 * g;
 #pragma unroll
-    for (int kb = 0; kb < KQ32; ++kb) qb32[kb] = *reinterpret_cast<const u32x4_t*>(qp + 16 * (kq32 + kb));
+    for (int kb = 0; kb < KQ; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(qp + 32 * kb);
   } else {
     const uint16_t* qp = &s_rows[0][0][0] + (ht * 16 + c) * RE + 8 * g;
 #pragma unroll
@@ -473,6 +473,9 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   }
   float m_run = -INFINITY;   // running max (base-2 units) of this lane's head; rescaled lazily
   float l_run = 0.f;         // lane-partial sum of exp2(s - m_run)
+  // 64 heads: m_run and l_run belong to the lane's score head (16 hx + c of the half); m_o is
+  // the same running max for the lane's value head (l32), kept in step with it
+  float m_o = -INFINITY;
   f32x4_t o[kW32 ? 1 : GD][8];
   f32x16_t o32[kW32 ? CPL : 1];
 #pragma unroll
@@ -556,82 +559,79 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     const u32x4_t sl1 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm + 16]);
 
     if constexpr (kW32) {
-      // ---- S^T partial over this wave's quarter of the contraction: 32 rows x 32 heads
-      f32x16_t sp = {};
+      // ---- S^T tile: rows 16 rx + (lane & 15) of the block against this wave's 16 heads,
+      // the whole contraction (A = rows from LDS, B = q in registers)
+      f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
-        const uint16_t* rp = &s_rows[cur][l32][8 * hl + 16 * kq32];
+        const uint16_t* rp = &s_rows[cur][16 * rx + c][8 * g];
 #pragma unroll
-        for (int kb = 0; kb < KQ32; ++kb) sp = mfma_bf16_32x32x16(*reinterpret_cast<const u32x4_t*>(rp + 16 * kb), qb32[kb], sp);
+        for (int kb = 0; kb < KQ; ++kb) sacc = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 32 * kb), qb[kb], sacc);
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) s_sp32[wave][q][lane] = f32x4_t{sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]};
-      // Each wave finishes the softmax of its own 8 rows only: accumulator group vh of the
-      // head half's partials, i.e. rows 8 vh + 4 hl + i (i = 0..3) of head 32 hh + l32.
-      const u32x4_t slv = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + 8 * vh + 4 * hl]);
-      lds_barrier();
-      // the four partials in a fixed order, so that a score does not depend on who sums it
-      f32x4_t st = s_sp32[hh][vh][lane];
-#pragma unroll
-      for (int v = 1; v < NVS; ++v) st += s_sp32[hh + 2 * v][vh][lane];
+      // accumulator i of lane l: row 16 rx + 4 g + i, head 16 hx + c of the half
+      const u32x4_t slv = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + 16 * rx + 4 * g]);
       float x[4];
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = (int32_t)slv[i] >= 0 ? st[i] * a.scale_log2 : -INFINITY;
+        x[i] = (int32_t)slv[i] >= 0 ? sacc[i] * a.scale_log2 : -INFINITY;
         mx = fmaxf(mx, x[i]);
       }
-      mx = max_xor32(mx);                          // over the wave's 8 rows, per head
-      // Weights against the running max, published as packed bf16 for the value product of
-      // every wave of the head half. They stand unless some wave's rows raise a head's max
-      // by more than 2^8; then every wave of the workgroup rescales and publishes again.
+      mx = max_xor32(max_xor16(mx));               // over the tile's 16 rows, per head
+      // Weights against the running max, published as P^T (bf16) for the value product of
+      // every wave of the half. They stand unless some wave's rows raise a head's max by more
+      // than 2^8; then every wave rescales (its value heads and its score heads alike) and
+      // publishes again.
       float p[4];
       auto weights = [&]() {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;   // no valid row yet: x = -inf
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = exp2_hw(x[i] - m_use);
-        s_pw[wave][lane] = u32x2_t{pack_bf16_rne(p[0], p[1]), pack_bf16_rne(p[2], p[3])};
+        *reinterpret_cast<u32x2_t*>(&s_pt[hh][16 * hx + c][16 * rx + 4 * g]) =
+            u32x2_t{pack_bf16_rne(p[0], p[1]), pack_bf16_rne(p[2], p[3])};
       };
       weights();
       const bool grow = __any(mx > m_run + 8.f);
       if (lane == 0) s_grow[wave] = grow ? 1 : 0;
-      if (hl == 0) s_mx[wave][l32] = mx;
+      if (g == 0) s_mx[wave][c] = mx;
       lds_barrier();
       bool any_grow = false;
 #pragma unroll
       for (int w = 0; w < NW; ++w) any_grow |= s_grow[w] != 0;
       if (any_grow) {                              // the same branch in every wave
-        float bm = s_mx[hh][l32];
+        // a head's block max: the two row tiles of its head quarter
+        const float bs = fmaxf(s_mx[wv(0, hx)][c], s_mx[wv(1, hx)][c]);
+        const float bo = fmaxf(s_mx[wv(0, l32 >> 4)][l32 & 15], s_mx[wv(1, l32 >> 4)][l32 & 15]);
+        const float ms_new = fmaxf(m_run, bs);
+        const float mo_new = fmaxf(m_o, bo);
+        if (m_o != -INFINITY) {
+          const float alpha_o = exp2_hw(m_o - mo_new);
 #pragma unroll
-        for (int v = 1; v < NVS; ++v) bm = fmaxf(bm, s_mx[hh + 2 * v][l32]);
-        const float m_new = fmaxf(m_run, bm);
-        const float alpha = m_run == -INFINITY ? 0.f : exp2_hw(m_run - m_new);
-        if (m_run != -INFINITY || __any(l_run != 0.f)) {
-          l_run *= alpha;
-#pragma unroll
-          for (int e = 0; e < CPL; ++e) o32[e] *= alpha;
+          for (int e = 0; e < CPL; ++e) o32[e] *= alpha_o;
         }
-        m_run = m_new;
+        if (m_run != -INFINITY) l_run *= exp2_hw(m_run - ms_new);
+        m_run = ms_new;
+        m_o = mo_new;
         weights();
         lds_barrier();
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l_run += p[i];   // this wave's rows; the waves meet at the end
+      for (int i = 0; i < 4; ++i) l_run += p[i];   // this lane's rows of its score head
       // ---- O^T += V^T P^T over this wave's VC value columns, two k-steps of 16 rows. k-slot
-      // 8 hl + j of k-step ks is row 16 ks + 4 hl + j (j < 4) or 16 ks + 8 + 4 hl + j - 4, i.e.
-      // the weights that the same lane of slices 2 ks and 2 ks + 1 published. m-tile e is
-      // columns VC vh + 32 e .. + 31, and its V^T operand comes from two transposing LDS reads
-      // (ds_read_b64_tr_b16): in each 16-lane group, lane 4 a + b receives element b of the
-      // 4-column pieces that lanes a, a + 4, a + 8, a + 12 address, so lane 16 G + 4 j + a
-      // addresses row 16 ks + 4 (G / 2) + j (+ 8 for k-slots 4..7) at column 16 (G % 2) + 4 a
-      // of the tile, and every lane ends with its column (lane % 32) of its 8 rows.
+      // 8 hl + j of k-step ks is row 16 ks + 4 hl + j (j < 4) or 16 ks + 8 + 4 hl + j - 4: two
+      // 8-byte reads of the value head's row of P^T. m-tile e is columns VC vh + 32 e .. + 31,
+      // and its V^T operand comes from two transposing LDS reads (ds_read_b64_tr_b16): in each
+      // 16-lane group, lane 4 a + b receives element b of the 4-column pieces that lanes a,
+      // a + 4, a + 8, a + 12 address, so lane 16 G + 4 j + a addresses row 16 ks + 4 (G / 2) + j
+      // (+ 8 for k-slots 4..7) at column 16 (G % 2) + 4 a of the tile, and every lane ends with
+      // its column (lane % 32) of its 8 rows.
       {
         const int tg = lane >> 4, tj = (lane >> 2) & 3, ta = lane & 3;
         const int tr_row = 4 * (tg >> 1) + tj;
         const int tr_col = VC * vh + 16 * (tg & 1) + 4 * ta;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const u32x2_t pa = s_pw[hh + 2 * (2 * ks)][lane];
-          const u32x2_t pc = s_pw[hh + 2 * (2 * ks + 1)][lane];
+          const u32x2_t pa = *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][16 * ks + 4 * hl]);
+          const u32x2_t pc = *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][16 * ks + 8 + 4 * hl]);
           const u32x4_t pb = u32x4_t{pa[0], pa[1], pc[0], pc[1]};
 #pragma unroll
           for (int e = 0; e < CPL; ++e) {
@@ -747,14 +747,14 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   if constexpr (kW32) {
     // lane l holds head 32 hh + l32 (of the workgroup's 64), columns VC vh + 32 e + m for
     // m = 8 (r / 4) + 4 hl + r % 4 of accumulator r of m-tile e: four consecutive columns per
-    // group of four accumulators. The weight sum: over the lane halves, then over the head
-    // half's four waves (each summed its own rows)
+    // group of four accumulators. The weight sum of that head: each score lane's rows summed
+    // over its tile's four row groups, then the head quarter's two row tiles
+    l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    if (hl == 0) s_lw[wave][l32] = l_run;
+    if (g == 0) s_lw[wave][c] = l_run;
     __syncthreads();
-    l_run = s_lw[hh][l32];
-#pragma unroll
-    for (int v = 1; v < NVS; ++v) l_run += s_lw[hh + 2 * v][l32];
+    l_run = s_lw[wv(0, l32 >> 4)][l32 & 15] + s_lw[wv(1, l32 >> 4)][l32 & 15];
+    m_run = m_o;
     const int headw = hg * 64 + 32 * hh + l32;
     const bool hv = headw < a.H;                        // not a padding head
     if constexpr (!SPLIT) {
