@@ -563,9 +563,20 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       // the whole contraction (A = rows from LDS, B = q in registers)
       f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
+        // operands read three k-steps ahead of their MFMA, so that no MFMA waits out a whole
+        // LDS round trip (left to itself the compiler keeps one buffer and waits every step)
         const uint16_t* rp = &s_rows[cur][16 * rx + c][8 * g];
+        constexpr int DEPTH = 3;
+        u32x4_t av[DEPTH];
 #pragma unroll
-        for (int kb = 0; kb < KQ; ++kb) sacc = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 32 * kb), qb[kb], sacc);
+        for (int d = 0; d < DEPTH; ++d) av[d] = *reinterpret_cast<const u32x4_t*>(rp + 32 * d);
+#pragma unroll
+        for (int kb = 0; kb < KQ; ++kb) {
+          sacc = mfma_bf16_16x16x32(av[kb % DEPTH], qb[kb], sacc);
+          if (kb + DEPTH < KQ) av[kb % DEPTH] = *reinterpret_cast<const u32x4_t*>(rp + 32 * (kb + DEPTH));
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA,
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then the next read
+        }
       }
       // accumulator i of lane l: row 16 rx + 4 g + i, head 16 hx + c of the half
       const u32x4_t slv = *reinterpret_cast<const u32x4_t*>(&s_slot[jb + 16 * rx + 4 * g]);
