@@ -220,10 +220,11 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
 
   // Entries [p0, p1) of the split (at most kResolve) to slots, all at once: every index read
   // of the thread, then every table read, then the slots (two round trips per pass instead
-  // of two per block). Padding entries (-1) are dropped: the listed rows are packed to the
-  // front of the slot table in list order (a ballot per wave and entry group, their counts
-  // through LDS), so that blocks hold listed rows only and a list padded with -1 costs no
-  // blocks for its padding. Returns the number of listed rows; the table reads -1 past it.
+  // of two per block). Padding entries (-1) are dropped from passes longer than two blocks:
+  // the listed rows are packed to the front of the slot table in list order (a ballot per
+  // wave and entry group, their counts through LDS), so that blocks hold listed rows only and
+  // a list padded with -1 costs no blocks for its padding. Returns the number of table rows
+  // to process; the table reads -1 past them (and at padding entries of a short pass).
   auto resolve_pass = [&](int p0, int p1) -> int {
     int e[RPT];
     bool li[RPT];
@@ -238,14 +239,23 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
 #pragma unroll
     for (int k = 0; k < RPT; ++k) sr[k] = slot_read(pick_paging(li[k], kv1.pg, kv0.pg), b, max(e[k], 0));
     int32_t sv[RPT];
-    uint64_t vm[RPT];
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int j = threadIdx.x + k * NT;
       const int64_t slot = slot_done(pick_paging(li[k], kv1.pg, kv0.pg), sr[k]);
-      const bool v = j < p1 - p0 && e[k] >= 0;
-      sv[k] = v ? (int32_t)slot | ((int32_t)li[k] << 30) : -1;
-      vm[k] = __ballot(v);
+      sv[k] = j < p1 - p0 && e[k] >= 0 ? (int32_t)slot | ((int32_t)li[k] << 30) : -1;
+    }
+    // a pass of at most two blocks (a decode split) keeps its entries in place: packing could
+    // save at most one block, less than the barrier and the LDS round trip it costs
+    if (p1 - p0 <= 2 * kNB) {
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) s_slot[threadIdx.x + k * NT] = sv[k];
+      return p1 - p0;
+    }
+    uint64_t vm[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      vm[k] = __ballot(sv[k] >= 0);
       if (lane == 0) s_cnt[k * NW + wave] = (uint32_t)__popcll(vm[k]);
     }
     __syncthreads();
