@@ -12,6 +12,6 @@ from ._binding import (  # noqa: F401
     dsa_decode_static, STATIC_SCRATCH_BYTES, DSA_ERR_SCRATCH_LIMIT,
     dsa_sparse_mla_backward,
     dsa_workspace_size, dsa_workspace_init, dsa_status_string, dsa_abi_version,
-    dsa_profile_enable, dsa_profile_collect, dsa_kv_cache_write, dsa_key_cache_write,
+    dsa_profile_enable, dsa_profile_collect, dsa_launch_override, dsa_kv_cache_write, dsa_key_cache_write,
     Workspace, ENTRY_TOPK, ENTRY_MLA_DECODE, ENTRY_MLA_PREFILL, ENTRY_DECODE, ENTRY_MLA_BACKWARD,
 )

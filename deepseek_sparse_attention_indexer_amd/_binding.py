@@ -99,7 +99,7 @@ _lib.dsa_status_string.argtypes = [_I32]
 _lib.dsa_status_string.restype = C.c_char_p
 _lib.dsa_abi_version.argtypes = []
 _lib.dsa_abi_version.restype = _I32
-ABI_VERSION = 6   # the signatures above
+ABI_VERSION = 7   # the signatures above
 if _lib.dsa_abi_version() != ABI_VERSION:
     raise ImportError(f"{lib_path()} has ABI version {_lib.dsa_abi_version()}, this binding needs "
                       f"{ABI_VERSION}: rebuild the library")
@@ -114,6 +114,8 @@ _lib.dsa_profile_enable.argtypes = [_I32]
 _lib.dsa_profile_enable.restype = _I32
 _lib.dsa_profile_collect.argtypes = [C.POINTER(_KernelTime), _I32]
 _lib.dsa_profile_collect.restype = _I32
+_lib.dsa_launch_override.argtypes = [_I32, _I32]
+_lib.dsa_launch_override.restype = _I32
 
 
 class DSAError(RuntimeError):
@@ -132,6 +134,12 @@ def dsa_abi_version() -> int:
 
 def dsa_profile_enable(on: bool):
     _check(_lib.dsa_profile_enable(1 if on else 0), "dsa_profile_enable")
+
+
+def dsa_launch_override(head_tiles: int = 0, n_split: int = 0):
+    """Force the attention launch plan of later calls (0 = the compiled-in table's choice);
+    (0, 0) restores the table. See include/dsa.h."""
+    _check(_lib.dsa_launch_override(int(head_tiles), int(n_split)), "dsa_launch_override")
 
 
 def dsa_profile_collect(max_entries: int = 32) -> dict:

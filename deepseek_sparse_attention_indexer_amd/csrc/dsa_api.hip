@@ -158,6 +158,10 @@ struct MlaPlan {
   int rows_per_split;
 };
 
+// dsa_launch_override: 0 = the table's choice
+int g_force_ht = 0;
+int g_force_split = 0;
+
 MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   // A CU sustains only ~25 GB/s of gathers and a lone wave far less, so a decode step with
   // few rows spreads rows AND partial outputs over every CU: one 16-head tile per 4-wave
@@ -183,6 +187,8 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
       s = (int)std::min<int64_t>((256 + base - 1) / base, nblk);  // about one workgroup per CU
     }
   }
+  if (g_force_ht > 0) p.ht = g_force_ht;        // validated against the heads by the callers
+  if (g_force_split > 0 && decode) s = std::min(g_force_split, nblk);
   s = std::max(1, s);
   const int bps = (nblk + s - 1) / s;           // blocks per split
   p.rows_per_split = bps * 32;
@@ -190,6 +196,9 @@ MlaPlan plan_mla(int T, int H, int ntot, bool decode) {
   p.nbuf = 2;
   return p;
 }
+
+// an overridden head-tile count that does not divide the padded tiles has no kernel
+bool plan_ok(int H, const MlaPlan& p) { return (heads_padded(H) / 16) % p.ht == 0; }
 
 void set_mla_row(int T, int H, int n_main, int n_extra, int fmt, int d_qk, bool decode, const MlaPlan& p) {
   set_row("T=%d H=%d (padded %d) list %d+%d fmt=%d d_qk=%d %s: %d head tile(s) of 16 per workgroup, "
@@ -339,6 +348,7 @@ dsa_status run_mla(const MlaIn& m, bool decode, void* ws, size_t ws_bytes, hipSt
   if (m.T == 0) return DSA_OK;
   const int ntot = m.n_idx + m.n_extra;
   const MlaPlan p = plan_mla(m.T, m.H, ntot, decode);
+  if (!plan_ok(m.H, p)) return DSA_ERR_UNSUPPORTED;
   MlaArgs a;
   memset(&a, 0, sizeof(a));
   a.q = static_cast<const uint16_t*>(m.q);
@@ -618,6 +628,7 @@ dsa_status decode_run(const DecodeIn& d, uint8_t* wsb, size_t ws_bytes, hipStrea
   // step 3: attention over the selection; split partials after our regions
   const bool decode = T <= 1024;
   const MlaPlan p = plan_mla(T, d.H, d.topk, decode);
+  if (!plan_ok(d.H, p)) return DSA_ERR_UNSUPPORTED;
   MlaArgs a;
   memset(&a, 0, sizeof(a));
   a.q = static_cast<const uint16_t*>(d.q);
@@ -696,7 +707,15 @@ dsa_status static_scratch(hipStream_t st, StaticScratch** out) {
 // ==================================================================== exported entry points
 extern "C" {
 
-int32_t dsa_abi_version(void) { return 6; }
+int32_t dsa_abi_version(void) { return 7; }
+
+dsa_status dsa_launch_override(int32_t head_tiles, int32_t n_split) {
+  if (!(head_tiles == 0 || head_tiles == 1 || head_tiles == 2 || head_tiles == 4)) return DSA_ERR_ARG;
+  if (n_split < 0 || n_split > 65535) return DSA_ERR_ARG;
+  g_force_ht = head_tiles;
+  g_force_split = n_split;
+  return DSA_OK;
+}
 dsa_status dsa_kv_cache_write(const void* src, int64_t ld_src, int32_t n_tok, const int32_t* slots,
                               const dsa_kv_cache* kv, void* stream) {
   if (n_tok < 0 || !kv) return DSA_ERR_ARG;

@@ -338,6 +338,21 @@ typedef struct dsa_kernel_time {
 dsa_status dsa_profile_enable(int32_t on);
 int32_t dsa_profile_collect(dsa_kernel_time* out, int32_t max_entries);
 
+/* ---------------------------------------------------------------- launch override
+ * Tuning aid: force the sparse-attention launch plan of every later call in this process
+ * (dsa_sparse_mla_decode, dsa_sparse_mla_prefill, dsa_decode, and dsa_workspace_size for
+ * those entries) instead of the compiled-in launch table, for sweeps without a rebuild.
+ * head_tiles: 16-head tiles per workgroup, 1, 2 or 4 (0 = the table's choice); it must divide
+ *             the padded head count ceil(H / 16), or the affected calls return
+ *             DSA_ERR_UNSUPPORTED.
+ * n_split:    splits of each row's list for the split-KV entries (decode and the fused
+ *             layer), clamped to [1, the list's 32-row blocks]; 0 = the table's choice.
+ *             Prefill rows never split.
+ * Size the workspace after setting it. (0, 0) restores the table. DSA_ERR_ARG for other
+ * values. Not thread-safe against calls in flight on other threads. DSA_LOG=1 shows the plan
+ * each launch takes. */
+dsa_status dsa_launch_override(int32_t head_tiles, int32_t n_split);
+
 #ifdef __cplusplus
 }
 #endif

@@ -176,6 +176,27 @@ def test_workspace_sizes():
         dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=1, H=129, n_idx=64)
 
 
+def test_launch_override():
+    """The plan override is checked, moves the workspace size with the plan it forces, and a
+    head-tile count that does not divide the heads is refused before any launch."""
+    for bad in ((3, 0), (-1, 0), (8, 0), (0, -1)):
+        with pytest.raises(dsa.DSAError):
+            dsa.dsa_launch_override(*bad)
+    base = dsa.dsa_workspace_size(dsa.ENTRY_MLA_DECODE, T=1, H=64, n_idx=2048)
+    fused = dsa.dsa_workspace_size(dsa.ENTRY_DECODE, T=1, n_max=131072, topk=2048, H=64)
+    try:
+        dsa.dsa_launch_override(0, 8)       # 8 splits instead of the table's: fewer partials
+        assert dsa.dsa_workspace_size(dsa.ENTRY_MLA_DECODE, T=1, H=64, n_idx=2048) < base
+        assert dsa.dsa_workspace_size(dsa.ENTRY_DECODE, T=1, n_max=131072, topk=2048, H=64) < fused
+        dsa.dsa_launch_override(4, 0)       # 64-head workgroups cannot serve 16 heads
+        assert mla() == B.DSA_ERR_UNSUPPORTED
+        dsa.dsa_launch_override(2, 0)       # 32-head workgroups: 48 heads are three 16-head tiles
+        assert mla(H=48, ld_q=48 * 576, ld_out=48 * 512) == B.DSA_ERR_UNSUPPORTED
+    finally:
+        dsa.dsa_launch_override(0, 0)
+    assert dsa.dsa_workspace_size(dsa.ENTRY_MLA_DECODE, T=1, H=64, n_idx=2048) == base
+
+
 def test_workspace_init_rejects():
     assert B._lib.dsa_workspace_init(None, 1 << 24, None) == B.DSA_ERR_ARG
     assert B._lib.dsa_workspace_init(FAKE, 16, None) == B.DSA_ERR_WORKSPACE

@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 from oracle.compare import attention_ok
-from dev import need_gpu, run_attention, say, upload, workload
+from dev import dsa, need_gpu, run_attention, say, upload, workload
 
 pytestmark = [pytest.mark.gpu, need_gpu]
 
@@ -129,4 +129,21 @@ def test_attention_dsv4_fp8_full_size():
     prob = workload("dsv4_fp8_decode")
     say("attention dsv4 full")
     out, lse = run_attention(prob, mode="decode")
+    _check_all(prob, out, lse)
+
+
+# forced launch plans (dsa_launch_override): every head-tile layout and split count the table
+# would not pick for this shape gives the same results
+@pytest.mark.parametrize("ht,split", [(1, 1), (1, 7), (2, 3), (4, 1), (4, 5), (0, 24)])
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_attention_forced_plans(ht, split, mode):
+    m = dsa()
+    prob = workload("attention_case", fmt="bf16", B=5, H=64, n_ctx=3000, n_idx=700, pad="shuffled",
+                    n_pad=40, sink=True)
+    say(f"attention forced plan ht={ht} split={split} {mode}")
+    try:
+        m.dsa_launch_override(ht, split)
+        out, lse = run_attention(prob, mode=mode)
+    finally:
+        m.dsa_launch_override(0, 0)
     _check_all(prob, out, lse)
