@@ -470,7 +470,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   __shared__ __align__(8) uint16_t s_pt[kW32 ? 2 : 1][32][PTS];   // P^T per half: [head][row], bf16
   __shared__ float s_mx[kW32 ? NW : 1][16];           // each wave's block max per score head
   __shared__ float s_lw[kW32 ? NW : 1][16];           // each wave's weight sum per score head (end)
-  __shared__ int s_grow[kW32 ? NW : 1];
+  __shared__ __align__(8) uint8_t s_grow8[8];         // each wave's grow flag, in one word
   u32x4_t qb[KQ];
   if constexpr (kW32) {
     const uint16_t* qp = &s_rows[0][0][0] + (32 * hh + 16 * hx + c) * RE + 8 * g;
@@ -612,12 +612,15 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       };
       weights();
       const bool grow = __any(mx > m_run + 8.f);
-      if (lane == 0) s_grow[wave] = grow ? 1 : 0;
+      if (lane == 0) s_grow8[wave] = grow ? 1 : 0;
       if (g == 0) s_mx[wave][c] = mx;
       lds_barrier();
-      bool any_grow = false;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) any_grow |= s_grow[w] != 0;
+      // every wave's flag in one read, issued with the first k-step's weights (read again
+      // below only if a rescale republishes them)
+      const uint64_t flags = *reinterpret_cast<const uint64_t*>(s_grow8);
+      u32x2_t pa0 = *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][4 * hl]);
+      u32x2_t pc0 = *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][8 + 4 * hl]);
+      const bool any_grow = flags != 0;
       if (any_grow) {                              // the same branch in every wave
         // a head's block max: the two row tiles of its head quarter
         const float bs = fmaxf(s_mx[wv(0, hx)][c], s_mx[wv(1, hx)][c]);
@@ -634,6 +637,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         m_o = mo_new;
         weights();
         lds_barrier();
+        pa0 = *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][4 * hl]);
+        pc0 = *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][8 + 4 * hl]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) l_run += p[i];   // this lane's rows of its score head
@@ -651,8 +656,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         const int tr_col = VC * vh + 16 * (tg & 1) + 4 * ta;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const u32x2_t pa = *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][16 * ks + 4 * hl]);
-          const u32x2_t pc = *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][16 * ks + 8 + 4 * hl]);
+          const u32x2_t pa = ks == 0 ? pa0 : *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][16 + 4 * hl]);
+          const u32x2_t pc = ks == 0 ? pc0 : *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][24 + 4 * hl]);
           const u32x4_t pb = u32x4_t{pa[0], pa[1], pc[0], pc[1]};
 #pragma unroll
           for (int e = 0; e < CPL; ++e) {
