@@ -315,27 +315,37 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       constexpr int RW = DQK / 8 + 1;
       constexpr int SLOTS = kNB * RW;
       constexpr int NINS = (SLOTS + 63) / 64;
-      constexpr int PER = (NINS + NW - 1) / NW;        // instructions of a wave (at most)
+      // 64 heads: only waves NW/2.. (one on every SIMD) issue, so that the other wave of each
+      // SIMD starts its score product while the CU's memory path drains the block
+      constexpr int GI = (HT == 4 && WD == 2) ? NW / 2 : NW;   // issuing waves
+      const int gw = (HT == 4 && WD == 2) ? wave - NW / 2 : wave;
+      constexpr int PER = (NINS + GI - 1) / GI;        // instructions of a wave (at most)
+      constexpr int BAT = PER > 6 ? (PER + 1) / 2 : PER;   // addresses read per batch
       auto* lbase = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(
           reinterpret_cast<uintptr_t>(&s_rows[buf][0][0]) & 0xffffffffu);
-      // every address read of the wave first (one LDS round trip), then the loads
-      const uint8_t* src[PER];
+      if (gw >= 0) {
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int j = min((wave + k * NW) * 64 + lane, SLOTS - 1);
-        const int r = j / RW;
-        int cc = j - r * RW;
-        cc = cc == RW - 1 ? 0 : cc;
-        src[k] = s_ra[buf][0][r] + 16 * cc;
-      }
+        for (int k0 = 0; k0 < PER; k0 += BAT) {
+          // a batch's address reads first (one LDS round trip), then its loads
+          const uint8_t* src[BAT];
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int ins = wave + k * NW;
-        if (ins < NINS && ins * 64 + lane < SLOTS) {
-          // the builtin takes a named local: given an array element (or an expression over the
-          // template-shaped address array) the host compilation silently drops the kernel
-          const uint8_t* sp = src[k];
-          __builtin_amdgcn_global_load_lds(sp, lbase + ins * 1024, 16, 0, 0);
+          for (int k = 0; k < BAT; ++k) {
+            const int j = min((gw + (k0 + k) * GI) * 64 + lane, SLOTS - 1);
+            const int r = j / RW;
+            int cc = j - r * RW;
+            cc = cc == RW - 1 ? 0 : cc;
+            src[k] = s_ra[buf][0][r] + 16 * cc;
+          }
+#pragma unroll
+          for (int k = 0; k < BAT; ++k) {
+            const int ins = gw + (k0 + k) * GI;
+            if (k0 + k < PER && ins < NINS && ins * 64 + lane < SLOTS) {
+              // the builtin takes a named local: given an array element (or an expression over
+              // the template-shaped address array) the host compilation silently drops the kernel
+              const uint8_t* sp = src[k];
+              __builtin_amdgcn_global_load_lds(sp, lbase + ins * 1024, 16, 0, 0);
+            }
+          }
         }
       }
     }
@@ -504,8 +514,11 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   constexpr int PB_MAX = kRaw ? (NID + NW - 1) / NW + (NIS + NW - 1) / NW : (NINS + NW - 1) / NW;
   static_assert((NBUF - 2) * PB_MAX < 64, "vmcnt range");
   const int w_u = __builtin_amdgcn_readfirstlane(wave);
+  // (bf16 rows under 64 heads: only waves NW / 2 .. NW - 1 issue, see gather)
+  constexpr int kIssuers = kW32 ? NW / 2 : NW;
+  const int w_is = kW32 ? w_u - NW / 2 : w_u;           // this wave's rank among the issuers
   const int per_block = kRaw ? (NID - w_u + NW - 1) / NW + (NIS - w_u + NW - 1) / NW
-                             : (NINS - w_u + NW - 1) / NW;
+                             : (w_is >= 0 ? (NINS - w_is + kIssuers - 1) / kIssuers : 0);
   for (int p0 = u_begin; p0 < u_end; p0 += kResolve) {
     const int p1 = min(u_end, p0 + kResolve);
     if (p0 != u_begin) {
