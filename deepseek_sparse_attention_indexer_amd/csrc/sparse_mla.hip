@@ -14,13 +14,13 @@
 // Workgroup = HT x WD waves sharing each gathered 32-row block: a wave owns 16 heads (one of
 // HT head tiles) and 512 / WD value columns (decode runs one head tile with WD = 4, so four
 // waves issue the gather and the PV product and the score product is split over the waves).
-// 64 heads (HT = 4, WD = 2: 8 waves) take 32x32x16 MFMAs instead: wave w owns 32 heads (half
-// w & 1) and 128 value columns (quarter w >> 1); the four waves of a head half split the score
-// product's contraction four ways and meet in LDS: each wave sums the four partials (in a
-// fixed order) for its own 8 rows only, runs their softmax and publishes their packed weights,
-// which every wave of the head half then reads as its P^T operand. Each block is read from
-// LDS half as often as with 16 heads per wave, and a wave needs about 200 registers, so two
-// waves share each SIMD.
+// 64 heads (HT = 4, WD = 2: 8 waves) take 32x32x16 MFMAs for the value product instead: wave w
+// owns 128 value columns (quarter w >> 1) of the 32 heads of half w & 1, and a 16-row x 16-head
+// tile of the score product over the whole contraction, whose softmax it runs and whose packed
+// weights it publishes; every wave of the head half then reads them as its P^T operand. About
+// 240 registers per wave, so two waves share each SIMD. Each wave issues its share of the next
+// block's row loads at its own point of the score product, so that the eight shares reach the
+// CU's memory path one after another.
 // Blocks stream through a ring of NBUF buffers in LDS: while a block is computed, the next
 // NBUF - 1 blocks' rows are in flight (direct global->LDS loads; bf16 rows land in place, fp8
 // rows land as raw bytes; fp8_ds_mla rows under one 16-head tile are converted straight into
@@ -162,6 +162,18 @@ __device__ __forceinline__ Finish finish_softmax(float m, float l, float sink, b
   }
   f.lse = lse_log2 ? lse2 : lse2 * kLn2;
   return f;
+}
+
+// One direct global->LDS load (16 bytes per lane; lane l lands at lds_addr + 16 l) that the
+// compiler does not see as one. Issued through the builtin, every later transposing LDS read
+// waits for all such loads in flight (the compiler cannot tell them apart from the rows it
+// reads). Here the kernel's own waits (vmcnt on the loads of the block it reads, then a
+// barrier) order them. The load has no register result; M0 carries the LDS address (one wait
+// state after it is written).
+__device__ __forceinline__ void lds_dma16(const uint8_t* gptr, uint32_t lds_addr) {
+  // (the address is the same in every lane; said so, or the compiler may hold it in a VGPR)
+  const uint32_t lds_s = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_s) : "m0");
 }
 
 template <int FMT, int DQK, int HT, int WD, bool SPLIT, int NBUF>
@@ -315,15 +327,13 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       constexpr int RW = DQK / 8 + 1;
       constexpr int SLOTS = kNB * RW;
       constexpr int NINS = (SLOTS + 63) / 64;
-      // 64 heads: only waves NW/2.. (one on every SIMD) issue, so that the other wave of each
-      // SIMD starts its score product while the CU's memory path drains the block
-      constexpr int GI = (HT == 4 && WD == 2) ? NW / 2 : NW;   // issuing waves
-      const int gw = (HT == 4 && WD == 2) ? wave - NW / 2 : wave;
+      constexpr int GI = NW;                           // issuing waves: all
+      const int gw = wave;
       constexpr int PER = (NINS + GI - 1) / GI;        // instructions of a wave (at most)
       constexpr int BAT = PER > 6 ? (PER + 1) / 2 : PER;   // addresses read per batch
       auto* lbase = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(
           reinterpret_cast<uintptr_t>(&s_rows[buf][0][0]) & 0xffffffffu);
-      if (gw >= 0) {
+      {
 #pragma unroll
         for (int k0 = 0; k0 < PER; k0 += BAT) {
           // a batch's address reads first (one LDS round trip), then its loads
@@ -349,6 +359,29 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         }
       }
     }
+  };
+
+  // 64 heads, bf16 rows: every wave issues its share of a block's loads at its own point of
+  // the score product (wave w after k-step 2 w), so that the waves find the CU's memory path
+  // free in turn instead of all queueing on it at once (a load that finds it busy holds its
+  // wave at issue): instruction k of this wave's share (its source, then its issue). Issued
+  // as lds_dma16, since the builtin's loads would have to land before the value product.
+  constexpr bool kStagger = FMT == kFmtBf16 && HT == 4 && WD == 2;
+  constexpr int kGRW = DQK / 8 + 1;                       // 16-byte slots per padded row
+  constexpr int kGSlots = kNB * kGRW;
+  constexpr int kGIns = (kGSlots + 63) / 64;               // instructions per block
+  constexpr int kGPer = (kGIns + NW - 1) / NW;             // of one wave (at most)
+  auto gsrc = [&](int buf, int k) -> const uint8_t* {
+    const int j = min((wave + k * NW) * 64 + lane, kGSlots - 1);
+    const int r = j / kGRW;
+    int cc = j - r * kGRW;
+    cc = cc == kGRW - 1 ? 0 : cc;
+    return s_ra[buf][0][r] + 16 * cc;
+  };
+  auto gissue = [&](int buf, int k, const uint8_t* sp) {
+    const int ins = wave + k * NW;
+    const uint32_t lds = (uint32_t)(reinterpret_cast<uintptr_t>(&s_rows[buf][0][0]) & 0xffffffffu) + ins * 1024;
+    if (ins < kGIns && ins * 64 + lane < kGSlots) lds_dma16(sp, lds);
   };
 
   // fp8 rows: the block's raw bytes go into raw buffer `buf` by direct global->LDS loads
@@ -514,11 +547,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   constexpr int PB_MAX = kRaw ? (NID + NW - 1) / NW + (NIS + NW - 1) / NW : (NINS + NW - 1) / NW;
   static_assert((NBUF - 2) * PB_MAX < 64, "vmcnt range");
   const int w_u = __builtin_amdgcn_readfirstlane(wave);
-  // (bf16 rows under 64 heads: only waves NW / 2 .. NW - 1 issue, see gather)
-  constexpr int kIssuers = kW32 ? NW / 2 : NW;
-  const int w_is = kW32 ? w_u - NW / 2 : w_u;           // this wave's rank among the issuers
   const int per_block = kRaw ? (NID - w_u + NW - 1) / NW + (NIS - w_u + NW - 1) / NW
-                             : (w_is >= 0 ? (NINS - w_is + kIssuers - 1) / kIssuers : 0);
+                             : (NINS - w_u + NW - 1) / NW;
   for (int p0 = u_begin; p0 < u_end; p0 += kResolve) {
     const int p1 = min(u_end, p0 + kResolve);
     if (p0 != u_begin) {
@@ -532,12 +562,22 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     // the addresses of the first NBUF blocks (one thread per row), then the first NBUF - 1
     // blocks' loads
     for (int t = threadIdx.x; t < NBUF * kNB && t < nb * kNB; t += NT) row_addrs(t / kNB, (t / kNB) * kNB, t % kNB);
+    // staggered loads: nothing of the list reads is left in flight (their values are in use),
+    // but the compiler cannot prove it across the block loop and would wait for them there
+    // with small counts that also cover the row loads it does not see
+    if constexpr (kStagger) wait_vmcnt<0>();
     lds_barrier();
 #pragma unroll
     for (int k = 0; k < NBUF - 1; ++k) {
       if (k < nb) {
-        if constexpr (kRaw) gather_raw(k);
-        else gather(k);
+        if constexpr (kRaw) {
+          gather_raw(k);
+        } else if constexpr (kStagger) {   // (no builtin LDS loads anywhere in this layout)
+#pragma unroll
+          for (int j = 0; j < kGPer; ++j) gissue(k, j, gsrc(k, j));
+        } else {
+          gather(k);
+        }
       }
     }
   for (int it = 0; it < nb; ++it) {
@@ -547,7 +587,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     const int later = min(NBUF - 2, nb - 1 - it);
     wait_vmcnt_dyn<0, (NBUF - 2) * PB_MAX>(later * per_block);
     lds_barrier();                       // ... for every wave; and the buffer refilled below is free
-    if (it + NBUF - 1 < nb) {
+    if (!kStagger && it + NBUF - 1 < nb) {
       if constexpr (kRaw) gather_raw((it + NBUF - 1) % NBUF);
       else gather((it + NBUF - 1) % NBUF);
     }
@@ -593,12 +633,24 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         u32x4_t av[DEPTH];
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) av[d] = *reinterpret_cast<const u32x4_t*>(rp + 32 * d);
+        const bool gnext = kStagger && it + NBUF - 1 < nb;
+        const int gbuf = (it + NBUF - 1) % NBUF;
+        static_assert(!kStagger || 2 * (NW - 1) < KQ, "every wave's turn inside the product");
 #pragma unroll
         for (int kb = 0; kb < KQ; ++kb) {
           sacc = mfma_bf16_16x16x32(av[kb % DEPTH], qb[kb], sacc);
           if (kb + DEPTH < KQ) av[kb % DEPTH] = *reinterpret_cast<const u32x4_t*>(rp + 32 * (kb + DEPTH));
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA,
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then the next read
+          if constexpr (kStagger) {
+            if (gnext && kb == 2 * w_u) {       // this wave's turn: its share of the next block
+              const uint8_t* gs[kGPer];
+#pragma unroll
+              for (int k = 0; k < kGPer; ++k) gs[k] = gsrc(gbuf, k);
+#pragma unroll
+              for (int k = 0; k < kGPer; ++k) gissue(gbuf, k, gs[k]);
+            }
+          }
         }
       }
       // accumulator i of lane l: row 16 rx + 4 g + i, head 16 hx + c of the half
