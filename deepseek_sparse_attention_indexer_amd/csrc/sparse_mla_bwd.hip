@@ -28,7 +28,8 @@
 // heads first divides them by H / 16. An atomic instruction covers 32 consecutive columns of
 // 2 rows; rows of padding entries are skipped. With 16 heads there is nothing to sum first, and
 // the first kernel adds dKV itself (same products, no workspace round trip).
-// One block in flight per workgroup.
+// Blocks stream through a ring of two: the next block's rows are requested before the
+// current block's products (one workgroup per CU: nothing else hides a block's gather).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   constexpr int CT = DQK / 32;                // 32-column tiles of dKV
   constexpr int CTW = FUSED ? (CT + NW - 1) / NW : 1;   // per wave, at most
   static_assert(KS % 2 == 0, "shapes");
-  __shared__ __align__(16) uint16_t s_rows[kBwdNB][RE];
+  __shared__ __align__(16) uint16_t s_rows[2][kBwdNB][RE];
   __shared__ __align__(16) int32_t s_slot[kBwdResolve];
   __shared__ const uint8_t* s_ra[kBwdNB];
   __shared__ f32x4_t s_ss[NW][64];
@@ -101,8 +102,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   // ---- prologue: q and dout of the 16 heads staged in the row buffer, the register operands
   // built from them; D = dout . out and the lse in base 2 per head
   static_assert(16 * RE + 16 * (kBwdDV + 8) <= kBwdNB * RE, "staging");
-  uint16_t* const s_q = &s_rows[0][0];                  // [16][RE]
-  uint16_t* const s_do = &s_rows[0][0] + 16 * RE;       // [16][kBwdDV + 8]
+  uint16_t* const s_q = &s_rows[0][0][0];               // [16][RE]
+  uint16_t* const s_do = &s_rows[0][0][0] + 16 * RE;    // [16][kBwdDV + 8]
   constexpr int DOS = kBwdDV + 8;
   // Heads past H (a head count that is not a whole number of 16-head groups) read q, dout and
   // out as zero and lse as 0: their P is finite and their dZ and P dout are zero, so they add
@@ -213,49 +214,60 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
       }
     }
     __syncthreads();
-    for (int it = 0; it < nb; ++it) {
-      const int jb = it * kBwdNB;
-      // row addresses (one lane per row; padding reads row 0), then the block's loads
+    // row addresses of block ib (one lane per row; padding reads row 0)
+    auto row_addrs = [&](int ib) {
       if (threadIdx.x < kBwdNB) {
-        const int j = jb + threadIdx.x;
+        const int j = ib * kBwdNB + threadIdx.x;
         const int32_t v = j < pass_n ? s_slot[j] : -1;
         s_ra[threadIdx.x] = kv.data + (int64_t)max(v, 0) * (DQK * 2);
       }
-      lds_barrier();
-      {
-        constexpr int RW = DQK / 8 + 1;
-        constexpr int SLOTS = kBwdNB * RW;
-        constexpr int NINS = (SLOTS + 63) / 64;
-        constexpr int PER = (NINS + NW - 1) / NW;
-        auto* lbase = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(
-            reinterpret_cast<uintptr_t>(&s_rows[0][0]) & 0xffffffffu);
-        const uint8_t* src[PER];
+    };
+    // that block's loads into ring buffer buf (addresses in s_ra)
+    auto gather = [&](int buf) {
+      constexpr int RW = DQK / 8 + 1;
+      constexpr int SLOTS = kBwdNB * RW;
+      constexpr int NINS = (SLOTS + 63) / 64;
+      constexpr int PER = (NINS + NW - 1) / NW;
+      auto* lbase = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(
+          reinterpret_cast<uintptr_t>(&s_rows[buf][0][0]) & 0xffffffffu);
+      const uint8_t* src[PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const int j = min((wave + k * NW) * 64 + lane, SLOTS - 1);
-          const int r = j / RW;
-          int cc = j - r * RW;
-          cc = cc == RW - 1 ? 0 : cc;
-          src[k] = s_ra[r] + 16 * cc;
-        }
+      for (int k = 0; k < PER; ++k) {
+        const int j = min((wave + k * NW) * 64 + lane, SLOTS - 1);
+        const int r = j / RW;
+        int cc = j - r * RW;
+        cc = cc == RW - 1 ? 0 : cc;
+        src[k] = s_ra[r] + 16 * cc;
+      }
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const int ins = wave + k * NW;
-          if (ins < NINS && ins * 64 + lane < SLOTS) {
-            const uint8_t* sp = src[k];
-            __builtin_amdgcn_global_load_lds(sp, lbase + ins * 1024, 16, 0, 0);
-          }
+      for (int k = 0; k < PER; ++k) {
+        const int ins = wave + k * NW;
+        if (ins < NINS && ins * 64 + lane < SLOTS) {
+          const uint8_t* sp = src[k];
+          __builtin_amdgcn_global_load_lds(sp, lbase + ins * 1024, 16, 0, 0);
         }
       }
+    };
+    row_addrs(0);
+    lds_barrier();
+    gather(0);
+    for (int it = 0; it < nb; ++it) {
+      const int jb = it * kBwdNB;
+      const int cur = it & 1;
+      // this block's rows are in (and every vector-memory operation of the previous block is
+      // done); the next block's addresses (every wave is done with the previous ones: the
+      // products below pass barriers), then its loads, which land while this block is used
       wait_vmcnt<0>();
+      if (it + 1 < nb) row_addrs(it + 1);
       lds_barrier();
+      if (it + 1 < nb) gather(cur ^ 1);           // that buffer held block it - 1
 
       // ---- S^T and dP^T, split over the waves
       const int jm = jb + 4 * g;
       const u32x4_t sl0 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm]);
       const u32x4_t sl1 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm + 16]);
       {
-        const uint16_t* rp = &s_rows[16 * (wave >> 1) + c][8 * g];
+        const uint16_t* rp = &s_rows[cur][16 * (wave >> 1) + c][8 * g];
         f32x4_t sp = f32x4_t{0.f, 0.f, 0.f, 0.f}, dp = sp;
 #pragma unroll
         for (int kb = 0; kb < KQ; ++kb)
@@ -299,8 +311,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
         u32x4_t vr[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[4 * g + j][128 * wave + 8 * c]);
-          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[16 + 4 * g + j][128 * wave + 8 * c]);
+          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * wave + 8 * c]);
+          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * wave + 8 * c]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -317,8 +329,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
         uint32_t vw[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          vw[j] = *reinterpret_cast<const uint32_t*>(&s_rows[4 * g + j][kBwdDV + 8 * (c & 7) + 2 * wave]);
-          vw[4 + j] = *reinterpret_cast<const uint32_t*>(&s_rows[16 + 4 * g + j][kBwdDV + 8 * (c & 7) + 2 * wave]);
+          vw[j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][4 * g + j][kBwdDV + 8 * (c & 7) + 2 * wave]);
+          vw[4 + j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][16 + 4 * g + j][kBwdDV + 8 * (c & 7) + 2 * wave]);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
