@@ -4,6 +4,7 @@ import pytest
 
 import oracle
 from oracle.compare import attention_ok
+from workloads.gen import to_bf16_bits
 from dev import dsa, need_gpu, run_attention, say, upload, workload
 
 pytestmark = [pytest.mark.gpu, need_gpu]
@@ -146,4 +147,33 @@ def test_attention_forced_plans(ht, split, mode):
         out, lse = run_attention(prob, mode=mode)
     finally:
         m.dsa_launch_override(0, 0)
+    _check_all(prob, out, lse)
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("H,B", [(16, 2), (64, 2), (64, 16)])
+def test_attention_late_score_jumps(mode, H, B):
+    """Listed rows whose scores jump far above the running maximum late in the list: by about
+    12, 45 and 150 in base-2 units (averaged over the heads) in blocks 20, 40 and 60 of the 64
+    (the lazy rescale of the online softmax, taken when a maximum grows by more than 2^8, and
+    the split merge across partials whose maxima differ by as much). A jumping row keeps its
+    value columns and gets a multiple of the request's mean query head in its RoPE columns, so
+    its score rises in every head while the outputs stay of the usual size. Random rows alone
+    never grow a maximum past the first block. In decode, 16 rows x 64 heads take the 8-wave
+    64-head workgroups with splits, 2 rows the 16-head ones."""
+    import dataclasses
+    prob = workload("attention_case", fmt="bf16", B=B, H=H, n_ctx=3000, n_idx=2048, pad="tail",
+                    n_pad=0, seed=11)
+    data = prob.kv.data.copy()
+    r0 = prob.d_v                                                        # first RoPE column
+    for b in range(prob.T):
+        q = oracle.bf16_to_f64(prob.q[b])[:, r0:]                        # [H, d_rope]
+        qm = q.mean(axis=0)
+        per_unit = float((q @ qm).mean()) * prob.softmax_scale / np.log(2.0)
+        for pos, jump in ((20 * 32 + 5, 12.0), (40 * 32 + 17, 45.0), (60 * 32 + 3, 150.0)):
+            slot = int(oracle.slots_of(prob.kv, b, np.array([prob.idx_main[b, pos]]))[0])
+            data[slot, r0:] = to_bf16_bits((jump / per_unit) * qm)
+    prob = dataclasses.replace(prob, kv=dataclasses.replace(prob.kv, data=data))
+    say("attention late score jumps", mode, H, B)
+    out, lse = run_attention(prob, mode=mode)
     _check_all(prob, out, lse)
