@@ -456,6 +456,9 @@ def main():
                     help="skip the measured copy / GEMM ceilings (e.g. under counter passes)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--attn-plan", default=None, metavar="HT,SPLITS",
+                    help="force the attention launch plan (head tiles per workgroup, splits per row; "
+                         "dsa_launch_override) instead of the library's table, for plan sweeps")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the single-GPU hot path only: the library runs the layer on one "
@@ -467,6 +470,11 @@ def main():
     from deepseek_sparse_attention_indexer_amd.upload import to_device
     import workloads
 
+    plan = None
+    if args.attn_plan:
+        ht, sp = (int(v) for v in args.attn_plan.split(","))
+        dsa.dsa_launch_override(head_tiles=ht, n_split=sp)
+        plan = f"{ht} head tiles x {sp} splits (forced)"
     prob = workloads.make_workload(args.workload)
     if prob.kpool is None:
         raise SystemExit("bench.py times the whole layer: pick a workload with an indexer")
@@ -568,7 +576,8 @@ def main():
         "config": {"workload": args.workload, "batch": T, "context": int(prob.row_len.max()),
                    "heads": H, "d_qk": prob.d_qk, "d_v": prob.d_v, "indexer": f"{prob.Hi}x{prob.di} {prob.kpool.dtype}",
                    "topk": prob.topk, "kv_cache": f"{prob.kv.fmt} paged {prob.kv.page_size} shuffled",
-                   "cache_state": "cold: 1 GiB read evicts L2 + MALL before each step"},
+                   "cache_state": "cold: 1 GiB read evicts L2 + MALL before each step",
+                   **({"attn_plan": plan} if plan else {})},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1) if achieved else None,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
