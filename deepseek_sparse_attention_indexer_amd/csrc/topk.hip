@@ -31,7 +31,7 @@ constexpr int kNT = 512;   // threads of the select workgroups
 
 // ------------------------------------------------------------------ rows that fit in LDS
 // CAP: key capacity. CAP = kTopkLdsMax takes 80 KiB + 48 B of LDS (one workgroup per CU);
-// rows of at most 8192 candidates (a causal prefill of 8K tokens) take CAP = 8192, 48 KiB,
+// rows of at most 8704 candidates (a causal prefill of 8K tokens) take CAP = 8704, 50 KiB,
 // three workgroups per CU.
 template <int CAP>
 __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
@@ -508,7 +508,9 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
 
 hipError_t launch_topk_lds(const TopkArgs& a, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  if (a.n_max <= 8192) launch_kernel(k_topk_lds<8192>, dim3(T), dim3(kNT), st, a);
+  // (8704 keeps the causal prefill of 8K tokens plus a few, e.g. the 8193 candidates of its last
+  // row, at three workgroups per CU)
+  if (a.n_max <= 8704) launch_kernel(k_topk_lds<8704>, dim3(T), dim3(kNT), st, a);
   else launch_kernel(k_topk_lds<kTopkLdsMax>, dim3(T), dim3(kNT), st, a);
   return hipGetLastError();
 }
