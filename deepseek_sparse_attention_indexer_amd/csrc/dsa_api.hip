@@ -448,7 +448,7 @@ dsa_status run_topk(const TopkIn& k, bool hist_ready, void* ws, size_t ws_bytes,
   a.ld_idx = k.ld_idx;
   a.lens = k.lens;
   if (r.n_max <= kTopkLdsMax) {
-    set_row("T=%d n_max=%d topk=%d: one workgroup per row, keys in LDS (capacity %d)", r.T, r.n_max, k.topk,
+    set_row("T=%d n_max=%d topk=%d: one workgroup per row, keys in registers (capacity %d)", r.T, r.n_max, k.topk,
             r.n_max <= 8704 ? 8704 : kTopkLdsMax);
     return hip_status(timed("topk_lds", st, [&] { return launch_topk_lds(a, r.T, st); }));
   }

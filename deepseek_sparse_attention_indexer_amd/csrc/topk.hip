@@ -12,7 +12,7 @@
 // complemented position. Output slots come from prefix sums of the selection counts, never
 // from racing atomics, so the list's order is the same on every run.
 //
-//  * k_topk_lds: one 512-thread workgroup per row, the row's keys held in LDS (<= 16K); the
+//  * k_topk_lds: one 512-thread workgroup per row, the row's keys held in registers (<= 16K); the
 //    list is in position order.
 //  * long rows: the first-digit histogram is built per chunk (k_topk_hist, or fused into
 //    the score kernel). k_topk_filter's workgroups (one per chunk) find the threshold bin and
@@ -30,12 +30,14 @@ namespace dsa {
 constexpr int kNT = 512;   // threads of the select workgroups
 
 // ------------------------------------------------------------------ rows that fit in LDS
-// CAP: key capacity. CAP = kTopkLdsMax takes 80 KiB + 48 B of LDS (one workgroup per CU);
-// rows of at most 8704 candidates (a causal prefill of 8K tokens) take CAP = 8704, 50 KiB,
-// three workgroups per CU.
+// CAP: key capacity (a multiple of the 512 threads). Key i of the row is held in register
+// i / 512 of thread i % 512, so every pass over the keys (three radix digits, the ties, the
+// compaction in position order) reads registers, and LDS holds only the 16 KiB histogram:
+// up to four workgroups per CU. CAP = 8704 covers a causal prefill of 8K tokens plus a few.
 template <int CAP>
 __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
-  __shared__ uint32_t s_key[CAP];
+  static_assert(CAP % kNT == 0, "whole registers");
+  constexpr int PER = CAP / kNT;
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_w[kNT / 64];
   __shared__ uint32_t s_res[4];
@@ -51,18 +53,25 @@ __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
     return;
   }
   const float* row = a.logits + (int64_t)t * a.ld_logits;
-  for (int i = threadIdx.x; i < n; i += kNT) s_key[i] = float_key(row[i]);
-  lds_barrier();
+  // every load of the thread in flight at once, from clamped positions (a loop of load, wait,
+  // store would pay one memory round trip per 512 keys); positions past n are never taken
+  uint32_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) key[j] = float_key(row[min((int)threadIdx.x + j * kNT, n - 1)]);
+  auto valid = [&](int j) { return (int)threadIdx.x + j * kNT < n; };
 
   uint32_t need = (uint32_t)k, eq = 0;
-  auto get_key = [&](int i, uint32_t& key) { key = s_key[i]; return true; };
-  const uint32_t thr = radix_select_desc<kNT>(n, get_key, 0u, 0u, 32, need, &eq, s_hist, s_w, s_res);
+  auto get_key = [&](int j, uint32_t& kk) { kk = key[j]; return valid(j); };
+  const uint32_t thr = radix_select_regs<kNT, PER>(get_key, 0u, 0u, 32, need, &eq, s_hist, s_w, s_res);
   // ties at thr: keep the `need` smallest positions (largest complemented positions)
   uint32_t pos_thr = 0u;
   if (eq > need) {
     uint32_t need2 = need, eq2 = 0;
-    auto get_tie = [&](int i, uint32_t& key) { key = ~(uint32_t)i; return s_key[i] == thr; };
-    pos_thr = radix_select_desc<kNT>(n, get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
+    auto get_tie = [&](int j, uint32_t& kk) {
+      kk = ~(uint32_t)((int)threadIdx.x + j * kNT);
+      return valid(j) && key[j] == thr;
+    };
+    pos_thr = radix_select_regs<kNT, PER>(get_tie, 0u, 0u, 32, need2, &eq2, s_hist, s_w, s_res);
   }
   const bool all_ties = eq <= need;
   // Compaction in position order, so the list (and everything computed from it in list order)
@@ -70,34 +79,36 @@ __global__ __launch_bounds__(kNT) void k_topk_lds(TopkArgs a) {
   // those counts (pass-major), then each lane writes at its pair's offset plus the selected
   // lanes below it. The histogram is free for the counts.
   constexpr int NW = kNT / 64;
-  static_assert((CAP / kNT) * NW <= kNT && (CAP / kNT) * NW <= kHistBins, "pair counts");
+  static_assert(PER * NW <= kNT && PER * NW <= kHistBins, "pair counts");
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int n_pass = (n + kNT - 1) / kNT;
-  auto selected = [&](int i) {
-    const uint32_t key = i < n ? s_key[i] : 0u;
-    return i < n && (key > thr || (key == thr && (all_ties || ~(uint32_t)i >= pos_thr)));
+  auto selected = [&](int j) {
+    const uint32_t kk = key[j];
+    const uint32_t i = (uint32_t)((int)threadIdx.x + j * kNT);
+    return valid(j) && (kk > thr || (kk == thr && (all_ties || ~i >= pos_thr)));
   };
-  for (int ps = 0; ps < n_pass; ++ps) {
-    const uint64_t m = __ballot(selected(ps * kNT + (int)threadIdx.x));
-    if (lane == 0) s_hist[ps * NW + wv] = (uint32_t)__popcll(m);
+  bool sel[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    sel[j] = selected(j);
+    const uint64_t m = __ballot(sel[j]);
+    if (lane == 0) s_hist[j * NW + wv] = (uint32_t)__popcll(m);
   }
   lds_barrier();
   {
     const int j = threadIdx.x;
-    const uint32_t c = j < n_pass * NW ? s_hist[j] : 0u;
+    const uint32_t c = j < PER * NW ? s_hist[j] : 0u;
     const uint32_t incl = block_incl_scan<kNT>(c, s_w, nullptr);
     lds_barrier();                             // every count read before the offsets replace them
-    if (j < n_pass * NW) s_hist[j] = incl - c;
+    if (j < PER * NW) s_hist[j] = incl - c;
   }
   lds_barrier();
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int ps = 0; ps < n_pass; ++ps) {
-    const int i = ps * kNT + threadIdx.x;
-    const bool sel = selected(i);
-    const uint64_t m = __ballot(sel);
-    const uint32_t o = s_hist[ps * NW + wv] + (uint32_t)__popcll(m & below);
-    if (sel && o < (uint32_t)k) out[o] = i;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint64_t m = __ballot(sel[j]);
+    const uint32_t o = s_hist[j * NW + wv] + (uint32_t)__popcll(m & below);
+    if (sel[j] && o < (uint32_t)k) out[o] = (int)threadIdx.x + j * kNT;
   }
   if (threadIdx.x == 0) a.lens[t] = k;
 }
@@ -511,7 +522,7 @@ hipError_t launch_topk_lds(const TopkArgs& a, int T, hipStream_t st) {
   // (8704 keeps the causal prefill of 8K tokens plus a few, e.g. the 8193 candidates of its last
   // row, at three workgroups per CU)
   if (a.n_max <= 8704) launch_kernel(k_topk_lds<8704>, dim3(T), dim3(kNT), st, a);
-  else launch_kernel(k_topk_lds<kTopkLdsMax>, dim3(T), dim3(kNT), st, a);
+  else launch_kernel(k_topk_lds<kTopkLdsMax>, dim3(T), dim3(kNT), st, a);   // 32 keys a thread
   return hipGetLastError();
 }
 

@@ -333,6 +333,6 @@ def test_dsa_log_prints_the_launch_rows(log):
     kernels = [ln.split()[1] for ln in lines]
     assert kernels == ["index_scores", "topk_lds", "sparse_mla", "mla_combine"], lines
     assert "T=1 n_max=512 Hi=4 di=64" in lines[0], lines[0]
-    assert "topk=128" in lines[1] and "in LDS" in lines[1], lines[1]
+    assert "topk=128" in lines[1] and "in registers" in lines[1], lines[1]
     assert "H=16 (padded 16) list 128+0" in lines[2] and "decode" in lines[2], lines[2]
     assert "split(s)" in lines[3], lines[3]
