@@ -110,14 +110,35 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   // nothing to dKV, and nothing of them is written.
   const int hval = a.H - head0;                         // valid heads of this group (>= 1)
   {
+    // q and dout of the group: every 16-byte load of the thread requested at once (clamped
+    // to valid heads), then stored (a loop of load, wait, store pays a round trip each)
     const uint16_t* qg = a.q + (int64_t)t * a.ld_q + (int64_t)head0 * DQK;
-    for (int o = threadIdx.x * 8; o < 16 * DQK; o += NT * 8)
-      *reinterpret_cast<u32x4_t*>(s_q + (o / DQK) * RE + o % DQK) =
-          o / DQK < hval ? *reinterpret_cast<const u32x4_t*>(qg + o) : u32x4_t{0u, 0u, 0u, 0u};
     const uint16_t* dg = a.dout + (int64_t)t * a.ld_dout + (int64_t)head0 * kBwdDV;
-    for (int o = threadIdx.x * 8; o < 16 * kBwdDV; o += NT * 8)
-      *reinterpret_cast<u32x4_t*>(s_do + (o / kBwdDV) * DOS + o % kBwdDV) =
-          o / kBwdDV < hval ? *reinterpret_cast<const u32x4_t*>(dg + o) : u32x4_t{0u, 0u, 0u, 0u};
+    constexpr int NQ = (16 * DQK / 8 + NT - 1) / NT;
+    constexpr int ND = 16 * kBwdDV / 8 / NT;
+    static_assert(16 * kBwdDV % (8 * NT) == 0, "whole dout loads");
+    u32x4_t vq[NQ], vd[ND];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int o = min(((int)threadIdx.x + j * NT) * 8, 16 * DQK - 8);
+      vq[j] = *reinterpret_cast<const u32x4_t*>(qg + min(o / DQK, hval - 1) * DQK + o % DQK);
+    }
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      const int o = ((int)threadIdx.x + j * NT) * 8;
+      vd[j] = *reinterpret_cast<const u32x4_t*>(dg + min(o / kBwdDV, hval - 1) * kBwdDV + o % kBwdDV);
+    }
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int o = ((int)threadIdx.x + j * NT) * 8;
+      if (o < 16 * DQK)
+        *reinterpret_cast<u32x4_t*>(s_q + (o / DQK) * RE + o % DQK) = o / DQK < hval ? vq[j] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      const int o = ((int)threadIdx.x + j * NT) * 8;
+      *reinterpret_cast<u32x4_t*>(s_do + (o / kBwdDV) * DOS + o % kBwdDV) = o / kBwdDV < hval ? vd[j] : u32x4_t{0u, 0u, 0u, 0u};
+    }
     // D: 16 threads per head, 32 columns each
     const int h = threadIdx.x >> 4;
     const int c0 = (threadIdx.x & 15) * 32;

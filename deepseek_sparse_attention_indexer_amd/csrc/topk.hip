@@ -121,12 +121,19 @@ __global__ __launch_bounds__(kNT) void k_topk_hist(TopkArgs a) {
   n = min(max(n, 0), a.n_max);
   const int s0 = blockIdx.x * kTopkChunk;
   if (s0 >= n) return;
-  for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
-  lds_barrier();
+  // the chunk's scores requested before the histogram is cleared, all at once (clamped
+  // positions; those past the row's end are not counted)
   const float* row = a.logits + (int64_t)t * a.ld_logits;
   const int s1 = min(n, s0 + kTopkChunk);
-  for (int s = s0 + threadIdx.x; s < s1; s += kNT)
-    atomicAdd(&s_hist[float_key(row[s]) >> (32 - kHistBits)], 1u);
+  constexpr int per = kTopkChunk / kNT;
+  float v[per];
+#pragma unroll
+  for (int j = 0; j < per; ++j) v[j] = row[min(s0 + j * kNT + (int)threadIdx.x, s1 - 1)];
+  for (int i = threadIdx.x; i < kHistBins; i += kNT) s_hist[i] = 0;
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < per; ++j)
+    if (s0 + j * kNT + (int)threadIdx.x < s1) atomicAdd(&s_hist[float_key(v[j]) >> (32 - kHistBits)], 1u);
   lds_barrier();
   uint32_t* gh = a.hist + ((int64_t)t * kHistSlices + (blockIdx.x % kHistSlices)) * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += kNT) {
