@@ -161,11 +161,16 @@ __global__ __launch_bounds__(kNT) void k_topk_filter(TopkArgs a) {
   uint32_t keys[per];
   const float* row = a.logits + (int64_t)t * a.ld_logits;
   {
+    // unconditional loads from clamped positions, all in flight together (a load under a
+    // branch gets its wait inside the branch: one round trip per load)
     const int s1_max = min(a.n_max, s0 + kTopkChunk);
+    float v[per];
+#pragma unroll
+    for (int j = 0; j < per; ++j) v[j] = row[min(s0 + j * kNT + (int)threadIdx.x, s1_max - 1)];
 #pragma unroll
     for (int j = 0; j < per; ++j) {
       const int s = s0 + j * kNT + threadIdx.x;
-      keys[j] = s < s1_max ? float_key(row[s]) : 0u;
+      keys[j] = s < s1_max ? float_key(v[j]) : 0u;
     }
   }
   int n = a.row_len[t];
@@ -287,11 +292,15 @@ __global__ __launch_bounds__(kNT) void k_topk_finalize(TopkArgs a) {
     uint32_t keys[per];
     const float* row = a.logits + (int64_t)t * a.ld_logits;
     {
+      // (unconditional loads from clamped positions, all in flight together, as in the filter)
       const int s1_max = min(a.n_max, s0 + kTopkChunk);
+      float v[per];
+#pragma unroll
+      for (int j = 0; j < per; ++j) v[j] = row[min(s0 + j * kNT + (int)threadIdx.x, s1_max - 1)];
 #pragma unroll
       for (int j = 0; j < per; ++j) {
         const int s = s0 + j * kNT + threadIdx.x;
-        keys[j] = s < s1_max ? float_key(row[s]) : 0u;
+        keys[j] = s < s1_max ? float_key(v[j]) : 0u;
       }
     }
     const uint32_t d1 = a.thr1[2 * t];
