@@ -324,9 +324,11 @@ def prefill_chain(dsa, to_device, workloads, torch, dev, reps=3, keep=None):
 
 
 def attention_backward(dsa, workloads, torch, dev, reps=5):
-    """The attention backward (dq, dKV by fp32 atomics, one list) on 64 rows x 64 heads x 2048
-    listed rows (of 4096-token contexts, bf16 576 rows), after its forward: time, atomics and
-    MFMA-equivalent rate. Its cost depends on the listed rows, not on the context length."""
+    """The attention backward (dq and dKV, one list) on 64 rows x 64 heads x 2048 listed rows
+    (of 4096-token contexts, bf16 576 rows), after its forward: time, dKV bytes and
+    MFMA-equivalent rate. Each row is its own request, so every listed cache row is named once
+    and the owner map sends every dKV add to a plain load and store of whole rows. Its cost
+    depends on the listed rows, not on the context length."""
     import numpy as np
     from deepseek_sparse_attention_indexer_amd.upload import to_device
     prob = workloads.attention_case(fmt="bf16", B=64, H=64, n_ctx=4096, n_idx=2048, pad="tail", n_pad=0)
@@ -341,7 +343,8 @@ def attention_backward(dsa, workloads, torch, dev, reps=5):
     dsa.dsa_sparse_mla_prefill(d.q, d.kv, d.idx_main, None, None, d.rows, H, prob.d_qk, prob.d_v,
                                prob.softmax_scale, out, lse)
 
-    ws = dsa.Workspace(dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=T, H=H, n_idx=int(d.idx_main.shape[1])), dev)
+    ws = dsa.Workspace(dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=T, H=H, n_idx=int(d.idx_main.shape[1]),
+                                              n_slots=int(d.kv.c.n_slots)), dev)
 
     def run():
         dsa.dsa_sparse_mla_backward(d.q, d.kv, d.idx_main, d.rows, H, prob.d_qk, prob.d_v,
@@ -360,12 +363,16 @@ def attention_backward(dsa, workloads, torch, dev, reps=5):
     us = sum(kernels.values())
     pairs = int((np.asarray(prob.idx_main) >= 0).sum())
     flops = pairs * H * 2 * (2 * prob.d_qk + prob.d_v + prob.d_qk + prob.d_v)
-    atomics = pairs * prob.d_qk                  # one per (entry, column): heads summed first
+    # dKV: one add per (listed entry, column), heads summed first; a row named once is read
+    # and written whole (4 + 4 bytes per column)
+    dkv_bytes = pairs * prob.d_qk * 8
+    dkv_us = kernels.get("sparse_mla_bwd_dkv")
     return {"workload": "attention backward, 64 rows x 64 heads x 2048 of 4096 rows (bf16 576)",
             "kernels_us": kernels, "avg_us": round(us, 1), "gflop": round(flops / 1e9, 2),
             "achieved_tflops": round(flops / (us * 1e-6) / 1e12, 1),
-            "fp32_atomics": atomics, "atomics_per_s": round(atomics / (us * 1e-6) / 1e9, 1),
-            "bound": "fp32 atomics of dKV (one per listed entry and column)",
+            "dkv_adds": pairs * prob.d_qk, "dkv_bytes": dkv_bytes,
+            "dkv_gbps": round(dkv_bytes / (dkv_us * 1e-6) / 1e9, 1) if dkv_us else None,
+            "bound": "dKV: the read and write of every listed cache row (HBM); dq/P/dZ: the row gathers",
             "timing": "HIP events from each dispatch, inputs resident"}
 
 

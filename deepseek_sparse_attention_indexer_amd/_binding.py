@@ -57,7 +57,7 @@ class _AttnOpts(C.Structure):
 
 class _Problem(C.Structure):
     _fields_ = [("T", C.c_int32), ("n_max", C.c_int32), ("topk", C.c_int32), ("H", C.c_int32),
-                ("n_idx", C.c_int32), ("_pad0", C.c_int32)]
+                ("n_idx", C.c_int32), ("n_slots", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -245,8 +245,8 @@ def _opts(sink, lse_log2: bool):
 
 
 def dsa_workspace_size(entry: int, T: int = 0, n_max: int = 0, topk: int = 0, H: int = 0,
-                       n_idx: int = 0) -> int:
-    p = _Problem(int(T), int(n_max), int(topk), int(H), int(n_idx), 0)
+                       n_idx: int = 0, n_slots: int = 0) -> int:
+    p = _Problem(int(T), int(n_max), int(topk), int(H), int(n_idx), int(n_slots))
     n = int(_lib.dsa_workspace_size(int(entry), C.byref(p)))
     if n == (1 << 64) - 1:
         raise DSAError(DSA_ERR_ARG, "dsa_workspace_size")

@@ -213,6 +213,9 @@ int64_t mla_bwd_ws_bytes(int T, int H, int n_idx) {
   return align256(e * heads_padded_bwd(H) * 2) * 2 + align256(e * 4);
 }
 
+// the backward's owner map: one int32 per cache slot, in whole 16-byte words
+int64_t mla_bwd_owner_bytes(int64_t n_slots) { return align256((n_slots + 3) / 4 * 16); }
+
 int64_t mla_ws_bytes(int T, int H, int ntot, bool decode) {
   const MlaPlan p = plan_mla(T, H, ntot, decode);
   if (p.n_split <= 1) return 0;
@@ -824,7 +827,9 @@ size_t dsa_workspace_size(int32_t entry, const dsa_problem* p) {
       return 0;
     case DSA_ENTRY_MLA_BACKWARD:
       if (p->H > 128) return SIZE_MAX;
-      return (size_t)(kHeaderBytes + mla_bwd_ws_bytes(p->T, p->H, p->n_idx));
+      if (p->n_slots < 0) return SIZE_MAX;
+      return (size_t)(kHeaderBytes + mla_bwd_ws_bytes(p->T, p->H, p->n_idx) +
+                      (p->n_slots > 0 ? mla_bwd_owner_bytes(p->n_slots) : 0));
     case DSA_ENTRY_DECODE: {
       const int64_t ld = logits_ld(p->n_max);
       int64_t b = kHeaderBytes;
@@ -959,11 +964,19 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
     a.ws_dz = reinterpret_cast<uint16_t*>(w + cv.take(e * a.Hp * 2));
     a.ws_p = reinterpret_cast<uint16_t*>(w + cv.take(e * a.Hp * 2));
     a.ws_slot = reinterpret_cast<int32_t*>(w + cv.take(e * 4));
+    // the owner map when the workspace has room for one over this cache's slots
+    const int64_t ob = mla_bwd_owner_bytes(kv->n_slots);
+    if ((a.Hp == 32 || a.Hp == 64) && n_idx > 0 && kv->n_slots <= INT32_MAX && (int64_t)ws_bytes >= need + ob) {
+      a.ws_owner = reinterpret_cast<int32_t*>(w + cv.take(ob));
+      a.n_slots = kv->n_slots;
+    }
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  set_row("T=%d H=%d (padded %d) list %d d_qk=%d: one workgroup per (row, 16 heads), dKV over all heads", T,
-          H, (int)a.Hp, n_idx, d_qk);
+  set_row("T=%d H=%d (padded %d) list %d d_qk=%d: one workgroup per (row, 16 heads), dKV over all heads%s", T,
+          H, (int)a.Hp, n_idx, d_qk, a.ws_owner ? ", owner map (plain adds for singly named slots)" : "");
   dsa_status s = hip_status(timed("sparse_mla_bwd", hs, [&] { return launch_sparse_mla_bwd(a, d_qk, T, hs); }));
+  if (s == DSA_OK && a.ws_owner)
+    s = hip_status(timed("sparse_mla_bwd_owner", hs, [&] { return launch_sparse_mla_bwd_owner(a, T, hs); }));
   if (s == DSA_OK)
     s = hip_status(timed("sparse_mla_bwd_dkv", hs, [&] { return launch_sparse_mla_bwd_dkv(a, d_qk, T, hs); }));
   return s;

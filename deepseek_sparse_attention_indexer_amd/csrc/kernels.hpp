@@ -154,9 +154,12 @@ struct MlaBwdArgs {
   uint16_t* ws_dz;         // workspace: bf16 [T, n_idx, Hp] softmax_scale * dZ
   uint16_t* ws_p;          // workspace: bf16 [T, n_idx, Hp] P
   int32_t* ws_slot;        // workspace: [T, n_idx] slots (-1: padding)
+  int32_t* ws_owner;       // workspace: [n_slots] who lists each slot (nullptr: atomics only)
+  int64_t n_slots;         // the cache's slot count (with ws_owner)
 };
 
 hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st);
+hipError_t launch_sparse_mla_bwd_owner(const MlaBwdArgs& a, int T, hipStream_t st);
 hipError_t launch_sparse_mla_bwd_dkv(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st);
 
 // cache writes: bf16 rows -> a cache format, one row per token at slots[token]

@@ -28,8 +28,18 @@
 // heads first divides them by H / 16. An atomic instruction covers 32 consecutive columns of
 // 2 rows; rows of padding entries are skipped. With 16 heads there is nothing to sum first, and
 // the first kernel adds dKV itself (same products, no workspace round trip).
+// A cache row that exactly one list entry names (over all rows of the call) needs no atomic:
+// with an owner map (one word per slot, cleared by the first kernel, marked by
+// k_sparse_mla_bwd_owner: the first entry's row + 1, bit 31 once a second entry names it),
+// k_sparse_mla_bwd_dkv_rows (32 or 64 padded heads) adds into such rows with plain loads and
+// stores of whole cache rows, and keeps atomics for rows that several entries name. fp32
+// atomics run at about one per L2 channel and clock; decode-shaped lists (each row its own
+// request) name every row once. Without the map (or with 128 padded heads) every add is
+// atomic (k_sparse_mla_bwd_dkv).
 // Blocks stream through a ring of two: the next block's rows are requested before the
 // current block's products (one workgroup per CU: nothing else hides a block's gather).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -417,6 +427,15 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
     __syncthreads();   // every wave is done with this pass's slots
   }
 
+  if (!FUSED && a.ws_owner) {   // the owner map to zero, in 16-byte words spread over the grid
+    // (at the end, where the stores hold up nothing; the marking kernel runs after this one)
+    const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
+    const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t n16 = (a.n_slots + 3) / 4;
+    for (int64_t i = wg * NT + threadIdx.x; i < n16; i += nwg * NT)
+      reinterpret_cast<u32x4_t*>(a.ws_owner)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+
   // ---- dq: lane (c = head, g) holds columns 128 wave + 8 (4g + r) + e (and the RoPE phases)
   if (c >= hval) return;                                // a padding head: no dq
   float* dqh = a.dq + (int64_t)t * a.ld_dq + (int64_t)(head0 + c) * DQK;
@@ -517,14 +536,215 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd_dkv(MlaBwdArgs a, int
   }
 }
 
+// The owner map of the call's list entries: slot -> first naming row + 1, bit 31 when a second
+// entry (of any row, or the same row again) names it. The map was zeroed by k_sparse_mla_bwd.
+__global__ __launch_bounds__(256) void k_sparse_mla_bwd_owner(const int32_t* slots, int ntot, int32_t* owner) {
+  const int t = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= ntot) return;
+  const int32_t s = slots[(int64_t)t * ntot + i];
+  if (s < 0) return;
+  const int32_t old = atomicCAS(owner + s, 0, t + 1);
+  if (old != 0) atomicOr(owner + s, (int32_t)0x80000000);
+}
+
+// dKV by whole cache rows (32 or 64 padded heads): a workgroup of 8 waves takes one query row
+// and a run of its 32-entry blocks. Per block the scale dZ and P rows are staged in LDS once,
+// each wave forms its column tiles (w, w + 8, w + 16) of the 32 x d_qk sums, the sums meet
+// in LDS, and every thread then adds whole 16-byte pieces of the cache rows: each row's d_qk
+// floats are read and written by one workgroup at once (the per-column-group kernel writes
+// each row in 128-byte pieces from 9 workgroups, which keeps the HBM writes scattered).
+// Rows named by this entry alone (owner map) take a plain load and store, rows named more
+// than once atomics, padding nothing. The current values are requested before the products.
+constexpr int kDkvBpwMax = 16;   // blocks per workgroup, at most
+
+template <int DQK, int HK>
+__global__ __launch_bounds__(512, 1) void k_sparse_mla_bwd_dkv_rows(MlaBwdArgs a, int bpw) {
+  constexpr int NWV = 8;
+  constexpr int CT = DQK / 32;                 // column tiles: 18 or 16
+  constexpr int TPW = (CT + NWV - 1) / NWV;    // per wave, at most
+  constexpr int HP = HK * 8;                   // padded heads of the workspace rows
+  constexpr int ZS = HP + 4;                   // LDS row of dZ / P (bf16), 8-byte aligned
+  constexpr int OS = DQK + 4;                  // LDS row of the sums (floats)
+  constexpr int F4 = DQK / 4;                  // 16-byte pieces per cache row
+  constexpr int NF = 32 * F4 / 512;            // pieces per thread and block
+  static_assert(32 * F4 % 512 == 0, "whole pieces per thread");
+  static_assert(HP % 8 == 0 && 32 * HP / 8 <= 256, "staging: one 16-byte piece per thread");
+  __shared__ __align__(16) float s_out[32][OS];
+  __shared__ __align__(16) uint16_t s_zp[2][32][ZS];
+  __shared__ int32_t s_rs[kDkvBpwMax * 32];
+  __shared__ uint32_t s_shared;                // bit b: block b0 + b has a row named more than once
+  if (threadIdx.x == 0) s_shared = 0u;
+  __syncthreads();
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int ntot = a.n_idx;
+  const int nbt = (ntot + 31) / 32;
+  const int b0 = blockIdx.x * bpw;
+  const int b1 = min(b0 + bpw, nbt);
+  if (b0 >= b1) return;
+  const int64_t rowe = (int64_t)t * ntot;      // this row's first workspace entry
+
+  // the entries' slots and owner words, decoded into s_rs: >= 0 named by this entry alone,
+  // -1 padding, <= -2 slot -(v + 2) named more than once
+  static_assert(kDkvBpwMax * 32 % 512 == 0, "whole entries per thread");
+  {
+    constexpr int EPT = kDkvBpwMax * 32 / 512;
+    int32_t v[EPT], o[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) v[i] = a.ws_slot[rowe + min(b0 * 32 + (int)threadIdx.x + 512 * i, ntot - 1)];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) o[i] = a.ws_owner ? a.ws_owner[max(v[i], 0)] : -1;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int j = threadIdx.x + 512 * i;
+      const int32_t d = b0 * 32 + j >= ntot || v[i] < 0 ? -1 : o[i] > 0 ? v[i] : -(v[i] + 2);
+      if (j < (b1 - b0) * 32) {
+        s_rs[j] = d;
+        if (d <= -2) atomicOr(&s_shared, 1u << (j >> 5));   // the block has a row named twice
+      }
+    }
+  }
+  // B operands of this wave's column tiles (k = heads in steps of 8, n = 32 columns): q, then
+  // dout, of the row staged in the sums' LDS (whole 16-byte loads, padding heads zero) and
+  // gathered from there once
+  u32x2_t qkb[TPW][HK], dkb[TPW][HK];
+  {
+    uint16_t* const stg = reinterpret_cast<uint16_t*>(&s_out[0][0]);
+    static_assert(HP * DQK * 2 <= 32 * OS * 4, "staging fits");
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int W = m == 0 ? DQK : kBwdDV;               // row width (bf16)
+      const int RS = W;                                  // LDS row (bf16)
+      const uint16_t* src = m == 0 ? a.q + (int64_t)t * a.ld_q : a.dout + (int64_t)t * a.ld_dout;
+      const int n16 = HP * W / 8;                        // 16-byte pieces
+      constexpr int MAXP = (HP * DQK / 8 + 511) / 512;
+      u32x4_t v[MAXP];
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int pc = min((int)threadIdx.x + 512 * i, n16 - 1);
+        const int head = pc / (W / 8);
+        v[i] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)min(head, a.H - 1) * W + 8 * (pc % (W / 8)));
+      }
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int pc = threadIdx.x + 512 * i;
+        const int head = pc / (W / 8);
+        if (pc < n16)
+          *reinterpret_cast<u32x4_t*>(stg + head * RS + 8 * (pc % (W / 8))) = head < a.H ? v[i] : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        const int col = min(wave + NWV * k, CT - 1) * 32 + l32;
+#pragma unroll
+        for (int ks = 0; ks < HK; ++ks) {
+          uint32_t h4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) h4[j] = col < W ? stg[(8 * ks + 4 * hh + j) * RS + col] : 0u;
+          const u32x2_t b = u32x2_t{h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
+          if (m == 0) qkb[k][ks] = b;
+          else dkb[k][ks] = b;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  for (int blk = b0; blk < b1; ++blk) {
+    const int jb = (blk - b0) * 32;
+    // the current values of this thread's pieces of the block's rows (exclusively named rows;
+    // other pieces read row 0 and drop it), and the block's dZ / P rows
+    int32_t rsk[NF];
+#pragma unroll
+    for (int k = 0; k < NF; ++k) rsk[k] = s_rs[jb + ((int)threadIdx.x + 512 * k) / F4];
+    f32x4_t cur[NF];
+#pragma unroll
+    for (int k = 0; k < NF; ++k)
+      cur[k] = *reinterpret_cast<const f32x4_t*>(a.dkv + (int64_t)max(rsk[k], 0) * DQK + 4 * (((int)threadIdx.x + 512 * k) % F4));
+    u32x4_t zp;
+    const int zj = threadIdx.x & 255;                   // piece (row, 8 heads) of array zarr
+    const int zarr = threadIdx.x >> 8;
+    const int zrow = zj / (HP / 8);
+    const int zpc = zj % (HP / 8);
+    const bool zok = zj < 32 * HP / 8;
+    {
+      const int e = min(blk * 32 + zrow, ntot - 1);
+      const uint16_t* src = (zarr ? a.ws_p : a.ws_dz) + (rowe + e) * a.Hp + 8 * zpc;
+      zp = *reinterpret_cast<const u32x4_t*>(src);
+    }
+    if (zok) *reinterpret_cast<u32x4_t*>(&s_zp[zarr][zrow][8 * zpc]) = zp;
+    __syncthreads();                                    // staged; the last block's sums are read
+    u32x2_t az[HK], ap[HK];
+#pragma unroll
+    for (int ks = 0; ks < HK; ++ks) {
+      az[ks] = *reinterpret_cast<const u32x2_t*>(&s_zp[0][l32][8 * ks + 4 * hh]);
+      ap[ks] = *reinterpret_cast<const u32x2_t*>(&s_zp[1][l32][8 * ks + 4 * hh]);
+    }
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int ct = wave + NWV * k;
+      if (ct < CT) {
+        f32x16_t acc = {};
+#pragma unroll
+        for (int ks = 0; ks < HK; ++ks) acc = mfma_bf16_32x32x8(az[ks], qkb[k][ks], acc);
+        if (ct * 32 < kBwdDV) {
+#pragma unroll
+          for (int ks = 0; ks < HK; ++ks) acc = mfma_bf16_32x32x8(ap[ks], dkb[k][ks], acc);
+        }
+        // accumulator r is row 8 (r / 4) + 4 hh + r % 4, column 32 ct + l32
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_out[8 * (r >> 2) + 4 * hh + (r & 3)][32 * ct + l32] = acc[r];
+      }
+    }
+    __syncthreads();
+    {
+      f32x4_t v[NF];   // every sum of the thread read first (one LDS round trip), then stored
+#pragma unroll
+      for (int k = 0; k < NF; ++k) {
+        const int f = threadIdx.x + 512 * k;
+        v[k] = *reinterpret_cast<const f32x4_t*>(&s_out[f / F4][4 * (f % F4)]);
+      }
+#pragma unroll
+      for (int k = 0; k < NF; ++k)
+        if (rsk[k] >= 0)
+          *reinterpret_cast<f32x4_t*>(a.dkv + (int64_t)rsk[k] * DQK + 4 * (((int)threadIdx.x + 512 * k) % F4)) = cur[k] + v[k];
+    }
+    // rows named more than once: atomics whose 64 lanes cover 64 consecutive floats (an atomic
+    // instruction over 16-byte strided lanes costs the L2 about three times as much)
+    if (s_shared >> (blk - b0) & 1u) {
+#pragma unroll 1
+      for (int k = 0; k < 4 * NF; ++k) {
+        const int flat = 64 * ((int)(threadIdx.x >> 6) + 8 * k) + lane;
+        const int r = flat / DQK;
+        const int c = flat % DQK;
+        const int32_t rs = s_rs[jb + r];
+        if (rs <= -2) unsafeAtomicAdd(a.dkv + (int64_t)(-(rs + 2)) * DQK + c, s_out[r][c]);
+      }
+    }
+  }
+}
+
 template <int DQK>
 static void launch_dkv(const MlaBwdArgs& a, int T, hipStream_t st) {
   constexpr int CT = DQK / 32;
   const int hk = a.Hp / 8;
+  if (hk <= 8 && a.ws_owner) {   // whole rows per workgroup (with the owner map)
+    // blocks per workgroup: up to 16 (the row's q and dout are staged once per workgroup), fewer
+    // when that leaves under about one workgroup per CU
+    const int nb = (a.n_idx + 31) / 32;
+    const int bpw = (int)std::min<int64_t>(kDkvBpwMax, std::max<int64_t>(2, ((int64_t)nb * T + 255) / 256));
+    const dim3 grid((nb + bpw - 1) / bpw, T);
+    if (hk == 4) launch_kernel(k_sparse_mla_bwd_dkv_rows<DQK, 4>, grid, dim3(512), st, a, bpw);
+    else launch_kernel(k_sparse_mla_bwd_dkv_rows<DQK, 8>, grid, dim3(512), st, a, bpw);
+    return;
+  }
   const int cg = hk >= 16 ? 2 : 3;
   const dim3 grid((CT + cg - 1) / cg, T);
-  if (hk == 2) launch_kernel(k_sparse_mla_bwd_dkv<DQK, 2>, grid, dim3(256), st, a, cg);
-  else if (hk == 4) launch_kernel(k_sparse_mla_bwd_dkv<DQK, 4>, grid, dim3(256), st, a, cg);
+  if (hk == 4) launch_kernel(k_sparse_mla_bwd_dkv<DQK, 4>, grid, dim3(256), st, a, cg);
   else if (hk == 8) launch_kernel(k_sparse_mla_bwd_dkv<DQK, 8>, grid, dim3(256), st, a, cg);
   else launch_kernel(k_sparse_mla_bwd_dkv<DQK, 16>, grid, dim3(256), st, a, cg);
 }
@@ -540,6 +760,13 @@ hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream
     if (fused) launch_kernel(k_sparse_mla_bwd<512, true>, grid, dim3(256), st, a);
     else launch_kernel(k_sparse_mla_bwd<512, false>, grid, dim3(256), st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_mla_bwd_owner(const MlaBwdArgs& a, int T, hipStream_t st) {
+  if (T <= 0 || a.n_idx <= 0 || a.Hp == 16 || !a.ws_owner) return hipSuccess;
+  launch_kernel(k_sparse_mla_bwd_owner, dim3((a.n_idx + 255) / 256, T), dim3(256), st, a.ws_slot, (int)a.n_idx,
+                a.ws_owner);
   return hipGetLastError();
 }
 

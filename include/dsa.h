@@ -201,13 +201,18 @@ dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cach
  * dout: bf16 [T, H, d_v], row stride ld_dout (>= H*d_v, multiple of 8).
  * dq:  fp32 [T, H, d_qk], row stride ld_dq (>= H*d_qk, multiple of 4), 16-byte aligned;
  *      written.
- * dkv: fp32 [kv->n_slots, d_qk] indexed by cache slot; ADDED TO by fp32 atomics in no fixed
- *      order (the caller zeroes it first; the last bits vary between runs).
+ * dkv: fp32 [kv->n_slots, d_qk] indexed by cache slot; ADDED TO (the caller zeroes it first).
+ *      A slot that several entries of the call name (over all rows, or twice in one row)
+ *      takes fp32 atomics in no fixed order, so its last bits vary between runs; with the
+ *      owner map below, a slot that exactly one entry names takes one plain load and store.
  * dsink: fp32 [H] added to by atomics, or NULL; needs opts->sink.
- * Two kernels: per (row, 16 heads) dq, and P and dZ into the workspace (bf16, 4 bytes per
+ * Kernels: per (row, 16 heads) dq, and P and dZ into the workspace (bf16, 4 bytes per
  * (row, entry, head), plus the entries' slots); then per row dKV over all heads, so that an
- * entry costs one atomic per column whatever H is (H = 16: one kernel, the workspace unused).
- * Workspace: dsa_workspace_size(DSA_ENTRY_MLA_BACKWARD, {T, H, n_idx}).
+ * entry costs one add per column whatever H is (H = 16: one kernel, the workspace unused).
+ * For H > 16 and a workspace sized with n_slots = kv->n_slots, an owner map (one word per
+ * slot, marked by a kernel between the two) tells the dKV kernel which slots one entry alone
+ * names. Workspace: dsa_workspace_size(DSA_ENTRY_MLA_BACKWARD, {T, H, n_idx, n_slots});
+ * n_slots = 0 sizes it without the map (every dKV add atomic).
  * Envelope: DSA_KV_BF16 cache; 1 <= H <= 128 (heads padded to 16, 32, 64 or 128 inside, the
  * padding heads reading as zero); d_qk in {512, 576}; d_v = 512.
  * Errors: DSA_ERR_ARG for null pointers, bad strides or alignment, dsink without a sink;
@@ -274,7 +279,7 @@ typedef struct dsa_problem {
   int32_t topk;
   int32_t H;        /* attention heads */
   int32_t n_idx;    /* attention list length (main + extra) */
-  int32_t _pad0;
+  int32_t n_slots;  /* backward: the cache's slot count for the owner map (0: no map) */
 } dsa_problem;
 
 /* Bytes of workspace `entry` needs for problem `p` (0 if it needs none; SIZE_MAX on bad input). */

@@ -174,6 +174,12 @@ def test_workspace_sizes():
         dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=2, H=64, n_idx=256)
     with pytest.raises(dsa.DSAError):
         dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=1, H=129, n_idx=64)
+    # the backward's owner map: one int32 per cache slot in whole 16-byte words, 256-aligned
+    base = dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=2, H=64, n_idx=256)
+    for n_slots, extra in ((1, 256), (64, 256), (65, 512), (4096, 16384), (4099, 16640)):
+        assert dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=2, H=64, n_idx=256, n_slots=n_slots) == base + extra
+    with pytest.raises(dsa.DSAError):
+        dsa.dsa_workspace_size(dsa.ENTRY_MLA_BACKWARD, T=1, H=64, n_idx=64, n_slots=-1)
 
 
 def test_launch_override():

@@ -135,15 +135,51 @@ def test_backward_chained(name, kw):
     _check(prob, prob.idx_main, do, dq, dkv, dsink)
 
 
-def test_backward_repeated_entry():
-    """An entry listed twice contributes twice (to the softmax and to dKV)."""
+@pytest.mark.parametrize("name,kw", [c for c in CASES if c[1]["H"] > 16], ids=[c[0] for c in CASES if c[1]["H"] > 16])
+def test_backward_atomics_only(name, kw):
+    """The dKV kernel without the owner map (a workspace sized without n_slots): every add
+    atomic, same results."""
+    prob = workload("attention_case", **kw)
+    say("backward (atomics only)", name)
+    rng = np.random.default_rng(len(name))
+    dout = rng.standard_normal((prob.T, prob.H, prob.d_v)).astype(np.float32)
+    with_dsink = getattr(prob, "sink", None) is not None
+    fwd = _oracle_forward(prob, prob.idx_main)
+    dq, dkv, dsink, do = run_backward(prob, dout, with_dsink=with_dsink, fwd=fwd, owner=False)
+    _check(prob, prob.idx_main, do, dq, dkv, dsink, fwd=fwd)
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_backward_repeated_entry(H):
+    """An entry listed twice contributes twice (to the softmax and to dKV). With 64 heads the
+    owner map must see the slot named twice and keep its adds atomic."""
     import torch
-    prob = workload("attention_case", fmt="bf16", B=2, H=16, n_ctx=400, n_idx=40, n_pad=0)
+    prob = workload("attention_case", fmt="bf16", B=2, H=H, n_ctx=400, n_idx=40, n_pad=0)
     idx = prob.idx_main.copy()
     idx[:, 5] = idx[:, 3]
-    say("backward repeated entry")
+    say("backward repeated entry, H", H)
     d = upload(prob)
     rng = np.random.default_rng(3)
     dout = rng.standard_normal((prob.T, prob.H, prob.d_v)).astype(np.float32)
     dq, dkv, _, do = run_backward(prob, dout, d=d, idx=torch.from_numpy(idx).cuda())
     _check(prob, idx, do, dq, dkv)
+
+
+def test_backward_rows_sharing_a_request():
+    """Four rows of one request with overlapping lists (128 of 300 positions each): slots named
+    by several rows take atomics, the others plain adds; both against the oracle."""
+    import dataclasses
+    base = workload("attention_case", fmt="bf16", B=4, H=64, n_ctx=300, n_idx=128, pad="shuffled", n_pad=8)
+    prob = dataclasses.replace(base, row_req=np.zeros(4, dtype=np.int32))
+    say("backward, 4 rows of one request")
+    slots_named = {}
+    for t in range(prob.T):
+        for p in prob.idx_main[t]:
+            if p >= 0:
+                slots_named[int(p)] = slots_named.get(int(p), 0) + 1
+    assert 0 < sum(v == 1 for v in slots_named.values()) < len(slots_named)   # both kinds occur
+    rng = np.random.default_rng(11)
+    dout = rng.standard_normal((prob.T, prob.H, prob.d_v)).astype(np.float32)
+    fwd = _oracle_forward(prob, prob.idx_main)
+    dq, dkv, _, do = run_backward(prob, dout, fwd=fwd)
+    _check(prob, prob.idx_main, do, dq, dkv, fwd=fwd)
