@@ -29,8 +29,8 @@
 // 2 rows; rows of padding entries are skipped. With 16 heads there is nothing to sum first, and
 // the first kernel adds dKV itself (same products, no workspace round trip).
 // A cache row that exactly one list entry names (over all rows of the call) needs no atomic:
-// with an owner map (one word per slot, cleared by the first kernel, marked by
-// k_sparse_mla_bwd_owner: the first entry's row + 1, bit 31 once a second entry names it),
+// with an owner map (one word per slot, marked by k_sparse_mla_bwd_owner: the first entry's
+// row + 1 where the word was 0, bit 31 from every other entry and wherever it was not 0),
 // k_sparse_mla_bwd_dkv_rows (32 or 64 padded heads) adds into such rows with plain loads and
 // stores of whole cache rows, and keeps atomics for rows that several entries name. fp32
 // atomics run at about one per L2 channel and clock; decode-shaped lists (each row its own
@@ -427,15 +427,6 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
     __syncthreads();   // every wave is done with this pass's slots
   }
 
-  if (!FUSED && a.ws_owner) {   // the owner map to zero, in 16-byte words spread over the grid
-    // (at the end, where the stores hold up nothing; the marking kernel runs after this one)
-    const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
-    const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    const int64_t n16 = (a.n_slots + 3) / 4;
-    for (int64_t i = wg * NT + threadIdx.x; i < n16; i += nwg * NT)
-      reinterpret_cast<u32x4_t*>(a.ws_owner)[i] = u32x4_t{0u, 0u, 0u, 0u};
-  }
-
   // ---- dq: lane (c = head, g) holds columns 128 wave + 8 (4g + r) + e (and the RoPE phases)
   if (c >= hval) return;                                // a padding head: no dq
   float* dqh = a.dq + (int64_t)t * a.ld_dq + (int64_t)(head0 + c) * DQK;
@@ -537,7 +528,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd_dkv(MlaBwdArgs a, int
 }
 
 // The owner map of the call's list entries: slot -> first naming row + 1, bit 31 when a second
-// entry (of any row, or the same row again) names it. The map was zeroed by k_sparse_mla_bwd.
+// entry (of any row, or the same row again) names it. A word is positive afterwards only if it
+// was 0 before and one entry alone names the slot: words that start dirty (a fresh workspace,
+// or one whose layout moved) only send their rows to atomics. The dKV kernel clears every
+// word it reads, so a map is clean again for the next call.
 __global__ __launch_bounds__(256) void k_sparse_mla_bwd_owner(const int32_t* slots, int ntot, int32_t* owner) {
   const int t = blockIdx.y;
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -601,11 +595,15 @@ __global__ __launch_bounds__(512, 1) void k_sparse_mla_bwd_dkv_rows(MlaBwdArgs a
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const int j = threadIdx.x + 512 * i;
-      const int32_t d = b0 * 32 + j >= ntot || v[i] < 0 ? -1 : o[i] > 0 ? v[i] : -(v[i] + 2);
+      const bool mine = j < (b1 - b0) * 32 && b0 * 32 + j < ntot && v[i] >= 0;
+      const int32_t d = !mine ? -1 : o[i] > 0 ? v[i] : -(v[i] + 2);
       if (j < (b1 - b0) * 32) {
         s_rs[j] = d;
         if (d <= -2) atomicOr(&s_shared, 1u << (j >> 5));   // the block has a row named twice
       }
+      // the word back to 0 for the next call: a slot named once has no other reader, and
+      // another reader of a shared slot that finds 0 takes the atomic path all the same
+      if (mine && a.ws_owner) a.ws_owner[v[i]] = 0;
     }
   }
   // B operands of this wave's column tiles (k = heads in steps of 8, n = 32 columns): q, then

@@ -209,10 +209,12 @@ dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cach
  * Kernels: per (row, 16 heads) dq, and P and dZ into the workspace (bf16, 4 bytes per
  * (row, entry, head), plus the entries' slots); then per row dKV over all heads, so that an
  * entry costs one add per column whatever H is (H = 16: one kernel, the workspace unused).
- * For H > 16 and a workspace sized with n_slots = kv->n_slots, an owner map (one word per
- * slot, marked by a kernel between the two) tells the dKV kernel which slots one entry alone
- * names. Workspace: dsa_workspace_size(DSA_ENTRY_MLA_BACKWARD, {T, H, n_idx, n_slots});
- * n_slots = 0 sizes it without the map (every dKV add atomic).
+ * For 17 <= H <= 64 and a workspace sized with n_slots = kv->n_slots, an owner map (one word
+ * per slot, marked by a kernel between the two, cleared again by the dKV kernel) tells the dKV
+ * kernel which slots one entry alone names; words found non-zero (a workspace that held other
+ * data) only make their slots take atomics. Workspace: dsa_workspace_size(
+ * DSA_ENTRY_MLA_BACKWARD, {T, H, n_idx, n_slots}); n_slots = 0 sizes it without the map (every
+ * dKV add atomic).
  * Envelope: DSA_KV_BF16 cache; 1 <= H <= 128 (heads padded to 16, 32, 64 or 128 inside, the
  * padding heads reading as zero); d_qk in {512, 576}; d_v = 512.
  * Errors: DSA_ERR_ARG for null pointers, bad strides or alignment, dsink without a sink;

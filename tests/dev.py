@@ -104,13 +104,13 @@ def bf16_round(x):
         .astype(np.float64)
 
 
-def run_backward(prob, dout, d=None, idx=None, with_dsink=False, fwd=None, owner=True):
+def run_backward(prob, dout, d=None, idx=None, with_dsink=False, fwd=None, owner=True, ws=None):
     """The backward. Its forward outputs: fwd = (out [T, H, d_v], lse [T, H]) given as numpy
     (out is rounded to bf16, lse to fp32 on the way in), or None for the GPU's own forward
     (one workgroup per row). dout: float32 numpy [T, H, d_v], rounded to bf16 here (the tests
     hand the same bf16 values to the oracle).
     owner: size the workspace with the cache's slot count (the owner map: plain adds for slots
-    one entry alone names), else without (every dKV add atomic).
+    one entry alone names), else without (every dKV add atomic). ws: a workspace to use instead.
     Returns (dq [T, H, d_qk], dkv [n_slots, d_qk], dsink [H] or None, dout as float64)."""
     m = dsa()
     d = d or upload(prob)
@@ -128,8 +128,9 @@ def run_backward(prob, dout, d=None, idx=None, with_dsink=False, fwd=None, owner
     dq = torch.full((T, H, prob.d_qk), float("nan"), device="cuda")
     dkv = torch.zeros((int(d.kv.c.n_slots), prob.d_qk), device="cuda")
     dsink = torch.zeros((H,), device="cuda") if with_dsink else None
-    ws = m.Workspace(m.dsa_workspace_size(m.ENTRY_MLA_BACKWARD, T=T, H=H, n_idx=int(idx_main.shape[1]),
-                                          n_slots=int(d.kv.c.n_slots) if owner else 0))
+    if ws is None:
+        ws = m.Workspace(m.dsa_workspace_size(m.ENTRY_MLA_BACKWARD, T=T, H=H, n_idx=int(idx_main.shape[1]),
+                                              n_slots=int(d.kv.c.n_slots) if owner else 0))
     m.dsa_sparse_mla_backward(d.q, d.kv, idx_main, d.rows, H, prob.d_qk, prob.d_v, prob.softmax_scale,
                               out, lse, do, dq, dkv, ws, dsink, sink=d.sink, lse_log2=d.lse_log2)
     torch.cuda.synchronize()

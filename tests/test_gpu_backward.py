@@ -183,3 +183,37 @@ def test_backward_rows_sharing_a_request():
     fwd = _oracle_forward(prob, prob.idx_main)
     dq, dkv, _, do = run_backward(prob, dout, fwd=fwd)
     _check(prob, prob.idx_main, do, dq, dkv, fwd=fwd)
+
+
+def test_backward_owner_map_dirty_then_reused():
+    """The owner map may start dirty (a workspace that held other data, or one whose layout
+    moved): such words only send their rows to atomics. The dKV kernel clears the words it
+    reads, so a second call on the same workspace gets plain adds again. Both calls against
+    the oracle."""
+    import torch
+    from dev import dsa
+    m = dsa()
+    prob = workload("attention_case", fmt="bf16", B=3, H=64, n_ctx=600, n_idx=256, pad="shuffled", n_pad=16)
+    d = upload(prob)
+    n_slots = int(d.kv.c.n_slots)
+    start = m.dsa_workspace_size(m.ENTRY_MLA_BACKWARD, T=prob.T, H=prob.H, n_idx=256)
+    end = m.dsa_workspace_size(m.ENTRY_MLA_BACKWARD, T=prob.T, H=prob.H, n_idx=256, n_slots=n_slots)
+    ws = m.Workspace(end)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    ws.buf[start:end].copy_(torch.randint(0, 256, (end - start,), generator=g, dtype=torch.uint8))
+    rng = np.random.default_rng(21)
+    dout = rng.standard_normal((prob.T, prob.H, prob.d_v)).astype(np.float32)
+    fwd = _oracle_forward(prob, prob.idx_main)
+    for call in range(2):
+        say("backward on a dirty owner map, call", call)
+        dq, dkv, _, do = run_backward(prob, dout, d=d, fwd=fwd, ws=ws)
+        _check(prob, prob.idx_main, do, dq, dkv, fwd=fwd)
+        if call == 0:   # every listed slot's word is back to 0
+            words = ws.buf[start:end].view(torch.int32).cpu().numpy()
+            slots = set()
+            for t in range(prob.T):
+                for p in prob.idx_main[t]:
+                    if p >= 0:
+                        slots.add(int(prob.kv.block_table[t, p // prob.kv.page_size]) * prob.kv.page_size
+                                  + int(p) % prob.kv.page_size)
+            assert all(words[s] == 0 for s in slots)
