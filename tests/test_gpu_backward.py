@@ -217,3 +217,26 @@ def test_backward_owner_map_dirty_then_reused():
                         slots.add(int(prob.kv.block_table[t, p // prob.kv.page_size]) * prob.kv.page_size
                                   + int(p) % prob.kv.page_size)
             assert all(words[s] == 0 for s in slots)
+
+
+def test_backward_full_size_sampled_rows():
+    """The measured backward shape at full size: 64 rows (each its own request) x 64 heads x
+    2048 listed of 4096 cached rows, the GPU's forward then the backward with the owner map
+    (every listed cache row is named once: whole-row plain adds). dq and the dKV rows of five
+    sampled query rows against the exact gradient; each dKV row holds one entry's
+    contribution, so a row's slots compare on their own."""
+    prob = workload("attention_case", fmt="bf16", B=64, H=64, n_ctx=4096, n_idx=2048, pad="tail", n_pad=0)
+    say("backward full size, 64 x 64 x 2048")
+    rng = np.random.default_rng(64)
+    dout = rng.standard_normal((prob.T, prob.H, prob.d_v)).astype(np.float32)
+    dq, dkv, _, do = run_backward(prob, dout)
+    for t in (0, 1, 17, 40, 63):
+        dq_ref, slots, drows, _ = oracle.attention_backward_row(prob, t, prob.idx_main[t], do[t])
+        scale = np.abs(dq_ref).max(axis=1, keepdims=True)
+        err = np.abs(dq[t] - dq_ref)
+        ref = drows[:, :prob.d_qk]
+        e = np.abs(dkv[slots] - ref)
+        say("  row", t, "dq worst rel", float((err / (scale + 1e-30)).max()),
+            "dkv max err", float(e.max()), "max |ref|", float(np.abs(ref).max()))
+        assert np.all(err <= 2e-2 * scale + 1e-5), f"dq row {t}"
+        assert np.all(e <= 2e-2 * np.abs(ref).max() + 1e-5), f"dkv rows of row {t}"
