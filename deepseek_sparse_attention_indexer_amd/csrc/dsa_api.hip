@@ -210,7 +210,10 @@ void set_mla_row(int T, int H, int n_main, int n_extra, int fmt, int d_qk, bool 
 // backward: bf16 scale * dZ and P per (row, listed entry, padded head), and the entries' slots
 int64_t mla_bwd_ws_bytes(int T, int H, int n_idx) {
   const int64_t e = (int64_t)T * n_idx;
-  return align256(e * heads_padded_bwd(H) * 2) * 2 + align256(e * 4);
+  const int hp = heads_padded_bwd(H);
+  const int ns = bwd_splits(T, hp, n_idx);
+  // dZ and P, the slots, and the dq partial sums of list parts 1.. (sized at d_qk = 576)
+  return align256(e * hp * 2) * 2 + align256(e * 4) + (ns > 1 ? align256((int64_t)(ns - 1) * T * hp * 576 * 4) : 0);
 }
 
 // the backward's owner map: one int32 per cache slot, in whole 16-byte words
@@ -964,6 +967,8 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
     a.ws_dz = reinterpret_cast<uint16_t*>(w + cv.take(e * a.Hp * 2));
     a.ws_p = reinterpret_cast<uint16_t*>(w + cv.take(e * a.Hp * 2));
     a.ws_slot = reinterpret_cast<int32_t*>(w + cv.take(e * 4));
+    a.nsplit = bwd_splits(T, a.Hp, n_idx);
+    if (a.nsplit > 1) a.ws_dqp = reinterpret_cast<float*>(w + cv.take((int64_t)(a.nsplit - 1) * T * a.Hp * 576 * 4));
     // the owner map when the workspace has room for one over this cache's slots
     const int64_t ob = mla_bwd_owner_bytes(kv->n_slots);
     if ((a.Hp == 32 || a.Hp == 64) && n_idx > 0 && kv->n_slots <= INT32_MAX && (int64_t)ws_bytes >= need + ob) {
@@ -972,11 +977,12 @@ dsa_status dsa_sparse_mla_backward(const void* q, int64_t ld_q, const dsa_kv_cac
     }
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  set_row("T=%d H=%d (padded %d) list %d d_qk=%d: one workgroup per (row, 16 heads), dKV over all heads%s", T,
-          H, (int)a.Hp, n_idx, d_qk, a.ws_owner ? ", owner map (plain adds for singly named slots)" : "");
+  set_row("T=%d H=%d (padded %d) list %d d_qk=%d: one workgroup per (row, %d heads, list part of %d), dKV over "
+          "all heads%s", T, H, (int)a.Hp, n_idx, d_qk, a.Hp == 16 ? 16 : 32, (int)a.nsplit,
+          a.ws_owner ? ", owner map (plain adds for singly named slots)" : "");
   dsa_status s = hip_status(timed("sparse_mla_bwd", hs, [&] { return launch_sparse_mla_bwd(a, d_qk, T, hs); }));
-  if (s == DSA_OK && a.ws_owner)
-    s = hip_status(timed("sparse_mla_bwd_owner", hs, [&] { return launch_sparse_mla_bwd_owner(a, T, hs); }));
+  if (s == DSA_OK && (a.ws_owner || a.nsplit > 1))
+    s = hip_status(timed("sparse_mla_bwd_mid", hs, [&] { return launch_sparse_mla_bwd_mid(a, d_qk, T, hs); }));
   if (s == DSA_OK)
     s = hip_status(timed("sparse_mla_bwd_dkv", hs, [&] { return launch_sparse_mla_bwd_dkv(a, d_qk, T, hs); }));
   return s;

@@ -156,10 +156,16 @@ struct MlaBwdArgs {
   int32_t* ws_slot;        // workspace: [T, n_idx] slots (-1: padding)
   int32_t* ws_owner;       // workspace: [n_slots] who lists each slot (nullptr: atomics only)
   int64_t n_slots;         // the cache's slot count (with ws_owner)
+  float* ws_dqp;           // workspace: [nsplit - 1, T, H, d_qk] dq of list parts 1..nsplit-1
+  int32_t nsplit;          // parts each row's list is split into (first kernel's grid z)
 };
 
+// parts of each row's list in the backward's first kernel: enough workgroups (two 16-head
+// groups each) for about one per CU, every part at least 8 blocks of 32 entries
+int bwd_splits(int T, int Hp, int n_idx);
+
 hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st);
-hipError_t launch_sparse_mla_bwd_owner(const MlaBwdArgs& a, int T, hipStream_t st);
+hipError_t launch_sparse_mla_bwd_mid(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st);
 hipError_t launch_sparse_mla_bwd_dkv(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st);
 
 // cache writes: bf16 rows -> a cache format, one row per token at slots[token]

@@ -10,8 +10,9 @@
 // (radixark/miles PR 3608, section "What": the backward takes the forward's lse with the sink
 // folded in, and adds dKV through the listed indices atomically; the lse here may be in base 2).
 //
-// A workgroup takes one query row and 16 heads (4 waves) and walks the row's list in blocks of
-// 32 rows gathered into LDS (direct global->LDS loads). Per block, with S^T = K Q^T and
+// A workgroup takes one query row and 16 heads (4 waves), or 32 heads as two such groups of 4
+// waves sharing the gathered rows (when dZ and P go to the workspace), and walks the row's list
+// in blocks of 32 rows gathered into LDS (direct global->LDS loads). Per block, with S^T = K Q^T and
 // dP^T = V dO^T split over the waves as in the forward (two row tiles x two halves of the
 // contraction, the partials meeting in LDS):
 //   * P and dZ from the forward's lse (no second pass over the list);
@@ -29,7 +30,7 @@
 // 2 rows; rows of padding entries are skipped. With 16 heads there is nothing to sum first, and
 // the first kernel adds dKV itself (same products, no workspace round trip).
 // A cache row that exactly one list entry names (over all rows of the call) needs no atomic:
-// with an owner map (one word per slot, marked by k_sparse_mla_bwd_owner: the first entry's
+// with an owner map (one word per slot, marked by k_sparse_mla_bwd_mid: the first entry's
 // row + 1 where the word was 0, bit 31 from every other entry and wherever it was not 0),
 // k_sparse_mla_bwd_dkv_rows (32 or 64 padded heads) adds into such rows with plain loads and
 // stores of whole cache rows, and keeps atomics for rows that several entries name. fp32
@@ -74,9 +75,12 @@ __device__ __forceinline__ uint32_t lds_u16(const uint16_t* p) { return *p; }
 // FUSED: dKV of the workgroup's 16 heads added straight from this kernel (a single 16-head group
 // per row: nothing to sum first); else dZ and P go to the workspace for k_sparse_mla_bwd_dkv.
 template <int DQK, bool FUSED>
-__global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
-  constexpr int NW = 4;
-  constexpr int NT = 256;
+__global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
+  // 16-head groups per workgroup: two (8 waves) share the gathered rows when dZ and P go to
+  // the workspace, one with the fused dKV
+  constexpr int GRP = FUSED ? 1 : 2;
+  constexpr int NW = 4 * GRP;
+  constexpr int NT = 256 * GRP;
   constexpr int RE = DQK + 8;                 // padded bf16 row in LDS
   constexpr int KS = DQK / 32;                // k-steps of the score product
   constexpr int KQ = KS / 2;                  // per wave (split over the two halves)
@@ -87,20 +91,24 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   __shared__ __align__(16) uint16_t s_rows[2][kBwdNB][RE];
   __shared__ __align__(16) int32_t s_slot[kBwdResolve];
   __shared__ const uint8_t* s_ra[kBwdNB];
-  __shared__ f32x4_t s_ss[NW][64];
-  __shared__ f32x4_t s_sd[NW][64];
-  __shared__ __align__(16) uint16_t s_tz[kBwdNB][16];   // bf16 scale * dZ[row][head]
-  __shared__ __align__(16) uint16_t s_tp[kBwdNB][16];   // bf16 P[row][head]
-  __shared__ float s_D[16];
-  __shared__ float s_l2[16];
+  __shared__ f32x4_t s_ss[GRP][4][64];
+  __shared__ f32x4_t s_sd[GRP][4][64];
+  __shared__ __align__(16) uint16_t s_tz[GRP][kBwdNB][16];   // bf16 scale * dZ[row][head]
+  __shared__ __align__(16) uint16_t s_tp[GRP][kBwdNB][16];   // bf16 P[row][head]
+  __shared__ float s_D[GRP][16];
+  __shared__ float s_l2[GRP][16];
 
   const int t = blockIdx.y;
   const int hg = blockIdx.x;
+  const int sp = blockIdx.z;                  // part of the row's list
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int gi = wave >> 2;                   // head group of this wave
+  const int lw = wave & 3;                    // wave within its group
+  const int tg = threadIdx.x & 255;           // thread within its group
   const int g = lane >> 4;
   const int c = lane & 15;
-  const int head0 = hg * 16;
+  const int head0 = (hg * GRP + gi) * 16;
   const int b = min(max(a.row_req ? a.row_req[t] : t, 0), a.n_req - 1);
   const KvDev kv = a.kv;
   // the paging rebuilt field by field: a table/base select on the argument copy itself would
@@ -108,53 +116,60 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   const Paging pg = pick_paging(false, a.kv.pg, a.kv.pg);
   const int32_t* const idx = a.idx + (int64_t)t * a.ld_idx;
   const int ntot = a.n_idx;
+  // this workgroup's entries [e0, e1): whole blocks of the list, part sp of gridDim.z
+  const int eper = ((ntot + (int)gridDim.z - 1) / (int)gridDim.z + kBwdNB - 1) / kBwdNB * kBwdNB;
+  const int e0 = min(ntot, sp * eper);
+  const int e1 = min(ntot, e0 + eper);
 
   // ---- prologue: q and dout of the 16 heads staged in the row buffer, the register operands
   // built from them; D = dout . out and the lse in base 2 per head
-  static_assert(16 * RE + 16 * (kBwdDV + 8) <= kBwdNB * RE, "staging");
-  uint16_t* const s_q = &s_rows[0][0][0];               // [16][RE]
-  uint16_t* const s_do = &s_rows[0][0][0] + 16 * RE;    // [16][kBwdDV + 8]
   constexpr int DOS = kBwdDV + 8;
+  static_assert(GRP * (16 * RE + 16 * DOS) <= 2 * kBwdNB * RE, "staging");
+  uint16_t* const s_q = &s_rows[0][0][0] + gi * (16 * RE + 16 * DOS);   // [16][RE]
+  uint16_t* const s_do = s_q + 16 * RE;                                  // [16][DOS]
   // Heads past H (a head count that is not a whole number of 16-head groups) read q, dout and
   // out as zero and lse as 0: their P is finite and their dZ and P dout are zero, so they add
   // nothing to dKV, and nothing of them is written.
-  const int hval = a.H - head0;                         // valid heads of this group (>= 1)
+  // valid heads of this group (<= 0: a group of padding heads only, with two groups per
+  // workgroup); every read below takes a head of the row (min(head, H - 1)) and drops it
+  const int hval = a.H - head0;
   {
-    // q and dout of the group: every 16-byte load of the thread requested at once (clamped
-    // to valid heads), then stored (a loop of load, wait, store pays a round trip each)
-    const uint16_t* qg = a.q + (int64_t)t * a.ld_q + (int64_t)head0 * DQK;
-    const uint16_t* dg = a.dout + (int64_t)t * a.ld_dout + (int64_t)head0 * kBwdDV;
-    constexpr int NQ = (16 * DQK / 8 + NT - 1) / NT;
-    constexpr int ND = 16 * kBwdDV / 8 / NT;
-    static_assert(16 * kBwdDV % (8 * NT) == 0, "whole dout loads");
+    // q and dout of the group (its 256 threads): every 16-byte load of the thread requested at
+    // once, then stored (a loop of load, wait, store pays a round trip each)
+    const uint16_t* qr = a.q + (int64_t)t * a.ld_q;
+    const uint16_t* dr = a.dout + (int64_t)t * a.ld_dout;
+    constexpr int NTG = 256;
+    constexpr int NQ = (16 * DQK / 8 + NTG - 1) / NTG;
+    constexpr int ND = 16 * kBwdDV / 8 / NTG;
+    static_assert(16 * kBwdDV % (8 * NTG) == 0, "whole dout loads");
     u32x4_t vq[NQ], vd[ND];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const int o = min(((int)threadIdx.x + j * NT) * 8, 16 * DQK - 8);
-      vq[j] = *reinterpret_cast<const u32x4_t*>(qg + min(o / DQK, hval - 1) * DQK + o % DQK);
+      const int o = min((tg + j * NTG) * 8, 16 * DQK - 8);
+      vq[j] = *reinterpret_cast<const u32x4_t*>(qr + (int64_t)min(head0 + o / DQK, a.H - 1) * DQK + o % DQK);
     }
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
-      const int o = ((int)threadIdx.x + j * NT) * 8;
-      vd[j] = *reinterpret_cast<const u32x4_t*>(dg + min(o / kBwdDV, hval - 1) * kBwdDV + o % kBwdDV);
+      const int o = (tg + j * NTG) * 8;
+      vd[j] = *reinterpret_cast<const u32x4_t*>(dr + (int64_t)min(head0 + o / kBwdDV, a.H - 1) * kBwdDV + o % kBwdDV);
     }
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const int o = ((int)threadIdx.x + j * NT) * 8;
+      const int o = (tg + j * NTG) * 8;
       if (o < 16 * DQK)
         *reinterpret_cast<u32x4_t*>(s_q + (o / DQK) * RE + o % DQK) = o / DQK < hval ? vq[j] : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
-      const int o = ((int)threadIdx.x + j * NT) * 8;
+      const int o = (tg + j * NTG) * 8;
       *reinterpret_cast<u32x4_t*>(s_do + (o / kBwdDV) * DOS + o % kBwdDV) = o / kBwdDV < hval ? vd[j] : u32x4_t{0u, 0u, 0u, 0u};
     }
     // D: 16 threads per head, 32 columns each
-    const int h = threadIdx.x >> 4;
-    const int c0 = (threadIdx.x & 15) * 32;
-    const int hr = min(h, hval - 1);                    // padding heads read a valid row, then drop it
-    const uint16_t* og = a.out + (int64_t)t * a.ld_out + (int64_t)(head0 + hr) * kBwdDV + c0;
-    const uint16_t* dh = dg + hr * kBwdDV + c0;
+    const int h = tg >> 4;
+    const int c0 = (tg & 15) * 32;
+    const int hr = min(head0 + h, a.H - 1);             // padding heads read a valid row, then drop it
+    const uint16_t* og = a.out + (int64_t)t * a.ld_out + (int64_t)hr * kBwdDV + c0;
+    const uint16_t* dh = dr + (int64_t)hr * kBwdDV + c0;
     float d = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {
@@ -168,22 +183,22 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
     }
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) d += __shfl_xor(d, m);
-    if ((threadIdx.x & 15) == 0) {
-      s_D[h] = h < hval ? d : 0.f;
+    if ((tg & 15) == 0) {
+      s_D[gi][h] = h < hval ? d : 0.f;
       const float l = h < hval ? a.lse[(int64_t)t * a.H + head0 + h] : 0.f;
-      s_l2[h] = a.lse_log2 ? l : l * kLog2e;
+      s_l2[gi][h] = a.lse_log2 ? l : l * kLog2e;
     }
   }
   __syncthreads();
   // B operand of S^T = K Q^T for this wave's half of the contraction, and of dP^T = V dO^T
-  const int kq0 = (wave & 1) * KQ;
+  const int kq0 = (lw & 1) * KQ;
   u32x4_t qb[KQ];
 #pragma unroll
   for (int kb = 0; kb < KQ; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(s_q + c * RE + 32 * (kq0 + kb) + 8 * g);
   u32x4_t dob[8];
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb)
-    dob[kb] = *reinterpret_cast<const u32x4_t*>(s_do + c * DOS + 256 * (wave & 1) + 32 * kb + 8 * g);
+    dob[kb] = *reinterpret_cast<const u32x4_t*>(s_do + c * DOS + 256 * (lw & 1) + 32 * kb + 8 * g);
   // B operands of dKV (k = the 16 heads in two steps of 8, n = 32 columns): Q and dO for the
   // wave's column tiles ct0 .. ct0 + nct - 1 (tile counts (CT + 3 - w) / 4: 5, 5, 4, 4 of 18)
   const int nct = (CT + NW - 1 - wave) / NW;
@@ -208,16 +223,16 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
       dkb[k][ks] = u32x2_t{d4[0] | (d4[1] << 16), d4[2] | (d4[3] << 16)};
     }
   }
-  const float Dc = s_D[c];
-  const float l2c = s_l2[c];
-  if (a.sink && a.dsink && (int)threadIdx.x < min(16, hval)) {
-    const float sk = a.sink[head0 + threadIdx.x];
-    if (sk > -INFINITY) unsafeAtomicAdd(a.dsink + head0 + threadIdx.x, -exp2f(sk * kLog2e - s_l2[threadIdx.x]) * s_D[threadIdx.x]);
+  const float Dc = s_D[gi][c];
+  const float l2c = s_l2[gi][c];
+  if (sp == 0 && a.sink && a.dsink && tg < min(16, hval)) {
+    const float sk = a.sink[head0 + tg];
+    if (sk > -INFINITY) unsafeAtomicAdd(a.dsink + head0 + tg, -exp2f(sk * kLog2e - s_l2[gi][tg]) * s_D[gi][tg]);
   }
   __syncthreads();   // the staging area becomes the row buffer
 
-  // dq^T accumulators: 128 columns of group `wave` (8 column phases), and for d_qk = 576 two
-  // phases of the RoPE group (columns 512 + 8 m + e, e = 2 wave + i, m < 8)
+  // dq^T accumulators: 128 columns of group `lw` (8 column phases), and for d_qk = 576 two
+  // phases of the RoPE group (columns 512 + 8 m + e, e = 2 lw + i, m < 8)
   f32x4_t oq[8];
   f32x4_t o4[2];
 #pragma unroll
@@ -225,8 +240,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
   o4[0] = o4[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   int pass_n = 0;
-  for (int p0 = 0; p0 < ntot; p0 += kBwdResolve) {
-    const int p1 = min(ntot, p0 + kBwdResolve);
+  for (int p0 = e0; p0 < e1; p0 += kBwdResolve) {
+    const int p1 = min(e1, p0 + kBwdResolve);
     const int nb = (p1 - p0 + kBwdNB - 1) / kBwdNB;
     pass_n = p1 - p0;
     {   // the pass's entries to slots: every index read, then every table read
@@ -298,20 +313,20 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
       const u32x4_t sl0 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm]);
       const u32x4_t sl1 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm + 16]);
       {
-        const uint16_t* rp = &s_rows[cur][16 * (wave >> 1) + c][8 * g];
+        const uint16_t* rp = &s_rows[cur][16 * (lw >> 1) + c][8 * g];
         f32x4_t sp = f32x4_t{0.f, 0.f, 0.f, 0.f}, dp = sp;
 #pragma unroll
         for (int kb = 0; kb < KQ; ++kb)
           sp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 32 * (kq0 + kb)), qb[kb], sp);
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
-          dp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 256 * (wave & 1) + 32 * kb), dob[kb], dp);
-        s_ss[wave][lane] = sp;
-        s_sd[wave][lane] = dp;
+          dp = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(rp + 256 * (lw & 1) + 32 * kb), dob[kb], dp);
+        s_ss[gi][lw][lane] = sp;
+        s_sd[gi][lw][lane] = dp;
       }
       lds_barrier();
-      const f32x4_t s0 = s_ss[0][lane] + s_ss[1][lane], s1 = s_ss[2][lane] + s_ss[3][lane];
-      const f32x4_t d0 = s_sd[0][lane] + s_sd[1][lane], d1 = s_sd[2][lane] + s_sd[3][lane];
+      const f32x4_t s0 = s_ss[gi][0][lane] + s_ss[gi][1][lane], s1 = s_ss[gi][2][lane] + s_ss[gi][3][lane];
+      const f32x4_t d0 = s_sd[gi][0][lane] + s_sd[gi][1][lane], d1 = s_sd[gi][2][lane] + s_sd[gi][3][lane];
       // ---- P and dZ of rows 4g + r and 16 + 4g + r, head c
       float p[8], dz[8];
 #pragma unroll
@@ -326,10 +341,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
       // dZ and P into LDS, row-major by head, for the dKV product's B layout
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s_tz[4 * g + r][c] = (uint16_t)bf16_rne_bits(dz[r] * a.scale);
-        s_tz[16 + 4 * g + r][c] = (uint16_t)bf16_rne_bits(dz[4 + r] * a.scale);
-        s_tp[4 * g + r][c] = (uint16_t)bf16_rne_bits(p[r]);
-        s_tp[16 + 4 * g + r][c] = (uint16_t)bf16_rne_bits(p[4 + r]);
+        s_tz[gi][4 * g + r][c] = (uint16_t)bf16_rne_bits(dz[r] * a.scale);
+        s_tz[gi][16 + 4 * g + r][c] = (uint16_t)bf16_rne_bits(dz[4 + r] * a.scale);
+        s_tp[gi][4 * g + r][c] = (uint16_t)bf16_rne_bits(p[r]);
+        s_tp[gi][16 + 4 * g + r][c] = (uint16_t)bf16_rne_bits(p[4 + r]);
       }
       // ---- dq^T += K^T dZ^T: dZ^T from the accumulator layout (k-slot 8g + i of the B
       // operand is row 4g + i, then 16 + 4g + i - 4), K^T by 8x8 transposes of LDS rows
@@ -342,8 +357,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
         u32x4_t vr[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * wave + 8 * c]);
-          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * wave + 8 * c]);
+          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * lw + 8 * c]);
+          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * lw + 8 * c]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -355,13 +370,13 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
           oq[e] = mfma_bf16_16x16x32(av, zb, oq[e]);
         }
       }
-      if constexpr (kRope) {   // columns 512 + 8 m + e for m = c < 8; phases e = 2 wave + i
-        // (the two phases of a wave are the two halves of dword `wave` of the 8 columns)
+      if constexpr (kRope) {   // columns 512 + 8 m + e for m = c < 8; phases e = 2 lw + i
+        // (the two phases of a wave are the two halves of dword `lw` of the 8 columns)
         uint32_t vw[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          vw[j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][4 * g + j][kBwdDV + 8 * (c & 7) + 2 * wave]);
-          vw[4 + j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][16 + 4 * g + j][kBwdDV + 8 * (c & 7) + 2 * wave]);
+          vw[j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][4 * g + j][kBwdDV + 8 * (c & 7) + 2 * lw]);
+          vw[4 + j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][16 + 4 * g + j][kBwdDV + 8 * (c & 7) + 2 * lw]);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -379,8 +394,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
         u32x2_t az[2], ap[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          az[ks] = *reinterpret_cast<const u32x2_t*>(&s_tz[l32][8 * ks + 4 * hh]);
-          ap[ks] = *reinterpret_cast<const u32x2_t*>(&s_tp[l32][8 * ks + 4 * hh]);
+          az[ks] = *reinterpret_cast<const u32x2_t*>(&s_tz[gi][l32][8 * ks + 4 * hh]);
+          ap[ks] = *reinterpret_cast<const u32x2_t*>(&s_tp[gi][l32][8 * ks + 4 * hh]);
         }
         int32_t rs[16];
 #pragma unroll
@@ -409,13 +424,13 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
       } else {
       // ---- scale dZ, P (bf16, [row][head] with the row's heads contiguous) and the slots to
       // the workspace for the dKV kernel: 16 bytes (8 heads) per thread
-      if (threadIdx.x < 2 * 2 * kBwdNB) {
-        const int arr = threadIdx.x >> 6;              // 0: dZ, 1: P
-        const int row = (threadIdx.x >> 1) & (kBwdNB - 1);
-        const int half = threadIdx.x & 1;
+      if (tg < 2 * 2 * kBwdNB) {
+        const int arr = tg >> 6;                       // 0: dZ, 1: P
+        const int row = (tg >> 1) & (kBwdNB - 1);
+        const int half = tg & 1;
         const int j = jb + row;
         if (j < pass_n) {
-          const uint16_t* src = arr ? &s_tp[row][8 * half] : &s_tz[row][8 * half];
+          const uint16_t* src = arr ? &s_tp[gi][row][8 * half] : &s_tz[gi][row][8 * half];
           uint16_t* dst = (arr ? a.ws_p : a.ws_dz) + ((int64_t)t * ntot + p0 + j) * a.Hp + head0 + 8 * half;
           *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
         }
@@ -427,15 +442,17 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
     __syncthreads();   // every wave is done with this pass's slots
   }
 
-  // ---- dq: lane (c = head, g) holds columns 128 wave + 8 (4g + r) + e (and the RoPE phases)
+  // ---- dq: lane (c = head, g) holds columns 128 lw + 8 (4g + r) + e (and the RoPE phases);
+  // the list's first part writes dq, the others their partial sums for the next kernel to add
   if (c >= hval) return;                                // a padding head: no dq
-  float* dqh = a.dq + (int64_t)t * a.ld_dq + (int64_t)(head0 + c) * DQK;
+  float* dqh = sp == 0 ? a.dq + (int64_t)t * a.ld_dq + (int64_t)(head0 + c) * DQK
+                       : a.ws_dqp + (((int64_t)(sp - 1) * gridDim.y + t) * a.H + head0 + c) * DQK;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     f32x4_t v0, v1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) { v0[e] = oq[e][r] * a.scale; v1[e] = oq[4 + e][r] * a.scale; }
-    float* d = dqh + 128 * wave + 8 * (4 * g + r);
+    float* d = dqh + 128 * lw + 8 * (4 * g + r);
     *reinterpret_cast<f32x4_t*>(d) = v0;
     *reinterpret_cast<f32x4_t*>(d + 4) = v1;
   }
@@ -445,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd(MlaBwdArgs a) {
       const int m = 4 * g + r;
       if (m < 8) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dqh[kBwdDV + 8 * m + 2 * wave + i] = o4[i][r] * a.scale;
+        for (int i = 0; i < 2; ++i) dqh[kBwdDV + 8 * m + 2 * lw + i] = o4[i][r] * a.scale;
       }
     }
   }
@@ -527,19 +544,33 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla_bwd_dkv(MlaBwdArgs a, int
   }
 }
 
-// The owner map of the call's list entries: slot -> first naming row + 1, bit 31 when a second
-// entry (of any row, or the same row again) names it. A word is positive afterwards only if it
-// was 0 before and one entry alone names the slot: words that start dirty (a fresh workspace,
-// or one whose layout moved) only send their rows to atomics. The dKV kernel clears every
-// word it reads, so a map is clean again for the next call.
-__global__ __launch_bounds__(256) void k_sparse_mla_bwd_owner(const int32_t* slots, int ntot, int32_t* owner) {
-  const int t = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= ntot) return;
-  const int32_t s = slots[(int64_t)t * ntot + i];
-  if (s < 0) return;
-  const int32_t old = atomicCAS(owner + s, 0, t + 1);
-  if (old != 0) atomicOr(owner + s, (int32_t)0x80000000);
+// Between the backward's kernels, on one flat grid: blocks [0, nbm) mark the owner map (one
+// thread per list entry, if there is a map); the rest add the dq partial sums of list parts
+// 1..nsplit-1 into dq (one 16-byte piece per thread).
+// The owner map: slot -> first naming row + 1, bit 31 when a second entry (of any row, or the
+// same row again) names it. A word is positive afterwards only if it was 0 before and one
+// entry alone names the slot: words that start dirty (a fresh workspace, or one whose layout
+// moved) only send their rows to atomics. The dKV kernel clears every word it reads, so a map
+// is clean again for the next call.
+__global__ __launch_bounds__(256) void k_sparse_mla_bwd_mid(MlaBwdArgs a, int T, int d_qk, int nbm) {
+  if ((int)blockIdx.x < nbm) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)T * a.n_idx) return;
+    const int32_t s = a.ws_slot[e];
+    if (s < 0) return;
+    const int32_t old = atomicCAS(a.ws_owner + s, 0, (int32_t)(e / a.n_idx) + 1);
+    if (old != 0) atomicOr(a.ws_owner + s, (int32_t)0x80000000);
+    return;
+  }
+  const int64_t f = ((int64_t)blockIdx.x - nbm) * 256 + threadIdx.x;   // 16-byte piece of dq
+  const int per_row = a.H * d_qk / 4;
+  if (f >= (int64_t)T * per_row) return;
+  const int t = (int)(f / per_row);
+  const int o = (int)(f % per_row) * 4;
+  f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.dq + (int64_t)t * a.ld_dq + o);
+  for (int k = 1; k < a.nsplit; ++k)
+    v += *reinterpret_cast<const f32x4_t*>(a.ws_dqp + ((int64_t)(k - 1) * T + t) * a.H * d_qk + o);
+  *reinterpret_cast<f32x4_t*>(a.dq + (int64_t)t * a.ld_dq + o) = v;
 }
 
 // dKV by whole cache rows (32 or 64 padded heads): a workgroup of 8 waves takes one query row
@@ -749,22 +780,33 @@ static void launch_dkv(const MlaBwdArgs& a, int T, hipStream_t st) {
 
 hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid(a.Hp / 16, T);
   const bool fused = a.Hp == 16;
+  // 16-head groups: one workgroup (4 waves) when fused, else two groups per workgroup (8 waves)
+  const dim3 grid(fused ? 1 : a.Hp / 32, T, fused ? 1 : a.nsplit);
+  const dim3 block(fused ? 256 : 512);
   if (d_qk == 576) {
-    if (fused) launch_kernel(k_sparse_mla_bwd<576, true>, grid, dim3(256), st, a);
-    else launch_kernel(k_sparse_mla_bwd<576, false>, grid, dim3(256), st, a);
+    if (fused) launch_kernel(k_sparse_mla_bwd<576, true>, grid, block, st, a);
+    else launch_kernel(k_sparse_mla_bwd<576, false>, grid, block, st, a);
   } else {
-    if (fused) launch_kernel(k_sparse_mla_bwd<512, true>, grid, dim3(256), st, a);
-    else launch_kernel(k_sparse_mla_bwd<512, false>, grid, dim3(256), st, a);
+    if (fused) launch_kernel(k_sparse_mla_bwd<512, true>, grid, block, st, a);
+    else launch_kernel(k_sparse_mla_bwd<512, false>, grid, block, st, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_mla_bwd_owner(const MlaBwdArgs& a, int T, hipStream_t st) {
-  if (T <= 0 || a.n_idx <= 0 || a.Hp == 16 || !a.ws_owner) return hipSuccess;
-  launch_kernel(k_sparse_mla_bwd_owner, dim3((a.n_idx + 255) / 256, T), dim3(256), st, a.ws_slot, (int)a.n_idx,
-                a.ws_owner);
+int bwd_splits(int T, int Hp, int n_idx) {
+  if (Hp <= 16 || T <= 0) return 1;
+  const int64_t wgs = (int64_t)T * (Hp / 32);
+  int n = (int)std::min<int64_t>(4, (256 + wgs - 1) / wgs);
+  return std::max(1, std::min(n, n_idx / 256));
+}
+
+hipError_t launch_sparse_mla_bwd_mid(const MlaBwdArgs& a, int d_qk, int T, hipStream_t st) {
+  if (T <= 0 || a.Hp == 16) return hipSuccess;
+  const int nbm = a.ws_owner && a.n_idx > 0 ? (int)(((int64_t)T * a.n_idx + 255) / 256) : 0;
+  const int nbd = a.nsplit > 1 ? (int)(((int64_t)T * a.H * d_qk / 4 + 255) / 256) : 0;
+  if (nbm + nbd == 0) return hipSuccess;
+  launch_kernel(k_sparse_mla_bwd_mid, dim3(nbm + nbd), dim3(256), st, a, T, d_qk, nbm);
   return hipGetLastError();
 }
 

@@ -206,9 +206,10 @@ dsa_status dsa_sparse_mla_prefill(const void* q, int64_t ld_q, const dsa_kv_cach
  *      takes fp32 atomics in no fixed order, so its last bits vary between runs; with the
  *      owner map below, a slot that exactly one entry names takes one plain load and store.
  * dsink: fp32 [H] added to by atomics, or NULL; needs opts->sink.
- * Kernels: per (row, 16 heads) dq, and P and dZ into the workspace (bf16, 4 bytes per
- * (row, entry, head), plus the entries' slots); then per row dKV over all heads, so that an
- * entry costs one add per column whatever H is (H = 16: one kernel, the workspace unused).
+ * Kernels: per (row, 32 heads, part of the row's list) dq, and P and dZ into the workspace
+ * (bf16, 4 bytes per (row, entry, head), plus the entries' slots, and the list parts' dq sums
+ * when a row's list is split to fill the GPU); then per row dKV over all heads, so that an
+ * entry costs one add per column whatever H is (H <= 16: one kernel, the workspace unused).
  * For 17 <= H <= 64 and a workspace sized with n_slots = kv->n_slots, an owner map (one word
  * per slot, marked by a kernel between the two, cleared again by the dKV kernel) tells the dKV
  * kernel which slots one entry alone names; words found non-zero (a workspace that held other

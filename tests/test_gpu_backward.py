@@ -32,6 +32,9 @@ CASES = [
     # head counts padded inside: 8 (one 16-head group) and 40 (64 in the dKV head sum)
     ("bf16_576_h8_sink", dict(fmt="bf16", B=3, H=8, n_ctx=700, n_idx=96, pad="tail", n_pad=10, sink=True)),
     ("bf16_576_h40", dict(fmt="bf16", B=2, H=40, n_ctx=900, n_idx=300, pad="shuffled", n_pad=20)),
+    # a row's list in four parts (two rows fill too few workgroups) of 1280 entries: two
+    # resolve passes of 1024 each, and the parts' dq partial sums added afterwards
+    ("bf16_576_h64_parts_two_passes", dict(fmt="bf16", B=2, H=64, n_ctx=6000, n_idx=5000, pad="shuffled", n_pad=200)),
 ]
 
 
