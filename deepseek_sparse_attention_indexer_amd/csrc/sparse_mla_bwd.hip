@@ -705,7 +705,11 @@ __global__ __launch_bounds__(512, 1) void k_sparse_mla_bwd_dkv_rows(MlaBwdArgs a
       const uint16_t* src = (zarr ? a.ws_p : a.ws_dz) + (rowe + e) * a.Hp + 8 * zpc;
       zp = *reinterpret_cast<const u32x4_t*>(src);
     }
-    if (zok) *reinterpret_cast<u32x4_t*>(&s_zp[zarr][zrow][8 * zpc]) = zp;
+    if (zok) {   // two 8-byte stores: the padded LDS rows are 8-byte aligned, not 16
+      uint16_t* zd = &s_zp[zarr][zrow][8 * zpc];
+      reinterpret_cast<u32x2_t*>(zd)[0] = u32x2_t{zp[0], zp[1]};
+      reinterpret_cast<u32x2_t*>(zd)[1] = u32x2_t{zp[2], zp[3]};
+    }
     __syncthreads();                                    // staged; the last block's sums are read
     u32x2_t az[HK], ap[HK];
 #pragma unroll
