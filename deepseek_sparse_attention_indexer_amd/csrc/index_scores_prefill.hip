@@ -163,25 +163,28 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_index_scores_prefill(ScoreArg
     constexpr int NPW = NINS / kPfRows;         // load instructions per wave and tile
     static_assert(NINS % kPfRows == 0, "whole instructions per wave");
     int slot_nx[NPW];
+    // per load instruction k of this wave: the tile row its lane fetches and the swizzled
+    // byte offset inside that row (the same for every tile); the wave index taken as uniform
+    // so that each load's LDS destination is scalar arithmetic
+    const int w_u = __builtin_amdgcn_readfirstlane(wave);
+    int lrow[NPW], lswz[NPW];
+#pragma unroll
+    for (int k = 0; k < NPW; ++k) {
+      const int q = (w_u + k * kPfRows) * 64 + lane;
+      lrow[k] = q / CPR;
+      lswz[k] = ((q % CPR) ^ (lrow[k] % CPR)) * 16;
+    }
     auto read_slots = [&](int j) {
 #pragma unroll
-      for (int k = 0; k < NPW; ++k) {
-        const int r = ((wave + k * kPfRows) * 64 + lane) / CPR;
-        slot_nx[k] = s_slot[min(c0 + j * kPfTile + r, kend - 1) - c0];
-      }
+      for (int k = 0; k < NPW; ++k) slot_nx[k] = s_slot[min(j * kPfTile + lrow[k], kend - 1 - c0)];
     };
     auto dma_tile = [&](int buf) {
       auto* lbase = reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(
           reinterpret_cast<uintptr_t>(&s_k[buf][0]) & 0xffffffffu);
 #pragma unroll
       for (int k = 0; k < NPW; ++k) {
-        const int ins = wave + k * kPfRows;
-        const int q = ins * 64 + lane;
-        const int r = q / CPR;
-        const int p = q - r * CPR;
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)slot_nx[k] * RB +
-                             ((p ^ (r % CPR)) * 16);
-        __builtin_amdgcn_global_load_lds(src, lbase + ins * 1024, 16, 0, 0);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.keys) + (uint64_t)(uint32_t)slot_nx[k] * RB + lswz[k];
+        __builtin_amdgcn_global_load_lds(src, lbase + (w_u + k * kPfRows) * 1024, 16, 0, 0);
       }
     };
     read_slots(0);
