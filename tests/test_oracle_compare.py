@@ -1,6 +1,6 @@
 """Pins of the parity rules themselves (oracle/compare.py), on the CPU.
 
-Every GPU parity verdict goes through scores_ok, topk_ok and attention_ok, so each rule is fed
+Every GPU parity decision goes through scores_ok, topk_ok and attention_ok, so each rule is fed
 planted wrong "GPU" outputs that it must reject, beside near-misses on the right side of each
 bound that it must accept. The bounds are the ones the layer's statement of correctness fixes:
 scores within 1e-3 relative (with a row floor at scores near zero), top-k sets equal except for
