@@ -51,7 +51,11 @@ constexpr int kDV = 512;    // value width
 
 template <int FMT, int DQK>
 struct RowGeom {
-  static constexpr int kElems = DQK + 8;                       // padded bf16 row in LDS
+  // padded bf16 row in LDS: 16 elements (32 bytes) of padding put the rows of the score
+  // product's reads (16 rows at one column, 16 bytes each) in distinct banks. With 8 the reads
+  // cost 4 bank-conflict cycles per instruction (measured on gfx950 with the LDS conflict
+  // counter), and the 512-wide rows' transposing value reads 6 instead of 2.
+  static constexpr int kElems = DQK + 16;
   // 16-byte work units per row and what one unit produces
   static constexpr int kUnits = FMT == kFmtBf16 ? DQK / 8 : (kUniformFmt<FMT> ? DQK / 16 : 36);
 };
@@ -323,8 +327,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   auto gather = [&](int buf) {   // the block in ring slot buf (addresses in s_ra[buf])
     if constexpr (FMT == kFmtBf16) {
       // lane l of instruction ins fills 16-byte slot 64 * ins + l of the padded block; the pad
-      // slot of each row re-reads the row's first 16 bytes
-      constexpr int RW = DQK / 8 + 1;
+      // slots of each row re-read the row's first 32 bytes
+      constexpr int RW = RE / 8;
       constexpr int SLOTS = kNB * RW;
       constexpr int NINS = (SLOTS + 63) / 64;
       constexpr int GI = NW;                           // issuing waves: all
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
             const int j = min((gw + (k0 + k) * GI) * 64 + lane, SLOTS - 1);
             const int r = j / RW;
             int cc = j - r * RW;
-            cc = cc == RW - 1 ? 0 : cc;
+            cc = cc >= DQK / 8 ? cc - DQK / 8 : cc;
             src[k] = s_ra[buf][0][r] + 16 * cc;
           }
 #pragma unroll
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   // wave at issue): instruction k of this wave's share (its source, then its issue). Issued
   // as lds_dma16, since the builtin's loads would have to land before the value product.
   constexpr bool kStagger = FMT == kFmtBf16 && HT == 4 && WD == 2;
-  constexpr int kGRW = DQK / 8 + 1;                       // 16-byte slots per padded row
+  constexpr int kGRW = RE / 8;                            // 16-byte slots per padded row
   constexpr int kGSlots = kNB * kGRW;
   constexpr int kGIns = (kGSlots + 63) / 64;               // instructions per block
   constexpr int kGPer = (kGIns + NW - 1) / NW;             // of one wave (at most)
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     const int j = min((wave + k * NW) * 64 + lane, kGSlots - 1);
     const int r = j / kGRW;
     int cc = j - r * kGRW;
-    cc = cc == kGRW - 1 ? 0 : cc;
+    cc = cc >= DQK / 8 ? cc - DQK / 8 : cc;
     return s_ra[buf][0][r] + 16 * cc;
   };
   auto gissue = [&](int buf, int k, const uint8_t* sp) {
@@ -543,7 +547,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   // waves; every one of them has at least one active lane, so each counts once on vmcnt)
   constexpr int NID = kNB * RDB / 1024;                      // raw data instructions
   constexpr int NIS = (kNB * (RSB / 4) + 63) / 64;           // raw scale instructions
-  constexpr int NINS = (kNB * (DQK / 8 + 1) + 63) / 64;      // bf16 instructions
+  constexpr int NINS = (kNB * (RE / 8) + 63) / 64;           // bf16 instructions
   constexpr int PB_MAX = kRaw ? (NID + NW - 1) / NW + (NIS + NW - 1) / NW : (NINS + NW - 1) / NW;
   static_assert((NBUF - 2) * PB_MAX < 64, "vmcnt range");
   const int w_u = __builtin_amdgcn_readfirstlane(wave);

@@ -81,7 +81,9 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
   constexpr int GRP = FUSED ? 1 : 2;
   constexpr int NW = 4 * GRP;
   constexpr int NT = 256 * GRP;
-  constexpr int RE = DQK + 8;                 // padded bf16 row in LDS
+  // padded bf16 row in LDS: 16 elements of padding keep the score and dP products' reads
+  // (16 rows at one column, 16 bytes each) free of bank conflicts (8 cost 4 cycles each)
+  constexpr int RE = DQK + 16;
   constexpr int KS = DQK / 32;                // k-steps of the score product
   constexpr int KQ = KS / 2;                  // per wave (split over the two halves)
   constexpr bool kRope = DQK > kBwdDV;        // columns 512..575 (4 x 16) beyond the value
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
 
   // ---- prologue: q and dout of the 16 heads staged in the row buffer, the register operands
   // built from them; D = dout . out and the lse in base 2 per head
-  constexpr int DOS = kBwdDV + 8;
+  constexpr int DOS = kBwdDV + 16;           // padded like the rows
   static_assert(GRP * (16 * RE + 16 * DOS) <= 2 * kBwdNB * RE, "staging");
   uint16_t* const s_q = &s_rows[0][0][0] + gi * (16 * RE + 16 * DOS);   // [16][RE]
   uint16_t* const s_do = s_q + 16 * RE;                                  // [16][DOS]
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
     };
     // that block's loads into ring buffer buf (addresses in s_ra)
     auto gather = [&](int buf) {
-      constexpr int RW = DQK / 8 + 1;
+      constexpr int RW = RE / 8;                   // 16-byte slots per padded row
       constexpr int SLOTS = kBwdNB * RW;
       constexpr int NINS = (SLOTS + 63) / 64;
       constexpr int PER = (NINS + NW - 1) / NW;
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
         const int j = min((wave + k * NW) * 64 + lane, SLOTS - 1);
         const int r = j / RW;
         int cc = j - r * RW;
-        cc = cc == RW - 1 ? 0 : cc;
+        cc = cc >= DQK / 8 ? cc - DQK / 8 : cc;   // the pad slots re-read the row's start
         src[k] = s_ra[r] + 16 * cc;
       }
 #pragma unroll
