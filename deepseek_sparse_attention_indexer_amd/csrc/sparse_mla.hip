@@ -49,13 +49,15 @@ constexpr int kNB = 32;     // rows per block
 constexpr int kResolve = 1024;   // list entries resolved to slots per pass (multiple of kNB)
 constexpr int kDV = 512;    // value width
 
+// The reads of a block's rows: the score product's, 16 rows at one 16-byte column per 16
+// lanes; the value product's, 64 bytes of each of 8 consecutive rows (transposing, 64-head
+// path) or 256 bytes of rows 4 apart (16-head path). At this stride with row_swz (see there)
+// none of them has a bank conflict. (Padding by 8 elements cost 4 conflict cycles per score
+// read, by 16 none there but 2 per transposing read.)
 template <int FMT, int DQK>
 struct RowGeom {
-  // padded bf16 row in LDS: 16 elements (32 bytes) of padding put the rows of the score
-  // product's reads (16 rows at one column, 16 bytes each) in distinct banks. With 8 the reads
-  // cost 4 bank-conflict cycles per instruction (measured on gfx950 with the LDS conflict
-  // counter), and the 512-wide rows' transposing value reads 6 instead of 2.
-  static constexpr int kElems = DQK + 16;
+  static constexpr int kElems = DQK + 32;                      // padded bf16 row in LDS
+  static_assert((kElems * 2) % 128 == 64, "row stride");
   // 16-byte work units per row and what one unit produces
   static constexpr int kUnits = FMT == kFmtBf16 ? DQK / 8 : (kUniformFmt<FMT> ? DQK / 16 : 36);
 };
@@ -102,11 +104,12 @@ __device__ __forceinline__ RowOff row_offsets(const KvDev& kv, int64_t slot) {
   return o;
 }
 
+// unit u of a row into its LDS row lrow, whose chunks are swizzled by sw (row_swz of the row)
 template <int FMT, int DQK>
-__device__ __forceinline__ void store_unit(const RawUnit& r, int u, uint16_t* lrow) {
+__device__ __forceinline__ void store_unit(const RawUnit& r, int u, uint16_t* lrow, int sw) {
   const bool rope = FMT == kFmtDsMla && u >= 28;
   if (rope) {   // RoPE columns of fp8_ds_mla rows are bf16 already
-    *reinterpret_cast<u32x4_t*>(lrow + 448 + 8 * (u - 28)) = r.v;
+    *reinterpret_cast<u32x4_t*>(lrow + 8 * ((56 + u - 28) ^ sw)) = r.v;
     return;
   }
   if constexpr (FMT == kFmtDsMla) {   // UE8M0 scale, a power of two: one scaled conversion per pair
@@ -118,8 +121,8 @@ __device__ __forceinline__ void store_unit(const RawUnit& r, int u, uint16_t* lr
       hi[2 * k] = fp8x2_to_bf16x2_pow2<false>(r.v[2 + k], r.sc);
       hi[2 * k + 1] = fp8x2_to_bf16x2_pow2<true>(r.v[2 + k], r.sc);
     }
-    *reinterpret_cast<u32x4_t*>(lrow + 16 * u) = lo;
-    *reinterpret_cast<u32x4_t*>(lrow + 16 * u + 8) = hi;
+    *reinterpret_cast<u32x4_t*>(lrow + 8 * ((2 * u) ^ sw)) = lo;
+    *reinterpret_cast<u32x4_t*>(lrow + 8 * ((2 * u) ^ sw) + 8) = hi;
     return;
   }
   float f[16];
@@ -139,8 +142,8 @@ __device__ __forceinline__ void store_unit(const RawUnit& r, int u, uint16_t* lr
       hi[i] = pack_bf16_exact(f[8 + 2 * i] * r.sc, f[8 + 2 * i + 1] * r.sc);
     }
   }
-  *reinterpret_cast<u32x4_t*>(lrow + 16 * u) = lo;
-  *reinterpret_cast<u32x4_t*>(lrow + 16 * u + 8) = hi;
+  *reinterpret_cast<u32x4_t*>(lrow + 8 * ((2 * u) ^ sw)) = lo;
+  *reinterpret_cast<u32x4_t*>(lrow + 8 * ((2 * u) ^ sw) + 8) = hi;
 }
 
 // Final normalisation of one (row, head) from its base-2 running max m and sum l (l = 0: no
@@ -326,8 +329,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   // wait)
   auto gather = [&](int buf) {   // the block in ring slot buf (addresses in s_ra[buf])
     if constexpr (FMT == kFmtBf16) {
-      // lane l of instruction ins fills 16-byte slot 64 * ins + l of the padded block; the pad
-      // slots of each row re-read the row's first 32 bytes
+      // lane l of instruction ins fills 16-byte slot 64 * ins + l of the padded block: chunk
+      // cc ^ row_swz(r) of row r; the pad slots of each row re-read the row's first 64 bytes
       constexpr int RW = RE / 8;
       constexpr int SLOTS = kNB * RW;
       constexpr int NINS = (SLOTS + 63) / 64;
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
             const int j = min((gw + (k0 + k) * GI) * 64 + lane, SLOTS - 1);
             const int r = j / RW;
             int cc = j - r * RW;
-            cc = cc >= DQK / 8 ? cc - DQK / 8 : cc;
+            cc = cc >= DQK / 8 ? cc - DQK / 8 : cc ^ row_swz(r);
             src[k] = s_ra[buf][0][r] + 16 * cc;
           }
 #pragma unroll
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     const int j = min((wave + k * NW) * 64 + lane, kGSlots - 1);
     const int r = j / kGRW;
     int cc = j - r * kGRW;
-    cc = cc >= DQK / 8 ? cc - DQK / 8 : cc;
+    cc = cc >= DQK / 8 ? cc - DQK / 8 : cc ^ row_swz(r);
     return s_ra[buf][0][r] + 16 * cc;
   };
   auto gissue = [&](int buf, int k, const uint8_t* sp) {
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
             ru[q].v = u32x4_t{0u, 0u, 0u, 0u};
             ru[q].sc = 0.f;
           }
-          store_unit<FMT, DQK>(ru[q], u, &s_rows[0][r][0]);
+          store_unit<FMT, DQK>(ru[q], u, &s_rows[0][r][0], row_swz(r));
         }
       }
     }
@@ -488,7 +491,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
 #pragma unroll
     for (int i = 0; i < QIT; ++i) {
       const int o = (threadIdx.x + i * NT) * 16;
-      if (o < QBYTES) *reinterpret_cast<u32x4_t*>(qdst + (o / (DQK * 2)) * (RE * 2) + o % (DQK * 2)) = qreg[i];
+      const int h = o / (DQK * 2);   // staged like the rows: chunks swizzled by the head's row
+      if (o < QBYTES) *reinterpret_cast<u32x4_t*>(qdst + h * (RE * 2) + 16 * (((o % (DQK * 2)) / 16) ^ row_swz(h))) = qreg[i];
     }
   }
   __syncthreads();
@@ -520,11 +524,11 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   __shared__ __align__(8) uint8_t s_grow8[8];         // each wave's grow flag, in one word
   u32x4_t qb[KQ];
   if constexpr (kW32) {
-    const uint16_t* qp = &s_rows[0][0][0] + (32 * hh + 16 * hx + c) * RE + 8 * g;
+    const uint16_t* qp = &s_rows[0][0][0] + (32 * hh + 16 * hx + c) * RE + 8 * (g ^ row_swz(c));
 #pragma unroll
     for (int kb = 0; kb < KQ; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(qp + 32 * kb);
   } else {
-    const uint16_t* qp = &s_rows[0][0][0] + (ht * 16 + c) * RE + 8 * g;
+    const uint16_t* qp = &s_rows[0][0][0] + (ht * 16 + c) * RE + 8 * (g ^ row_swz(c));
 #pragma unroll
     for (int kb = 0; kb < KQ; ++kb) qb[kb] = *reinterpret_cast<const u32x4_t*>(qp + 32 * (kq0 + kb));
   }
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       {
         // operands read three k-steps ahead of their MFMA, so that no MFMA waits out a whole
         // LDS round trip (left to itself the compiler keeps one buffer and waits every step)
-        const uint16_t* rp = &s_rows[cur][16 * rx + c][8 * g];
+        const uint16_t* rp = &s_rows[cur][16 * rx + c][8 * (g ^ row_swz(c))];
         constexpr int DEPTH = 3;
         u32x4_t av[DEPTH];
 #pragma unroll
@@ -723,6 +727,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         const int tg = lane >> 4, tj = (lane >> 2) & 3, ta = lane & 3;
         const int tr_row = 4 * (tg >> 1) + tj;
         const int tr_col = VC * vh + 16 * (tg & 1) + 4 * ta;
+        const int tr_hi = (tg & 1) ? -16 : 16;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const u32x2_t pa = ks == 0 ? pa0 : *reinterpret_cast<const u32x2_t*>(&s_pt[hh][l32][16 + 4 * hl]);
@@ -730,9 +735,10 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
           const u32x4_t pb = u32x4_t{pa[0], pa[1], pc[0], pc[1]};
 #pragma unroll
           for (int e = 0; e < CPL; ++e) {
+            // rows tr_row < 8 unswizzled, rows 8 + tr_row with chunk bit 1 flipped
             const uint16_t* rp = &s_rows[cur][16 * ks + tr_row][tr_col + 32 * e];
             const u32x2_t lo = ds_read_tr16(rp);
-            const u32x2_t hi = ds_read_tr16(rp + 8 * RE);
+            const u32x2_t hi = ds_read_tr16(rp + 8 * RE + tr_hi);
             o32[e] = mfma_bf16_32x32x16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb, o32[e]);
           }
         }
@@ -741,7 +747,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
     // ---- S^T = K Q^T
       f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
       if constexpr (kSplitK) {
-        const uint16_t* rp = &s_rows[cur][16 * (wave >> 1) + c][8 * g + 32 * kq0];
+        const uint16_t* rp = &s_rows[cur][16 * (wave >> 1) + c][8 * (g ^ row_swz(c)) + 32 * kq0];
         f32x4_t sp = s0;
   #pragma unroll
         for (int kb = 0; kb < KQ; ++kb) {
@@ -755,8 +761,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         s0 = s_sp[0][lane] + s_sp[1][lane];
         s1 = s_sp[2][lane] + s_sp[3][lane];
       } else {
-        const uint16_t* r0 = &s_rows[cur][c][8 * g];
-        const uint16_t* r1 = &s_rows[cur][16 + c][8 * g];
+        const uint16_t* r0 = &s_rows[cur][c][8 * (g ^ row_swz(c))];
+        const uint16_t* r1 = &s_rows[cur][16 + c][8 * (g ^ row_swz(c))];
   #pragma unroll
         for (int kb = 0; kb < KS; ++kb) {
           s0 = mfma_bf16_16x16x32(*reinterpret_cast<const u32x4_t*>(r0 + 32 * kb), qb[kb], s0);
@@ -821,8 +827,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         } else {
   #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * gd + 8 * c]);
-            vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * gd + 8 * c]);
+            vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * gd + 8 * (c ^ row_swz(4 * g))]);
+            vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * gd + 8 * (c ^ row_swz(4 * g))]);
           }
         }
   #pragma unroll

@@ -81,9 +81,11 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
   constexpr int GRP = FUSED ? 1 : 2;
   constexpr int NW = 4 * GRP;
   constexpr int NT = 256 * GRP;
-  // padded bf16 row in LDS: 16 elements of padding keep the score and dP products' reads
-  // (16 rows at one column, 16 bytes each) free of bank conflicts (8 cost 4 cycles each)
-  constexpr int RE = DQK + 16;
+  // padded bf16 row in LDS, chunks swizzled by row_swz: the score and dP products' reads (16
+  // rows at one 16-byte column) and the dq product's (256 bytes of rows 4 apart) are free of
+  // bank conflicts (with 8 elements of padding and no swizzle they cost 4 cycles each)
+  constexpr int RE = DQK + 32;
+  static_assert((RE * 2) % 128 == 64, "row stride");
   constexpr int KS = DQK / 32;                // k-steps of the score product
   constexpr int KQ = KS / 2;                  // per wave (split over the two halves)
   constexpr bool kRope = DQK > kBwdDV;        // columns 512..575 (4 x 16) beyond the value
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
         const int j = min((wave + k * NW) * 64 + lane, SLOTS - 1);
         const int r = j / RW;
         int cc = j - r * RW;
-        cc = cc >= DQK / 8 ? cc - DQK / 8 : cc;   // the pad slots re-read the row's start
+        cc = cc >= DQK / 8 ? cc - DQK / 8 : cc ^ row_swz(r);   // pad slots: the row's start
         src[k] = s_ra[r] + 16 * cc;
       }
 #pragma unroll
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
       const u32x4_t sl0 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm]);
       const u32x4_t sl1 = *reinterpret_cast<const u32x4_t*>(&s_slot[jm + 16]);
       {
-        const uint16_t* rp = &s_rows[cur][16 * (lw >> 1) + c][8 * g];
+        const uint16_t* rp = &s_rows[cur][16 * (lw >> 1) + c][8 * (g ^ row_swz(c))];
         f32x4_t sp = f32x4_t{0.f, 0.f, 0.f, 0.f}, dp = sp;
 #pragma unroll
         for (int kb = 0; kb < KQ; ++kb)
@@ -359,8 +361,8 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
         u32x4_t vr[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * lw + 8 * c]);
-          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * lw + 8 * c]);
+          vr[j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][4 * g + j][128 * lw + 8 * (c ^ row_swz(4 * g))]);
+          vr[4 + j] = *reinterpret_cast<const u32x4_t*>(&s_rows[cur][16 + 4 * g + j][128 * lw + 8 * (c ^ row_swz(4 * g))]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -377,8 +379,8 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
         uint32_t vw[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          vw[j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][4 * g + j][kBwdDV + 8 * (c & 7) + 2 * lw]);
-          vw[4 + j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][16 + 4 * g + j][kBwdDV + 8 * (c & 7) + 2 * lw]);
+          vw[j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][4 * g + j][kBwdDV + 8 * ((c & 7) ^ row_swz(4 * g)) + 2 * lw]);
+          vw[4 + j] = *reinterpret_cast<const uint32_t*>(&s_rows[cur][16 + 4 * g + j][kBwdDV + 8 * ((c & 7) ^ row_swz(4 * g)) + 2 * lw]);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
