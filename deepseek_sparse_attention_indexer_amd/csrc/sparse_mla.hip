@@ -517,7 +517,8 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   const int l32 = lane & 31, hl = lane >> 5;
   const int rx = vh & 1, hx = vh >> 1;
   auto wv = [&](int r, int h) { return hh + 2 * (r + 2 * h); };   // the half's wave of tile (r, h)
-  constexpr int PTS = 32 + 4;                         // padded row count of a head's weights
+  constexpr int PTS = 32 + 8;                         // padded row count of a head's weights (80-byte
+                                                      // rows: the 8-byte reads of 32 heads conflict-free)
   __shared__ __align__(8) uint16_t s_pt[kW32 ? 2 : 1][32][PTS];   // P^T per half: [head][row], bf16
   __shared__ float s_mx[kW32 ? NW : 1][16];           // each wave's block max per score head
   __shared__ float s_lw[kW32 ? NW : 1][16];           // each wave's weight sum per score head (end)
