@@ -635,10 +635,10 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
       // the whole contraction (A = rows from LDS, B = q in registers)
       f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
-        // operands read three k-steps ahead of their MFMA, so that no MFMA waits out a whole
+        // operands read four k-steps ahead of their MFMA, so that no MFMA waits out a whole
         // LDS round trip (left to itself the compiler keeps one buffer and waits every step)
         const uint16_t* rp = &s_rows[cur][16 * rx + c][8 * (g ^ row_swz(c))];
-        constexpr int DEPTH = 3;
+        constexpr int DEPTH = 4;
         u32x4_t av[DEPTH];
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) av[d] = *reinterpret_cast<const u32x4_t*>(rp + 32 * d);
