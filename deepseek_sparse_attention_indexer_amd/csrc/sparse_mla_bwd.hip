@@ -350,6 +350,26 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
         s_tp[gi][4 * g + r][c] = (uint16_t)bf16_rne_bits(p[r]);
         s_tp[gi][16 + 4 * g + r][c] = (uint16_t)bf16_rne_bits(p[4 + r]);
       }
+      if constexpr (!FUSED) {
+        // every wave's dZ and P in LDS; they go out before the dq product, so that the stores
+        // have its time to complete before the next block's wait
+        lds_barrier();
+        // ---- scale dZ, P (bf16, [row][head] with the row's heads contiguous) and the slots to
+        // the workspace for the dKV kernel: 16 bytes (8 heads) per thread
+        if (tg < 2 * 2 * kBwdNB) {
+          const int arr = tg >> 6;                       // 0: dZ, 1: P
+          const int row = (tg >> 1) & (kBwdNB - 1);
+          const int half = tg & 1;
+          const int j = jb + row;
+          if (j < pass_n) {
+            const uint16_t* src = arr ? &s_tp[gi][row][8 * half] : &s_tz[gi][row][8 * half];
+            uint16_t* dst = (arr ? a.ws_p : a.ws_dz) + ((int64_t)t * ntot + p0 + j) * a.Hp + head0 + 8 * half;
+            *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+          }
+        }
+        if (hg == 0 && threadIdx.x < kBwdNB && jb + (int)threadIdx.x < pass_n)
+          a.ws_slot[(int64_t)t * ntot + p0 + jb + threadIdx.x] = s_slot[jb + threadIdx.x];
+      }
       // ---- dq^T += K^T dZ^T: dZ^T from the accumulator layout (k-slot 8g + i of the B
       // operand is row 4g + i, then 16 + 4g + i - 4), K^T by 8x8 transposes of LDS rows
       u32x4_t zb;
@@ -391,8 +411,8 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
           o4[i] = mfma_bf16_16x16x32(av, zb, o4[i]);
         }
       }
-      lds_barrier();
       if constexpr (FUSED) {
+        lds_barrier();
         // ---- dKV = (scale dZ)^T Q + P^T dO over the 16 heads (m = the 32 rows, n = 32 columns):
         // accumulator r of lane l is row 8 (r / 4) + 4 hh + r % 4 and column tile * 32 + l32
         u32x2_t az[2], ap[2];
@@ -425,22 +445,6 @@ __global__ __launch_bounds__(FUSED ? 256 : 512, 1) void k_sparse_mla_bwd(MlaBwdA
               if (rs[r] >= 0) unsafeAtomicAdd(a.dkv + (int64_t)rs[r] * DQK + col, acc[r]);
           }
         }
-      } else {
-      // ---- scale dZ, P (bf16, [row][head] with the row's heads contiguous) and the slots to
-      // the workspace for the dKV kernel: 16 bytes (8 heads) per thread
-      if (tg < 2 * 2 * kBwdNB) {
-        const int arr = tg >> 6;                       // 0: dZ, 1: P
-        const int row = (tg >> 1) & (kBwdNB - 1);
-        const int half = tg & 1;
-        const int j = jb + row;
-        if (j < pass_n) {
-          const uint16_t* src = arr ? &s_tp[gi][row][8 * half] : &s_tz[gi][row][8 * half];
-          uint16_t* dst = (arr ? a.ws_p : a.ws_dz) + ((int64_t)t * ntot + p0 + j) * a.Hp + head0 + 8 * half;
-          *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
-        }
-      }
-      if (hg == 0 && threadIdx.x < kBwdNB && jb + (int)threadIdx.x < pass_n)
-        a.ws_slot[(int64_t)t * ntot + p0 + jb + threadIdx.x] = s_slot[jb + threadIdx.x];
       }
     }
     __syncthreads();   // every wave is done with this pass's slots
