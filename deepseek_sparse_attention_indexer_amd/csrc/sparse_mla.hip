@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
   };
 
   // 64 heads, bf16 rows: every wave issues its share of a block's loads at its own point of
-  // the score product (wave w after k-step 2 w), so that the waves find the CU's memory path
+  // the score product (wave w after k-step 2 w + 1), so that the waves find the CU's memory path
   // free in turn instead of all queueing on it at once (a load that finds it busy holds its
   // wave at issue): instruction k of this wave's share (its source, then its issue). Issued
   // as lds_dma16, since the builtin's loads would have to land before the value product.
@@ -644,7 +644,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
         for (int d = 0; d < DEPTH; ++d) av[d] = *reinterpret_cast<const u32x4_t*>(rp + 32 * d);
         const bool gnext = kStagger && it + NBUF - 1 < nb;
         const int gbuf = (it + NBUF - 1) % NBUF;
-        static_assert(!kStagger || 2 * (NW - 1) < KQ, "every wave's turn inside the product");
+        static_assert(!kStagger || 2 * (NW - 1) + 1 < KQ, "every wave's turn inside the product");
 #pragma unroll
         for (int kb = 0; kb < KQ; ++kb) {
           sacc = mfma_bf16_16x16x32(av[kb % DEPTH], qb[kb], sacc);
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(64 * HT * WD, (HT == 1 || (HT == 4 && WD == 2)) ? 2
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA,
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then the next read
           if constexpr (kStagger) {
-            if (gnext && kb == 2 * w_u) {       // this wave's turn: its share of the next block
+            if (gnext && kb == 2 * w_u + 1) {   // this wave's turn: its share of the next block
               const uint8_t* gs[kGPer];
 #pragma unroll
               for (int k = 0; k < kGPer; ++k) gs[k] = gsrc(gbuf, k);
